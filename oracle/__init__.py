@@ -1,0 +1,318 @@
+"""CPU oracle for 3D Deformable Slide Attention (3D-DSA) -- test infrastructure.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package. It shares no code with the GPU library.
+
+The attention itself lives in `dsa3d_oracle.c` (plain fp64 C, one query at a
+time; see that file's header for the operator's steps and the passages they
+follow). This module loads it with ctypes, splits whole tensors into one call
+per (batch item, head) -- heads are independent given the offsets -- and runs
+those calls on a thread pool. The offset projection is a textbook fp64 GEMM
+done with numpy: the offset network ends in a pointwise convolution / linear
+layer [MegaSlide-DiT, §5.3 Implementation considerations; Dutch and French
+summaries, "3D Deformable Slide Attention", Implementation], read here as a
+Linear layer of the token's full query row.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+import threading
+from concurrent.futures import ThreadPoolExecutor
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_DIR, "dsa3d_oracle.c")
+_LIB_PATH = os.path.join(_DIR, "libdsa3d_oracle.so")
+_lib = None
+_lock = threading.Lock()
+
+OUTSIDE = np.iinfo(np.int32).min  # base coordinate of a sample that is entirely outside
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("W", ctypes.c_int32),
+                ("d", ctypes.c_int32),
+                ("kt", ctypes.c_int32), ("kh", ctypes.c_int32), ("kw", ctypes.c_int32),
+                ("dil_t", ctypes.c_int32), ("dil_h", ctypes.c_int32), ("dil_w", ctypes.c_int32),
+                ("scale", ctypes.c_double),
+                ("bt0", ctypes.c_int32), ("bh0", ctypes.c_int32), ("bw0", ctypes.c_int32),
+                ("BT", ctypes.c_int32), ("BH", ctypes.c_int32), ("BW", ctypes.c_int32)]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast-math, no FP contraction)."""
+    if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+           "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded oracle library (built first if it is not there)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                build()
+            L = ctypes.CDLL(_LIB_PATH)
+            P = ctypes.POINTER
+            L.orc_geometry.argtypes = [P(_Problem), ctypes.c_long, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+            L.orc_forward.argtypes = [P(_Problem), ctypes.c_long] + [ctypes.c_void_p] * 8
+            L.orc_backward.argtypes = [P(_Problem), ctypes.c_long] + [ctypes.c_void_p] * 10
+            for f in (L.orc_geometry, L.orc_forward, L.orc_backward):
+                f.restype = ctypes.c_int
+            _lib = L
+    return _lib
+
+
+def _use_library(path: Optional[str]):
+    """Test hook: load the oracle from another build (e.g. a planted mistake)
+    and return the previously loaded library handle; None restores the default."""
+    global _lib
+    prev = _lib
+    with _lock:
+        _lib = None
+    if path is not None:
+        global _LIB_PATH
+        saved = _LIB_PATH
+        _LIB_PATH = path
+        try:
+            lib()
+        finally:
+            _LIB_PATH = saved
+    return prev
+
+
+def _restore_library(handle):
+    global _lib
+    with _lock:
+        _lib = handle
+
+
+def build_variant(src_text: str, out_path: str) -> str:
+    """Compile C source text with the oracle's flags into out_path (tests only)."""
+    src = out_path + ".c"
+    with open(src, "w") as f:
+        f.write(src_text)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+                    "-w", "-o", out_path, src, "-lm"], check=True)
+    return out_path
+
+
+def source_text() -> str:
+    with open(_SRC) as f:
+        return f.read()
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def default_scale(d: int) -> float:
+    """Logit scale 1/sqrt(d)."""
+    return 1.0 / math.sqrt(d)
+
+
+def _problem(grid, d, window, dilation, scale, box_origin, box_shape) -> _Problem:
+    T, H, W = grid
+    kt, kh, kw = window
+    if kt % 2 == 0 or kh % 2 == 0 or kw % 2 == 0:
+        raise ValueError("window sizes must be odd")
+    return _Problem(T, H, W, d, kt, kh, kw, dilation[0], dilation[1], dilation[2], float(scale),
+                    box_origin[0], box_origin[1], box_origin[2], box_shape[0], box_shape[1], box_shape[2])
+
+
+def _check(rc: int, what: str):
+    if rc == -1:
+        raise RuntimeError(f"oracle {what}: a sampled corner lies in the grid but outside the K/V box")
+    if rc != 0:
+        raise RuntimeError(f"oracle {what}: error {rc}")
+
+
+# ----------------------------------------------------------------------------
+# One (batch item, head): explicit query list and K/V box.
+# ----------------------------------------------------------------------------
+
+def forward_queries(grid, window, dilation, scale, qpos, q, off, box_origin, K, V,
+                    want_attn=False):
+    """Forward of listed queries of one head.
+
+    grid (T,H,W); qpos [n,3] int absolute coordinates; q [n,d]; off [n,P,3]
+    (rounded to single precision first); K, V [BT,BH,BW,d] the box at
+    box_origin. Returns o [n,d], lse [n] (and attn [n,P]).
+    """
+    qpos = np.ascontiguousarray(qpos, dtype=np.int32)
+    q, K, V, off = _f64(q), _f64(K), _f64(V), _f32(off)
+    n, d = q.shape
+    P = window[0] * window[1] * window[2]
+    pr = _problem(grid, d, window, dilation, scale, box_origin, K.shape[:3])
+    o = np.zeros((n, d)); lse = np.zeros(n)
+    attn = np.zeros((n, P)) if want_attn else None
+    rc = lib().orc_forward(ctypes.byref(pr), n, _ptr(qpos), _ptr(q), _ptr(off), _ptr(K), _ptr(V),
+                           _ptr(o), _ptr(lse), _ptr(attn))
+    _check(rc, "forward")
+    return (o, lse, attn) if want_attn else (o, lse)
+
+
+def backward_queries(grid, window, dilation, scale, qpos, q, off, box_origin, K, V, dout,
+                     dK=None, dV=None):
+    """Backward of listed queries of one head.
+
+    Returns dq [n,d], doff [n,P,3], and dK, dV [BT,BH,BW,d] holding the
+    contributions of these queries only (accumulated into dK/dV if given).
+    """
+    qpos = np.ascontiguousarray(qpos, dtype=np.int32)
+    q, K, V, off, dout = _f64(q), _f64(K), _f64(V), _f32(off), _f64(dout)
+    n, d = q.shape
+    P = window[0] * window[1] * window[2]
+    pr = _problem(grid, d, window, dilation, scale, box_origin, K.shape[:3])
+    dq = np.zeros((n, d)); doff = np.zeros((n, P, 3))
+    dK = np.zeros(K.shape) if dK is None else dK
+    dV = np.zeros(V.shape) if dV is None else dV
+    assert dK.dtype == np.float64 and dK.flags.c_contiguous and dV.flags.c_contiguous
+    rc = lib().orc_backward(ctypes.byref(pr), n, _ptr(qpos), _ptr(q), _ptr(off), _ptr(K), _ptr(V),
+                            _ptr(dout), _ptr(dq), _ptr(doff), _ptr(dK), _ptr(dV))
+    _check(rc, "backward")
+    return dq, doff, dK, dV
+
+
+def geometry_queries(grid, window, dilation, qpos, off):
+    """Base corner [n,P,3] int32 and fraction [n,P,3] float32 of listed queries."""
+    qpos = np.ascontiguousarray(qpos, dtype=np.int32)
+    off = _f32(off)
+    n = qpos.shape[0]
+    P = window[0] * window[1] * window[2]
+    pr = _problem(grid, 1, window, dilation, 1.0, (0, 0, 0), (0, 0, 0))
+    base = np.zeros((n, P, 3), dtype=np.int32); frac = np.zeros((n, P, 3), dtype=np.float32)
+    rc = lib().orc_geometry(ctypes.byref(pr), n, _ptr(qpos), _ptr(off), _ptr(base), _ptr(frac))
+    _check(rc, "geometry")
+    return base, frac
+
+
+# ----------------------------------------------------------------------------
+# Whole tensors in the [B,T,H,W,heads,d] layout.
+# ----------------------------------------------------------------------------
+
+def grid_positions(T: int, H: int, W: int) -> np.ndarray:
+    """All token coordinates of a T x H x W grid in row-major order, [N,3]."""
+    t, h, w = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    return np.stack([t.ravel(), h.ravel(), w.ravel()], axis=1).astype(np.int32)
+
+
+def _pool_map(fn, items, threads):
+    threads = threads or min(len(items), os.cpu_count() or 1)
+    if threads <= 1 or len(items) <= 1:
+        return [fn(x) for x in items]
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        return list(ex.map(fn, items))
+
+
+def forward(q, k, v, off, window, dilation=(1, 1, 1), scale=None, want_attn=False,
+            threads=None):
+    """Forward over whole tensors: q,k,v [B,T,H,W,heads,d], off [B,T,H,W,heads,P,3].
+
+    Returns o [B,T,H,W,heads,d] and lse [B,T,H,W,heads] (and attn [..,heads,P]).
+    """
+    q, k, v, off = _f64(q), _f64(k), _f64(v), _f32(off)
+    B, T, H, W, nh, d = q.shape
+    P = window[0] * window[1] * window[2]
+    if off.shape != (B, T, H, W, nh, P, 3):
+        raise ValueError(f"offsets shape {off.shape} != {(B, T, H, W, nh, P, 3)}")
+    scale = default_scale(d) if scale is None else scale
+    pos = grid_positions(T, H, W)
+    N = T * H * W
+    o = np.zeros_like(q); lse = np.zeros((B, T, H, W, nh))
+    attn = np.zeros((B, T, H, W, nh, P)) if want_attn else None
+
+    def one(bh):
+        b, h = bh
+        res = forward_queries((T, H, W), window, dilation, scale, pos,
+                              q[b, :, :, :, h].reshape(N, d), off[b, :, :, :, h].reshape(N, P, 3),
+                              (0, 0, 0), k[b, :, :, :, h], v[b, :, :, :, h], want_attn)
+        o[b, :, :, :, h] = res[0].reshape(T, H, W, d)
+        lse[b, :, :, :, h] = res[1].reshape(T, H, W)
+        if want_attn:
+            attn[b, :, :, :, h] = res[2].reshape(T, H, W, P)
+
+    _pool_map(one, [(b, h) for b in range(B) for h in range(nh)], threads)
+    return (o, lse, attn) if want_attn else (o, lse)
+
+
+def backward(q, k, v, off, dout, window, dilation=(1, 1, 1), scale=None, threads=None):
+    """Backward over whole tensors. Returns dq, dk, dv [B,T,H,W,heads,d] and
+    doff [B,T,H,W,heads,P,3] (all float64)."""
+    q, k, v, off, dout = _f64(q), _f64(k), _f64(v), _f32(off), _f64(dout)
+    B, T, H, W, nh, d = q.shape
+    P = window[0] * window[1] * window[2]
+    scale = default_scale(d) if scale is None else scale
+    pos = grid_positions(T, H, W)
+    N = T * H * W
+    dq = np.zeros_like(q); dk = np.zeros_like(k); dv = np.zeros_like(v)
+    doff = np.zeros(off.shape)
+
+    def one(bh):
+        b, h = bh
+        r = backward_queries((T, H, W), window, dilation, scale, pos,
+                             q[b, :, :, :, h].reshape(N, d), off[b, :, :, :, h].reshape(N, P, 3),
+                             (0, 0, 0), k[b, :, :, :, h], v[b, :, :, :, h],
+                             dout[b, :, :, :, h].reshape(N, d))
+        dq[b, :, :, :, h] = r[0].reshape(T, H, W, d)
+        doff[b, :, :, :, h] = r[1].reshape(T, H, W, P, 3)
+        dk[b, :, :, :, h] = r[2]
+        dv[b, :, :, :, h] = r[3]
+
+    _pool_map(one, [(b, h) for b in range(B) for h in range(nh)], threads)
+    return dq, dk, dv, doff
+
+
+def geometry(off, window, dilation=(1, 1, 1)):
+    """Base corner and fraction of every sample: off [B,T,H,W,heads,P,3] ->
+    base int32 and frac float32 of the same shape."""
+    off = _f32(off)
+    B, T, H, W, nh, P, _ = off.shape
+    pos = grid_positions(T, H, W)
+    base = np.zeros(off.shape, dtype=np.int32); frac = np.zeros(off.shape, dtype=np.float32)
+    for b in range(B):
+        for h in range(nh):
+            bb, ff = geometry_queries((T, H, W), window, dilation, pos,
+                                      off[b, :, :, :, h].reshape(-1, P, 3))
+            base[b, :, :, :, h] = bb.reshape(T, H, W, P, 3)
+            frac[b, :, :, :, h] = ff.reshape(T, H, W, P, 3)
+    return base, frac
+
+
+# ----------------------------------------------------------------------------
+# Offset projection: Linear(C -> heads*P*3) of each token's query row.
+# ----------------------------------------------------------------------------
+
+def offset_proj(q2d, w, b=None) -> np.ndarray:
+    """offsets[N, F] = q[N, C] @ w[F, C]^T + b[F], in float64."""
+    out = _f64(q2d) @ _f64(w).T
+    if b is not None:
+        out += _f64(b)[None, :]
+    return out
+
+
+def offset_proj_backward(q2d, w, doff2d) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of the projection, in float64: (dq share = doff @ w,
+    dW = doff^T @ q, db = column sums of doff)."""
+    g = _f64(doff2d)
+    return g @ _f64(w), g.T @ _f64(q2d), g.sum(axis=0)
