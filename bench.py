@@ -1,0 +1,253 @@
+#!/usr/bin/env python
+"""3D-DSA fwd+bwd throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--cpu-baseline on|off]
+
+One step is one pass of the whole hot path over one batch of synthetic input
+(the 256x68x120-token grid, 24 heads x 128, 3x5x5 window, offsets N(0,2),
+deterministic K/V gradients by default): forward then backward, every kernel
+included. Inputs are drawn on the GPU (seed 0) and are resident in HBM before
+the timed region starts. Prints one JSON line on stdout; progress goes to
+stderr.
+
+`roofline` is taken for the kernel with the largest share of the timed
+region, timed per launch with HIP events that libdsa3d records around each of
+its launches (dsa3d_set_launch_log) on the launch stream. Its achieved rate
+is the algorithmic bytes (each tensor read or written once; sampled K/V rows
+are never counted) of one launch over its mean launch duration.
+
+`--copy-calibration` instead runs a plain device copy of a known size, whose
+rocprofv3 FETCH_SIZE / WRITE_SIZE readings scale the counters of the kernels.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+VALU_F32_PEAK_TFLOPS = 157.3   # MI355X vector fp32, published (dual-issue/packed)
+METRIC = "3D-DSA fwd+bwd tokens/sec at 256×68×120 tokens; achieved HBM GB/s vs peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(wl):
+    """Per (token, head): algorithmic bytes and flops of the forward and backward.
+
+    bytes: forward reads q, k, v (3d elements) and offsets (3P) and writes o
+    (d) and lse (4 B); backward reads q, k, v, o, dO (5d), offsets (3P) and
+    lse (4 B) and writes dq, dk, dv (3d) and doffsets (3P).
+    flops: forward 32*d*P (per sample: 8 corner dot products of length d
+    weighted into the logit, 8 weighted row updates of o); backward 80*d*P.
+    """
+    s = 4 if wl.dtype == "f32" else 2
+    d, P = wl.head_dim, wl.P
+    return {
+        "fwd_bytes": 4 * d * s + 3 * P * s + 4,
+        "bwd_bytes": 8 * d * s + 6 * P * s + 4,
+        "proj_fwd_bytes_per_token": (wl.C + wl.F) * s,
+        "fwd_flops": 32 * d * P,
+        "bwd_flops": 80 * d * P,
+    }
+
+
+def cpu_baseline(wl, budget_s: float = 20.0):
+    """The oracle, as it is, on a bounded sample of the same workload: the
+    interior queries of a 16x24x24-token crop drawn with the workload's
+    distributions, on as many heads as there are usable host cores (heads are
+    independent and run in parallel). Returns tokens/s for whole tokens (all
+    heads), scaled from the heads sampled."""
+    import numpy as np
+
+    import oracle
+    from deformable_local_attention_amd import synth
+
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cores = max(1, min(cores, 16, wl.heads))
+    crop = wl.with_grid(B=1, T=min(wl.T, 16), H=min(wl.H, 24), W=min(wl.W, 24), heads=cores, name=wl.name + "-crop")
+    x = synth.make_inputs(crop, "cpu", seed=0, with_grad=True)
+    if crop.offsets == "proj":
+        q2 = x["q"].double().numpy().reshape(crop.tokens, crop.C)
+        off = oracle.offset_proj(q2, x["proj_w"].double().numpy(), None).astype(np.float32)
+        off = off.reshape(crop.B, crop.T, crop.H, crop.W, crop.heads, crop.P, 3)
+    else:
+        off = x["offsets"].float().numpy()
+    np64 = lambda t: t.double().numpy()
+    q, k, v, g = np64(x["q"]), np64(x["k"]), np64(x["v"]), np64(x["dout"])
+    T, H, W = crop.T, crop.H, crop.W
+    m = [min(4, T // 4), min(8, H // 4), min(8, W // 4)]
+    pos = oracle.grid_positions(T, H, W)
+    interior = np.all((pos >= m) & (pos < np.array([T, H, W]) - m), axis=1)
+    pos = pos[interior]
+    scale = 1.0 / np.sqrt(crop.head_dim)
+
+    def one_pass():
+        from concurrent.futures import ThreadPoolExecutor
+
+        def one(h):
+            qq = q[0][pos[:, 0], pos[:, 1], pos[:, 2], h]
+            oo = off[0][pos[:, 0], pos[:, 1], pos[:, 2], h]
+            oracle.forward_queries((T, H, W), crop.window, crop.dilation, scale, pos, qq, oo, (0, 0, 0),
+                                   k[0, :, :, :, h], v[0, :, :, :, h])
+            if crop.backward:
+                gg = g[0][pos[:, 0], pos[:, 1], pos[:, 2], h]
+                oracle.backward_queries((T, H, W), crop.window, crop.dilation, scale, pos, qq, oo, (0, 0, 0),
+                                        k[0, :, :, :, h], v[0, :, :, :, h], gg)
+
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=cores) as ex:
+            list(ex.map(one, range(cores)))
+        return time.perf_counter() - t0
+
+    dt1 = one_pass()
+    reps = max(1, int(math.ceil((budget_s - dt1) / dt1)))
+    dt = sum(one_pass() for _ in range(reps))
+    n = len(pos) * reps
+    token_heads_per_s = n * cores / dt
+    return {"value": token_heads_per_s / wl.heads, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"fp64 oracle, {'fwd+bwd' if crop.backward else 'fwd'}: the {len(pos)} interior queries of a "
+                       f"{T}x{H}x{W}-token crop (the workload's window, dilation and input distributions), "
+                       f"{cores} heads in parallel, {reps} passes, {dt:.1f} s on {cores} threads; tokens/s counts "
+                       f"whole tokens ({wl.heads} heads)")}
+
+
+def copy_calibration(gib: float = 4.0, reps: int = 5):
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "ms": dt * 1e3,
+                      "gbs": 2 * n * 4 / dt / 1e9}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--fast", action="store_true", help="float32 (non-deterministic) K/V-gradient accumulation")
+    ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the 3D-DSA path here runs on a single MI355X "
+              "(multi-GPU sharding is not built). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import deformable_local_attention_amd as dsa
+    from deformable_local_attention_amd import synth
+    from deformable_local_attention_amd.chain import Chain
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    wl = synth.WORKLOADS[args.workload or synth.HEADLINE]
+    if args.fast:
+        import dataclasses
+        wl = dataclasses.replace(wl, deterministic=False)
+    log(f"[bench] {synth.describe(wl)}; steps={args.steps} warmup={args.warmup}")
+    t0 = time.perf_counter()
+    x = synth.make_inputs(wl, "cuda:0", seed=0)
+    ch = Chain(wl, x)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs drawn and buffers allocated in {time.perf_counter() - t0:.1f} s; "
+        f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB on the device")
+
+    for i in range(args.warmup):
+        ch.run()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {i + 1}/{args.warmup} done")
+
+    stream = torch.cuda.current_stream()
+    timer = dsa.launch_timer(capacity=max(64, 64 * args.steps))
+    torch.cuda.synchronize()
+    with timer:
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        t_wall = time.perf_counter()
+        ev0.record(stream)
+        for i in range(args.steps):
+            ch.run()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter() - t_wall
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+    tokens_per_s = wl.tokens * args.steps / (ms_total / 1e3)
+    log(f"[bench] timed {args.steps} steps: {ms_per_step:.2f} ms/step (wall {t_wall:.2f} s), "
+        f"{tokens_per_s / 1e6:.3f} M tokens/s")
+
+    durs = timer.durations_ms()
+    if timer.count >= timer.log.capacity:
+        log("[bench] warning: launch log full; per-kernel figures cover the first launches only")
+    per_kernel = {k: {"launches": len(v), "mean_ms": sum(v) / len(v), "total_ms": sum(v)} for k, v in durs.items()}
+    for k, v in sorted(per_kernel.items(), key=lambda kv: -kv[1]["total_ms"]):
+        log(f"[bench]   {k:14s} {v['launches']:4d} launches, mean {v['mean_ms']:.3f} ms, total {v['total_ms']:.1f} ms")
+
+    alg = algorithmic(wl)
+    dom = max(per_kernel, key=lambda k: per_kernel[k]["total_ms"])
+    nheads_launch = wl.heads
+    if dom == "backward":
+        per_head = dsa.dsa3d_workspace_min(ch.desc, dsa.WS_BACKWARD)
+        nbytes = ch.ws.numel() if ch.ws is not None else 0
+        nheads_launch = wl.heads if per_head == 0 else min(wl.heads, nbytes // per_head)
+        unit_bytes, unit_flops = alg["bwd_bytes"], alg["bwd_flops"]
+    elif dom == "forward":
+        unit_bytes, unit_flops = alg["fwd_bytes"], alg["fwd_flops"]
+    else:
+        unit_bytes, unit_flops = 0, 0
+    units = wl.tokens * nheads_launch
+    mean_s = per_kernel[dom]["mean_ms"] / 1e3
+    achieved_gbs = unit_bytes * units / mean_s / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved_gbs, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 5), "traffic": None,
+                "launch_ms": round(per_kernel[dom]["mean_ms"], 3), "units_per_launch": units,
+                "bytes_per_unit": unit_bytes}
+    roofline_alu = {"bound": "alu", "kernel": dom,
+                    "achieved": round(unit_flops * units / mean_s / 1e12, 3), "peak": VALU_F32_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(unit_flops * units / mean_s / 1e12 / VALU_F32_PEAK_TFLOPS, 5),
+                    "flops_per_unit": unit_flops}
+
+    result = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32", "data": "synthetic (seeded N(0,1) q/k/v/dO; offsets "
+        + (f"N(0,{wl.offset_sigma})" if wl.offsets == "direct" else "from a Linear with N(0,0.02) weights") + ")",
+        "config": {"workload": wl.name, "grid": [wl.B, wl.T, wl.H, wl.W], "heads": wl.heads, "head_dim": wl.head_dim,
+                   "window": list(wl.window), "P": wl.P, "dilation": list(wl.dilation), "offsets": wl.offsets,
+                   "chain": ("proj+" if wl.offsets == "proj" else "") + ("fwd+bwd" if wl.backward else "fwd"),
+                   "deterministic": wl.deterministic},
+        "roofline": roofline, "roofline_alu": roofline_alu,
+        "kernels": {k: {"launches": v["launches"], "mean_ms": round(v["mean_ms"], 3)} for k, v in per_kernel.items()},
+    }
+    if args.cpu_baseline == "on":
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(wl)
+        log(f"[bench] cpu baseline: {result['cpu_baseline']['value']:.1f} tokens/s")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,293 @@
+"""Python binding of libdsa3d -- 3D Deformable Slide Attention on MI355X.
+
+Argument marshalling only: every step of the operator runs in the HIP kernels
+of libdsa3d.so (built by `python -m deformable_local_attention_amd.build`).
+torch supplies device memory and the current stream. There is no CPU or
+PyTorch fallback: if the library is missing, every call raises.
+
+Low-level functions carry the C names (dsa3d_forward, dsa3d_backward, ...)
+and take a `Desc` plus torch tensors; `forward`, `backward`, `offset_proj`
+and `offset_proj_backward` are conveniences that build the descriptor and
+allocate outputs and workspaces with torch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+__all__ = [
+    "Desc", "DSA3DError", "lib", "library_path", "make_desc",
+    "dsa3d_version", "dsa3d_status_string", "dsa3d_validate", "dsa3d_workspace_size", "dsa3d_workspace_min",
+    "dsa3d_offset_proj_forward", "dsa3d_forward", "dsa3d_backward", "dsa3d_offset_proj_backward",
+    "dsa3d_debug_geometry", "forward", "backward", "offset_proj", "offset_proj_backward",
+    "DSA3D_F32", "DSA3D_BF16", "WS_FORWARD", "WS_BACKWARD", "WS_PROJ_BACKWARD",
+    "dsa3d_set_launch_log", "LaunchLog", "launch_timer", "KERNELS",
+]
+
+DSA3D_F32, DSA3D_BF16 = 0, 1
+WS_FORWARD, WS_BACKWARD, WS_PROJ_BACKWARD = 0, 1, 2
+EXPORTS = ("dsa3d_version", "dsa3d_status_string", "dsa3d_validate", "dsa3d_workspace_size",
+           "dsa3d_workspace_min", "dsa3d_offset_proj_forward", "dsa3d_forward", "dsa3d_backward",
+           "dsa3d_offset_proj_backward", "dsa3d_debug_geometry", "dsa3d_set_launch_log")
+# kernel ids of the launch log (dsa3d_kernel)
+KERNELS = {1: "proj_forward", 2: "forward", 3: "backward", 4: "bwd_finalize", 5: "fill", 6: "proj_bwd_dq",
+           7: "proj_bwd_dw", 8: "split_sum", 9: "colsum", 10: "geometry"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+_lock = threading.Lock()
+
+
+def library_path() -> str:
+    return os.environ.get("DSA3D_LIBRARY", os.path.join(_HERE, "libdsa3d.so"))
+
+
+class DSA3DError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed: {message} (status {status})")
+        self.status = status
+
+
+class Desc(ctypes.Structure):
+    """Mirror of `dsa3d_desc` (include/dsa3d.h)."""
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64), ("W", ctypes.c_int64),
+                ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("kt", ctypes.c_int32), ("kh", ctypes.c_int32), ("kw", ctypes.c_int32),
+                ("P", ctypes.c_int32),
+                ("dil_t", ctypes.c_int32), ("dil_h", ctypes.c_int32), ("dil_w", ctypes.c_int32),
+                ("dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float),
+                ("deterministic", ctypes.c_int32)]
+
+
+class LaunchLog(ctypes.Structure):
+    """Mirror of `dsa3d_launch_log`."""
+    _fields_ = [("capacity", ctypes.c_int32), ("count", ctypes.c_int32),
+                ("kernel", ctypes.POINTER(ctypes.c_int32)),
+                ("start", ctypes.POINTER(ctypes.c_void_p)), ("stop", ctypes.POINTER(ctypes.c_void_p))]
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdsa3d.so once; raise if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            path = library_path()
+            if not os.path.exists(path):
+                raise ImportError(f"libdsa3d.so not found at {path}: build it with "
+                                  "`python -m deformable_local_attention_amd.build` (needs ROCm hipcc)")
+            L = ctypes.CDLL(path)
+            vp, sz, dp = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Desc)
+            sig = {
+                "dsa3d_version": ([], ctypes.c_int),
+                "dsa3d_status_string": ([ctypes.c_int], ctypes.c_char_p),
+                "dsa3d_validate": ([dp], ctypes.c_int),
+                "dsa3d_workspace_size": ([dp, ctypes.c_int], sz),
+                "dsa3d_workspace_min": ([dp, ctypes.c_int], sz),
+                "dsa3d_offset_proj_forward": ([dp, vp, vp, vp, vp, vp], ctypes.c_int),
+                "dsa3d_forward": ([dp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+                "dsa3d_backward": ([dp] + [vp] * 11 + [vp, sz, vp], ctypes.c_int),
+                "dsa3d_offset_proj_backward": ([dp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+                "dsa3d_debug_geometry": ([dp, vp, vp, vp, vp], ctypes.c_int),
+                "dsa3d_set_launch_log": ([ctypes.POINTER(LaunchLog)], ctypes.c_int),
+            }
+            for name, (args, res) in sig.items():
+                f = getattr(L, name)
+                f.argtypes = args
+                f.restype = res
+            _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------------------
+# descriptors and marshalling
+# ---------------------------------------------------------------------------
+
+def make_desc(B: int, T: int, H: int, W: int, heads: int, head_dim: int, window: Sequence[int],
+              dilation: Sequence[int] = (1, 1, 1), dtype=torch.bfloat16, scale: float = 0.0,
+              deterministic: bool = False) -> Desc:
+    kt, kh, kw = window
+    code = {torch.float32: DSA3D_F32, torch.bfloat16: DSA3D_BF16}.get(dtype, -1)
+    return Desc(B, T, H, W, heads, head_dim, kt, kh, kw, kt * kh * kw, dilation[0], dilation[1], dilation[2],
+                code, float(scale), 1 if deterministic else 0)
+
+
+def desc_like(q: torch.Tensor, window, dilation=(1, 1, 1), scale: float = 0.0, deterministic: bool = False) -> Desc:
+    B, T, H, W, nh, d = q.shape
+    return make_desc(B, T, H, W, nh, d, window, dilation, q.dtype, scale, deterministic)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("libdsa3d needs contiguous tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise DSA3DError(fn, status, dsa3d_status_string(status))
+
+
+# ---------------------------------------------------------------------------
+# the C entry points, one to one
+# ---------------------------------------------------------------------------
+
+def dsa3d_version() -> int:
+    return lib().dsa3d_version()
+
+
+def dsa3d_status_string(status: int) -> str:
+    return lib().dsa3d_status_string(status).decode()
+
+
+def dsa3d_validate(desc: Desc) -> int:
+    return lib().dsa3d_validate(ctypes.byref(desc))
+
+
+def dsa3d_workspace_size(desc: Desc, kind: int) -> int:
+    return lib().dsa3d_workspace_size(ctypes.byref(desc), kind)
+
+
+def dsa3d_workspace_min(desc: Desc, kind: int) -> int:
+    return lib().dsa3d_workspace_min(ctypes.byref(desc), kind)
+
+
+def dsa3d_offset_proj_forward(desc: Desc, q, w, bias, offsets, stream=None):
+    _check("dsa3d_offset_proj_forward",
+           lib().dsa3d_offset_proj_forward(ctypes.byref(desc), _ptr(q), _ptr(w), _ptr(bias), _ptr(offsets),
+                                           _stream(stream)))
+
+
+def dsa3d_forward(desc: Desc, q, k, v, offsets, out, lse, stream=None):
+    _check("dsa3d_forward",
+           lib().dsa3d_forward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(offsets), _ptr(out), _ptr(lse),
+                               _stream(stream)))
+
+
+def dsa3d_backward(desc: Desc, q, k, v, offsets, out, lse, dout, dq, dk, dv, doffsets, workspace,
+                   stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dsa3d_backward",
+           lib().dsa3d_backward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(offsets), _ptr(out), _ptr(lse),
+                                _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(doffsets), _ptr(workspace), nbytes,
+                                _stream(stream)))
+
+
+def dsa3d_offset_proj_backward(desc: Desc, q, w, doffsets, dq_accum, dw, dbias, workspace, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dsa3d_offset_proj_backward",
+           lib().dsa3d_offset_proj_backward(ctypes.byref(desc), _ptr(q), _ptr(w), _ptr(doffsets), _ptr(dq_accum),
+                                            _ptr(dw), _ptr(dbias), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def dsa3d_set_launch_log(log: Optional[LaunchLog]):
+    _check("dsa3d_set_launch_log", lib().dsa3d_set_launch_log(None if log is None else ctypes.byref(log)))
+
+
+def dsa3d_debug_geometry(desc: Desc, offsets, base, frac, stream=None):
+    _check("dsa3d_debug_geometry",
+           lib().dsa3d_debug_geometry(ctypes.byref(desc), _ptr(offsets), _ptr(base), _ptr(frac), _stream(stream)))
+
+
+class launch_timer:
+    """Context manager: log every libdsa3d kernel launched on this thread with
+    HIP events (torch.cuda.Event handles) and report per-kernel durations.
+
+        with launch_timer(capacity=256) as lt:
+            ...libdsa3d calls...
+        torch.cuda.synchronize(); lt.durations_ms() -> {"backward": [..], ...}
+    """
+
+    def __init__(self, capacity: int = 256):
+        self.events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(capacity)]
+        for a, b in self.events:  # torch creates the HIP event at its first record
+            a.record(); b.record()
+        self._kern = (ctypes.c_int32 * capacity)()
+        self._start = (ctypes.c_void_p * capacity)(*[a.cuda_event for a, _ in self.events])
+        self._stop = (ctypes.c_void_p * capacity)(*[b.cuda_event for _, b in self.events])
+        self.log = LaunchLog(capacity, 0, self._kern, self._start, self._stop)
+
+    def __enter__(self):
+        torch.cuda.synchronize()
+        _check("dsa3d_set_launch_log", lib().dsa3d_set_launch_log(ctypes.byref(self.log)))
+        return self
+
+    def __exit__(self, *exc):
+        lib().dsa3d_set_launch_log(None)
+        return False
+
+    @property
+    def count(self) -> int:
+        return self.log.count
+
+    def durations_ms(self):
+        out = {}
+        for i in range(self.log.count):
+            a, b = self.events[i]
+            out.setdefault(KERNELS.get(self._kern[i], str(self._kern[i])), []).append(a.elapsed_time(b))
+        return out
+
+
+# ---------------------------------------------------------------------------
+# conveniences: descriptor + output/workspace allocation with torch
+# ---------------------------------------------------------------------------
+
+def _workspace(desc: Desc, kind: int, device, nbytes: Optional[int] = None) -> Optional[torch.Tensor]:
+    n = dsa3d_workspace_size(desc, kind) if nbytes is None else nbytes
+    if n == 0:
+        return None
+    return torch.empty((n + 15) // 16 * 16, dtype=torch.uint8, device=device)
+
+
+def forward(q, k, v, offsets, window, dilation=(1, 1, 1), scale: float = 0.0, stream=None):
+    """Returns (out, lse)."""
+    desc = desc_like(q, window, dilation, scale)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:5], dtype=torch.float32, device=q.device)
+    dsa3d_forward(desc, q, k, v, offsets, out, lse, stream)
+    return out, lse
+
+
+def backward(q, k, v, offsets, out, lse, dout, window, dilation=(1, 1, 1), scale: float = 0.0,
+             deterministic: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Returns (dq, dk, dv, doffsets)."""
+    desc = desc_like(q, window, dilation, scale, deterministic)
+    if workspace is None:
+        workspace = _workspace(desc, WS_BACKWARD, q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    doff = torch.empty_like(offsets)
+    dsa3d_backward(desc, q, k, v, offsets, out, lse, dout, dq, dk, dv, doff, workspace, stream)
+    return dq, dk, dv, doff
+
+
+def offset_proj(q, w, bias, window, stream=None):
+    """offsets [B,T,H,W,heads,P,3] = Linear(q's C-wide row) with weight w [heads*P*3, C]."""
+    B, T, H, W, nh, d = q.shape
+    desc = desc_like(q, window)
+    P = desc.P
+    off = torch.empty((B, T, H, W, nh, P, 3), dtype=q.dtype, device=q.device)
+    dsa3d_offset_proj_forward(desc, q, w, bias, off, stream)
+    return off
+
+
+def offset_proj_backward(q, w, doffsets, dq_accum, window, with_bias: bool = True, stream=None):
+    """Adds doff.W into dq_accum; returns (dW, db) in float32."""
+    desc = desc_like(q, window)
+    dw = torch.empty(w.shape, dtype=torch.float32, device=q.device)
+    db = torch.empty(w.shape[0], dtype=torch.float32, device=q.device) if with_bias else None
+    ws = _workspace(desc, WS_PROJ_BACKWARD, q.device)
+    dsa3d_offset_proj_backward(desc, q, w, doffsets, dq_accum, dw, db, ws, stream)
+    return dw, db

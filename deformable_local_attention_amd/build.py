@@ -1,0 +1,70 @@
+"""Build libdsa3d.so for gfx950 with hipcc (in-tree, next to this file).
+
+    python -m deformable_local_attention_amd.build
+
+Every HIP source is compiled with packed-FP32 instruction generation turned
+off (-Xclang -target-feature -Xclang -packed-fp32-ops); the host pass warns
+that it does not know that feature, which is harmless.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libdsa3d.so")
+SOURCES = ["dsa3d_attn.hip", "dsa3d_proj.hip", "dsa3d_api.cpp"]
+ARCH = os.environ.get("DSA3D_OFFLOAD_ARCH", "gfx950")
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found (ROCm is required to build libdsa3d)")
+
+
+def flags():
+    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-function"]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source (always) and link libdsa3d.so atomically."""
+    cc = hipcc()
+    bdir = os.path.join(PKG, "_build")
+    os.makedirs(bdir, exist_ok=True)
+
+    def compile_one(src):
+        obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
+        cmd = [cc] + flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+        if src.endswith(".cpp"):
+            cmd[1:1] = ["-x", "hip"]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        noise = "is not a recognized feature for this target"
+        msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{msg}")
+        if verbose and msg.strip():
+            print(msg, file=sys.stderr)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    tmp = LIB + f".tmp{os.getpid()}"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

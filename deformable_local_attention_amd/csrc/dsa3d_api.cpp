@@ -1,0 +1,164 @@
+// dsa3d_api.cpp -- the extern "C" boundary of libdsa3d: argument checks,
+// workspace sizing and launches on the caller's stream. No C++ exception and
+// no HIP allocation happens here.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "dsa3d.h"
+#include "dsa3d_internal.h"
+
+namespace {
+
+constexpr size_t kBackwardPassCap = size_t(8) << 30;  // recommended cap on one backward pass's accumulators
+
+bool pow2_in(int32_t x, int32_t lo, int32_t hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_ptrs(std::initializer_list<const void*> ps) {
+    for (const void* p : ps) {
+        if (p == nullptr) return DSA3D_ERR_INVALID_ARG;
+    }
+    for (const void* p : ps) {
+        if (!aligned16(p)) return DSA3D_ERR_MISALIGNED;
+    }
+    return DSA3D_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DSA3D_OK : DSA3D_ERR_HIP; }
+
+int64_t tokens(const dsa3d_desc& d) { return d.B * d.T * d.H * d.W; }
+
+}  // namespace
+
+namespace dsa3d {
+dsa3d_launch_log*& launch_log() {
+    static thread_local dsa3d_launch_log* log = nullptr;
+    return log;
+}
+}  // namespace dsa3d
+
+extern "C" {
+
+int dsa3d_version(void) { return 100; }
+
+int dsa3d_set_launch_log(dsa3d_launch_log* log) {
+    if (log != nullptr && log->capacity > 0 &&
+        (log->kernel == nullptr || log->start == nullptr || log->stop == nullptr))
+        return DSA3D_ERR_INVALID_ARG;
+    dsa3d::launch_log() = log;
+    return DSA3D_OK;
+}
+
+const char* dsa3d_status_string(int status) {
+    switch (status) {
+        case DSA3D_OK: return "ok";
+        case DSA3D_ERR_INVALID_ARG: return "invalid argument";
+        case DSA3D_ERR_UNSUPPORTED: return "unsupported configuration";
+        case DSA3D_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+        case DSA3D_ERR_WORKSPACE: return "workspace missing or too small";
+        case DSA3D_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int dsa3d_validate(const dsa3d_desc* d) {
+    if (d == nullptr) return DSA3D_ERR_INVALID_ARG;
+    if (d->B < 1 || d->T < 1 || d->H < 1 || d->W < 1) return DSA3D_ERR_INVALID_ARG;
+    if (d->T >= (1 << 30) || d->H >= (1 << 30) || d->W >= (1 << 30)) return DSA3D_ERR_INVALID_ARG;
+    const int64_t ntok = tokens(*d);
+    if (ntok / d->B / d->T / d->H != d->W || ntok >= (int64_t(1) << 31)) return DSA3D_ERR_INVALID_ARG;
+    if (d->heads < 1 || d->head_dim < 1) return DSA3D_ERR_INVALID_ARG;
+    if (d->kt < 1 || d->kh < 1 || d->kw < 1) return DSA3D_ERR_INVALID_ARG;
+    if (d->kt % 2 == 0 || d->kh % 2 == 0 || d->kw % 2 == 0) return DSA3D_ERR_INVALID_ARG;
+    if (d->kt > 1023 || d->kh > 1023 || d->kw > 1023) return DSA3D_ERR_INVALID_ARG;
+    if ((int64_t)d->kt * d->kh * d->kw != d->P) return DSA3D_ERR_INVALID_ARG;
+    if (d->dil_t < 1 || d->dil_h < 1 || d->dil_w < 1) return DSA3D_ERR_INVALID_ARG;
+    if (d->dil_t > (1 << 20) || d->dil_h > (1 << 20) || d->dil_w > (1 << 20)) return DSA3D_ERR_INVALID_ARG;
+    if (!(d->scale >= 0.0f) || d->scale == __builtin_inff()) return DSA3D_ERR_INVALID_ARG;
+    if (d->deterministic != 0 && d->deterministic != 1) return DSA3D_ERR_INVALID_ARG;
+    if (d->dtype != DSA3D_F32 && d->dtype != DSA3D_BF16) return DSA3D_ERR_UNSUPPORTED;
+    if (!pow2_in(d->head_dim, 8, 256)) return DSA3D_ERR_UNSUPPORTED;
+    if (d->P > 1024) return DSA3D_ERR_UNSUPPORTED;
+    if ((int64_t)d->heads * d->head_dim > (1 << 20)) return DSA3D_ERR_UNSUPPORTED;
+    if (dsa3d::fwd_groups_per_block(d->head_dim, d->P) == 0) return DSA3D_ERR_UNSUPPORTED;
+    return DSA3D_OK;
+}
+
+size_t dsa3d_workspace_min(const dsa3d_desc* d, int kind) {
+    if (dsa3d_validate(d) != DSA3D_OK) return 0;
+    switch (kind) {
+        case DSA3D_WS_BACKWARD: return dsa3d::bwd_accumulator_bytes_per_head(*d);
+        case DSA3D_WS_PROJ_BACKWARD: return dsa3d::proj_bwd_workspace_bytes(*d);
+        default: return 0;
+    }
+}
+
+size_t dsa3d_workspace_size(const dsa3d_desc* d, int kind) {
+    if (dsa3d_validate(d) != DSA3D_OK) return 0;
+    if (kind == DSA3D_WS_BACKWARD) {
+        const size_t per_head = dsa3d::bwd_accumulator_bytes_per_head(*d);
+        if (per_head == 0) return 0;
+        size_t heads = kBackwardPassCap / per_head;
+        if (heads < 1) heads = 1;
+        if (heads > (size_t)d->heads) heads = d->heads;
+        return heads * per_head;
+    }
+    return dsa3d_workspace_min(d, kind);
+}
+
+int dsa3d_offset_proj_forward(const dsa3d_desc* d, const void* q, const void* w, const void* bias, void* offsets,
+                              void* stream) {
+    int rc = dsa3d_validate(d);
+    if (rc != DSA3D_OK) return rc;
+    if ((rc = check_ptrs({q, w, offsets})) != DSA3D_OK) return rc;
+    if (bias != nullptr && !aligned16(bias)) return DSA3D_ERR_MISALIGNED;
+    return hip_status(dsa3d::launch_proj_forward(*d, q, w, bias, offsets, static_cast<hipStream_t>(stream)));
+}
+
+int dsa3d_forward(const dsa3d_desc* d, const void* q, const void* k, const void* v, const void* offsets, void* out,
+                  float* lse, void* stream) {
+    int rc = dsa3d_validate(d);
+    if (rc != DSA3D_OK) return rc;
+    if ((rc = check_ptrs({q, k, v, offsets, out, lse})) != DSA3D_OK) return rc;
+    return hip_status(dsa3d::launch_forward(*d, q, k, v, offsets, out, lse, static_cast<hipStream_t>(stream)));
+}
+
+int dsa3d_backward(const dsa3d_desc* d, const void* q, const void* k, const void* v, const void* offsets,
+                   const void* out, const float* lse, const void* dout, void* dq, void* dk, void* dv, void* doffsets,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = dsa3d_validate(d);
+    if (rc != DSA3D_OK) return rc;
+    if ((rc = check_ptrs({q, k, v, offsets, out, lse, dout, dq, dk, dv, doffsets})) != DSA3D_OK) return rc;
+    const size_t need = dsa3d::bwd_accumulator_bytes_per_head(*d);
+    if (need > 0) {
+        if (workspace == nullptr || workspace_bytes < need) return DSA3D_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return DSA3D_ERR_MISALIGNED;
+    }
+    return hip_status(dsa3d::launch_backward(*d, q, k, v, offsets, out, lse, dout, dq, dk, dv, doffsets, workspace,
+                                             workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
+int dsa3d_offset_proj_backward(const dsa3d_desc* d, const void* q, const void* w, const void* doffsets,
+                               void* dq_accum, float* dw, float* dbias, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    int rc = dsa3d_validate(d);
+    if (rc != DSA3D_OK) return rc;
+    if ((rc = check_ptrs({q, w, doffsets, dq_accum, dw})) != DSA3D_OK) return rc;
+    if (dbias != nullptr && !aligned16(dbias)) return DSA3D_ERR_MISALIGNED;
+    const size_t need = dsa3d::proj_bwd_workspace_bytes(*d);
+    if (workspace == nullptr || workspace_bytes < need) return DSA3D_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return DSA3D_ERR_MISALIGNED;
+    return hip_status(dsa3d::launch_proj_backward(*d, q, w, doffsets, dq_accum, dw, dbias, workspace,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+int dsa3d_debug_geometry(const dsa3d_desc* d, const void* offsets, int32_t* base, float* frac, void* stream) {
+    int rc = dsa3d_validate(d);
+    if (rc != DSA3D_OK) return rc;
+    if ((rc = check_ptrs({offsets, base, frac})) != DSA3D_OK) return rc;
+    return hip_status(dsa3d::launch_geometry(*d, offsets, base, frac, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,187 @@
+/*
+ * dsa3d.h -- C ABI of libdsa3d: 3D Deformable Slide Attention (3D-DSA) on
+ * AMD MI355X (gfx950).
+ *
+ * The operator. 3D-DSA is deformable attention carried over to video tokens:
+ * each token (t,h,w) of a [B,T,H,W] token grid attends, per head, to the P
+ * points of its k_t x k_h x k_w spatiotemporal neighbourhood, each displaced by
+ * a learned offset (dt,dh,dw) [MegaSlide-DiT, §5.1 Rationale; Dutch and French
+ * summaries, "3D Deformable Slide Attention", Mechanism]. Keys and values are
+ * read at the displaced points by trilinear interpolation -- the pages use
+ * grid_sample in bilinear mode on 5-D tensors [MegaSlide-DiT, §5.3
+ * Implementation considerations] -- with zero padding outside the grid. Each
+ * head takes a softmax over the P scaled dot products q.k_p/sqrt(d) and
+ * returns the weighted sum of the sampled values. There is no causal mask
+ * [same section]. With every offset zero this is fixed-window local attention
+ * [MegaSlide-DiT, §9.1 Effect of local offsets]. The offsets come from a
+ * pointwise (linear) projection of the query [§5.3; Dutch summary,
+ * Implementation].
+ *
+ * Exact definition (the formula section §5.2 is empty in the page text; this
+ * is the plain reading of the statements above):
+ *   point p = (i_t,i_h,i_w), row-major over the window (w fastest);
+ *   ref = (t,h,w) + dil * (i - (k-1)/2)                       (integers)
+ *   pos = (float)ref + offset[p]                               (one fp32 add per axis)
+ *   x0 = floorf(pos), f = pos - x0                             (fp32)
+ *   k_p = sum_{c in {0,1}^3} prod_axis(c ? f : 1-f) * K[x0 + c]  (0 outside the grid)
+ *   s_p = scale * <q, k_p>, a = softmax_p(s), o = sum_p a_p v_p, lse = log sum_p exp(s_p)
+ * A position that is NaN, infinite or |pos| >= 2^30 makes its sample read
+ * zeros. Samples outside the grid stay in the softmax with logit 0.
+ *
+ * Conventions for every call:
+ *  - Tensors are dense, row-major, on the device, owned by the caller:
+ *      q, k, v, out, dout, dq, dk, dv:  [B,T,H,W,heads,head_dim]
+ *      offsets, doffsets:               [B,T,H,W,heads,P,3], last axis (dt,dh,dw)
+ *      lse:                             [B,T,H,W,heads] float32
+ *    Element type: desc->dtype (DSA3D_F32 = float32, DSA3D_BF16 = bfloat16 bits),
+ *    except lse, dW and dbias, which are always float32.
+ *  - Base pointers must be 16-byte aligned (DSA3D_ERR_MISALIGNED otherwise).
+ *  - Calls only enqueue work on `stream` (a hipStream_t; NULL = the null
+ *    stream) and return; they never synchronise and never allocate device
+ *    memory. Scratch memory is the caller's workspace, sized by
+ *    dsa3d_workspace_size().
+ *  - Errors: a negative dsa3d_status. Argument errors are found before any
+ *    work is enqueued. A HIP launch error gives DSA3D_ERR_HIP. No C++
+ *    exception crosses this boundary.
+ *  - Calls on distinct streams may run concurrently if they share no output
+ *    or workspace. The only mutable state is the opt-in, per-thread launch
+ *    log (dsa3d_set_launch_log).
+ */
+#ifndef DSA3D_H
+#define DSA3D_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSA3D_OK = 0,
+    DSA3D_ERR_INVALID_ARG = -1,  /* bad shape, window, P, dilation, null pointer */
+    DSA3D_ERR_UNSUPPORTED = -2,  /* valid but not built: head_dim, P, dtype */
+    DSA3D_ERR_MISALIGNED = -3,   /* a base pointer is not 16-byte aligned */
+    DSA3D_ERR_WORKSPACE = -4,    /* workspace missing or too small */
+    DSA3D_ERR_HIP = -5           /* the HIP runtime reported an error */
+} dsa3d_status;
+
+typedef enum { DSA3D_F32 = 0, DSA3D_BF16 = 1 } dsa3d_dtype;
+
+typedef struct dsa3d_desc {
+    int64_t B, T, H, W;           /* token grid; each >= 1; B*T*H*W < 2^31 */
+    int32_t heads, head_dim;      /* C = heads * head_dim; head_dim a power of two in [8, 256] */
+    int32_t kt, kh, kw;           /* window shape; each odd, >= 1 */
+    int32_t P;                    /* sampling points; must equal kt*kh*kw, <= 1024 */
+    int32_t dil_t, dil_h, dil_w;  /* window dilation, each >= 1 (it spaces the
+                                     reference grid; offsets are not scaled) */
+    int32_t dtype;                /* dsa3d_dtype of every tensor except lse/dW/dbias */
+    float scale;                  /* logit scale; 0 means 1/sqrt(head_dim) */
+    int32_t deterministic;        /* backward: 1 = bitwise-reproducible dk/dv */
+} dsa3d_desc;
+
+/* Which call a workspace is for. */
+typedef enum {
+    DSA3D_WS_FORWARD = 0,
+    DSA3D_WS_BACKWARD = 1,
+    DSA3D_WS_PROJ_BACKWARD = 2
+} dsa3d_ws_kind;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int dsa3d_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* dsa3d_status_string(int status);
+
+/* Check a descriptor on the host; no GPU is touched. Returns DSA3D_OK or the
+ * error that every compute call would return for it. */
+int dsa3d_validate(const dsa3d_desc* desc);
+
+/* Recommended workspace bytes for `kind` (0 if none is needed; 0 also for an
+ * invalid descriptor). The backward accepts any workspace of at least its
+ * per-head minimum (dsa3d_workspace_min) and runs fewer, larger passes over
+ * the heads the more it gets; the recommended size caps one pass at 8 GiB. */
+size_t dsa3d_workspace_size(const dsa3d_desc* desc, int kind);
+size_t dsa3d_workspace_min(const dsa3d_desc* desc, int kind);
+
+/* Offset projection: offsets[n, f] = sum_c q[n, c] * w[f, c] + bias[f], with n
+ * over the B*T*H*W tokens, c over C = heads*head_dim and f = (head*P + p)*3 +
+ * axis over F = heads*P*3 -- a Linear layer (weight [F, C], row-major) applied
+ * to each token's full query row [MegaSlide-DiT, §5.3: pointwise convolution;
+ * Dutch summary, Implementation: a linear layer]. bias may be NULL. The
+ * result is accumulated in float32 and rounded once to the output dtype. */
+int dsa3d_offset_proj_forward(const dsa3d_desc* desc, const void* q, const void* w,
+                              const void* bias, void* offsets, void* stream);
+
+/* Forward. Writes out and lse (log of the softmax denominator, float32, used
+ * by the backward). No workspace is needed. */
+int dsa3d_forward(const dsa3d_desc* desc, const void* q, const void* k, const void* v,
+                  const void* offsets, void* out, float* lse, void* stream);
+
+/* Backward for a loss L given dout = dL/dout. Writes dq (the attention path's
+ * share), dk, dv and doffsets (dL/doffsets). `out` and `lse` are the forward's
+ * outputs for the same inputs. dk and dv are accumulated in float32 (fast
+ * mode) or in 64-bit fixed point with 2^-32 resolution (deterministic = 1: the
+ * result is bitwise identical from run to run; each term is clamped to
+ * |x| <= 2^18) and rounded once to the output dtype. The workspace holds those
+ * accumulators; see dsa3d_workspace_size(desc, DSA3D_WS_BACKWARD). */
+int dsa3d_backward(const dsa3d_desc* desc, const void* q, const void* k, const void* v,
+                   const void* offsets, const void* out, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, void* doffsets,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of the offset projection for doffsets [N, F]:
+ *   dq_accum[n, c] += sum_f doffsets[n, f] * w[f, c]   (added to the dtype tensor,
+ *                                                      one rounding per element)
+ *   dw[f, c]  = sum_n doffsets[n, f] * q[n, c]          (float32, overwritten)
+ *   dbias[f]  = sum_n doffsets[n, f]                    (float32, overwritten; may be NULL)
+ * dw and dbias are summed in a fixed order (bitwise reproducible). The
+ * workspace (DSA3D_WS_PROJ_BACKWARD) holds split-sum partials. */
+int dsa3d_offset_proj_backward(const dsa3d_desc* desc, const void* q, const void* w,
+                               const void* doffsets, void* dq_accum, float* dw, float* dbias,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Test hook: the integer base corner floor(pos) and the float32 fraction f of
+ * every sample, both [B,T,H,W,heads,P,3] (int32, float32). A sample whose
+ * position is NaN, infinite or |pos| >= 2^30 reports base INT32_MIN and f 0. */
+int dsa3d_debug_geometry(const dsa3d_desc* desc, const void* offsets, int32_t* base,
+                         float* frac, void* stream);
+
+/* Profiling aid: per-launch HIP events.
+ *
+ * Kernels of libdsa3d, as reported in dsa3d_launch_log.kernel[]: */
+typedef enum {
+    DSA3D_K_PROJ_FORWARD = 1,   /* projection GEMM */
+    DSA3D_K_FORWARD = 2,        /* fused sample + softmax + aggregate */
+    DSA3D_K_BACKWARD = 3,       /* fused backward: dq, doffsets, dk/dv scatter */
+    DSA3D_K_BWD_FINALIZE = 4,   /* dk/dv accumulators -> output dtype */
+    DSA3D_K_FILL = 5,           /* workspace / output clearing */
+    DSA3D_K_PROJ_BWD_DQ = 6,    /* dq += doffsets . W */
+    DSA3D_K_PROJ_BWD_DW = 7,    /* split dW = doffsets^T . q */
+    DSA3D_K_SPLIT_SUM = 8,      /* fixed-order sum of split partials */
+    DSA3D_K_COLSUM = 9,         /* split column sums for dbias */
+    DSA3D_K_GEOMETRY = 10       /* test hook */
+} dsa3d_kernel;
+
+typedef struct dsa3d_launch_log {
+    int32_t capacity;  /* entries available in kernel[], start[] and stop[] */
+    int32_t count;     /* entries used; the library increments it */
+    int32_t* kernel;   /* dsa3d_kernel of each entry */
+    void** start;      /* hipEvent_t handles created by the caller with timing */
+    void** stop;       /* enabled; recorded on the launch's stream */
+} dsa3d_launch_log;
+
+/* While `log` is set on the calling host thread, every kernel that a libdsa3d
+ * call made on this thread launches is bracketed by hipEventRecord(start[i])
+ * and hipEventRecord(stop[i]) on the call's stream, for i = count, count+1, ...
+ * up to capacity (launches beyond it are not logged). NULL stops logging.
+ * The log is only read and written by calls on the same thread; it must stay
+ * valid while set. Returns DSA3D_OK, or DSA3D_ERR_INVALID_ARG for a log with
+ * capacity > 0 and a NULL array. */
+int dsa3d_set_launch_log(dsa3d_launch_log* log);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA3D_H */

@@ -1,0 +1,145 @@
+"""The C ABI of libdsa3d on the host: exports, validation and workspace sizing.
+
+No kernel is launched here; these run without a GPU.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import deformable_local_attention_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa3d.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(dsa3d_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    declared = _declared_functions()
+    assert len(declared) == 11, declared
+    out = subprocess.run(["nm", "-D", "--defined-only", dsa.library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (dsa3d_\w+)", out))
+    assert set(declared) <= exported, set(declared) - exported
+    assert set(dsa.EXPORTS) == set(declared)
+    L = dsa.lib()
+    for name in declared:
+        assert getattr(L, name) is not None
+
+
+def test_descriptor_layout_matches_header():
+    # int64 x4, int32 x10, float, int32 -> 80 bytes with 8-byte alignment
+    import ctypes
+    assert ctypes.sizeof(dsa.Desc) == 80
+    fields = [f[0] for f in dsa.Desc._fields_]
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct dsa3d_desc"):text.index("} dsa3d_desc;")]
+    in_header = re.findall(r"\b(\w+)\s*[,;]", re.sub(r"/\*.*?\*/", "", body, flags=re.S))
+    assert fields == in_header
+
+
+def _desc(**kw):
+    base = dict(B=1, T=4, H=8, W=8, heads=2, head_dim=32, window=(3, 3, 3), dilation=(1, 1, 1),
+                dtype=torch.float32)
+    base.update(kw)
+    return dsa.make_desc(base["B"], base["T"], base["H"], base["W"], base["heads"], base["head_dim"],
+                         base["window"], base["dilation"], base["dtype"])
+
+
+OK, INVALID, UNSUPPORTED = 0, -1, -2
+
+
+@pytest.mark.parametrize("kw,expect", [
+    ({}, OK),
+    ({"window": (3, 5, 5)}, OK),
+    ({"window": (1, 1, 1)}, OK),
+    ({"dtype": torch.bfloat16, "head_dim": 128, "heads": 24}, OK),
+    ({"head_dim": 8}, OK), ({"head_dim": 256}, OK),
+    ({"window": (2, 3, 3)}, INVALID),        # even window
+    ({"window": (3, 3, 0)}, INVALID),
+    ({"dilation": (0, 1, 1)}, INVALID),
+    ({"B": 0}, INVALID), ({"T": -1}, INVALID),
+    ({"heads": 0}, INVALID),
+    ({"head_dim": 48}, UNSUPPORTED),         # not a power of two
+    ({"head_dim": 512}, UNSUPPORTED),
+    ({"head_dim": 4}, UNSUPPORTED),
+    ({"dtype": torch.float16}, UNSUPPORTED),
+    ({"window": (11, 11, 11)}, UNSUPPORTED), # P = 1331 > 1024
+    ({"B": 1, "T": 2048, "H": 2048, "W": 1024}, INVALID),  # 2^32 tokens
+])
+def test_validate(kw, expect):
+    assert dsa.dsa3d_validate(_desc(**kw)) == expect
+
+
+def test_validate_rejects_p_mismatch_and_bad_flags():
+    d = _desc()
+    d.P = 26
+    assert dsa.dsa3d_validate(d) == INVALID
+    d = _desc()
+    d.deterministic = 2
+    assert dsa.dsa3d_validate(d) == INVALID
+    d = _desc()
+    d.scale = -1.0
+    assert dsa.dsa3d_validate(d) == INVALID
+    d = _desc()
+    d.scale = float("nan")
+    assert dsa.dsa3d_validate(d) == INVALID
+
+
+def test_workspace_sizes():
+    # float32 fast mode accumulates straight into dk/dv: no workspace
+    d = _desc()
+    assert dsa.dsa3d_workspace_size(d, dsa.WS_BACKWARD) == 0
+    assert dsa.dsa3d_workspace_size(d, dsa.WS_FORWARD) == 0
+    d.deterministic = 1
+    per_head = 2 * 256 * 32 * 8
+    assert dsa.dsa3d_workspace_min(d, dsa.WS_BACKWARD) == per_head
+    assert dsa.dsa3d_workspace_size(d, dsa.WS_BACKWARD) == 2 * per_head
+    # 1080p, 24 x 128, deterministic: one head of int64 dK/dV accumulators = 4 GiB - a bit;
+    # the recommended size caps one pass at 8 GiB
+    big = dsa.make_desc(1, 256, 68, 120, 24, 128, (3, 5, 5), dtype=torch.bfloat16, deterministic=True)
+    ph = 2 * 256 * 68 * 120 * 128 * 8
+    assert dsa.dsa3d_workspace_min(big, dsa.WS_BACKWARD) == ph
+    assert dsa.dsa3d_workspace_size(big, dsa.WS_BACKWARD) == (8 << 30) // ph * ph
+    fast = dsa.make_desc(1, 256, 68, 120, 24, 128, (3, 5, 5), dtype=torch.bfloat16)
+    assert dsa.dsa3d_workspace_min(fast, dsa.WS_BACKWARD) == ph // 2
+    assert dsa.dsa3d_workspace_size(dsa.make_desc(1, 1, 1, 1, 1, 8, (1, 1, 1), dtype=torch.bfloat16),
+                                    dsa.WS_PROJ_BACKWARD) > 0
+    bad = _desc(window=(2, 2, 2))
+    assert dsa.dsa3d_workspace_size(bad, dsa.WS_BACKWARD) == 0
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert dsa.dsa3d_status_string(s)
+    assert dsa.dsa3d_status_string(-99) == "unknown status"
+    assert dsa.dsa3d_version() >= 100
+
+
+def test_binding_has_no_cpu_fallback(monkeypatch, tmp_path):
+    # a missing library is an error, never a silent substitute
+    import importlib
+    monkeypatch.setenv("DSA3D_LIBRARY", str(tmp_path / "missing.so"))
+    mod = importlib.reload(dsa)
+    try:
+        with pytest.raises(ImportError):
+            mod.lib()
+    finally:
+        monkeypatch.delenv("DSA3D_LIBRARY")
+        importlib.reload(dsa)
+
+
+def test_product_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "deformable_local_attention_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower() or f == "synth.py" and "import oracle" not in text, f

@@ -1,0 +1,310 @@
+"""GPU parity: libdsa3d on an MI355X against the CPU oracle, element by element.
+
+Acceptance: sample corners bit-exact; float32 runs max |err| <= 1e-4 on every
+output; bf16 runs ||gpu - oracle|| / ||oracle|| <= 1e-2 per output tensor
+(lse, always float32, within 1e-3 absolute), with the oracle fed the same bf16
+values widened exactly. Small grids are checked whole; the full-size
+workloads on sampled queries and key tokens, in the same launch configuration
+as the benchmark.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import deformable_local_attention_amd as dsa
+from deformable_local_attention_amd import synth
+from deformable_local_attention_amd.chain import Chain
+from gpu_helpers import (gather, oracle_dkdv_at_keys, oracle_queries, rel_l2, sample_queries, to_np, to_np32)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+F32_TOL = 1e-4
+BF16_TOL = 1e-2
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _wl(name="case", B=1, T=3, H=4, W=5, heads=2, d=32, window=(3, 3, 3), dil=(1, 1, 1), dtype="f32",
+        sigma=1.0, backward=True, det=False):
+    return synth.Workload(name, B, T, H, W, heads, d, window, dil, dtype, "direct", offset_sigma=sigma,
+                          backward=backward, deterministic=det)
+
+
+def _check(name, gpu, ref, dtype, tol_f32=F32_TOL, tol_bf16=BF16_TOL):
+    if dtype == "f32":
+        err = float(np.abs(gpu - ref).max()) if gpu.size else 0.0
+        assert err <= tol_f32, f"{name}: max abs err {err:.3e} > {tol_f32}"
+    else:
+        err = rel_l2(gpu, ref)
+        assert err <= tol_bf16, f"{name}: rel-L2 err {err:.3e} > {tol_bf16}"
+    return err
+
+
+def _run_whole(wl, x, det=None, ws_bytes=None):
+    """Run the chain on the GPU and the oracle on the whole grid; compare all."""
+    say(f"[parity] {synth.describe(wl)} det={det}")
+    xd = {k: v.to(DEV) for k, v in x.items()}
+    ch = Chain(wl, xd, bwd_workspace_bytes=ws_bytes, deterministic=det)
+    ch.run()
+    torch.cuda.synchronize()
+    off = to_np32(ch.offsets)
+    o, lse = oracle.forward(to_np(x["q"]), to_np(x["k"]), to_np(x["v"]), off, wl.window, wl.dilation)
+    _check("o", to_np(ch.out), o, wl.dtype)
+    lerr = float(np.abs(to_np(ch.lse) - lse).max())
+    assert lerr <= (F32_TOL if wl.dtype == "f32" else 1e-3), f"lse err {lerr}"
+    if wl.backward:
+        dq, dk, dv, doff = oracle.backward(to_np(x["q"]), to_np(x["k"]), to_np(x["v"]), off, to_np(x["dout"]),
+                                           wl.window, wl.dilation)
+        _check("dq", to_np(ch.dq), dq, wl.dtype)
+        _check("dk", to_np(ch.dk), dk, wl.dtype)
+        _check("dv", to_np(ch.dv), dv, wl.dtype)
+        _check("doff", to_np(ch.doff), doff, wl.dtype)
+    return ch
+
+
+# ---------------------------------------------------------------------------
+# whole-grid parity on small and ragged grids
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("det", [False, True])
+def test_tiny_f32_workload(det):
+    wl = synth.WORKLOADS["tiny-f32"]
+    _run_whole(wl, synth.make_inputs(wl, "cpu"), det=det)
+
+
+CASES = {
+    "f32-ragged-b2-h3-d16": dict(B=2, T=3, H=5, W=7, heads=3, d=16, sigma=1.5),
+    "bf16-ragged-p75-d128": dict(T=5, H=6, W=9, heads=2, d=128, window=(3, 5, 5), sigma=2.0, dtype="bf16"),
+    "f32-p1-d8": dict(T=4, H=5, W=6, heads=2, d=8, window=(1, 1, 1), sigma=0.7),
+    "f32-d256-dil": dict(T=2, H=3, W=4, heads=1, d=256, window=(3, 3, 3), dil=(2, 1, 3), sigma=1.0),
+    "bf16-d64-513": dict(T=4, H=7, W=6, heads=3, d=64, window=(5, 1, 3), dil=(1, 2, 2), sigma=0.3, dtype="bf16"),
+    "bf16-d32-wide": dict(T=3, H=9, W=11, heads=2, d=32, window=(3, 7, 7), sigma=3.0, dtype="bf16"),
+    "f32-single-token": dict(T=1, H=1, W=1, heads=2, d=32, sigma=0.4),
+    "f32-window-wider-than-grid": dict(T=2, H=2, W=3, heads=1, d=64, window=(5, 5, 7), sigma=0.8),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+@pytest.mark.parametrize("det", [False, True])
+def test_small_grids(name, det):
+    wl = _wl(name, **CASES[name])
+    _run_whole(wl, synth.make_inputs(wl, "cpu", seed=7), det=det)
+
+
+@pytest.mark.parametrize("fill", ["zero", "integer", "huge", "nan", "inf", "beyond2p30", "tiny_negative"])
+def test_special_offsets(fill):
+    wl = _wl("special-" + fill, T=3, H=4, W=5, heads=2, d=32, sigma=1.0)
+    x = synth.make_inputs(wl, "cpu", seed=11)
+    off = x["offsets"]
+    g = torch.Generator().manual_seed(5)
+    if fill == "zero":
+        off.zero_()
+    elif fill == "integer":
+        off.copy_(torch.randint(-3, 4, off.shape, generator=g).float())
+    elif fill == "huge":
+        off.fill_(1.0e6)
+    elif fill == "nan":
+        off[..., ::2, :] = float("nan")
+    elif fill == "inf":
+        off[..., 1::3, 0] = float("inf")
+        off[..., 2::3, 2] = -float("inf")
+    elif fill == "beyond2p30":
+        off[..., ::2, 1] = 3.0e9
+    elif fill == "tiny_negative":
+        off.fill_(-1e-9)
+        off[..., 1::2, :] = 1e-9
+    _run_whole(wl, x, det=False)
+    _check_geometry(wl, x["offsets"])
+
+
+def _check_geometry(wl, off_cpu):
+    desc = dsa.desc_like(torch.empty((wl.B, wl.T, wl.H, wl.W, wl.heads, wl.head_dim), dtype=wl.torch_dtype),
+                         wl.window, wl.dilation)
+    offd = off_cpu.to(DEV)
+    base = torch.empty(offd.shape, dtype=torch.int32, device=DEV)
+    frac = torch.empty(offd.shape, dtype=torch.float32, device=DEV)
+    dsa.dsa3d_debug_geometry(desc, offd, base, frac)
+    torch.cuda.synchronize()
+    ob, of = oracle.geometry(to_np32(off_cpu), wl.window, wl.dilation)
+    assert np.array_equal(base.cpu().numpy(), ob), "sample base corners differ"
+    assert np.array_equal(frac.cpu().numpy().view(np.int32), of.view(np.int32)), "sample fractions differ"
+
+
+@pytest.mark.parametrize("name", ["tiny-f32", "bf16-ragged-p75-d128", "bf16-d64-513"])
+def test_geometry_is_bit_exact(name):
+    wl = synth.WORKLOADS["tiny-f32"] if name == "tiny-f32" else _wl(name, **CASES[name])
+    say(f"[geometry] {synth.describe(wl)}")
+    _check_geometry(wl, synth.make_inputs(wl, "cpu", seed=13)["offsets"])
+
+
+# ---------------------------------------------------------------------------
+# determinism of the K/V gradients
+# ---------------------------------------------------------------------------
+
+def test_deterministic_mode_is_bitwise_reproducible_across_runs_and_pass_splits():
+    wl = _wl("det-p75", T=6, H=12, W=20, heads=4, d=128, window=(3, 5, 5), sigma=2.0, dtype="bf16", det=True)
+    say(f"[determinism] {synth.describe(wl)}")
+    x = {k: v.to(DEV) for k, v in synth.make_inputs(wl, "cpu", seed=17).items()}
+    desc = dsa.desc_like(x["q"], wl.window, wl.dilation, 0.0, True)
+    full = dsa.dsa3d_workspace_size(desc, dsa.WS_BACKWARD)
+    one = dsa.dsa3d_workspace_min(desc, dsa.WS_BACKWARD)
+    assert full == 4 * one
+    outs = []
+    for ws in (full, full, one, 3 * one):
+        ch = Chain(wl, x, bwd_workspace_bytes=ws)
+        ch.run()
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (ch.out, ch.lse, ch.dq, ch.dk, ch.dv, ch.doff)])
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
+# ---------------------------------------------------------------------------
+# offset projection
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_projection_forward_and_backward(dtype):
+    wl = synth.Workload("proj-" + dtype, 1, 3, 10, 13, 3, 32, (3, 3, 3), (1, 1, 1), dtype, "proj", backward=True)
+    say(f"[projection] {synth.describe(wl)}")
+    x = synth.make_inputs(wl, "cpu", seed=19)
+    x["proj_b"].normal_(0, 0.1, generator=torch.Generator().manual_seed(2))
+    xd = {k: v.to(DEV) for k, v in x.items()}
+    N, C, F = wl.tokens, wl.C, wl.F
+    off = dsa.offset_proj(xd["q"], xd["proj_w"], xd["proj_b"], wl.window)
+    g = torch.randn(off.shape, generator=torch.Generator().manual_seed(3)).to(wl.torch_dtype)
+    dq0 = torch.randn(x["q"].shape, generator=torch.Generator().manual_seed(4)).to(wl.torch_dtype)
+    dq = dq0.to(DEV).clone()
+    dw, db = dsa.offset_proj_backward(xd["q"], xd["proj_w"], g.to(DEV), dq, wl.window)
+    torch.cuda.synchronize()
+    q2 = to_np(x["q"]).reshape(N, C)
+    ref = oracle.offset_proj(q2, to_np(x["proj_w"]), to_np(x["proj_b"]))
+    tol = 1e-4 if dtype == "f32" else BF16_TOL
+    _check("offsets", to_np(off).reshape(N, F), ref, dtype, tol_f32=1e-4)
+    add, dw_ref, db_ref = oracle.offset_proj_backward(q2, to_np(x["proj_w"]), to_np(g).reshape(N, F))
+    _check("dq_accum", to_np(dq).reshape(N, C), to_np(dq0).reshape(N, C) + add, dtype)
+    # dW and db are float32 sums of exactly widened inputs: tight for both dtypes
+    assert rel_l2(to_np(dw), dw_ref) <= 1e-5, rel_l2(to_np(dw), dw_ref)
+    assert rel_l2(to_np(db), db_ref) <= 1e-5
+    assert tol > 0
+
+
+# ---------------------------------------------------------------------------
+# the named workloads: small one whole, full-size ones sampled
+# ---------------------------------------------------------------------------
+
+def test_small_bf16_projection_workload_whole():
+    wl = synth.WORKLOADS["small-bf16-proj"]
+    x = synth.make_inputs(wl, "cpu")
+    ch = _run_whole(wl, x)
+    N = wl.tokens
+    ref = oracle.offset_proj(to_np(x["q"]).reshape(N, wl.C), to_np(x["proj_w"]), to_np(x["proj_b"]))
+    _check("offsets", to_np(ch.offsets).reshape(N, wl.F), ref, "bf16")
+
+
+def _free():
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _sampled_attention_checks(wl, ch, xd, n_random, seed, dkdv_keys=0):
+    qs = sample_queries(wl, heads=[0, wl.heads - 1], n_random=n_random, seed=seed)
+    say(f"[sampled] {len(qs)} queries")
+    r = oracle_queries(wl, xd, ch.offsets, qs, dout=xd.get("dout") if wl.backward else None)
+    _check("o (sampled)", gather(ch.out, qs), r["o"], wl.dtype)
+    lerr = float(np.abs(gather(ch.lse.unsqueeze(-1), qs)[:, 0] - r["lse"]).max())
+    assert lerr <= 1e-3, lerr
+    if wl.backward:
+        _check("doff (sampled)", gather(ch.doff, qs), r["doff"], wl.dtype)
+        return qs, r
+    return qs, r
+
+
+@pytest.mark.slow
+def test_720p_dil2_workload_full_size_sampled():
+    wl = synth.WORKLOADS["720p-bf16-proj-dil2"]
+    say(f"[full] {synth.describe(wl)}")
+    xd = synth.make_inputs(wl, DEV)
+    ch = Chain(wl, xd)
+    # run the pieces so that the attention's dq can be checked before the projection adds to it
+    desc = ch.desc
+    dsa.dsa3d_offset_proj_forward(desc, xd["q"], xd["proj_w"], xd["proj_b"], ch.offsets)
+    dsa.dsa3d_forward(desc, xd["q"], xd["k"], xd["v"], ch.offsets, ch.out, ch.lse)
+    dsa.dsa3d_backward(desc, xd["q"], xd["k"], xd["v"], ch.offsets, ch.out, ch.lse, xd["dout"], ch.dq, ch.dk, ch.dv,
+                       ch.doff, ch.ws)
+    torch.cuda.synchronize()
+    dq_attn = ch.dq.clone()
+    dsa.dsa3d_offset_proj_backward(desc, xd["q"], xd["proj_w"], ch.doff, ch.dq, ch.dw, ch.db, ch.pws)
+    torch.cuda.synchronize()
+    N, C, F = wl.tokens, wl.C, wl.F
+    rows = np.random.default_rng(0).choice(N, 512, replace=False)
+    q2 = xd["q"].view(N, C)
+    ref = oracle.offset_proj(to_np(q2[rows]), to_np(xd["proj_w"]), to_np(xd["proj_b"]))
+    _check("offsets rows", to_np(ch.offsets.view(N, F)[rows]), ref, "bf16")
+    qs, r = _sampled_attention_checks(wl, ch, xd, n_random=96, seed=1)
+    _check("dq_attn (sampled)", gather(dq_attn, qs), r["dq"], "bf16")
+    keys = sample_queries(wl, heads=[0, wl.heads - 1], n_random=4, seed=2, faces=0)[:12]
+    kk, vv = oracle_dkdv_at_keys(wl, xd, ch.offsets, xd["dout"], keys)
+    _check("dk (keys)", gather(ch.dk, keys), kk, "bf16")
+    _check("dv (keys)", gather(ch.dv, keys), vv, "bf16")
+    # projection backward on the GPU's doffsets (its input)
+    g = to_np(ch.doff.view(N, F))
+    add = g[rows] @ to_np(xd["proj_w"])
+    _check("dq total rows", to_np(ch.dq.view(N, C)[rows]), to_np(dq_attn.view(N, C)[rows]) + add, "bf16")
+    cols = np.random.default_rng(1).choice(C, 64, replace=False)
+    dw_ref = g.T @ to_np(q2[:, torch.tensor(cols)])
+    assert rel_l2(to_np(ch.dw)[:, cols], dw_ref) <= 1e-5
+    assert rel_l2(to_np(ch.db), g.sum(0)) <= 1e-5
+    del ch, xd
+    _free()
+
+
+@pytest.mark.slow
+def test_1080p_projection_workload_full_size_sampled():
+    wl = synth.WORKLOADS["1080p-bf16-proj"]
+    say(f"[full] {synth.describe(wl)}")
+    xd = synth.make_inputs(wl, DEV)
+    ch = Chain(wl, xd)
+    ch.run()
+    torch.cuda.synchronize()
+    N, C, F = wl.tokens, wl.C, wl.F
+    rows = np.random.default_rng(0).choice(N, 256, replace=False)
+    ref = oracle.offset_proj(to_np(xd["q"].view(N, C)[rows]), to_np(xd["proj_w"]), to_np(xd["proj_b"]))
+    _check("offsets rows", to_np(ch.offsets.view(N, F)[rows]), ref, "bf16")
+    _sampled_attention_checks(wl, ch, xd, n_random=64, seed=3)
+    del ch, xd
+    _free()
+
+
+@pytest.mark.slow
+def test_1080p_p75_deterministic_workload_full_size_sampled():
+    """The benchmark's workload and launch configuration (default workspace)."""
+    wl = synth.WORKLOADS[synth.HEADLINE]
+    say(f"[full] {synth.describe(wl)}")
+    xd = synth.make_inputs(wl, DEV)
+    ch = Chain(wl, xd)
+    ch.run()
+    torch.cuda.synchronize()
+    qs, r = _sampled_attention_checks(wl, ch, xd, n_random=64, seed=5)
+    _check("dq (sampled)", gather(ch.dq, qs), r["dq"], "bf16")
+    keys = sample_queries(wl, heads=[0, wl.heads - 1], n_random=3, seed=6, faces=0)[:10]
+    kk, vv = oracle_dkdv_at_keys(wl, xd, ch.offsets, xd["dout"], keys)
+    _check("dk (keys)", gather(ch.dk, keys), kk, "bf16")
+    _check("dv (keys)", gather(ch.dv, keys), vv, "bf16")
+    # bitwise reproducibility of the whole chain at full size
+    ref = [t.clone() for t in (ch.dk, ch.dv)]
+    ch.run()
+    torch.cuda.synchronize()
+    assert torch.equal(ref[0].view(torch.int16), ch.dk.view(torch.int16))
+    assert torch.equal(ref[1].view(torch.int16), ch.dv.view(torch.int16))
+    del ch, xd, ref
+    _free()
