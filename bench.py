@@ -42,20 +42,26 @@ def log(*a):
 
 
 def algorithmic(wl):
-    """Per (token, head): algorithmic bytes and flops of the forward and backward.
+    """Algorithmic bytes and flops per (token, head), each tensor read or
+    written once (sampled key/value rows are never counted: they are the
+    gathers the fused kernels exist to avoid materialising).
 
-    bytes: forward reads q, k, v (3d elements) and offsets (3P) and writes o
-    (d) and lse (4 B); backward reads q, k, v, o, dO (5d), offsets (3P) and
-    lse (4 B) and writes dq, dk, dv (3d) and doffsets (3P).
-    flops: forward 32*d*P (per sample: 8 corner dot products of length d
-    weighted into the logit, 8 weighted row updates of o); backward 80*d*P.
+    forward:   reads q, k, v (3d elements) and the offsets (3P), writes o (d)
+               and lse (4 B); flops 32*d*P (per sample: 8 corner dot products
+               of length d weighted into the logit, 8 weighted row updates).
+    bwd_query: reads q, k, v, o, dO (5d), offsets (3P) and lse (4 B), writes
+               dq (d) and doffsets (3P).
+    bwd_key:   reads q and dO (2d), writes dk and dv (2d).
+    The whole backward is then 8d + 6P elements + 4 B, flops 80*d*P.
     """
     s = 4 if wl.dtype == "f32" else 2
     d, P = wl.head_dim, wl.P
     return {
+        "forward": 4 * d * s + 3 * P * s + 4,
+        "bwd_query": 6 * d * s + 6 * P * s + 4,
+        "bwd_key": 4 * d * s,
         "fwd_bytes": 4 * d * s + 3 * P * s + 4,
         "bwd_bytes": 8 * d * s + 6 * P * s + 4,
-        "proj_fwd_bytes_per_token": (wl.C + wl.F) * s,
         "fwd_flops": 32 * d * P,
         "bwd_flops": 80 * d * P,
     }
@@ -206,28 +212,23 @@ def main():
         log(f"[bench]   {k:14s} {v['launches']:4d} launches, mean {v['mean_ms']:.3f} ms, total {v['total_ms']:.1f} ms")
 
     alg = algorithmic(wl)
-    dom = max(per_kernel, key=lambda k: per_kernel[k]["total_ms"])
-    nheads_launch = wl.heads
-    if dom == "backward":
-        per_head = dsa.dsa3d_workspace_min(ch.desc, dsa.WS_BACKWARD)
-        nbytes = ch.ws.numel() if ch.ws is not None else 0
-        nheads_launch = wl.heads if per_head == 0 else min(wl.heads, nbytes // per_head)
-        unit_bytes, unit_flops = alg["bwd_bytes"], alg["bwd_flops"]
-    elif dom == "forward":
-        unit_bytes, unit_flops = alg["fwd_bytes"], alg["fwd_flops"]
-    else:
-        unit_bytes, unit_flops = 0, 0
-    units = wl.tokens * nheads_launch
+    attn = [k for k in per_kernel if k in ("forward", "bwd_query", "bwd_key")]
+    dom = max(attn, key=lambda k: per_kernel[k]["total_ms"])
+    # the backward runs in passes over ranges of heads: a launch covers, on
+    # average, (all (token, head) units of the timed steps) / (its launches)
+    units = wl.tokens * wl.heads * args.steps / per_kernel[dom]["launches"]
     mean_s = per_kernel[dom]["mean_ms"] / 1e3
+    unit_bytes = alg[dom]
     achieved_gbs = unit_bytes * units / mean_s / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved_gbs, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 5), "traffic": None,
                 "launch_ms": round(per_kernel[dom]["mean_ms"], 3), "units_per_launch": units,
                 "bytes_per_unit": unit_bytes}
-    roofline_alu = {"bound": "alu", "kernel": dom,
-                    "achieved": round(unit_flops * units / mean_s / 1e12, 3), "peak": VALU_F32_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(unit_flops * units / mean_s / 1e12 / VALU_F32_PEAK_TFLOPS, 5),
-                    "flops_per_unit": unit_flops}
+    step_flops = wl.tokens * wl.heads * (alg["fwd_flops"] + (alg["bwd_flops"] if wl.backward else 0))
+    roofline_alu = {"bound": "alu", "scope": "whole step",
+                    "achieved": round(step_flops / (ms_per_step / 1e3) / 1e12, 3), "peak": VALU_F32_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(step_flops / (ms_per_step / 1e3) / 1e12 / VALU_F32_PEAK_TFLOPS, 5),
+                    "flops_per_token": step_flops // wl.tokens}
 
     result = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,

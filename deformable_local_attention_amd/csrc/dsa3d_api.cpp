@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr size_t kBackwardPassCap = size_t(8) << 30;  // recommended cap on one backward pass's accumulators
+constexpr size_t kBackwardPassCap = size_t(16) << 30;  // recommended cap on one backward pass's workspace
 
 bool pow2_in(int32_t x, int32_t lo, int32_t hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
 
@@ -89,7 +89,7 @@ int dsa3d_validate(const dsa3d_desc* d) {
 size_t dsa3d_workspace_min(const dsa3d_desc* d, int kind) {
     if (dsa3d_validate(d) != DSA3D_OK) return 0;
     switch (kind) {
-        case DSA3D_WS_BACKWARD: return dsa3d::bwd_accumulator_bytes_per_head(*d);
+        case DSA3D_WS_BACKWARD: return dsa3d::bwd_workspace_bytes(*d, 1);
         case DSA3D_WS_PROJ_BACKWARD: return dsa3d::proj_bwd_workspace_bytes(*d);
         default: return 0;
     }
@@ -98,12 +98,10 @@ size_t dsa3d_workspace_min(const dsa3d_desc* d, int kind) {
 size_t dsa3d_workspace_size(const dsa3d_desc* d, int kind) {
     if (dsa3d_validate(d) != DSA3D_OK) return 0;
     if (kind == DSA3D_WS_BACKWARD) {
-        const size_t per_head = dsa3d::bwd_accumulator_bytes_per_head(*d);
-        if (per_head == 0) return 0;
-        size_t heads = kBackwardPassCap / per_head;
-        if (heads < 1) heads = 1;
-        if (heads > (size_t)d->heads) heads = d->heads;
-        return heads * per_head;
+        const size_t one = dsa3d::bwd_workspace_bytes(*d, 1);
+        if (one == 0) return 0;
+        const int64_t nh = dsa3d::bwd_heads_per_pass(*d, kBackwardPassCap);
+        return nh >= 1 ? dsa3d::bwd_workspace_bytes(*d, nh) : one;
     }
     return dsa3d_workspace_min(d, kind);
 }
@@ -131,11 +129,10 @@ int dsa3d_backward(const dsa3d_desc* d, const void* q, const void* k, const void
     int rc = dsa3d_validate(d);
     if (rc != DSA3D_OK) return rc;
     if ((rc = check_ptrs({q, k, v, offsets, out, lse, dout, dq, dk, dv, doffsets})) != DSA3D_OK) return rc;
-    const size_t need = dsa3d::bwd_accumulator_bytes_per_head(*d);
-    if (need > 0) {
-        if (workspace == nullptr || workspace_bytes < need) return DSA3D_ERR_WORKSPACE;
-        if (!aligned16(workspace)) return DSA3D_ERR_MISALIGNED;
-    }
+    const size_t need = dsa3d::bwd_workspace_bytes(*d, 1);
+    if (need == 0) return DSA3D_ERR_UNSUPPORTED;  // sample or cell numbers of one head exceed 32 bits
+    if (workspace == nullptr || workspace_bytes < need) return DSA3D_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return DSA3D_ERR_MISALIGNED;
     return hip_status(dsa3d::launch_backward(*d, q, k, v, offsets, out, lse, dout, dq, dk, dv, doffsets, workspace,
                                              workspace_bytes, static_cast<hipStream_t>(stream)));
 }

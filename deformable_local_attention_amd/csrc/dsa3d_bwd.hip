@@ -1,0 +1,548 @@
+// dsa3d_bwd.hip -- 3D-DSA backward for gfx950, without atomics on the gradients.
+//
+// The gradient of one sample p of query x (head eta) reaches the query side
+// (dq, doffsets) and the eight key/value rows at the corners of its trilinear
+// cell. Pushing those corner contributions with atomics costs 16*head_dim
+// atomic adds per sample; instead the backward pulls them per key:
+//
+//  1. query kernel (one task = one (query, head), as in the forward): recompute
+//     the logits, a_p = exp(s_p - lse), da_p = sum_c w_c <dO, V[c]>,
+//     ds_p = a_p (da_p - <dO, o>); write dq = scale sum_p ds_p sum_c w_c K[c]
+//     and doffsets; store per sample a 32-byte record (scale*ds_p, a_p, the
+//     fraction f, the query token) and count it in the bucket of its base cell
+//     floor(pos) -- one 32-bit atomic per sample, whose return value is the
+//     sample's slot in that bucket;
+//  2. an exclusive scan turns the bucket counts into bucket starts;
+//  3. index kernel: write each sample's number into its slot (a CSR list of
+//     the samples of every base cell);
+//  4. deterministic mode only: sort every bucket by sample number, so that the
+//     summation order below does not depend on the order the atomics of
+//     step 1 landed in;
+//  5. key kernel (one task = one (key token, head)): the samples whose cell
+//     has key y as corner c are exactly those with base cell y - c, so the key
+//     walks the 8 buckets y - c and accumulates
+//        dK[y] += w_c * scale * ds_p * q_x,   dV[y] += w_c * a_p * dO_x
+//     in float32 registers, then writes its rows once.
+// Base cells run over the grid extended by one cell on the low side of each
+// axis (a cell with base -1 still has its upper corner at 0), per (batch,
+// head). A pass covers a range of heads whose index fits in the workspace;
+// sample and cell numbers are 32-bit within a pass.
+#include "dsa3d_attn_common.h"
+#include "dsa3d_internal.h"
+
+namespace dsa3d {
+
+constexpr uint32_t kNoCell = 0xffffffffu;
+constexpr int kScanThreads = 256;
+constexpr int kScanItems = 16;
+constexpr uint32_t kScanChunk = kScanThreads * kScanItems;
+constexpr uint32_t kWaveSortMax = 1024;    // buckets up to this size: one wave, in LDS
+constexpr uint32_t kBlockSortMax = 16384;  // up to this size: one 1024-thread block, in LDS
+constexpr int kSortBucketsPerBlock = 64;
+
+// Per-sample record written by the query kernel and read by the key kernel.
+struct __attribute__((aligned(16))) SampleRec {
+    float ck;       // scale * ds_p
+    float cv;       // a_p
+    float ft, fh, fw;
+    uint32_t qtok;  // query token index in [B,T,H,W]
+    uint32_t rank;  // slot within the bucket
+    uint32_t cell;  // base cell, or kNoCell when no corner is in the grid
+};
+
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* off;
+    const void* o;
+    const void* dout;
+    const float* lse;
+    void* dq;
+    void* doff;
+    void* dk;
+    void* dv;
+    uint32_t* cnt;    // [ncell] bucket counts
+    uint32_t* start;  // [ncell + 1] bucket starts
+    uint32_t* csr;    // [nsamp] sample numbers by bucket
+    SampleRec* rec;   // [nsamp]
+    TaskGrid g;
+    int32_t P;
+    float scale;
+    Window win;
+};
+
+__device__ __forceinline__ uint32_t cell_index(const TaskGrid& g, int64_t bh, int32_t t0, int32_t h0, int32_t w0) {
+    return (uint32_t)((((bh * (g.T + 1) + (t0 + 1)) * (g.H + 1) + (h0 + 1)) * (int64_t)(g.W + 1)) + (w0 + 1));
+}
+
+// ---------------------------------------------------------------------------
+// 1. query kernel
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ void __launch_bounds__(256) dsa3d_bwd_query_kernel(BwdArgs a) {
+    constexpr int L = D / 8;
+    const int groups = blockDim.x / L;
+    const int g = threadIdx.x / L;
+    const int li = threadIdx.x % L;
+    const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int64_t task = (int64_t)lb * groups + g;
+    if (task >= a.g.ntasks) return;  // no block-wide barrier below
+
+    int32_t b, eta, t, h, w;
+    int64_t tok;
+    task_coords(a.g, task, b, eta, t, h, w, tok);
+    const int64_t bh = (int64_t)b * a.g.nheads + (eta - a.g.head0);
+    const int64_t C = (int64_t)a.g.heads * D;
+    const int64_t row_off = (int64_t)eta * D + li * 8;
+    const T* Kb = reinterpret_cast<const T*>(a.k) + row_off;
+    const T* Vb = reinterpret_cast<const T*>(a.v) + row_off;
+    const T* zero = reinterpret_cast<const T*>(g_zero_row);
+    const int64_t offrow = (tok * a.g.heads + eta) * (int64_t)a.P * 3;
+    const T* offq = reinterpret_cast<const T*>(a.off) + offrow;
+    T* doffq = reinterpret_cast<T*>(a.doff) + offrow;
+    SampleRec* recq = a.rec + task * a.P;
+
+    Frag8<T> qf, gf, of;
+    qf.load(reinterpret_cast<const T*>(a.q) + tok * C + row_off);
+    gf.load(reinterpret_cast<const T*>(a.dout) + tok * C + row_off);
+    of.load(reinterpret_cast<const T*>(a.o) + tok * C + row_off);
+    const float Dsum = group_sum<L>(gf.dot(of, 0.0f));
+    const float lse = a.lse[tok * a.g.heads + eta];
+
+    float dq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < a.P; ++p) {
+        float dt, dh, dw;
+        load_offsets<T>(offq + p * 3, dt, dh, dw);
+        int32_t t0 = 0, h0 = 0, w0 = 0;
+        float ft = 0.f, fh = 0.f, fw = 0.f;
+        const bool inside = sample_geometry(a.win, t, h, w, p, dt, dh, dw, t0, h0, w0, ft, fh, fw);
+        Corners c;
+        make_corners(a.g, b, t0, h0, w0, ft, fh, fw, inside, c);
+        Frag8<T> kf[8], vf[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            kf[i].load(c.tok[i] >= 0 ? Kb + c.tok[i] * C : zero);
+            vf[i].load(c.tok[i] >= 0 ? Vb + c.tok[i] * C : zero);
+        }
+        float qk[8], dv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            qk[i] = kf[i].dot(qf, 0.0f);
+            dv[i] = vf[i].dot(gf, 0.0f);
+        }
+        // weighted sums: logit, dL/da, and the offset-derivative sums per axis
+        const float at[2] = {1.0f - ft, ft}, ah[2] = {1.0f - fh, fh}, aw[2] = {1.0f - fw, fw};
+        float r[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int ct = (i >> 2) & 1, ch = (i >> 1) & 1, cw = i & 1;
+            const float st = ct ? 1.f : -1.f, sh = ch ? 1.f : -1.f, sw = cw ? 1.f : -1.f;
+            const float gt = st * ah[ch] * aw[cw], gh = at[ct] * sh * aw[cw], gw = at[ct] * ah[ch] * sw;
+            // zero rows give zero dot products, so no validity test is needed here
+            r[0] = fmaf(c.w[i], qk[i], r[0]);
+            r[1] = fmaf(c.w[i], dv[i], r[1]);
+            r[2] = fmaf(gt, qk[i], r[2]);
+            r[3] = fmaf(gh, qk[i], r[3]);
+            r[4] = fmaf(gw, qk[i], r[4]);
+            r[5] = fmaf(gt, dv[i], r[5]);
+            r[6] = fmaf(gh, dv[i], r[6]);
+            r[7] = fmaf(gw, dv[i], r[7]);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = group_sum<L>(r[j]);
+        const float s = a.scale * r[0];
+        const float ap = __expf(s - lse);
+        const float ds = ap * (r[1] - Dsum);
+        const float ck = a.scale * ds;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kf[i].axpy(ck * c.w[i], dq);
+        if (li == 0) {
+            store_scalar<T>(doffq + p * 3 + 0, fmaf(ck, r[2], ap * r[5]));
+            store_scalar<T>(doffq + p * 3 + 1, fmaf(ck, r[3], ap * r[6]));
+            store_scalar<T>(doffq + p * 3 + 2, fmaf(ck, r[4], ap * r[7]));
+            const bool reaches = inside && t0 >= -1 && t0 < a.g.T && h0 >= -1 && h0 < a.g.H && w0 >= -1 &&
+                                 w0 < a.g.W;
+            uint32_t cell = kNoCell, rank = 0;
+            if (reaches) {
+                cell = cell_index(a.g, bh, t0, h0, w0);
+                rank = atomicAdd(a.cnt + cell, 1u);
+            }
+            uint4* dst = reinterpret_cast<uint4*>(recq + p);
+            dst[0] = make_uint4(__float_as_uint(ck), __float_as_uint(ap), __float_as_uint(ft), __float_as_uint(fh));
+            dst[1] = make_uint4(__float_as_uint(fw), (uint32_t)tok, rank, cell);
+        }
+    }
+    Frag8<T> dqf;
+    dqf.from_f32(dq);
+    dqf.store(reinterpret_cast<T*>(a.dq) + tok * C + row_off);
+}
+
+// ---------------------------------------------------------------------------
+// 2. exclusive scan of the bucket counts: start[i] = sum_{j<i} cnt[j],
+//    start[n] = total. Three kernels: chunk sums, a one-block scan of the chunk
+//    sums, and the chunk-local scans.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* lds, uint32_t& total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    uint32_t incl = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) lds[wid] = incl;
+    __syncthreads();
+    if (wid == 0) {
+        const uint32_t v = lane < nw ? lds[lane] : 0u;
+        uint32_t inc = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += y;
+        }
+        if (lane < nw) lds[lane] = inc - v;
+        if (lane == nw - 1) lds[nw] = inc;
+    }
+    __syncthreads();
+    const uint32_t excl = incl - x + lds[wid];
+    total = lds[nw];
+    __syncthreads();
+    return excl;
+}
+
+__global__ void __launch_bounds__(kScanThreads) dsa3d_scan_sums_kernel(const uint32_t* cnt, uint32_t n, uint32_t* bsum) {
+    __shared__ uint32_t lds[kScanThreads / 64 + 1];
+    const uint64_t i0 = (uint64_t)blockIdx.x * kScanChunk + (uint64_t)threadIdx.x * kScanItems;
+    uint32_t s = 0;
+#pragma unroll
+    for (int j = 0; j < kScanItems; ++j)
+        if (i0 + j < n) s += cnt[i0 + j];
+    uint32_t total;
+    (void)block_exclusive_scan(s, lds, total);
+    if (threadIdx.x == 0) bsum[blockIdx.x] = total;
+}
+
+__global__ void __launch_bounds__(1024) dsa3d_scan_top_kernel(uint32_t* bsum, uint32_t nb, uint32_t* start, uint32_t n) {
+    __shared__ uint32_t lds[1024 / 64 + 1];
+    uint32_t carry = 0;
+    for (uint32_t base = 0; base < nb; base += 1024) {
+        const uint32_t i = base + threadIdx.x;
+        const uint32_t x = i < nb ? bsum[i] : 0u;
+        uint32_t total;
+        const uint32_t e = block_exclusive_scan(x, lds, total);
+        if (i < nb) bsum[i] = carry + e;
+        carry += total;
+    }
+    if (threadIdx.x == 0) start[n] = carry;
+}
+
+__global__ void __launch_bounds__(kScanThreads) dsa3d_scan_apply_kernel(const uint32_t* cnt, uint32_t n,
+                                                                        const uint32_t* bsum, uint32_t* start) {
+    __shared__ uint32_t lds[kScanThreads / 64 + 1];
+    const uint64_t i0 = (uint64_t)blockIdx.x * kScanChunk + (uint64_t)threadIdx.x * kScanItems;
+    uint32_t x[kScanItems];
+    uint32_t s = 0;
+#pragma unroll
+    for (int j = 0; j < kScanItems; ++j) {
+        x[j] = i0 + j < n ? cnt[i0 + j] : 0u;
+        s += x[j];
+    }
+    uint32_t total;
+    uint32_t run = block_exclusive_scan(s, lds, total) + bsum[blockIdx.x];
+#pragma unroll
+    for (int j = 0; j < kScanItems; ++j) {
+        if (i0 + j < n) start[i0 + j] = run;
+        run += x[j];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. bucket index
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) dsa3d_bwd_index_kernel(const SampleRec* rec, uint64_t nsamp,
+                                                              const uint32_t* start, uint32_t* csr) {
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nsamp; i += (uint64_t)gridDim.x * blockDim.x) {
+        const uint2 rc = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint32_t*>(rec + i) + 6);  // rank, cell
+        if (rc.y != kNoCell) csr[start[rc.y] + rc.x] = (uint32_t)i;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 4. deterministic mode: sort every bucket ascending.
+//
+// Bitonic network in the form whose comparators all put the smaller key at
+// the lower index (a "flip" stage, then half-cleaners), so a bucket of n keys
+// sorts as if padded with +infinity up to a power of two while only the real
+// n entries are touched: a comparator whose upper index is >= n would leave
+// its pair unchanged and is skipped. The keys (sample numbers) are distinct.
+// ---------------------------------------------------------------------------
+template <typename Sync>
+__device__ __forceinline__ void bitonic_sort_u32(uint32_t* buf, uint32_t n, uint32_t tid, uint32_t nthr, Sync sync) {
+    uint64_t npad = 1;  // 64-bit: a bucket may hold up to 2^32 - 1 keys
+    while (npad < n) npad <<= 1;
+    const uint64_t pairs = npad / 2;
+    for (uint64_t k = 2; k <= npad; k <<= 1) {
+        const uint64_t half = k >> 1;
+        for (uint64_t i = tid; i < pairs; i += nthr) {
+            const uint64_t blk = (i / half) * k, off = i % half;
+            const uint64_t lo = blk + off, hi = blk + k - 1 - off;
+            if (hi < n) {
+                const uint32_t x = buf[lo], y = buf[hi];
+                if (x > y) { buf[lo] = y; buf[hi] = x; }
+            }
+        }
+        sync();
+        for (uint64_t j = half >> 1; j >= 1; j >>= 1) {
+            for (uint64_t i = tid; i < pairs; i += nthr) {
+                const uint64_t lo = (i / j) * 2 * j + (i % j), hi = lo + j;
+                if (hi < n) {
+                    const uint32_t x = buf[lo], y = buf[hi];
+                    if (x > y) { buf[lo] = y; buf[hi] = x; }
+                }
+            }
+            sync();
+        }
+    }
+}
+
+struct BlockSync {
+    __device__ __forceinline__ void operator()() const { __syncthreads(); }
+};
+
+// One wave per block; the block walks kSortBucketsPerBlock consecutive
+// buckets. Buckets larger than kWaveSortMax are queued in `large`
+// ([0] = count, [1..cap] = bucket numbers) for the next kernel.
+__global__ void __launch_bounds__(64) dsa3d_sort_small_kernel(const uint32_t* start, uint32_t ncell, uint32_t* csr,
+                                                              uint32_t* large, uint32_t large_cap) {
+    __shared__ uint32_t buf[kWaveSortMax];
+    const uint32_t c0 = blockIdx.x * kSortBucketsPerBlock;
+    const uint32_t c1 = min(ncell, c0 + kSortBucketsPerBlock);
+    for (uint32_t c = c0; c < c1; ++c) {
+        const uint32_t s = start[c], n = start[c + 1] - s;
+        if (n < 2) continue;
+        if (n > kWaveSortMax) {
+            if (threadIdx.x == 0) {
+                const uint32_t slot = atomicAdd(large, 1u);
+                if (slot < large_cap) large[1 + slot] = c;
+            }
+            continue;
+        }
+        for (uint32_t i = threadIdx.x; i < n; i += 64) buf[i] = csr[s + i];
+        __syncthreads();
+        bitonic_sort_u32(buf, n, threadIdx.x, 64, BlockSync());
+        for (uint32_t i = threadIdx.x; i < n; i += 64) csr[s + i] = buf[i];
+        __syncthreads();
+    }
+}
+
+// Buckets queued by the previous kernel: in LDS up to kBlockSortMax keys,
+// otherwise in place in global memory (same network; slow, but only a
+// pathological offset field puts that many samples into one cell).
+__global__ void __launch_bounds__(1024) dsa3d_sort_large_kernel(const uint32_t* start, uint32_t* csr,
+                                                                const uint32_t* large, uint32_t large_cap) {
+    __shared__ uint32_t buf[kBlockSortMax];
+    const uint32_t count = min(large[0], large_cap);
+    for (uint32_t item = blockIdx.x; item < count; item += gridDim.x) {
+        const uint32_t c = large[1 + item];
+        const uint32_t s = start[c], n = start[c + 1] - s;
+        if (n <= kBlockSortMax) {
+            for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) buf[i] = csr[s + i];
+            __syncthreads();
+            bitonic_sort_u32(buf, n, threadIdx.x, blockDim.x, BlockSync());
+            for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) csr[s + i] = buf[i];
+        } else {
+            bitonic_sort_u32(csr + s, n, threadIdx.x, blockDim.x, BlockSync());
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 5. key kernel
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ void __launch_bounds__(256) dsa3d_bwd_key_kernel(BwdArgs a) {
+    constexpr int L = D / 8;
+    const int groups = blockDim.x / L;
+    const int g = threadIdx.x / L;
+    const int li = threadIdx.x % L;
+    const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int64_t task = (int64_t)lb * groups + g;
+    if (task >= a.g.ntasks) return;
+
+    int32_t b, eta, t, h, w;
+    int64_t tok;
+    task_coords(a.g, task, b, eta, t, h, w, tok);
+    const int64_t bh = (int64_t)b * a.g.nheads + (eta - a.g.head0);
+    const int64_t C = (int64_t)a.g.heads * D;
+    const int64_t row_off = (int64_t)eta * D + li * 8;
+    const T* Qb = reinterpret_cast<const T*>(a.q) + row_off;
+    const T* Gb = reinterpret_cast<const T*>(a.dout) + row_off;
+
+    float ak[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float av[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int c = 0; c < 8; ++c) {
+        const int ct = (c >> 2) & 1, ch = (c >> 1) & 1, cw = c & 1;
+        const uint32_t cell = cell_index(a.g, bh, t - ct, h - ch, w - cw);
+        const uint32_t e1 = a.start[cell + 1];
+        for (uint32_t e = a.start[cell]; e < e1; ++e) {
+            const uint32_t sid = a.csr[e];
+            const uint4 r0 = *reinterpret_cast<const uint4*>(a.rec + sid);
+            const uint2 r1 = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint32_t*>(a.rec + sid) + 4);
+            const float ft = __uint_as_float(r0.z), fh = __uint_as_float(r0.w), fw = __uint_as_float(r1.x);
+            const float wt = (ct ? ft : 1.0f - ft) * (ch ? fh : 1.0f - fh) * (cw ? fw : 1.0f - fw);
+            const int64_t qrow = (int64_t)r1.y * C;
+            Frag8<T> qf, gf;
+            qf.load(Qb + qrow);
+            gf.load(Gb + qrow);
+            qf.axpy(__uint_as_float(r0.x) * wt, ak);
+            gf.axpy(__uint_as_float(r0.y) * wt, av);
+        }
+    }
+    Frag8<T> kf, vf;
+    kf.from_f32(ak);
+    vf.from_f32(av);
+    kf.store(reinterpret_cast<T*>(a.dk) + tok * C + row_off);
+    vf.store(reinterpret_cast<T*>(a.dv) + tok * C + row_off);
+}
+
+// ---------------------------------------------------------------------------
+// Host side: workspace layout and launch sequence
+// ---------------------------------------------------------------------------
+namespace {
+
+struct BwdLayout {
+    uint64_t ncell, nsamp, nscan, large_cap;
+    size_t off_cnt, off_start, off_bsum, off_large, off_rec, off_csr, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool bwd_layout(const dsa3d_desc& d, int64_t nh, BwdLayout& L) {
+    const uint64_t ntok = (uint64_t)(d.B * d.T * d.H * d.W);
+    const uint64_t cells_per_bh = (uint64_t)(d.T + 1) * (uint64_t)(d.H + 1) * (uint64_t)(d.W + 1);
+    L.ncell = (uint64_t)nh * (uint64_t)d.B * cells_per_bh;
+    L.nsamp = (uint64_t)nh * ntok * (uint64_t)d.P;
+    if (L.ncell + 1 >= (uint64_t(1) << 32) || L.nsamp >= (uint64_t(1) << 32)) return false;
+    L.nscan = (L.ncell + kScanChunk - 1) / kScanChunk;
+    L.large_cap = L.nsamp / (kWaveSortMax + 1) + 1;
+    size_t o = 0;
+    L.off_cnt = o;   o += align256(L.ncell * 4);
+    L.off_start = o; o += align256((L.ncell + 1) * 4);
+    L.off_bsum = o;  o += align256(L.nscan * 4 + 4);
+    L.off_large = o; o += align256((L.large_cap + 1) * 4);
+    L.off_rec = o;   o += align256(L.nsamp * sizeof(SampleRec));
+    L.off_csr = o;   o += align256(L.nsamp * 4);
+    L.total = o;
+    return true;
+}
+
+template <typename T, int D>
+hipError_t bwd_query_t(const BwdArgs& a, hipStream_t s) {
+    const int groups = 256 / (D / 8);
+    const int64_t nb = (a.g.ntasks + groups - 1) / groups;
+    LaunchScope ls(DSA3D_K_BWD_QUERY, s);
+    hipLaunchKernelGGL((dsa3d_bwd_query_kernel<T, D>), dim3((unsigned)nb), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+template <int D> hipError_t bwd_query_f32(const BwdArgs& a, hipStream_t s) { return bwd_query_t<float, D>(a, s); }
+template <int D> hipError_t bwd_query_bf16(const BwdArgs& a, hipStream_t s) { return bwd_query_t<bf16_t, D>(a, s); }
+
+template <typename T, int D>
+hipError_t bwd_key_t(const BwdArgs& a, hipStream_t s) {
+    const int groups = 256 / (D / 8);
+    const int64_t nb = (a.g.ntasks + groups - 1) / groups;
+    LaunchScope ls(DSA3D_K_BWD_KEY, s);
+    hipLaunchKernelGGL((dsa3d_bwd_key_kernel<T, D>), dim3((unsigned)nb), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+template <int D> hipError_t bwd_key_f32(const BwdArgs& a, hipStream_t s) { return bwd_key_t<float, D>(a, s); }
+template <int D> hipError_t bwd_key_bf16(const BwdArgs& a, hipStream_t s) { return bwd_key_t<bf16_t, D>(a, s); }
+
+}  // namespace
+
+size_t bwd_workspace_bytes(const dsa3d_desc& d, int64_t nheads) {
+    BwdLayout L;
+    if (nheads < 1 || !bwd_layout(d, nheads, L)) return 0;
+    return L.total;
+}
+
+int64_t bwd_heads_per_pass(const dsa3d_desc& d, size_t ws_bytes) {
+    int64_t lo = 0, hi = d.heads;  // largest nh in [1, heads] that fits, or 0
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) / 2;
+        const size_t need = bwd_workspace_bytes(d, mid);
+        if (need != 0 && need <= ws_bytes) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+hipError_t launch_backward(const dsa3d_desc& d, const void* q, const void* k, const void* v, const void* off,
+                           const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           void* doff, void* ws, size_t ws_bytes, hipStream_t s) {
+    const int64_t ntok = d.B * d.T * d.H * d.W;
+    if (ntok == 0) return hipSuccess;
+    const int64_t chunk = bwd_heads_per_pass(d, ws_bytes);
+    if (chunk < 1) return hipErrorInvalidValue;
+    const bool f32 = d.dtype == DSA3D_F32;
+    hipError_t e;
+    for (int64_t h0 = 0; h0 < d.heads; h0 += chunk) {
+        const int32_t nh = (int32_t)std::min<int64_t>(chunk, d.heads - h0);
+        BwdLayout L;
+        bwd_layout(d, nh, L);
+        char* base = static_cast<char*>(ws);
+        BwdArgs a{};
+        a.q = q; a.k = k; a.v = v; a.off = off; a.o = o; a.dout = dout; a.lse = lse;
+        a.dq = dq; a.doff = doff; a.dk = dk; a.dv = dv;
+        a.cnt = reinterpret_cast<uint32_t*>(base + L.off_cnt);
+        a.start = reinterpret_cast<uint32_t*>(base + L.off_start);
+        a.csr = reinterpret_cast<uint32_t*>(base + L.off_csr);
+        a.rec = reinterpret_cast<SampleRec*>(base + L.off_rec);
+        a.g = make_task_grid(d, (int32_t)h0, nh);
+        a.P = d.P;
+        a.scale = logit_scale(d);
+        a.win = make_window(d);
+        uint32_t* bsum = reinterpret_cast<uint32_t*>(base + L.off_bsum);
+        uint32_t* large = reinterpret_cast<uint32_t*>(base + L.off_large);
+        const uint32_t ncell = (uint32_t)L.ncell;
+
+        // counts and the large-bucket queue start at zero
+        if ((e = fill_zero(a.cnt, L.ncell * 4, s)) != hipSuccess) return e;
+        if ((e = fill_zero(large, 4, s)) != hipSuccess) return e;
+        if (f32) { DSA3D_DISPATCH_D_E(d.head_dim, bwd_query_f32, e, a, s); }
+        else { DSA3D_DISPATCH_D_E(d.head_dim, bwd_query_bf16, e, a, s); }
+        if (e != hipSuccess) return e;
+        {
+            LaunchScope ls(DSA3D_K_BWD_SCAN, s);
+            hipLaunchKernelGGL(dsa3d_scan_sums_kernel, dim3((unsigned)L.nscan), dim3(kScanThreads), 0, s, a.cnt, ncell,
+                               bsum);
+            hipLaunchKernelGGL(dsa3d_scan_top_kernel, dim3(1), dim3(1024), 0, s, bsum, (uint32_t)L.nscan, a.start, ncell);
+            hipLaunchKernelGGL(dsa3d_scan_apply_kernel, dim3((unsigned)L.nscan), dim3(kScanThreads), 0, s, a.cnt,
+                               ncell, bsum, a.start);
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        {
+            LaunchScope ls(DSA3D_K_BWD_INDEX, s);
+            hipLaunchKernelGGL(dsa3d_bwd_index_kernel, dim3(grid_for((int64_t)L.nsamp, 256, 1 << 16)), dim3(256), 0, s,
+                               a.rec, (uint64_t)L.nsamp, a.start, a.csr);
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (d.deterministic) {
+            LaunchScope ls(DSA3D_K_BWD_SORT, s);
+            const unsigned nblk = (unsigned)((L.ncell + kSortBucketsPerBlock - 1) / kSortBucketsPerBlock);
+            hipLaunchKernelGGL(dsa3d_sort_small_kernel, dim3(nblk), dim3(64), 0, s, a.start, ncell, a.csr, large,
+                               (uint32_t)L.large_cap);
+            hipLaunchKernelGGL(dsa3d_sort_large_kernel, dim3(256), dim3(1024), 0, s, a.start, a.csr, large,
+                               (uint32_t)L.large_cap);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        if (f32) { DSA3D_DISPATCH_D_E(d.head_dim, bwd_key_f32, e, a, s); }
+        else { DSA3D_DISPATCH_D_E(d.head_dim, bwd_key_bf16, e, a, s); }
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace dsa3d

@@ -151,18 +151,4 @@ __device__ __forceinline__ bool sample_geometry(const Window& win, int32_t t, in
     return true;
 }
 
-// 64-bit fixed point with 2^-32 resolution for the deterministic K/V-gradient
-// sums: integer addition is associative, so the total is independent of the
-// order in which the atomics land. Each term is clamped to |x| <= 2^18 so that
-// x * 2^32 stays below 2^51, where the round-to-nearest trick below is exact.
-__device__ __forceinline__ unsigned long long to_fixed(float x) {
-    x = fminf(fmaxf(x, -262144.0f), 262144.0f);
-    const double magic = 6755399441055744.0;  // 1.5 * 2^52
-    const double d = fma((double)x, 4294967296.0, magic);
-    return (unsigned long long)(__double_as_longlong(d) - 0x4338000000000000LL);
-}
-__device__ __forceinline__ float from_fixed(unsigned long long v) {
-    return (float)((double)(long long)v * (1.0 / 4294967296.0));
-}
-
 }  // namespace dsa3d

@@ -36,8 +36,46 @@ private:
     int slot_;
 };
 
+// Instantiates FN<D>(args...) for the supported head dimensions.
+#define DSA3D_DISPATCH_D(D_, FN, ...)                 \
+    switch (D_) {                                    \
+        case 8: return FN<8>(__VA_ARGS__);           \
+        case 16: return FN<16>(__VA_ARGS__);         \
+        case 32: return FN<32>(__VA_ARGS__);         \
+        case 64: return FN<64>(__VA_ARGS__);         \
+        case 128: return FN<128>(__VA_ARGS__);       \
+        case 256: return FN<256>(__VA_ARGS__);       \
+        default: return hipErrorInvalidValue;        \
+    }
+
+// Same, assigning FN<D>(args...) to E_ instead of returning it.
+#define DSA3D_DISPATCH_D_E(D_, FN, E_, ...)                  \
+    switch (D_) {                                           \
+        case 8: E_ = FN<8>(__VA_ARGS__); break;             \
+        case 16: E_ = FN<16>(__VA_ARGS__); break;           \
+        case 32: E_ = FN<32>(__VA_ARGS__); break;           \
+        case 64: E_ = FN<64>(__VA_ARGS__); break;           \
+        case 128: E_ = FN<128>(__VA_ARGS__); break;         \
+        case 256: E_ = FN<256>(__VA_ARGS__); break;         \
+        default: E_ = hipErrorInvalidValue; break;          \
+    }
+
+struct Window;
+struct TaskGrid;
+Window make_window(const dsa3d_desc& d);
+TaskGrid make_task_grid(const dsa3d_desc& d, int32_t head0, int32_t nheads);
+float logit_scale(const dsa3d_desc& d);
+unsigned grid_for(int64_t n, int threads, int64_t cap = 1 << 20);
+hipError_t fill_zero(void* p, size_t bytes, hipStream_t s);
+
 int fwd_groups_per_block(int head_dim, int P);
-size_t bwd_accumulator_bytes_per_head(const dsa3d_desc& d);
+
+// Backward workspace: bytes for a pass over `nheads` heads (0 if such a pass
+// cannot be indexed with 32-bit sample and cell numbers) and the largest head
+// count per pass that fits in `ws_bytes`.
+size_t bwd_workspace_bytes(const dsa3d_desc& d, int64_t nheads);
+int64_t bwd_heads_per_pass(const dsa3d_desc& d, size_t ws_bytes);
+
 void proj_bwd_splits(const dsa3d_desc& d, int& dw_splits, int& db_splits);
 size_t proj_bwd_workspace_bytes(const dsa3d_desc& d);
 

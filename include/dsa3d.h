@@ -99,8 +99,8 @@ int dsa3d_validate(const dsa3d_desc* desc);
 
 /* Recommended workspace bytes for `kind` (0 if none is needed; 0 also for an
  * invalid descriptor). The backward accepts any workspace of at least its
- * per-head minimum (dsa3d_workspace_min) and runs fewer, larger passes over
- * the heads the more it gets; the recommended size caps one pass at 8 GiB. */
+ * one-head minimum (dsa3d_workspace_min) and runs fewer passes over the heads
+ * the more it gets; the recommended size caps one pass at 16 GiB. */
 size_t dsa3d_workspace_size(const dsa3d_desc* desc, int kind);
 size_t dsa3d_workspace_min(const dsa3d_desc* desc, int kind);
 
@@ -119,12 +119,21 @@ int dsa3d_forward(const dsa3d_desc* desc, const void* q, const void* k, const vo
                   const void* offsets, void* out, float* lse, void* stream);
 
 /* Backward for a loss L given dout = dL/dout. Writes dq (the attention path's
- * share), dk, dv and doffsets (dL/doffsets). `out` and `lse` are the forward's
- * outputs for the same inputs. dk and dv are accumulated in float32 (fast
- * mode) or in 64-bit fixed point with 2^-32 resolution (deterministic = 1: the
- * result is bitwise identical from run to run; each term is clamped to
- * |x| <= 2^18) and rounded once to the output dtype. The workspace holds those
- * accumulators; see dsa3d_workspace_size(desc, DSA3D_WS_BACKWARD). */
+ * share), dk, dv and doffsets (dL/doffsets); every element of the four
+ * outputs is overwritten. `out` and `lse` are the forward's outputs for the
+ * same inputs. No atomic operation touches a gradient: each query's dq and
+ * doffsets are summed by the thread group that owns the query, and each key's
+ * dk/dv row by the group that owns the key, which walks the samples whose
+ * trilinear cell has that key as a corner (found through a per-cell index of
+ * the samples kept in the workspace) and sums their contributions in float32
+ * before one rounding to the output dtype. With deterministic = 1 that index
+ * is sorted, so every sum runs in a fixed order and all outputs are bitwise
+ * identical from run to run and for any workspace size; with deterministic = 0
+ * the order of dk/dv terms may vary in the last bits.
+ * The workspace (at least dsa3d_workspace_min(desc, DSA3D_WS_BACKWARD), the
+ * size of a pass over one head) holds the index; a larger one lets one pass
+ * cover more heads. A single head whose B*T*H*W*P samples, or whose
+ * B*(T+1)*(H+1)*(W+1) cells, reach 2^32 gives DSA3D_ERR_UNSUPPORTED. */
 int dsa3d_backward(const dsa3d_desc* desc, const void* q, const void* k, const void* v,
                    const void* offsets, const void* out, const float* lse, const void* dout,
                    void* dq, void* dk, void* dv, void* doffsets,
@@ -153,14 +162,17 @@ int dsa3d_debug_geometry(const dsa3d_desc* desc, const void* offsets, int32_t* b
 typedef enum {
     DSA3D_K_PROJ_FORWARD = 1,   /* projection GEMM */
     DSA3D_K_FORWARD = 2,        /* fused sample + softmax + aggregate */
-    DSA3D_K_BACKWARD = 3,       /* fused backward: dq, doffsets, dk/dv scatter */
-    DSA3D_K_BWD_FINALIZE = 4,   /* dk/dv accumulators -> output dtype */
-    DSA3D_K_FILL = 5,           /* workspace / output clearing */
+    DSA3D_K_BWD_QUERY = 3,      /* backward per query: dq, doffsets, sample records */
+    DSA3D_K_BWD_KEY = 4,        /* backward per key: dk, dv */
+    DSA3D_K_FILL = 5,           /* workspace clearing */
     DSA3D_K_PROJ_BWD_DQ = 6,    /* dq += doffsets . W */
     DSA3D_K_PROJ_BWD_DW = 7,    /* split dW = doffsets^T . q */
     DSA3D_K_SPLIT_SUM = 8,      /* fixed-order sum of split partials */
     DSA3D_K_COLSUM = 9,         /* split column sums for dbias */
-    DSA3D_K_GEOMETRY = 10       /* test hook */
+    DSA3D_K_GEOMETRY = 10,      /* test hook */
+    DSA3D_K_BWD_SCAN = 11,      /* backward: bucket starts (3 small kernels, one entry) */
+    DSA3D_K_BWD_INDEX = 12,     /* backward: per-cell sample index */
+    DSA3D_K_BWD_SORT = 13       /* backward, deterministic: bucket sort (2 kernels, one entry) */
 } dsa3d_kernel;
 
 typedef struct dsa3d_launch_log {

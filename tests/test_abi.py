@@ -93,27 +93,45 @@ def test_validate_rejects_p_mismatch_and_bad_flags():
     assert dsa.dsa3d_validate(d) == INVALID
 
 
+def _bwd_bounds(B, T, H, W, P, nh):
+    """Bounds on the backward workspace of a pass over nh heads: a 32-byte
+    record and a 4-byte index entry per sample, two 4-byte words per base cell
+    (count and start) of the grid extended by one cell per axis, plus small
+    scan and queue buffers and 256-byte alignment."""
+    nsamp = nh * B * T * H * W * P
+    ncell = nh * B * (T + 1) * (H + 1) * (W + 1)
+    lo = nsamp * 36 + ncell * 8
+    return lo, lo + nsamp // 1025 * 4 + ncell // 4096 * 4 + 8 * 256 + 64
+
+
 def test_workspace_sizes():
-    # float32 fast mode accumulates straight into dk/dv: no workspace
-    d = _desc()
-    assert dsa.dsa3d_workspace_size(d, dsa.WS_BACKWARD) == 0
+    d = _desc()  # B=1, 4x8x8, 2 heads x 32, 3x3x3
     assert dsa.dsa3d_workspace_size(d, dsa.WS_FORWARD) == 0
+    one = dsa.dsa3d_workspace_min(d, dsa.WS_BACKWARD)
+    lo, hi = _bwd_bounds(1, 4, 8, 8, 27, 1)
+    assert lo <= one <= hi
+    lo2, hi2 = _bwd_bounds(1, 4, 8, 8, 27, 2)
+    assert lo2 <= dsa.dsa3d_workspace_size(d, dsa.WS_BACKWARD) <= hi2
+    # the accumulation mode does not change the workspace
     d.deterministic = 1
-    per_head = 2 * 256 * 32 * 8
-    assert dsa.dsa3d_workspace_min(d, dsa.WS_BACKWARD) == per_head
-    assert dsa.dsa3d_workspace_size(d, dsa.WS_BACKWARD) == 2 * per_head
-    # 1080p, 24 x 128, deterministic: one head of int64 dK/dV accumulators = 4 GiB - a bit;
-    # the recommended size caps one pass at 8 GiB
+    assert dsa.dsa3d_workspace_min(d, dsa.WS_BACKWARD) == one
+    # 1080p, 24 x 128, 3x5x5: one head needs ~5.6 GB; the recommended size
+    # takes as many heads as fit in 16 GiB
     big = dsa.make_desc(1, 256, 68, 120, 24, 128, (3, 5, 5), dtype=torch.bfloat16, deterministic=True)
-    ph = 2 * 256 * 68 * 120 * 128 * 8
-    assert dsa.dsa3d_workspace_min(big, dsa.WS_BACKWARD) == ph
-    assert dsa.dsa3d_workspace_size(big, dsa.WS_BACKWARD) == (8 << 30) // ph * ph
-    fast = dsa.make_desc(1, 256, 68, 120, 24, 128, (3, 5, 5), dtype=torch.bfloat16)
-    assert dsa.dsa3d_workspace_min(fast, dsa.WS_BACKWARD) == ph // 2
+    ph = dsa.dsa3d_workspace_min(big, dsa.WS_BACKWARD)
+    lo, hi = _bwd_bounds(1, 256, 68, 120, 75, 1)
+    assert lo <= ph <= hi
+    rec = dsa.dsa3d_workspace_size(big, dsa.WS_BACKWARD)
+    assert rec <= (16 << 30) < rec + ph
     assert dsa.dsa3d_workspace_size(dsa.make_desc(1, 1, 1, 1, 1, 8, (1, 1, 1), dtype=torch.bfloat16),
                                     dsa.WS_PROJ_BACKWARD) > 0
     bad = _desc(window=(2, 2, 2))
     assert dsa.dsa3d_workspace_size(bad, dsa.WS_BACKWARD) == 0
+    # one head with 2^30 tokens x 27 samples cannot be numbered in 32 bits
+    huge = dsa.make_desc(1, 1024, 1024, 1024, 1, 8, (3, 3, 3), dtype=torch.bfloat16)
+    assert dsa.dsa3d_validate(huge) == 0
+    assert dsa.dsa3d_workspace_min(huge, dsa.WS_BACKWARD) == 0
+    assert dsa.dsa3d_workspace_size(huge, dsa.WS_BACKWARD) == 0
 
 
 def test_status_strings():

@@ -154,7 +154,7 @@ def test_deterministic_mode_is_bitwise_reproducible_across_runs_and_pass_splits(
     desc = dsa.desc_like(x["q"], wl.window, wl.dilation, 0.0, True)
     full = dsa.dsa3d_workspace_size(desc, dsa.WS_BACKWARD)
     one = dsa.dsa3d_workspace_min(desc, dsa.WS_BACKWARD)
-    assert full == 4 * one
+    assert 3 * one < full <= 4 * one  # one pass of 4 heads; then 1 and 3 heads per pass
     outs = []
     for ws in (full, full, one, 3 * one):
         ch = Chain(wl, x, bwd_workspace_bytes=ws)
