@@ -186,7 +186,7 @@ def main():
         log(f"[bench] warmup step {i + 1}/{args.warmup} done")
 
     stream = torch.cuda.current_stream()
-    timer = dsa.launch_timer(capacity=max(64, 64 * args.steps))
+    timer = dsa.launch_timer(capacity=max(256, 160 * args.steps))
     torch.cuda.synchronize()
     with timer:
         ev0 = torch.cuda.Event(enable_timing=True)

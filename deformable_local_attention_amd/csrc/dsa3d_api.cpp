@@ -82,7 +82,6 @@ int dsa3d_validate(const dsa3d_desc* d) {
     if (!pow2_in(d->head_dim, 8, 256)) return DSA3D_ERR_UNSUPPORTED;
     if (d->P > 1024) return DSA3D_ERR_UNSUPPORTED;
     if ((int64_t)d->heads * d->head_dim > (1 << 20)) return DSA3D_ERR_UNSUPPORTED;
-    if (dsa3d::fwd_groups_per_block(d->head_dim, d->P) == 0) return DSA3D_ERR_UNSUPPORTED;
     return DSA3D_OK;
 }
 

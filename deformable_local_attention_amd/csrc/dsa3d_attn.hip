@@ -9,12 +9,13 @@
 // neighbouring queries of one head whose sampled neighbourhoods overlap; the
 // block id is remapped so that each XCD walks one contiguous range of them.
 //
-// Per task: pass 1 computes the P logits s_p = scale * sum_c w_c <q, K[c]>
-// over the 8 trilinear corners c of each sample (keys are never interpolated
-// into a row: the corner dot products are weighted instead), keeping them in
-// LDS; the exact softmax follows; pass 2 accumulates
-// o = sum_p a_p sum_c w_c V[c] in float32 registers. Corners outside the grid
-// read a shared zero row, so no lane diverges on the border.
+// Per task, one pass over the P samples with an online softmax: the logit
+// s_p = scale * sum_c w_c <q, K[c]> weights the 8 corner dot products (keys are
+// never interpolated into a row), then the running maximum m, denominator z
+// and output o = sum_p exp(s_p - m) sum_c w_c V[c] are updated, o being
+// rescaled by exp(m_old - m_new) when m grows; o/z and lse = m + log z are
+// written at the end. Corners outside the grid read a shared zero row, so no
+// lane diverges on the border.
 #include "dsa3d_attn_common.h"
 #include "dsa3d_internal.h"
 
@@ -28,6 +29,7 @@ struct FwdArgs {
     void* out;
     float* lse;
     TaskGrid g;
+    BlockOrder ord;
     int32_t P;
     float scale;
     Window win;
@@ -36,18 +38,16 @@ struct FwdArgs {
 template <typename T, int D>
 __global__ void __launch_bounds__(256) dsa3d_fwd_kernel(FwdArgs a) {
     constexpr int L = D / 8;
-    extern __shared__ float s_logit[];  // [groups_per_block][P]
-    const int groups = blockDim.x / L;
     const int g = threadIdx.x / L;
     const int li = threadIdx.x % L;
-    const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
-    const int64_t task = (int64_t)lb * groups + g;
-    const bool active = task < a.g.ntasks;
-    const int64_t task_c = active ? task : a.g.ntasks - 1;  // inactive groups shadow the last task
-
-    int32_t b, eta, t, h, w;
-    int64_t tok;
-    task_coords(a.g, task_c, b, eta, t, h, w, tok);
+    int64_t bh;
+    int32_t t, h, w0;
+    block_coords(a.g, a.ord, xcd_logical_block(blockIdx.x, gridDim.x), bh, t, h, w0);
+    const int32_t w = w0 + g;
+    if (w >= a.g.W) return;  // no block-wide barrier below
+    const int32_t b = (int32_t)(bh / a.g.nheads);
+    const int32_t eta = a.g.head0 + (int32_t)(bh - (int64_t)b * a.g.nheads);
+    const int64_t tok = (((int64_t)b * a.g.T + t) * a.g.H + h) * a.g.W + w;
     const int64_t C = (int64_t)a.g.heads * D;
     const int64_t row_off = (int64_t)eta * D + li * 8;
     const T* Kb = reinterpret_cast<const T*>(a.k) + row_off;
@@ -58,56 +58,43 @@ __global__ void __launch_bounds__(256) dsa3d_fwd_kernel(FwdArgs a) {
     Frag8<T> qf;
     qf.load(reinterpret_cast<const T*>(a.q) + tok * C + row_off);
 
-    float* sl = s_logit + g * a.P;
-    float m = -INFINITY;
-    for (int p = 0; p < a.P; ++p) {
-        float dt, dh, dw;
-        load_offsets<T>(offq + p * 3, dt, dh, dw);
-        int32_t t0 = 0, h0 = 0, w0 = 0;
-        float ft = 0.f, fh = 0.f, fw = 0.f;
-        const bool inside = sample_geometry(a.win, t, h, w, p, dt, dh, dw, t0, h0, w0, ft, fh, fw);
-        Corners c;
-        make_corners(a.g, b, t0, h0, w0, ft, fh, fw, inside, c);
-        float acc = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            Frag8<T> kf;
-            kf.load(c.tok[i] >= 0 ? Kb + c.tok[i] * C : zero);
-            acc = fmaf(c.w[i], kf.dot(qf, 0.0f), acc);
-        }
-        const float s = a.scale * group_sum<L>(acc);
-        if (li == 0) sl[p] = s;
-        m = fmaxf(m, s);
-    }
-    __syncthreads();
-    float z = 0.0f;
-    for (int p = li; p < a.P; p += L) z += __expf(sl[p] - m);
-    z = group_sum<L>(z);
-    const float inv_z = 1.0f / z;
-
+    float m = -INFINITY, z = 0.0f;
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int p = 0; p < a.P; ++p) {
         float dt, dh, dw;
         load_offsets<T>(offq + p * 3, dt, dh, dw);
-        int32_t t0 = 0, h0 = 0, w0 = 0;
+        int32_t t0 = 0, h0 = 0, w0c = 0;
         float ft = 0.f, fh = 0.f, fw = 0.f;
-        const bool inside = sample_geometry(a.win, t, h, w, p, dt, dh, dw, t0, h0, w0, ft, fh, fw);
+        const bool inside = sample_geometry(a.win, t, h, w, p, dt, dh, dw, t0, h0, w0c, ft, fh, fw);
         Corners c;
-        make_corners(a.g, b, t0, h0, w0, ft, fh, fw, inside, c);
-        const float ap = __expf(sl[p] - m) * inv_z;
+        make_corners(a.g, b, t0, h0, w0c, ft, fh, fw, inside, c);
+        Frag8<T> kf[8], vf[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            Frag8<T> vf;
-            vf.load(c.tok[i] >= 0 ? Vb + c.tok[i] * C : zero);
-            vf.axpy(ap * c.w[i], o);
+            kf[i].load(c.tok[i] >= 0 ? Kb + c.tok[i] * C : zero);
+            vf[i].load(c.tok[i] >= 0 ? Vb + c.tok[i] * C : zero);
         }
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc = fmaf(c.w[i], kf[i].dot(qf, 0.0f), acc);
+        const float s = a.scale * group_sum<L>(acc);
+        const float m_new = fmaxf(m, s);
+        const float alpha = __expf(m - m_new);  // 0 for the first sample (m = -inf)
+        const float beta = __expf(s - m_new);
+        z = fmaf(z, alpha, beta);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vf[i].axpy(beta * c.w[i], o);
+        m = m_new;
     }
-    if (active) {
-        Frag8<T> of;
-        of.from_f32(o);
-        of.store(reinterpret_cast<T*>(a.out) + tok * C + row_off);
-        if (li == 0) a.lse[tok * a.g.heads + eta] = m + __logf(z);
-    }
+    const float inv_z = 1.0f / z;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= inv_z;
+    Frag8<T> of;
+    of.from_f32(o);
+    of.store(reinterpret_cast<T*>(a.out) + tok * C + row_off);
+    if (li == 0) a.lse[tok * a.g.heads + eta] = m + __logf(z);
 }
 
 __global__ void __launch_bounds__(256) dsa3d_fill_zero_kernel(uint32_t* p, int64_t nwords) {
@@ -168,29 +155,31 @@ unsigned grid_for(int64_t n, int threads, int64_t cap) {
     return (unsigned)b;
 }
 
-int fwd_groups_per_block(int head_dim, int P) {
-    const int L = head_dim / 8;
-    int groups = 256 / L;
-    const int per_wave = 64 / L;
-    while (groups > per_wave && (size_t)groups * P * sizeof(float) > 65536) groups -= per_wave;
-    if ((size_t)groups * P * sizeof(float) > 65536) return 0;
-    return groups;
+BlockOrder make_block_order(const dsa3d_desc& d, int G) {
+    BlockOrder o;
+    o.G = G;
+    o.BW = (int32_t)((d.W + G - 1) / G);
+    // supertile: 4 frames x 8 rows x 64 tokens (at most; clipped at the grid)
+    o.ST = 4;
+    o.SH = 8;
+    o.SW = std::max(1, 64 / G);
+    o.nblk_bh = d.T * d.H * (int64_t)o.BW;
+    return o;
 }
 
+int attn_tokens_per_block(int head_dim) { return 256 / (head_dim / 8); }
+
 template <typename T, int D>
-static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
-    const int groups = fwd_groups_per_block(D, a.P);
-    const int threads = groups * (D / 8);
-    const int64_t nb = (a.g.ntasks + groups - 1) / groups;
+static hipError_t launch_fwd_t(const FwdArgs& a, int64_t nblocks, hipStream_t s) {
     LaunchScope ls(DSA3D_K_FORWARD, s);
-    hipLaunchKernelGGL((dsa3d_fwd_kernel<T, D>), dim3((unsigned)nb), dim3(threads), groups * a.P * sizeof(float), s, a);
+    hipLaunchKernelGGL((dsa3d_fwd_kernel<T, D>), dim3((unsigned)nblocks), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 template <int D>
-static hipError_t fwd_f32(const FwdArgs& a, hipStream_t s) { return launch_fwd_t<float, D>(a, s); }
+static hipError_t fwd_f32(const FwdArgs& a, int64_t nb, hipStream_t s) { return launch_fwd_t<float, D>(a, nb, s); }
 template <int D>
-static hipError_t fwd_bf16(const FwdArgs& a, hipStream_t s) { return launch_fwd_t<bf16_t, D>(a, s); }
+static hipError_t fwd_bf16(const FwdArgs& a, int64_t nb, hipStream_t s) { return launch_fwd_t<bf16_t, D>(a, nb, s); }
 
 hipError_t launch_forward(const dsa3d_desc& d, const void* q, const void* k, const void* v, const void* off,
                           void* out, float* lse, hipStream_t s) {
@@ -200,9 +189,11 @@ hipError_t launch_forward(const dsa3d_desc& d, const void* q, const void* k, con
     a.P = d.P;
     a.scale = logit_scale(d);
     a.win = make_window(d);
-    if (a.g.ntasks == 0) return hipSuccess;
-    if (d.dtype == DSA3D_F32) { DSA3D_DISPATCH_D(d.head_dim, fwd_f32, a, s); }
-    DSA3D_DISPATCH_D(d.head_dim, fwd_bf16, a, s);
+    a.ord = make_block_order(d, attn_tokens_per_block(d.head_dim));
+    const int64_t nb = a.ord.nblk_bh * d.B * d.heads;
+    if (nb == 0) return hipSuccess;
+    if (d.dtype == DSA3D_F32) { DSA3D_DISPATCH_D(d.head_dim, fwd_f32, a, nb, s); }
+    DSA3D_DISPATCH_D(d.head_dim, fwd_bf16, a, nb, s);
 }
 
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t s) {

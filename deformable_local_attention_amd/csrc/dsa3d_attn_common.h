@@ -35,6 +35,46 @@ __device__ __forceinline__ void task_coords(const TaskGrid& g, int64_t task, int
     tok = (int64_t)b * THW + (int64_t)t * HW + (int64_t)h * g.W + w;
 }
 
+// Block order of the attention kernels. A workgroup owns G consecutive
+// tokens of one row (t, h, w0 .. w0+G-1) of one (batch, head); blocks are
+// dealt out in "supertiles" of ST x SH x SW blocks (t, h, block column), one
+// supertile after another, so that the blocks running at the same time on an
+// XCD cover a compact 3-D region: the neighbourhoods their samples read then
+// overlap, and the key/value (or query/gradient) rows they gather stay in that
+// XCD's L2 longer than with a row-by-row order.
+struct BlockOrder {
+    int32_t G;            // tokens per block along w
+    int32_t BW;           // blocks per row: ceil(W / G)
+    int32_t ST, SH, SW;   // supertile extent in (t, h, block column)
+    int64_t nblk_bh;      // blocks per (batch, head): T * H * BW
+};
+
+// Logical block -> (batch*nheads + local head, t, h, first w).
+__device__ __forceinline__ void block_coords(const TaskGrid& g, const BlockOrder& o, int64_t lb, int64_t& bh,
+                                             int32_t& t, int32_t& h, int32_t& w0) {
+    bh = lb / o.nblk_bh;
+    int64_t r = lb - bh * o.nblk_bh;
+    const int64_t slab = (int64_t)o.ST * g.H * o.BW;       // full t-slab of supertiles
+    const int32_t i = (int32_t)(r / slab);
+    r -= (int64_t)i * slab;
+    const int32_t st = min(o.ST, g.T - i * o.ST);
+    const int64_t hrow = (int64_t)st * o.SH * o.BW;        // one h-row of supertiles in this slab
+    const int32_t j = (int32_t)(r / hrow);
+    r -= (int64_t)j * hrow;
+    const int32_t sh = min(o.SH, g.H - j * o.SH);
+    const int64_t tile = (int64_t)st * sh * o.SW;          // one full supertile of this row
+    const int32_t k = (int32_t)(r / tile);
+    r -= (int64_t)k * tile;
+    const int32_t sw = min(o.SW, o.BW - k * o.SW);
+    const int32_t dt = (int32_t)(r / (sh * sw));
+    const int32_t rr = (int32_t)(r - (int64_t)dt * sh * sw);
+    const int32_t dh = rr / sw;
+    const int32_t dw = rr - dh * sw;
+    t = i * o.ST + dt;
+    h = j * o.SH + dh;
+    w0 = (k * o.SW + dw) * o.G;
+}
+
 // The eight trilinear corners x0 + {0,1}^3 of one sample: token index (or -1
 // outside the grid) and weight prod_axis (c ? f : 1 - f). Corner i has offset
 // (i>>2 & 1, i>>1 & 1, i & 1) in (t, h, w).

@@ -5,22 +5,21 @@
 // cell. Pushing those corner contributions with atomics costs 16*head_dim
 // atomic adds per sample; instead the backward pulls them per key:
 //
-//  1. query kernel (one task = one (query, head), as in the forward): recompute
-//     the logits, a_p = exp(s_p - lse), da_p = sum_c w_c <dO, V[c]>,
+//  1. count kernel: the base cell floor(pos) of every sample (geometry only)
+//     and one 32-bit atomic increment of that cell's bucket count;
+//  2. an exclusive scan turns the counts into bucket starts (the counts are
+//     then cleared to serve as fill cursors);
+//  3. query kernel (one task = one (query, head), as in the forward):
+//     recompute the logits, a_p = exp(s_p - lse), da_p = sum_c w_c <dO, V[c]>,
 //     ds_p = a_p (da_p - <dO, o>); write dq = scale sum_p ds_p sum_c w_c K[c]
-//     and doffsets; store per sample a 32-byte record (scale*ds_p, a_p, the
-//     fraction f, the query token) and count it in the bucket of its base cell
-//     floor(pos) -- one 32-bit atomic per sample, whose return value is the
-//     sample's slot in that bucket;
-//  2. an exclusive scan turns the bucket counts into bucket starts;
-//  3. index kernel: write each sample's number into its slot (a CSR list of
-//     the samples of every base cell);
+//     and doffsets; and write per sample a 32-byte record (scale*ds_p, a_p,
+//     the fraction f, the query token, the sample number) straight into a free
+//     slot of its bucket (one more atomic on the cursor);
 //  4. deterministic mode only: sort every bucket by sample number, so that the
-//     summation order below does not depend on the order the atomics of
-//     step 1 landed in;
+//     summation order below does not depend on the order the slots were taken;
 //  5. key kernel (one task = one (key token, head)): the samples whose cell
 //     has key y as corner c are exactly those with base cell y - c, so the key
-//     walks the 8 buckets y - c and accumulates
+//     streams the records of the 8 buckets y - c and accumulates
 //        dK[y] += w_c * scale * ds_p * q_x,   dV[y] += w_c * a_p * dO_x
 //     in float32 registers, then writes its rows once.
 // Base cells run over the grid extended by one cell on the low side of each
@@ -32,22 +31,21 @@
 
 namespace dsa3d {
 
-constexpr uint32_t kNoCell = 0xffffffffu;
 constexpr int kScanThreads = 256;
 constexpr int kScanItems = 16;
 constexpr uint32_t kScanChunk = kScanThreads * kScanItems;
-constexpr uint32_t kWaveSortMax = 1024;    // buckets up to this size: one wave, in LDS
-constexpr uint32_t kBlockSortMax = 16384;  // up to this size: one 1024-thread block, in LDS
+constexpr uint32_t kWaveSortMax = 512;  // buckets up to this size: one wave, in LDS
 constexpr int kSortBucketsPerBlock = 64;
 
-// Per-sample record written by the query kernel and read by the key kernel.
+// Per-sample record, written by the query kernel into its bucket and read by
+// the key kernel.
 struct __attribute__((aligned(16))) SampleRec {
     float ck;       // scale * ds_p
     float cv;       // a_p
     float ft, fh, fw;
     uint32_t qtok;  // query token index in [B,T,H,W]
-    uint32_t rank;  // slot within the bucket
-    uint32_t cell;  // base cell, or kNoCell when no corner is in the grid
+    uint32_t sid;   // sample number within the pass: task * P + p
+    uint32_t pad;
 };
 
 struct BwdArgs {
@@ -62,11 +60,11 @@ struct BwdArgs {
     void* doff;
     void* dk;
     void* dv;
-    uint32_t* cnt;    // [ncell] bucket counts
+    uint32_t* cnt;    // [ncell] bucket counts, then fill cursors
     uint32_t* start;  // [ncell + 1] bucket starts
-    uint32_t* csr;    // [nsamp] sample numbers by bucket
-    SampleRec* rec;   // [nsamp]
+    SampleRec* rec;   // [nsamp] records, bucket by bucket
     TaskGrid g;
+    BlockOrder ord;
     int32_t P;
     float scale;
     Window win;
@@ -77,105 +75,27 @@ __device__ __forceinline__ uint32_t cell_index(const TaskGrid& g, int64_t bh, in
 }
 
 // ---------------------------------------------------------------------------
-// 1. query kernel
+// 1. count kernel: one thread per sample, in sample-number order
 // ---------------------------------------------------------------------------
-template <typename T, int D>
-__global__ void __launch_bounds__(256) dsa3d_bwd_query_kernel(BwdArgs a) {
-    constexpr int L = D / 8;
-    const int groups = blockDim.x / L;
-    const int g = threadIdx.x / L;
-    const int li = threadIdx.x % L;
-    const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
-    const int64_t task = (int64_t)lb * groups + g;
-    if (task >= a.g.ntasks) return;  // no block-wide barrier below
-
-    int32_t b, eta, t, h, w;
-    int64_t tok;
-    task_coords(a.g, task, b, eta, t, h, w, tok);
-    const int64_t bh = (int64_t)b * a.g.nheads + (eta - a.g.head0);
-    const int64_t C = (int64_t)a.g.heads * D;
-    const int64_t row_off = (int64_t)eta * D + li * 8;
-    const T* Kb = reinterpret_cast<const T*>(a.k) + row_off;
-    const T* Vb = reinterpret_cast<const T*>(a.v) + row_off;
-    const T* zero = reinterpret_cast<const T*>(g_zero_row);
-    const int64_t offrow = (tok * a.g.heads + eta) * (int64_t)a.P * 3;
-    const T* offq = reinterpret_cast<const T*>(a.off) + offrow;
-    T* doffq = reinterpret_cast<T*>(a.doff) + offrow;
-    SampleRec* recq = a.rec + task * a.P;
-
-    Frag8<T> qf, gf, of;
-    qf.load(reinterpret_cast<const T*>(a.q) + tok * C + row_off);
-    gf.load(reinterpret_cast<const T*>(a.dout) + tok * C + row_off);
-    of.load(reinterpret_cast<const T*>(a.o) + tok * C + row_off);
-    const float Dsum = group_sum<L>(gf.dot(of, 0.0f));
-    const float lse = a.lse[tok * a.g.heads + eta];
-
-    float dq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int p = 0; p < a.P; ++p) {
+template <typename T>
+__global__ void __launch_bounds__(256) dsa3d_bwd_count_kernel(BwdArgs a) {
+    const uint64_t nsamp = (uint64_t)a.g.ntasks * a.P;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nsamp; i += (uint64_t)gridDim.x * blockDim.x) {
+        const int64_t task = (int64_t)(i / (uint32_t)a.P);
+        const int32_t p = (int32_t)(i - (uint64_t)task * a.P);
+        int32_t b, eta, t, h, w;
+        int64_t tok;
+        task_coords(a.g, task, b, eta, t, h, w, tok);
         float dt, dh, dw;
-        load_offsets<T>(offq + p * 3, dt, dh, dw);
-        int32_t t0 = 0, h0 = 0, w0 = 0;
-        float ft = 0.f, fh = 0.f, fw = 0.f;
-        const bool inside = sample_geometry(a.win, t, h, w, p, dt, dh, dw, t0, h0, w0, ft, fh, fw);
-        Corners c;
-        make_corners(a.g, b, t0, h0, w0, ft, fh, fw, inside, c);
-        Frag8<T> kf[8], vf[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            kf[i].load(c.tok[i] >= 0 ? Kb + c.tok[i] * C : zero);
-            vf[i].load(c.tok[i] >= 0 ? Vb + c.tok[i] * C : zero);
-        }
-        float qk[8], dv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            qk[i] = kf[i].dot(qf, 0.0f);
-            dv[i] = vf[i].dot(gf, 0.0f);
-        }
-        // weighted sums: logit, dL/da, and the offset-derivative sums per axis
-        const float at[2] = {1.0f - ft, ft}, ah[2] = {1.0f - fh, fh}, aw[2] = {1.0f - fw, fw};
-        float r[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int ct = (i >> 2) & 1, ch = (i >> 1) & 1, cw = i & 1;
-            const float st = ct ? 1.f : -1.f, sh = ch ? 1.f : -1.f, sw = cw ? 1.f : -1.f;
-            const float gt = st * ah[ch] * aw[cw], gh = at[ct] * sh * aw[cw], gw = at[ct] * ah[ch] * sw;
-            // zero rows give zero dot products, so no validity test is needed here
-            r[0] = fmaf(c.w[i], qk[i], r[0]);
-            r[1] = fmaf(c.w[i], dv[i], r[1]);
-            r[2] = fmaf(gt, qk[i], r[2]);
-            r[3] = fmaf(gh, qk[i], r[3]);
-            r[4] = fmaf(gw, qk[i], r[4]);
-            r[5] = fmaf(gt, dv[i], r[5]);
-            r[6] = fmaf(gh, dv[i], r[6]);
-            r[7] = fmaf(gw, dv[i], r[7]);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) r[j] = group_sum<L>(r[j]);
-        const float s = a.scale * r[0];
-        const float ap = __expf(s - lse);
-        const float ds = ap * (r[1] - Dsum);
-        const float ck = a.scale * ds;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) kf[i].axpy(ck * c.w[i], dq);
-        if (li == 0) {
-            store_scalar<T>(doffq + p * 3 + 0, fmaf(ck, r[2], ap * r[5]));
-            store_scalar<T>(doffq + p * 3 + 1, fmaf(ck, r[3], ap * r[6]));
-            store_scalar<T>(doffq + p * 3 + 2, fmaf(ck, r[4], ap * r[7]));
-            const bool reaches = inside && t0 >= -1 && t0 < a.g.T && h0 >= -1 && h0 < a.g.H && w0 >= -1 &&
-                                 w0 < a.g.W;
-            uint32_t cell = kNoCell, rank = 0;
-            if (reaches) {
-                cell = cell_index(a.g, bh, t0, h0, w0);
-                rank = atomicAdd(a.cnt + cell, 1u);
-            }
-            uint4* dst = reinterpret_cast<uint4*>(recq + p);
-            dst[0] = make_uint4(__float_as_uint(ck), __float_as_uint(ap), __float_as_uint(ft), __float_as_uint(fh));
-            dst[1] = make_uint4(__float_as_uint(fw), (uint32_t)tok, rank, cell);
-        }
+        load_offsets<T>(reinterpret_cast<const T*>(a.off) + ((tok * a.g.heads + eta) * (int64_t)a.P + p) * 3, dt, dh,
+                        dw);
+        int32_t t0, h0, w0;
+        float ft, fh, fw;
+        if (!sample_geometry(a.win, t, h, w, p, dt, dh, dw, t0, h0, w0, ft, fh, fw)) continue;
+        if (t0 < -1 || t0 >= a.g.T || h0 < -1 || h0 >= a.g.H || w0 < -1 || w0 >= a.g.W) continue;
+        const int64_t bh = (int64_t)b * a.g.nheads + (eta - a.g.head0);
+        atomicAdd(a.cnt + cell_index(a.g, bh, t0, h0, w0), 1u);
     }
-    Frag8<T> dqf;
-    dqf.from_f32(dq);
-    dqf.store(reinterpret_cast<T*>(a.dq) + tok * C + row_off);
 }
 
 // ---------------------------------------------------------------------------
@@ -258,28 +178,118 @@ __global__ void __launch_bounds__(kScanThreads) dsa3d_scan_apply_kernel(const ui
 }
 
 // ---------------------------------------------------------------------------
-// 3. bucket index
+// 3. query kernel
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) dsa3d_bwd_index_kernel(const SampleRec* rec, uint64_t nsamp,
-                                                              const uint32_t* start, uint32_t* csr) {
-    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nsamp; i += (uint64_t)gridDim.x * blockDim.x) {
-        const uint2 rc = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint32_t*>(rec + i) + 6);  // rank, cell
-        if (rc.y != kNoCell) csr[start[rc.y] + rc.x] = (uint32_t)i;
+template <typename T, int D>
+__global__ void __launch_bounds__(256) dsa3d_bwd_query_kernel(BwdArgs a) {
+    constexpr int L = D / 8;
+    const int g = threadIdx.x / L;
+    const int li = threadIdx.x % L;
+    int64_t bh;
+    int32_t t, h, wb;
+    block_coords(a.g, a.ord, xcd_logical_block(blockIdx.x, gridDim.x), bh, t, h, wb);
+    const int32_t w = wb + g;
+    if (w >= a.g.W) return;  // no block-wide barrier below
+    const int32_t b = (int32_t)(bh / a.g.nheads);
+    const int32_t eta = a.g.head0 + (int32_t)(bh - (int64_t)b * a.g.nheads);
+    const int64_t tok = (((int64_t)b * a.g.T + t) * a.g.H + h) * a.g.W + w;
+    const int64_t task = ((bh * a.g.T + t) * a.g.H + h) * (int64_t)a.g.W + w;
+    const int64_t C = (int64_t)a.g.heads * D;
+    const int64_t row_off = (int64_t)eta * D + li * 8;
+    const T* Kb = reinterpret_cast<const T*>(a.k) + row_off;
+    const T* Vb = reinterpret_cast<const T*>(a.v) + row_off;
+    const T* zero = reinterpret_cast<const T*>(g_zero_row);
+    const int64_t offrow = (tok * a.g.heads + eta) * (int64_t)a.P * 3;
+    const T* offq = reinterpret_cast<const T*>(a.off) + offrow;
+    T* doffq = reinterpret_cast<T*>(a.doff) + offrow;
+    const uint32_t sid0 = (uint32_t)(task * a.P);
+
+    Frag8<T> qf, gf, of;
+    qf.load(reinterpret_cast<const T*>(a.q) + tok * C + row_off);
+    gf.load(reinterpret_cast<const T*>(a.dout) + tok * C + row_off);
+    of.load(reinterpret_cast<const T*>(a.o) + tok * C + row_off);
+    const float Dsum = group_sum<L>(gf.dot(of, 0.0f));
+    const float lse = a.lse[tok * a.g.heads + eta];
+
+    float dq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < a.P; ++p) {
+        float dt, dh, dw;
+        load_offsets<T>(offq + p * 3, dt, dh, dw);
+        int32_t t0 = 0, h0 = 0, w0 = 0;
+        float ft = 0.f, fh = 0.f, fw = 0.f;
+        const bool inside = sample_geometry(a.win, t, h, w, p, dt, dh, dw, t0, h0, w0, ft, fh, fw);
+        Corners c;
+        make_corners(a.g, b, t0, h0, w0, ft, fh, fw, inside, c);
+        Frag8<T> kf[8], vf[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            kf[i].load(c.tok[i] >= 0 ? Kb + c.tok[i] * C : zero);
+            vf[i].load(c.tok[i] >= 0 ? Vb + c.tok[i] * C : zero);
+        }
+        float qk[8], dv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            qk[i] = kf[i].dot(qf, 0.0f);
+            dv[i] = vf[i].dot(gf, 0.0f);
+        }
+        // weighted sums: logit, dL/da, and the offset-derivative sums per axis
+        const float at[2] = {1.0f - ft, ft}, ah[2] = {1.0f - fh, fh}, aw[2] = {1.0f - fw, fw};
+        float r[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int ct = (i >> 2) & 1, ch = (i >> 1) & 1, cw = i & 1;
+            const float st = ct ? 1.f : -1.f, sh = ch ? 1.f : -1.f, sw = cw ? 1.f : -1.f;
+            const float gt = st * ah[ch] * aw[cw], gh = at[ct] * sh * aw[cw], gw = at[ct] * ah[ch] * sw;
+            // zero rows give zero dot products, so no validity test is needed here
+            r[0] = fmaf(c.w[i], qk[i], r[0]);
+            r[1] = fmaf(c.w[i], dv[i], r[1]);
+            r[2] = fmaf(gt, qk[i], r[2]);
+            r[3] = fmaf(gh, qk[i], r[3]);
+            r[4] = fmaf(gw, qk[i], r[4]);
+            r[5] = fmaf(gt, dv[i], r[5]);
+            r[6] = fmaf(gh, dv[i], r[6]);
+            r[7] = fmaf(gw, dv[i], r[7]);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = group_sum<L>(r[j]);
+        const float s = a.scale * r[0];
+        const float ap = __expf(s - lse);
+        const float ds = ap * (r[1] - Dsum);
+        const float ck = a.scale * ds;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kf[i].axpy(ck * c.w[i], dq);
+        if (li == 0) {
+            store_scalar<T>(doffq + p * 3 + 0, fmaf(ck, r[2], ap * r[5]));
+            store_scalar<T>(doffq + p * 3 + 1, fmaf(ck, r[3], ap * r[6]));
+            store_scalar<T>(doffq + p * 3 + 2, fmaf(ck, r[4], ap * r[7]));
+            const bool reaches = inside && t0 >= -1 && t0 < a.g.T && h0 >= -1 && h0 < a.g.H && w0 >= -1 &&
+                                 w0 < a.g.W;
+            if (reaches) {
+                const uint32_t cell = cell_index(a.g, bh, t0, h0, w0);
+                const uint32_t slot = a.start[cell] + atomicAdd(a.cnt + cell, 1u);
+                uint4* dst = reinterpret_cast<uint4*>(a.rec + slot);
+                dst[0] = make_uint4(__float_as_uint(ck), __float_as_uint(ap), __float_as_uint(ft), __float_as_uint(fh));
+                dst[1] = make_uint4(__float_as_uint(fw), (uint32_t)tok, sid0 + (uint32_t)p, 0u);
+            }
+        }
     }
+    Frag8<T> dqf;
+    dqf.from_f32(dq);
+    dqf.store(reinterpret_cast<T*>(a.dq) + tok * C + row_off);
 }
 
 // ---------------------------------------------------------------------------
-// 4. deterministic mode: sort every bucket ascending.
+// 4. deterministic mode: sort the records of every bucket by sample number.
 //
 // Bitonic network in the form whose comparators all put the smaller key at
 // the lower index (a "flip" stage, then half-cleaners), so a bucket of n keys
 // sorts as if padded with +infinity up to a power of two while only the real
 // n entries are touched: a comparator whose upper index is >= n would leave
-// its pair unchanged and is skipped. The keys (sample numbers) are distinct.
+// its pair unchanged and is skipped. Sample numbers are distinct.
 // ---------------------------------------------------------------------------
-template <typename Sync>
-__device__ __forceinline__ void bitonic_sort_u32(uint32_t* buf, uint32_t n, uint32_t tid, uint32_t nthr, Sync sync) {
-    uint64_t npad = 1;  // 64-bit: a bucket may hold up to 2^32 - 1 keys
+template <typename Swap, typename Sync>
+__device__ __forceinline__ void bitonic_sort(uint32_t n, uint32_t tid, uint32_t nthr, Swap cmpswap, Sync sync) {
+    uint64_t npad = 1;  // 64-bit: a bucket may hold up to 2^32 - 1 entries
     while (npad < n) npad <<= 1;
     const uint64_t pairs = npad / 2;
     for (uint64_t k = 2; k <= npad; k <<= 1) {
@@ -287,19 +297,13 @@ __device__ __forceinline__ void bitonic_sort_u32(uint32_t* buf, uint32_t n, uint
         for (uint64_t i = tid; i < pairs; i += nthr) {
             const uint64_t blk = (i / half) * k, off = i % half;
             const uint64_t lo = blk + off, hi = blk + k - 1 - off;
-            if (hi < n) {
-                const uint32_t x = buf[lo], y = buf[hi];
-                if (x > y) { buf[lo] = y; buf[hi] = x; }
-            }
+            if (hi < n) cmpswap(lo, hi);
         }
         sync();
         for (uint64_t j = half >> 1; j >= 1; j >>= 1) {
             for (uint64_t i = tid; i < pairs; i += nthr) {
                 const uint64_t lo = (i / j) * 2 * j + (i % j), hi = lo + j;
-                if (hi < n) {
-                    const uint32_t x = buf[lo], y = buf[hi];
-                    if (x > y) { buf[lo] = y; buf[hi] = x; }
-                }
+                if (hi < n) cmpswap(lo, hi);
             }
             sync();
         }
@@ -310,14 +314,40 @@ struct BlockSync {
     __device__ __forceinline__ void operator()() const { __syncthreads(); }
 };
 
+// (sample number << 32 | position) keys in LDS, compare-exchanged.
+struct LdsKeySwap {
+    uint64_t* key;
+    __device__ __forceinline__ void operator()(uint64_t lo, uint64_t hi) const {
+        const uint64_t x = key[lo], y = key[hi];
+        if (x > y) { key[lo] = y; key[hi] = x; }
+    }
+};
+
+// Whole 32-byte records in global memory, compared by sample number.
+struct GlobalRecSwap {
+    uint4* rec;  // two uint4 per record; the sample number is word 6
+    __device__ __forceinline__ void operator()(uint64_t lo, uint64_t hi) const {
+        const uint4 a1 = rec[2 * hi + 1];
+        const uint4 b1 = rec[2 * lo + 1];
+        if (b1.z > a1.z) {
+            const uint4 a0 = rec[2 * hi], b0 = rec[2 * lo];
+            rec[2 * lo] = a0; rec[2 * lo + 1] = a1;
+            rec[2 * hi] = b0; rec[2 * hi + 1] = b1;
+        }
+    }
+};
+
 // One wave per block; the block walks kSortBucketsPerBlock consecutive
-// buckets. Buckets larger than kWaveSortMax are queued in `large`
-// ([0] = count, [1..cap] = bucket numbers) for the next kernel.
-__global__ void __launch_bounds__(64) dsa3d_sort_small_kernel(const uint32_t* start, uint32_t ncell, uint32_t* csr,
+// buckets. A bucket of up to kWaveSortMax records is staged in LDS, its keys
+// sorted and the records written back in order; larger buckets are queued in
+// `large` ([0] = count, [1..cap] = bucket numbers) for the next kernel.
+__global__ void __launch_bounds__(64) dsa3d_sort_small_kernel(const uint32_t* start, uint32_t ncell, SampleRec* rec,
                                                               uint32_t* large, uint32_t large_cap) {
-    __shared__ uint32_t buf[kWaveSortMax];
+    __shared__ uint4 srec[2 * kWaveSortMax];
+    __shared__ uint64_t skey[kWaveSortMax];
     const uint32_t c0 = blockIdx.x * kSortBucketsPerBlock;
     const uint32_t c1 = min(ncell, c0 + kSortBucketsPerBlock);
+    uint4* grec = reinterpret_cast<uint4*>(rec);
     for (uint32_t c = c0; c < c1; ++c) {
         const uint32_t s = start[c], n = start[c + 1] - s;
         if (n < 2) continue;
@@ -328,32 +358,33 @@ __global__ void __launch_bounds__(64) dsa3d_sort_small_kernel(const uint32_t* st
             }
             continue;
         }
-        for (uint32_t i = threadIdx.x; i < n; i += 64) buf[i] = csr[s + i];
+        for (uint32_t i = threadIdx.x; i < n; i += 64) {
+            const uint4 r0 = grec[2 * ((uint64_t)s + i)], r1 = grec[2 * ((uint64_t)s + i) + 1];
+            srec[2 * i] = r0;
+            srec[2 * i + 1] = r1;
+            skey[i] = ((uint64_t)r1.z << 32) | i;
+        }
         __syncthreads();
-        bitonic_sort_u32(buf, n, threadIdx.x, 64, BlockSync());
-        for (uint32_t i = threadIdx.x; i < n; i += 64) csr[s + i] = buf[i];
+        bitonic_sort(n, threadIdx.x, 64, LdsKeySwap{skey}, BlockSync());
+        for (uint32_t i = threadIdx.x; i < n; i += 64) {
+            const uint32_t from = (uint32_t)skey[i];
+            grec[2 * ((uint64_t)s + i)] = srec[2 * from];
+            grec[2 * ((uint64_t)s + i) + 1] = srec[2 * from + 1];
+        }
         __syncthreads();
     }
 }
 
-// Buckets queued by the previous kernel: in LDS up to kBlockSortMax keys,
-// otherwise in place in global memory (same network; slow, but only a
-// pathological offset field puts that many samples into one cell).
-__global__ void __launch_bounds__(1024) dsa3d_sort_large_kernel(const uint32_t* start, uint32_t* csr,
+// Buckets queued by the previous kernel, sorted in place in global memory by
+// one 1024-thread block each (same network). Only an offset field that sends
+// hundreds of samples into one cell takes this path.
+__global__ void __launch_bounds__(1024) dsa3d_sort_large_kernel(const uint32_t* start, SampleRec* rec,
                                                                 const uint32_t* large, uint32_t large_cap) {
-    __shared__ uint32_t buf[kBlockSortMax];
     const uint32_t count = min(large[0], large_cap);
     for (uint32_t item = blockIdx.x; item < count; item += gridDim.x) {
         const uint32_t c = large[1 + item];
         const uint32_t s = start[c], n = start[c + 1] - s;
-        if (n <= kBlockSortMax) {
-            for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) buf[i] = csr[s + i];
-            __syncthreads();
-            bitonic_sort_u32(buf, n, threadIdx.x, blockDim.x, BlockSync());
-            for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) csr[s + i] = buf[i];
-        } else {
-            bitonic_sort_u32(csr + s, n, threadIdx.x, blockDim.x, BlockSync());
-        }
+        bitonic_sort(n, threadIdx.x, blockDim.x, GlobalRecSwap{reinterpret_cast<uint4*>(rec + s)}, BlockSync());
         __syncthreads();
     }
 }
@@ -364,21 +395,21 @@ __global__ void __launch_bounds__(1024) dsa3d_sort_large_kernel(const uint32_t* 
 template <typename T, int D>
 __global__ void __launch_bounds__(256) dsa3d_bwd_key_kernel(BwdArgs a) {
     constexpr int L = D / 8;
-    const int groups = blockDim.x / L;
     const int g = threadIdx.x / L;
     const int li = threadIdx.x % L;
-    const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
-    const int64_t task = (int64_t)lb * groups + g;
-    if (task >= a.g.ntasks) return;
-
-    int32_t b, eta, t, h, w;
-    int64_t tok;
-    task_coords(a.g, task, b, eta, t, h, w, tok);
-    const int64_t bh = (int64_t)b * a.g.nheads + (eta - a.g.head0);
+    int64_t bh;
+    int32_t t, h, wb;
+    block_coords(a.g, a.ord, xcd_logical_block(blockIdx.x, gridDim.x), bh, t, h, wb);
+    const int32_t w = wb + g;
+    if (w >= a.g.W) return;
+    const int32_t b = (int32_t)(bh / a.g.nheads);
+    const int32_t eta = a.g.head0 + (int32_t)(bh - (int64_t)b * a.g.nheads);
+    const int64_t tok = (((int64_t)b * a.g.T + t) * a.g.H + h) * a.g.W + w;
     const int64_t C = (int64_t)a.g.heads * D;
     const int64_t row_off = (int64_t)eta * D + li * 8;
     const T* Qb = reinterpret_cast<const T*>(a.q) + row_off;
     const T* Gb = reinterpret_cast<const T*>(a.dout) + row_off;
+    const uint4* rec = reinterpret_cast<const uint4*>(a.rec);
 
     float ak[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float av[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -388,9 +419,8 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_key_kernel(BwdArgs a) {
         const uint32_t cell = cell_index(a.g, bh, t - ct, h - ch, w - cw);
         const uint32_t e1 = a.start[cell + 1];
         for (uint32_t e = a.start[cell]; e < e1; ++e) {
-            const uint32_t sid = a.csr[e];
-            const uint4 r0 = *reinterpret_cast<const uint4*>(a.rec + sid);
-            const uint2 r1 = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint32_t*>(a.rec + sid) + 4);
+            const uint4 r0 = rec[2 * (uint64_t)e];
+            const uint4 r1 = rec[2 * (uint64_t)e + 1];
             const float ft = __uint_as_float(r0.z), fh = __uint_as_float(r0.w), fw = __uint_as_float(r1.x);
             const float wt = (ct ? ft : 1.0f - ft) * (ch ? fh : 1.0f - fh) * (cw ? fw : 1.0f - fw);
             const int64_t qrow = (int64_t)r1.y * C;
@@ -415,7 +445,7 @@ namespace {
 
 struct BwdLayout {
     uint64_t ncell, nsamp, nscan, large_cap;
-    size_t off_cnt, off_start, off_bsum, off_large, off_rec, off_csr, total;
+    size_t off_cnt, off_start, off_bsum, off_large, off_rec, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -434,32 +464,27 @@ bool bwd_layout(const dsa3d_desc& d, int64_t nh, BwdLayout& L) {
     L.off_bsum = o;  o += align256(L.nscan * 4 + 4);
     L.off_large = o; o += align256((L.large_cap + 1) * 4);
     L.off_rec = o;   o += align256(L.nsamp * sizeof(SampleRec));
-    L.off_csr = o;   o += align256(L.nsamp * 4);
     L.total = o;
     return true;
 }
 
 template <typename T, int D>
-hipError_t bwd_query_t(const BwdArgs& a, hipStream_t s) {
-    const int groups = 256 / (D / 8);
-    const int64_t nb = (a.g.ntasks + groups - 1) / groups;
+hipError_t bwd_query_t(const BwdArgs& a, int64_t nb, hipStream_t s) {
     LaunchScope ls(DSA3D_K_BWD_QUERY, s);
     hipLaunchKernelGGL((dsa3d_bwd_query_kernel<T, D>), dim3((unsigned)nb), dim3(256), 0, s, a);
     return hipGetLastError();
 }
-template <int D> hipError_t bwd_query_f32(const BwdArgs& a, hipStream_t s) { return bwd_query_t<float, D>(a, s); }
-template <int D> hipError_t bwd_query_bf16(const BwdArgs& a, hipStream_t s) { return bwd_query_t<bf16_t, D>(a, s); }
+template <int D> hipError_t bwd_query_f32(const BwdArgs& a, int64_t nb, hipStream_t s) { return bwd_query_t<float, D>(a, nb, s); }
+template <int D> hipError_t bwd_query_bf16(const BwdArgs& a, int64_t nb, hipStream_t s) { return bwd_query_t<bf16_t, D>(a, nb, s); }
 
 template <typename T, int D>
-hipError_t bwd_key_t(const BwdArgs& a, hipStream_t s) {
-    const int groups = 256 / (D / 8);
-    const int64_t nb = (a.g.ntasks + groups - 1) / groups;
+hipError_t bwd_key_t(const BwdArgs& a, int64_t nb, hipStream_t s) {
     LaunchScope ls(DSA3D_K_BWD_KEY, s);
     hipLaunchKernelGGL((dsa3d_bwd_key_kernel<T, D>), dim3((unsigned)nb), dim3(256), 0, s, a);
     return hipGetLastError();
 }
-template <int D> hipError_t bwd_key_f32(const BwdArgs& a, hipStream_t s) { return bwd_key_t<float, D>(a, s); }
-template <int D> hipError_t bwd_key_bf16(const BwdArgs& a, hipStream_t s) { return bwd_key_t<bf16_t, D>(a, s); }
+template <int D> hipError_t bwd_key_f32(const BwdArgs& a, int64_t nb, hipStream_t s) { return bwd_key_t<float, D>(a, nb, s); }
+template <int D> hipError_t bwd_key_bf16(const BwdArgs& a, int64_t nb, hipStream_t s) { return bwd_key_t<bf16_t, D>(a, nb, s); }
 
 }  // namespace
 
@@ -487,6 +512,7 @@ hipError_t launch_backward(const dsa3d_desc& d, const void* q, const void* k, co
     const int64_t chunk = bwd_heads_per_pass(d, ws_bytes);
     if (chunk < 1) return hipErrorInvalidValue;
     const bool f32 = d.dtype == DSA3D_F32;
+    const BlockOrder ord = make_block_order(d, attn_tokens_per_block(d.head_dim));
     hipError_t e;
     for (int64_t h0 = 0; h0 < d.heads; h0 += chunk) {
         const int32_t nh = (int32_t)std::min<int64_t>(chunk, d.heads - h0);
@@ -498,22 +524,28 @@ hipError_t launch_backward(const dsa3d_desc& d, const void* q, const void* k, co
         a.dq = dq; a.doff = doff; a.dk = dk; a.dv = dv;
         a.cnt = reinterpret_cast<uint32_t*>(base + L.off_cnt);
         a.start = reinterpret_cast<uint32_t*>(base + L.off_start);
-        a.csr = reinterpret_cast<uint32_t*>(base + L.off_csr);
         a.rec = reinterpret_cast<SampleRec*>(base + L.off_rec);
         a.g = make_task_grid(d, (int32_t)h0, nh);
+        a.ord = ord;
         a.P = d.P;
         a.scale = logit_scale(d);
         a.win = make_window(d);
         uint32_t* bsum = reinterpret_cast<uint32_t*>(base + L.off_bsum);
         uint32_t* large = reinterpret_cast<uint32_t*>(base + L.off_large);
         const uint32_t ncell = (uint32_t)L.ncell;
+        const int64_t nblocks = ord.nblk_bh * d.B * nh;
 
-        // counts and the large-bucket queue start at zero
+        // 1. bucket counts
         if ((e = fill_zero(a.cnt, L.ncell * 4, s)) != hipSuccess) return e;
         if ((e = fill_zero(large, 4, s)) != hipSuccess) return e;
-        if (f32) { DSA3D_DISPATCH_D_E(d.head_dim, bwd_query_f32, e, a, s); }
-        else { DSA3D_DISPATCH_D_E(d.head_dim, bwd_query_bf16, e, a, s); }
-        if (e != hipSuccess) return e;
+        {
+            LaunchScope ls(DSA3D_K_BWD_COUNT, s);
+            const unsigned gb = grid_for((int64_t)L.nsamp, 256, 1 << 16);
+            if (f32) hipLaunchKernelGGL(dsa3d_bwd_count_kernel<float>, dim3(gb), dim3(256), 0, s, a);
+            else hipLaunchKernelGGL(dsa3d_bwd_count_kernel<bf16_t>, dim3(gb), dim3(256), 0, s, a);
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        // 2. bucket starts; the counts become fill cursors
         {
             LaunchScope ls(DSA3D_K_BWD_SCAN, s);
             hipLaunchKernelGGL(dsa3d_scan_sums_kernel, dim3((unsigned)L.nscan), dim3(kScanThreads), 0, s, a.cnt, ncell,
@@ -523,23 +555,24 @@ hipError_t launch_backward(const dsa3d_desc& d, const void* q, const void* k, co
                                ncell, bsum, a.start);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        {
-            LaunchScope ls(DSA3D_K_BWD_INDEX, s);
-            hipLaunchKernelGGL(dsa3d_bwd_index_kernel, dim3(grid_for((int64_t)L.nsamp, 256, 1 << 16)), dim3(256), 0, s,
-                               a.rec, (uint64_t)L.nsamp, a.start, a.csr);
-        }
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = fill_zero(a.cnt, L.ncell * 4, s)) != hipSuccess) return e;
+        // 3. dq, doffsets and the sample records
+        if (f32) { DSA3D_DISPATCH_D_E(d.head_dim, bwd_query_f32, e, a, nblocks, s); }
+        else { DSA3D_DISPATCH_D_E(d.head_dim, bwd_query_bf16, e, a, nblocks, s); }
+        if (e != hipSuccess) return e;
+        // 4. fixed summation order
         if (d.deterministic) {
             LaunchScope ls(DSA3D_K_BWD_SORT, s);
             const unsigned nblk = (unsigned)((L.ncell + kSortBucketsPerBlock - 1) / kSortBucketsPerBlock);
-            hipLaunchKernelGGL(dsa3d_sort_small_kernel, dim3(nblk), dim3(64), 0, s, a.start, ncell, a.csr, large,
+            hipLaunchKernelGGL(dsa3d_sort_small_kernel, dim3(nblk), dim3(64), 0, s, a.start, ncell, a.rec, large,
                                (uint32_t)L.large_cap);
-            hipLaunchKernelGGL(dsa3d_sort_large_kernel, dim3(256), dim3(1024), 0, s, a.start, a.csr, large,
+            hipLaunchKernelGGL(dsa3d_sort_large_kernel, dim3(256), dim3(1024), 0, s, a.start, a.rec, large,
                                (uint32_t)L.large_cap);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        if (f32) { DSA3D_DISPATCH_D_E(d.head_dim, bwd_key_f32, e, a, s); }
-        else { DSA3D_DISPATCH_D_E(d.head_dim, bwd_key_bf16, e, a, s); }
+        // 5. dk, dv
+        if (f32) { DSA3D_DISPATCH_D_E(d.head_dim, bwd_key_f32, e, a, nblocks, s); }
+        else { DSA3D_DISPATCH_D_E(d.head_dim, bwd_key_bf16, e, a, nblocks, s); }
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -62,13 +62,14 @@ private:
 
 struct Window;
 struct TaskGrid;
+struct BlockOrder;
+BlockOrder make_block_order(const dsa3d_desc& d, int G);
+int attn_tokens_per_block(int head_dim);
 Window make_window(const dsa3d_desc& d);
 TaskGrid make_task_grid(const dsa3d_desc& d, int32_t head0, int32_t nheads);
 float logit_scale(const dsa3d_desc& d);
 unsigned grid_for(int64_t n, int threads, int64_t cap = 1 << 20);
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t s);
-
-int fwd_groups_per_block(int head_dim, int P);
 
 // Backward workspace: bytes for a pass over `nheads` heads (0 if such a pass
 // cannot be indexed with 32-bit sample and cell numbers) and the largest head

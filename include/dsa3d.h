@@ -123,13 +123,14 @@ int dsa3d_forward(const dsa3d_desc* desc, const void* q, const void* k, const vo
  * outputs is overwritten. `out` and `lse` are the forward's outputs for the
  * same inputs. No atomic operation touches a gradient: each query's dq and
  * doffsets are summed by the thread group that owns the query, and each key's
- * dk/dv row by the group that owns the key, which walks the samples whose
- * trilinear cell has that key as a corner (found through a per-cell index of
- * the samples kept in the workspace) and sums their contributions in float32
- * before one rounding to the output dtype. With deterministic = 1 that index
- * is sorted, so every sum runs in a fixed order and all outputs are bitwise
- * identical from run to run and for any workspace size; with deterministic = 0
- * the order of dk/dv terms may vary in the last bits.
+ * dk/dv row by the group that owns the key, which streams the records of the
+ * samples whose trilinear cell has that key as a corner (the samples are
+ * filed by base cell in the workspace) and sums their contributions in
+ * float32 before one rounding to the output dtype. With deterministic = 1 the
+ * records of every cell are sorted by sample, so every sum runs in a fixed
+ * order and all outputs are bitwise identical from run to run and for any
+ * workspace size; with deterministic = 0 the order of dk/dv terms, and so
+ * their last bits, may vary.
  * The workspace (at least dsa3d_workspace_min(desc, DSA3D_WS_BACKWARD), the
  * size of a pass over one head) holds the index; a larger one lets one pass
  * cover more heads. A single head whose B*T*H*W*P samples, or whose
@@ -162,7 +163,7 @@ int dsa3d_debug_geometry(const dsa3d_desc* desc, const void* offsets, int32_t* b
 typedef enum {
     DSA3D_K_PROJ_FORWARD = 1,   /* projection GEMM */
     DSA3D_K_FORWARD = 2,        /* fused sample + softmax + aggregate */
-    DSA3D_K_BWD_QUERY = 3,      /* backward per query: dq, doffsets, sample records */
+    DSA3D_K_BWD_QUERY = 3,      /* backward per query: dq, doffsets, sample records by cell */
     DSA3D_K_BWD_KEY = 4,        /* backward per key: dk, dv */
     DSA3D_K_FILL = 5,           /* workspace clearing */
     DSA3D_K_PROJ_BWD_DQ = 6,    /* dq += doffsets . W */
@@ -171,7 +172,7 @@ typedef enum {
     DSA3D_K_COLSUM = 9,         /* split column sums for dbias */
     DSA3D_K_GEOMETRY = 10,      /* test hook */
     DSA3D_K_BWD_SCAN = 11,      /* backward: bucket starts (3 small kernels, one entry) */
-    DSA3D_K_BWD_INDEX = 12,     /* backward: per-cell sample index */
+    DSA3D_K_BWD_COUNT = 12,     /* backward: samples per base cell */
     DSA3D_K_BWD_SORT = 13       /* backward, deterministic: bucket sort (2 kernels, one entry) */
 } dsa3d_kernel;
 

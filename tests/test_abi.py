@@ -95,13 +95,13 @@ def test_validate_rejects_p_mismatch_and_bad_flags():
 
 def _bwd_bounds(B, T, H, W, P, nh):
     """Bounds on the backward workspace of a pass over nh heads: a 32-byte
-    record and a 4-byte index entry per sample, two 4-byte words per base cell
-    (count and start) of the grid extended by one cell per axis, plus small
-    scan and queue buffers and 256-byte alignment."""
+    record per sample, two 4-byte words per base cell (count and start) of the
+    grid extended by one cell per axis, plus small scan and queue buffers and
+    256-byte alignment."""
     nsamp = nh * B * T * H * W * P
     ncell = nh * B * (T + 1) * (H + 1) * (W + 1)
-    lo = nsamp * 36 + ncell * 8
-    return lo, lo + nsamp // 1025 * 4 + ncell // 4096 * 4 + 8 * 256 + 64
+    lo = nsamp * 32 + ncell * 8
+    return lo, lo + nsamp // 513 * 4 + ncell // 4096 * 4 + 8 * 256 + 64
 
 
 def test_workspace_sizes():
@@ -115,7 +115,7 @@ def test_workspace_sizes():
     # the accumulation mode does not change the workspace
     d.deterministic = 1
     assert dsa.dsa3d_workspace_min(d, dsa.WS_BACKWARD) == one
-    # 1080p, 24 x 128, 3x5x5: one head needs ~5.6 GB; the recommended size
+    # 1080p, 24 x 128, 3x5x5: one head needs ~5.0 GB; the recommended size
     # takes as many heads as fit in 16 GiB
     big = dsa.make_desc(1, 256, 68, 120, 24, 128, (3, 5, 5), dtype=torch.bfloat16, deterministic=True)
     ph = dsa.dsa3d_workspace_min(big, dsa.WS_BACKWARD)
