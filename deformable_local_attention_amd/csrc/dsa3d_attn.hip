@@ -47,12 +47,14 @@ __global__ void __launch_bounds__(256) dsa3d_fwd_kernel(FwdArgs a) {
     if (w >= a.g.W) return;  // no block-wide barrier below
     const int32_t b = (int32_t)(bh / a.g.nheads);
     const int32_t eta = a.g.head0 + (int32_t)(bh - (int64_t)b * a.g.nheads);
-    const int64_t tok = (((int64_t)b * a.g.T + t) * a.g.H + h) * a.g.W + w;
+    const uint32_t tok_b = (uint32_t)b * (uint32_t)a.g.T * (uint32_t)a.g.H * (uint32_t)a.g.W;
+    const int64_t tok = (int64_t)tok_b + ((int64_t)t * a.g.H + h) * a.g.W + w;
     const int64_t C = (int64_t)a.g.heads * D;
     const int64_t row_off = (int64_t)eta * D + li * 8;
-    const T* Kb = reinterpret_cast<const T*>(a.k) + row_off;
-    const T* Vb = reinterpret_cast<const T*>(a.v) + row_off;
-    const T* zero = reinterpret_cast<const T*>(g_zero_row);
+    const CornerStrides cs = corner_strides(a.g, C * (int64_t)sizeof(T));
+    const char* Kb = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.k) + row_off);
+    const char* Vb = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.v) + row_off);
+    const char* zero = reinterpret_cast<const char*>(g_zero_row);
     const T* offq = reinterpret_cast<const T*>(a.off) + (tok * a.g.heads + eta) * (int64_t)a.P * 3;
 
     Frag8<T> qf;
@@ -60,33 +62,46 @@ __global__ void __launch_bounds__(256) dsa3d_fwd_kernel(FwdArgs a) {
 
     float m = -INFINITY, z = 0.0f;
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int p = 0; p < a.P; ++p) {
-        float dt, dh, dw;
-        load_offsets<T>(offq + p * 3, dt, dh, dw);
-        int32_t t0 = 0, h0 = 0, w0c = 0;
-        float ft = 0.f, fh = 0.f, fw = 0.f;
-        const bool inside = sample_geometry(a.win, t, h, w, p, dt, dh, dw, t0, h0, w0c, ft, fh, fw);
-        Corners c;
-        make_corners(a.g, b, t0, h0, w0c, ft, fh, fw, inside, c);
-        Frag8<T> kf[8], vf[8];
+    const Window& win = a.win;
+    for (int it = 0; it < win.kt; ++it) {
+        const float rt = (float)(t + win.dil_t * (it - win.rt));
+        for (int ih = 0; ih < win.kh; ++ih) {
+            const float rh = (float)(h + win.dil_h * (ih - win.rh));
+            for (int iw = 0; iw < win.kw; ++iw) {
+                const float rw = (float)(w + win.dil_w * (iw - win.rw));
+                float dt, dh, dw;
+                load_offsets<T>(offq, dt, dh, dw);
+                offq += 3;
+                int32_t t0 = 0, h0 = 0, w0c = 0;
+                float ft = 0.f, fh = 0.f, fw = 0.f;
+                const bool inside = sample_cell(rt, rh, rw, dt, dh, dw, t0, h0, w0c, ft, fh, fw);
+                CellCorners cc;
+                cell_corners(a.g, tok_b, inside, t0, h0, w0c, ft, fh, fw, cc);
+                CornerAddr ca;
+                corner_addresses(cc, Kb, Vb, cs, zero, __all(cc.all_in), ca);
+                Frag8<T> kf[8], vf[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            kf[i].load(c.tok[i] >= 0 ? Kb + c.tok[i] * C : zero);
-            vf[i].load(c.tok[i] >= 0 ? Vb + c.tok[i] * C : zero);
+                for (int i = 0; i < 8; ++i) {
+                    kf[i].load(reinterpret_cast<const T*>(ca.a[i]));
+                    vf[i].load(reinterpret_cast<const T*>(ca.b[i]));
+                }
+                float acc = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc = fmaf(cc.w[i], kf[i].dot(qf, 0.0f), acc);
+                const float s = a.scale * group_sum<L>(acc);
+                const float m_new = fmaxf(m, s);
+                const float alpha = __expf(m - m_new);  // 0 for the first sample (m = -inf)
+                const float beta = __expf(s - m_new);
+                z = fmaf(z, alpha, beta);
+                if (!__all(m_new == m)) {  // the running max rarely moves after the first samples
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o[e] *= alpha;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) vf[i].axpy(beta * cc.w[i], o);
+                m = m_new;
+            }
         }
-        float acc = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc = fmaf(c.w[i], kf[i].dot(qf, 0.0f), acc);
-        const float s = a.scale * group_sum<L>(acc);
-        const float m_new = fmaxf(m, s);
-        const float alpha = __expf(m - m_new);  // 0 for the first sample (m = -inf)
-        const float beta = __expf(s - m_new);
-        z = fmaf(z, alpha, beta);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] *= alpha;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) vf[i].axpy(beta * c.w[i], o);
-        m = m_new;
     }
     const float inv_z = 1.0f / z;
 #pragma unroll

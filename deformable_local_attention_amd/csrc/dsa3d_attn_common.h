@@ -75,26 +75,88 @@ __device__ __forceinline__ void block_coords(const TaskGrid& g, const BlockOrder
     w0 = (k * o.SW + dw) * o.G;
 }
 
-// The eight trilinear corners x0 + {0,1}^3 of one sample: token index (or -1
-// outside the grid) and weight prod_axis (c ? f : 1 - f). Corner i has offset
-// (i>>2 & 1, i>>1 & 1, i & 1) in (t, h, w).
-struct Corners {
-    int64_t tok[8];
+// The eight corners of a sample's cell, for the gathering kernels: weights
+// with the grid bounds folded in (a corner outside the grid has weight 0 and
+// must be read as a zero row), the token of corner 0 and whether all eight
+// corners lie in the grid. Corner i is token tok0 + ct*H*W + ch*W + cw for
+// (ct, ch, cw) = (i>>2 & 1, i>>1 & 1, i & 1).
+struct CellCorners {
     float w[8];
+    uint32_t tok0;  // meaningful for the corners that are in the grid
+    uint32_t valid; // bit i: corner i is in the grid
+    bool all_in;
 };
 
-__device__ __forceinline__ void make_corners(const TaskGrid& g, int32_t b, int32_t t0, int32_t h0, int32_t w0,
-                                             float ft, float fh, float fw, bool inside, Corners& c) {
-    const float at[2] = {1.0f - ft, ft}, ah[2] = {1.0f - fh, fh}, aw[2] = {1.0f - fw, fw};
-    const int64_t base_b = (int64_t)b * g.T;
+__device__ __forceinline__ void cell_corners(const TaskGrid& g, uint32_t tok_b, bool inside, int32_t t0, int32_t h0,
+                                             int32_t w0, float ft, float fh, float fw, CellCorners& cc) {
+    const bool ta = inside && (uint32_t)t0 < (uint32_t)g.T, tb = inside && (uint32_t)(t0 + 1) < (uint32_t)g.T;
+    const bool ha = inside && (uint32_t)h0 < (uint32_t)g.H, hb = inside && (uint32_t)(h0 + 1) < (uint32_t)g.H;
+    const bool wa = inside && (uint32_t)w0 < (uint32_t)g.W, wb = inside && (uint32_t)(w0 + 1) < (uint32_t)g.W;
+    const float at[2] = {ta ? 1.0f - ft : 0.0f, tb ? ft : 0.0f};
+    const float ah[2] = {ha ? 1.0f - fh : 0.0f, hb ? fh : 0.0f};
+    const float aw[2] = {wa ? 1.0f - fw : 0.0f, wb ? fw : 0.0f};
+    const bool vt[2] = {ta, tb}, vh[2] = {ha, hb}, vw[2] = {wa, wb};
+    uint32_t valid = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int ct = (i >> 2) & 1, ch = (i >> 1) & 1, cw = i & 1;
-        const int32_t tt = t0 + ct, hh = h0 + ch, ww = w0 + cw;
-        const bool ok = inside && (uint32_t)tt < (uint32_t)g.T && (uint32_t)hh < (uint32_t)g.H &&
-                        (uint32_t)ww < (uint32_t)g.W;
-        c.tok[i] = ok ? ((base_b + tt) * g.H + hh) * (int64_t)g.W + ww : -1;
-        c.w[i] = ok ? at[ct] * ah[ch] * aw[cw] : 0.0f;
+        cc.w[i] = at[ct] * ah[ch] * aw[cw];
+        valid |= (vt[ct] && vh[ch] && vw[cw]) ? (1u << i) : 0u;
+    }
+    cc.valid = valid;
+    cc.all_in = valid == 0xffu;
+    cc.tok0 = tok_b + ((uint32_t)t0 * (uint32_t)g.H + (uint32_t)h0) * (uint32_t)g.W + (uint32_t)w0;
+}
+
+// Strides of the corner rows of one tensor: tokens per frame and per row,
+// and the same in bytes (row_bytes = bytes per token).
+struct CornerStrides {
+    uint32_t hw_tok, w_tok;
+    int64_t row_bytes, dh_bytes, dt_bytes;
+};
+
+__device__ __forceinline__ CornerStrides corner_strides(const TaskGrid& g, int64_t row_bytes) {
+    CornerStrides s;
+    s.hw_tok = (uint32_t)g.H * (uint32_t)g.W;
+    s.w_tok = (uint32_t)g.W;
+    s.row_bytes = row_bytes;
+    s.dh_bytes = (int64_t)g.W * row_bytes;
+    s.dt_bytes = (int64_t)s.hw_tok * row_bytes;
+    return s;
+}
+
+// Byte addresses of the eight corner rows in two tensors of the same layout
+// (keys and values, or queries and output gradients), starting at `base_a` /
+// `base_b` (the lane's part of the head's row of token 0); corners outside the
+// grid get `zero`. When every lane of the wave has its whole cell in the grid
+// the selects are skipped.
+struct CornerAddr {
+    const char* a[8];
+    const char* b[8];
+};
+
+__device__ __forceinline__ void corner_addresses(const CellCorners& cc, const char* base_a, const char* base_b,
+                                                 const CornerStrides& s, const char* zero, bool wave_all_in,
+                                                 CornerAddr& ca) {
+    const int64_t b_minus_a = base_b - base_a;
+    if (wave_all_in) {
+        const char* p0 = base_a + (int64_t)(int32_t)cc.tok0 * s.row_bytes;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            ca.a[i] = p0 + (((i >> 2) & 1) ? s.dt_bytes : 0) + (((i >> 1) & 1) ? s.dh_bytes : 0) +
+                      ((i & 1) ? s.row_bytes : 0);
+            ca.b[i] = ca.a[i] + b_minus_a;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t tok = cc.tok0 + (((i >> 2) & 1) ? s.hw_tok : 0u) + (((i >> 1) & 1) ? s.w_tok : 0u) +
+                                 (uint32_t)(i & 1);
+            const bool ok = (cc.valid >> i) & 1u;
+            const int64_t off = (int64_t)(int32_t)tok * s.row_bytes;
+            ca.a[i] = ok ? base_a + off : zero;
+            ca.b[i] = ok ? base_b + off : zero;
+        }
     }
 }
 
@@ -106,7 +168,9 @@ __device__ __forceinline__ void load_offsets(const T* off, float& dt, float& dh,
 }
 
 // Zero row read in place of a corner outside the grid (256 floats: the widest
-// row); each code object holds its own copy.
-static __device__ __attribute__((aligned(16))) const float g_zero_row[256] = {0.0f};
+// row); each code object holds its own copy. It is never written; it is not
+// declared const so that it lives in the global address space like the
+// tensors, which keeps the row loads global rather than flat.
+static __device__ __attribute__((aligned(16))) float g_zero_row[256] = {0.0f};
 
 }  // namespace dsa3d

@@ -192,17 +192,19 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_query_kernel(BwdArgs a) {
     if (w >= a.g.W) return;  // no block-wide barrier below
     const int32_t b = (int32_t)(bh / a.g.nheads);
     const int32_t eta = a.g.head0 + (int32_t)(bh - (int64_t)b * a.g.nheads);
-    const int64_t tok = (((int64_t)b * a.g.T + t) * a.g.H + h) * a.g.W + w;
+    const uint32_t tok_b = (uint32_t)b * (uint32_t)a.g.T * (uint32_t)a.g.H * (uint32_t)a.g.W;
+    const int64_t tok = (int64_t)tok_b + ((int64_t)t * a.g.H + h) * a.g.W + w;
     const int64_t task = ((bh * a.g.T + t) * a.g.H + h) * (int64_t)a.g.W + w;
     const int64_t C = (int64_t)a.g.heads * D;
     const int64_t row_off = (int64_t)eta * D + li * 8;
-    const T* Kb = reinterpret_cast<const T*>(a.k) + row_off;
-    const T* Vb = reinterpret_cast<const T*>(a.v) + row_off;
-    const T* zero = reinterpret_cast<const T*>(g_zero_row);
+    const CornerStrides cs = corner_strides(a.g, C * (int64_t)sizeof(T));
+    const char* Kb = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.k) + row_off);
+    const char* Vb = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.v) + row_off);
+    const char* zero = reinterpret_cast<const char*>(g_zero_row);
     const int64_t offrow = (tok * a.g.heads + eta) * (int64_t)a.P * 3;
     const T* offq = reinterpret_cast<const T*>(a.off) + offrow;
     T* doffq = reinterpret_cast<T*>(a.doff) + offrow;
-    const uint32_t sid0 = (uint32_t)(task * a.P);
+    uint32_t sid = (uint32_t)(task * a.P);
 
     Frag8<T> qf, gf, of;
     qf.load(reinterpret_cast<const T*>(a.q) + tok * C + row_off);
@@ -212,64 +214,78 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_query_kernel(BwdArgs a) {
     const float lse = a.lse[tok * a.g.heads + eta];
 
     float dq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int p = 0; p < a.P; ++p) {
-        float dt, dh, dw;
-        load_offsets<T>(offq + p * 3, dt, dh, dw);
-        int32_t t0 = 0, h0 = 0, w0 = 0;
-        float ft = 0.f, fh = 0.f, fw = 0.f;
-        const bool inside = sample_geometry(a.win, t, h, w, p, dt, dh, dw, t0, h0, w0, ft, fh, fw);
-        Corners c;
-        make_corners(a.g, b, t0, h0, w0, ft, fh, fw, inside, c);
-        Frag8<T> kf[8], vf[8];
+    const Window& win = a.win;
+    for (int it = 0; it < win.kt; ++it) {
+        const float rt = (float)(t + win.dil_t * (it - win.rt));
+        for (int ih = 0; ih < win.kh; ++ih) {
+            const float rh = (float)(h + win.dil_h * (ih - win.rh));
+            for (int iw = 0; iw < win.kw; ++iw, offq += 3, doffq += 3, ++sid) {
+                const float rw = (float)(w + win.dil_w * (iw - win.rw));
+                float dt, dh, dw;
+                load_offsets<T>(offq, dt, dh, dw);
+                int32_t t0 = 0, h0 = 0, w0 = 0;
+                float ft = 0.f, fh = 0.f, fw = 0.f;
+                const bool inside = sample_cell(rt, rh, rw, dt, dh, dw, t0, h0, w0, ft, fh, fw);
+                CellCorners cc;
+                cell_corners(a.g, tok_b, inside, t0, h0, w0, ft, fh, fw, cc);
+                CornerAddr ca;
+                corner_addresses(cc, Kb, Vb, cs, zero, __all(cc.all_in), ca);
+                Frag8<T> kf[8], vf[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            kf[i].load(c.tok[i] >= 0 ? Kb + c.tok[i] * C : zero);
-            vf[i].load(c.tok[i] >= 0 ? Vb + c.tok[i] * C : zero);
-        }
-        float qk[8], dv[8];
+                for (int i = 0; i < 8; ++i) {
+                    kf[i].load(reinterpret_cast<const T*>(ca.a[i]));
+                    vf[i].load(reinterpret_cast<const T*>(ca.b[i]));
+                }
+                float qk[8], dv[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            qk[i] = kf[i].dot(qf, 0.0f);
-            dv[i] = vf[i].dot(gf, 0.0f);
-        }
-        // weighted sums: logit, dL/da, and the offset-derivative sums per axis
-        const float at[2] = {1.0f - ft, ft}, ah[2] = {1.0f - fh, fh}, aw[2] = {1.0f - fw, fw};
-        float r[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                for (int i = 0; i < 8; ++i) {
+                    qk[i] = kf[i].dot(qf, 0.0f);
+                    dv[i] = vf[i].dot(gf, 0.0f);
+                }
+                // weighted sums: logit, dL/da, and the offset-derivative sums per
+                // axis. The factors below carry the grid bounds: a corner outside
+                // the grid has a zero row, so its dot products are 0 anyway.
+                const float at[2] = {1.0f - ft, ft}, ah[2] = {1.0f - fh, fh}, aw[2] = {1.0f - fw, fw};
+                float r[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int ct = (i >> 2) & 1, ch = (i >> 1) & 1, cw = i & 1;
-            const float st = ct ? 1.f : -1.f, sh = ch ? 1.f : -1.f, sw = cw ? 1.f : -1.f;
-            const float gt = st * ah[ch] * aw[cw], gh = at[ct] * sh * aw[cw], gw = at[ct] * ah[ch] * sw;
-            // zero rows give zero dot products, so no validity test is needed here
-            r[0] = fmaf(c.w[i], qk[i], r[0]);
-            r[1] = fmaf(c.w[i], dv[i], r[1]);
-            r[2] = fmaf(gt, qk[i], r[2]);
-            r[3] = fmaf(gh, qk[i], r[3]);
-            r[4] = fmaf(gw, qk[i], r[4]);
-            r[5] = fmaf(gt, dv[i], r[5]);
-            r[6] = fmaf(gh, dv[i], r[6]);
-            r[7] = fmaf(gw, dv[i], r[7]);
-        }
+                for (int i = 0; i < 8; ++i) {
+                    const int ct = (i >> 2) & 1, ch = (i >> 1) & 1, cw = i & 1;
+                    const float st = ct ? 1.f : -1.f, sh = ch ? 1.f : -1.f, sw = cw ? 1.f : -1.f;
+                    const float gt = st * ah[ch] * aw[cw], gh = at[ct] * sh * aw[cw], gw = at[ct] * ah[ch] * sw;
+                    r[0] = fmaf(cc.w[i], qk[i], r[0]);
+                    r[1] = fmaf(cc.w[i], dv[i], r[1]);
+                    r[2] = fmaf(gt, qk[i], r[2]);
+                    r[3] = fmaf(gh, qk[i], r[3]);
+                    r[4] = fmaf(gw, qk[i], r[4]);
+                    r[5] = fmaf(gt, dv[i], r[5]);
+                    r[6] = fmaf(gh, dv[i], r[6]);
+                    r[7] = fmaf(gw, dv[i], r[7]);
+                }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) r[j] = group_sum<L>(r[j]);
-        const float s = a.scale * r[0];
-        const float ap = __expf(s - lse);
-        const float ds = ap * (r[1] - Dsum);
-        const float ck = a.scale * ds;
+                for (int j = 0; j < 8; ++j) r[j] = group_sum<L>(r[j]);
+                const float s = a.scale * r[0];
+                const float ap = __expf(s - lse);
+                const float ds = ap * (r[1] - Dsum);
+                const float ck = a.scale * ds;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) kf[i].axpy(ck * c.w[i], dq);
-        if (li == 0) {
-            store_scalar<T>(doffq + p * 3 + 0, fmaf(ck, r[2], ap * r[5]));
-            store_scalar<T>(doffq + p * 3 + 1, fmaf(ck, r[3], ap * r[6]));
-            store_scalar<T>(doffq + p * 3 + 2, fmaf(ck, r[4], ap * r[7]));
-            const bool reaches = inside && t0 >= -1 && t0 < a.g.T && h0 >= -1 && h0 < a.g.H && w0 >= -1 &&
-                                 w0 < a.g.W;
-            if (reaches) {
-                const uint32_t cell = cell_index(a.g, bh, t0, h0, w0);
-                const uint32_t slot = a.start[cell] + atomicAdd(a.cnt + cell, 1u);
-                uint4* dst = reinterpret_cast<uint4*>(a.rec + slot);
-                dst[0] = make_uint4(__float_as_uint(ck), __float_as_uint(ap), __float_as_uint(ft), __float_as_uint(fh));
-                dst[1] = make_uint4(__float_as_uint(fw), (uint32_t)tok, sid0 + (uint32_t)p, 0u);
+                for (int i = 0; i < 8; ++i) kf[i].axpy(ck * cc.w[i], dq);
+                if (li == 0) {
+                    store_scalar<T>(doffq + 0, fmaf(ck, r[2], ap * r[5]));
+                    store_scalar<T>(doffq + 1, fmaf(ck, r[3], ap * r[6]));
+                    store_scalar<T>(doffq + 2, fmaf(ck, r[4], ap * r[7]));
+                    if (cc.valid != 0u) {
+                        const uint32_t cell = cell_index(a.g, bh, t0, h0, w0);
+                        const uint32_t slot = a.start[cell] + atomicAdd(a.cnt + cell, 1u);
+                        // the count kernel filed exactly these samples; the bound
+                        // only keeps a write inside its bucket should they ever differ
+                        if (slot < a.start[cell + 1]) {
+                            uint4* dst = reinterpret_cast<uint4*>(a.rec + slot);
+                            dst[0] = make_uint4(__float_as_uint(ck), __float_as_uint(ap), __float_as_uint(ft),
+                                                __float_as_uint(fh));
+                            dst[1] = make_uint4(__float_as_uint(fw), (uint32_t)tok, sid, 0u);
+                        }
+                    }
+                }
             }
         }
     }

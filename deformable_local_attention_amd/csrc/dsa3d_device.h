@@ -101,11 +101,24 @@ template <> __device__ __forceinline__ void store_scalar<bf16_t>(bf16_t* p, floa
 }
 
 // Sum over the aligned group of L lanes that owns one (query, head); every
-// lane of the group receives the total.
+// lane of the group receives the total. Within a 16-lane DPP row the steps are
+// DPP moves that read lanes of the same group only: swap neighbours (quad
+// permutation 1,0,3,2), swap pairs (2,3,0,1), mirror each half row (lane i <->
+// 7-i) and mirror the row (i <-> 15-i); after the first k steps every lane
+// holds the sum of its aligned 2^k lanes. Wider groups finish with shuffles.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
 template <int L>
 __device__ __forceinline__ float group_sum(float x) {
+    if constexpr (L >= 2) x = dpp_add<0xB1>(x);   // quad_perm [1,0,3,2]
+    if constexpr (L >= 4) x = dpp_add<0x4E>(x);   // quad_perm [2,3,0,1]
+    if constexpr (L >= 8) x = dpp_add<0x141>(x);  // row_half_mirror
+    if constexpr (L >= 16) x = dpp_add<0x140>(x); // row_mirror
 #pragma unroll
-    for (int m = L / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+    for (int m = 16; m < L; m <<= 1) x += __shfl_xor(x, m, 64);
     return x;
 }
 
@@ -129,16 +142,13 @@ struct Window {
     int32_t rt, rh, rw;  // (k-1)/2
 };
 
-__device__ __forceinline__ bool sample_geometry(const Window& win, int32_t t, int32_t h, int32_t w, int32_t p,
-                                                float dt, float dh, float dw, int32_t& t0, int32_t& h0,
-                                                int32_t& w0, float& ft, float& fh, float& fw) {
-    const int32_t it = p / win.khw;
-    const int32_t rem = p - it * win.khw;
-    const int32_t ih = rem / win.kw;
-    const int32_t iw = rem - ih * win.kw;
-    const float pt = __fadd_rn((float)(t + win.dil_t * (it - win.rt)), dt);
-    const float ph = __fadd_rn((float)(h + win.dil_h * (ih - win.rh)), dh);
-    const float pw = __fadd_rn((float)(w + win.dil_w * (iw - win.rw)), dw);
+// The cell of a sample whose reference point (integers, converted exactly to
+// float32) is (rt, rh, rw) and whose offset is (dt, dh, dw).
+__device__ __forceinline__ bool sample_cell(float rt, float rh, float rw, float dt, float dh, float dw, int32_t& t0,
+                                            int32_t& h0, int32_t& w0, float& ft, float& fh, float& fw) {
+    const float pt = __fadd_rn(rt, dt);
+    const float ph = __fadd_rn(rh, dh);
+    const float pw = __fadd_rn(rw, dw);
     const float lim = 1073741824.0f;  // 2^30
     if (!(fabsf(pt) < lim) || !(fabsf(ph) < lim) || !(fabsf(pw) < lim)) return false;
     const float xt = floorf(pt), xh = floorf(ph), xw = floorf(pw);
@@ -149,6 +159,18 @@ __device__ __forceinline__ bool sample_geometry(const Window& win, int32_t t, in
     h0 = (int32_t)xh;
     w0 = (int32_t)xw;
     return true;
+}
+
+// Same, from the window point number p (row-major over the window).
+__device__ __forceinline__ bool sample_geometry(const Window& win, int32_t t, int32_t h, int32_t w, int32_t p,
+                                                float dt, float dh, float dw, int32_t& t0, int32_t& h0,
+                                                int32_t& w0, float& ft, float& fh, float& fw) {
+    const int32_t it = p / win.khw;
+    const int32_t rem = p - it * win.khw;
+    const int32_t ih = rem / win.kw;
+    const int32_t iw = rem - ih * win.kw;
+    return sample_cell((float)(t + win.dil_t * (it - win.rt)), (float)(h + win.dil_h * (ih - win.rh)),
+                       (float)(w + win.dil_w * (iw - win.rw)), dt, dh, dw, t0, h0, w0, ft, fh, fw);
 }
 
 }  // namespace dsa3d
