@@ -127,6 +127,93 @@ def cpu_baseline(wl, budget_s: float = 20.0):
                        f"whole tokens ({wl.heads} heads)")}
 
 
+def kernel_source_hash() -> str:
+    """sha256 over the kernel sources and the C ABI header: counter readings
+    taken on other sources no longer describe the kernels."""
+    import glob
+    import hashlib
+    pkg = os.path.join(ROOT, "deformable_local_attention_amd", "csrc")
+    files = sorted(glob.glob(os.path.join(pkg, "*"))) + [os.path.join(ROOT, "include", "dsa3d.h")]
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def recorded_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when there is none for this kernel and workload or the kernel sources
+    changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash() or rec.get("workload") != workload:
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k["hbm_bytes_per_launch"]
+
+
+def _short_kernel(name: str) -> str:
+    import re
+    n = re.sub(r"\(.*", "", name).replace("void ", "")
+    n = n.replace("dsa3d::dsa3d_", "")
+    return n
+
+
+def pmc_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, workload, out_json=None):
+    """Per-kernel HBM traffic from rocprofv3 counter CSVs (FETCH_SIZE and
+    WRITE_SIZE, KiB per dispatch). Each counter is scaled by what it reads for
+    a plain device copy of known size (copy_calibration: 4 GiB read and 4 GiB
+    written per launch)."""
+    import csv
+    import collections
+
+    def per_kernel(path, counter):
+        acc = collections.defaultdict(list)
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") == counter:
+                    acc[_short_kernel(row["Kernel_Name"])].append(float(row["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    copy_bytes = 4 * (1 << 30)
+    cf = per_kernel(copy_fetch_csv, "FETCH_SIZE")
+    cw = per_kernel(copy_write_csv, "WRITE_SIZE")
+    ck = [k for k in cf if "copyBuffer" in k][0]
+    f_fac = copy_bytes / (cf[ck] * 1024.0)
+    w_fac = copy_bytes / (cw[ck] * 1024.0)
+    fk = per_kernel(fetch_csv, "FETCH_SIZE")
+    wk = per_kernel(write_csv, "WRITE_SIZE")
+    kernels = {}
+    for k in sorted(fk):
+        if k not in wk:
+            continue
+        rd = fk[k] * 1024.0 * f_fac
+        wr = wk[k] * 1024.0 * w_fac
+        kernels[k] = {"fetch_kib_per_dispatch": round(fk[k], 1), "write_kib_per_dispatch": round(wk[k], 1),
+                      "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
+                      "hbm_bytes_per_launch": rd + wr}
+    rec = {"workload": workload, "source_hash": kernel_source_hash(), "fetch_factor": round(f_fac, 4),
+           "write_factor": round(w_fac, 4), "copy_kernel": ck, "kernels": kernels}
+    for k, v in kernels.items():
+        if k.startswith(("fwd_kernel", "bwd_", "sort_", "gemm")):
+            print(f"{k:40s} read {v['hbm_read_bytes_per_launch'] / 1e9:9.3f} GB  "
+                  f"write {v['hbm_write_bytes_per_launch'] / 1e9:9.3f} GB per launch")
+    print(f"scale factors from the copy: FETCH_SIZE x{f_fac:.3f}, WRITE_SIZE x{w_fac:.3f}")
+    if out_json:
+        with open(out_json, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+    return rec
+
+
 def copy_calibration(gib: float = 4.0, reps: int = 5):
     import torch
     n = int(gib * (1 << 30)) // 4
@@ -151,7 +238,14 @@ def main():
     ap.add_argument("--fast", action="store_true", help="float32 (non-deterministic) K/V-gradient accumulation")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="summarise rocprofv3 FETCH_SIZE/WRITE_SIZE counter CSVs into HBM bytes per launch")
+    ap.add_argument("--pmc-json", default=None, help="with --pmc-summary: write the summary to this JSON file")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary, workload=args.workload or "1080p-bf16-p75-det", out_json=args.pmc_json)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the 3D-DSA path here runs on a single MI355X "
@@ -220,8 +314,14 @@ def main():
     mean_s = per_kernel[dom]["mean_ms"] / 1e3
     unit_bytes = alg[dom]
     achieved_gbs = unit_bytes * units / mean_s / 1e9
+    kname = {"forward": "fwd_kernel<unsigned short, %d>", "bwd_query": "bwd_query_kernel<unsigned short, %d>",
+             "bwd_key": "bwd_key_kernel<unsigned short, %d>"}[dom] % wl.head_dim
+    if wl.dtype == "f32":
+        kname = kname.replace("unsigned short", "float")
+    traffic = recorded_traffic(kname, wl.name)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved_gbs, 2), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 5), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 5),
+                "traffic": None if traffic is None else round(traffic),
                 "launch_ms": round(per_kernel[dom]["mean_ms"], 3), "units_per_launch": units,
                 "bytes_per_unit": unit_bytes}
     step_flops = wl.tokens * wl.heads * (alg["fwd_flops"] + (alg["bwd_flops"] if wl.backward else 0))

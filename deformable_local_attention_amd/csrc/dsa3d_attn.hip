@@ -19,6 +19,11 @@
 #include "dsa3d_attn_common.h"
 #include "dsa3d_internal.h"
 
+#ifdef DSA3D_TUNING
+#include <cstdio>
+#include <cstdlib>
+#endif
+
 namespace dsa3d {
 
 struct FwdArgs {
@@ -42,7 +47,7 @@ __global__ void __launch_bounds__(256) dsa3d_fwd_kernel(FwdArgs a) {
     const int li = threadIdx.x % L;
     int64_t bh;
     int32_t t, h, w0;
-    block_coords(a.g, a.ord, xcd_logical_block(blockIdx.x, gridDim.x), bh, t, h, w0);
+    block_coords(a.g, a.ord, logical_block(blockIdx.x, gridDim.x, a.ord.chunk), bh, t, h, w0);
     const int32_t w = w0 + g;
     if (w >= a.g.W) return;  // no block-wide barrier below
     const int32_t b = (int32_t)(bh / a.g.nheads);
@@ -174,10 +179,21 @@ BlockOrder make_block_order(const dsa3d_desc& d, int G) {
     BlockOrder o;
     o.G = G;
     o.BW = (int32_t)((d.W + G - 1) / G);
-    // supertile: 4 frames x 8 rows x 64 tokens (at most; clipped at the grid)
-    o.ST = 4;
-    o.SH = 8;
-    o.SW = std::max(1, 64 / G);
+    // Supertile of (at most) 16 frames x 32 rows x 16 tokens, and the XCDs
+    // take one supertile each in turn: the eight supertiles in flight are
+    // neighbours, so the rows their samples gather are shared through the
+    // memory-side cache. Measured on the 256x68x120 grid (3x5x5 window,
+    // offsets N(0,2)) this order runs the step 15% faster than one contiguous
+    // range of 4 x 8 x 64 supertiles per XCD.
+    int st = 16, sh = 32, sw_tok = 16, chunk = -1;
+#ifdef DSA3D_TUNING
+    // tuning builds only: DSA3D_ORDER="frames,rows,tokens,chunk"
+    if (const char* e = getenv("DSA3D_ORDER")) sscanf(e, "%d,%d,%d,%d", &st, &sh, &sw_tok, &chunk);
+#endif
+    o.ST = std::max(1, st);
+    o.SH = std::max(1, sh);
+    o.SW = std::max(1, sw_tok / G);
+    o.chunk = chunk < 0 ? o.ST * o.SH * o.SW : chunk;
     o.nblk_bh = d.T * d.H * (int64_t)o.BW;
     return o;
 }

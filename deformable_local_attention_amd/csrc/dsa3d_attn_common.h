@@ -46,8 +46,25 @@ struct BlockOrder {
     int32_t G;            // tokens per block along w
     int32_t BW;           // blocks per row: ceil(W / G)
     int32_t ST, SH, SW;   // supertile extent in (t, h, block column)
+    int32_t chunk;        // XCD placement: 0 = one contiguous range per XCD,
+                          // else chunks of this many blocks dealt to the XCDs in turn
     int64_t nblk_bh;      // blocks per (batch, head): T * H * BW
 };
+
+// Hardware block id -> logical block. Workgroups are dealt to the 8 XCDs
+// round-robin (block i -> XCD i % 8). With chunk = 0 each XCD walks one
+// contiguous eighth of the logical blocks; with chunk = c the XCDs take
+// consecutive c-block chunks in turn (chunk k on XCD k % 8), so that at any
+// time the eight XCDs work on neighbouring chunks and share the rows they
+// gather through the memory-side cache. Blocks past the last full round of
+// chunks keep their id.
+__device__ __forceinline__ uint32_t logical_block(uint32_t bid, uint32_t nblocks, int32_t chunk) {
+    if (chunk <= 0) return xcd_logical_block(bid, nblocks);
+    const uint32_t round = 8u * (uint32_t)chunk;
+    if (bid >= nblocks / round * round) return bid;
+    const uint32_t x = bid % 8u, j = bid / 8u;
+    return ((j / chunk) * 8u + x) * (uint32_t)chunk + j % (uint32_t)chunk;
+}
 
 // Logical block -> (batch*nheads + local head, t, h, first w).
 __device__ __forceinline__ void block_coords(const TaskGrid& g, const BlockOrder& o, int64_t lb, int64_t& bh,

@@ -187,7 +187,7 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_query_kernel(BwdArgs a) {
     const int li = threadIdx.x % L;
     int64_t bh;
     int32_t t, h, wb;
-    block_coords(a.g, a.ord, xcd_logical_block(blockIdx.x, gridDim.x), bh, t, h, wb);
+    block_coords(a.g, a.ord, logical_block(blockIdx.x, gridDim.x, a.ord.chunk), bh, t, h, wb);
     const int32_t w = wb + g;
     if (w >= a.g.W) return;  // no block-wide barrier below
     const int32_t b = (int32_t)(bh / a.g.nheads);
@@ -415,7 +415,7 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_key_kernel(BwdArgs a) {
     const int li = threadIdx.x % L;
     int64_t bh;
     int32_t t, h, wb;
-    block_coords(a.g, a.ord, xcd_logical_block(blockIdx.x, gridDim.x), bh, t, h, wb);
+    block_coords(a.g, a.ord, logical_block(blockIdx.x, gridDim.x, a.ord.chunk), bh, t, h, wb);
     const int32_t w = wb + g;
     if (w >= a.g.W) return;
     const int32_t b = (int32_t)(bh / a.g.nheads);
