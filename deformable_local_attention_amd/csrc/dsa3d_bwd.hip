@@ -40,12 +40,12 @@ constexpr int kSortBucketsPerBlock = 64;
 // Per-sample record, written by the query kernel into its bucket and read by
 // the key kernel.
 struct __attribute__((aligned(16))) SampleRec {
-    float ck;       // scale * ds_p
-    float cv;       // a_p
+    float ck;          // scale * ds_p
+    float cv;          // a_p
     float ft, fh, fw;
-    uint32_t qtok;  // query token index in [B,T,H,W]
-    uint32_t sid;   // sample number within the pass: task * P + p
-    uint32_t pad;
+    uint32_t sid;      // sample number within the pass: task * P + p
+    uint32_t row_lo;   // byte offset of the query's row, token * heads * head_dim * elem_size
+    uint32_t row_hi;   // (split in two words)
 };
 
 struct BwdArgs {
@@ -282,7 +282,8 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_query_kernel(BwdArgs a) {
                             uint4* dst = reinterpret_cast<uint4*>(a.rec + slot);
                             dst[0] = make_uint4(__float_as_uint(ck), __float_as_uint(ap), __float_as_uint(ft),
                                                 __float_as_uint(fh));
-                            dst[1] = make_uint4(__float_as_uint(fw), (uint32_t)tok, sid, 0u);
+                            const uint64_t row = (uint64_t)tok * (uint64_t)cs.row_bytes;
+                            dst[1] = make_uint4(__float_as_uint(fw), sid, (uint32_t)row, (uint32_t)(row >> 32));
                         }
                     }
                 }
@@ -341,11 +342,11 @@ struct LdsKeySwap {
 
 // Whole 32-byte records in global memory, compared by sample number.
 struct GlobalRecSwap {
-    uint4* rec;  // two uint4 per record; the sample number is word 6
+    uint4* rec;  // two uint4 per record; the sample number is word 5
     __device__ __forceinline__ void operator()(uint64_t lo, uint64_t hi) const {
         const uint4 a1 = rec[2 * hi + 1];
         const uint4 b1 = rec[2 * lo + 1];
-        if (b1.z > a1.z) {
+        if (b1.y > a1.y) {
             const uint4 a0 = rec[2 * hi], b0 = rec[2 * lo];
             rec[2 * lo] = a0; rec[2 * lo + 1] = a1;
             rec[2 * hi] = b0; rec[2 * hi + 1] = b1;
@@ -378,7 +379,7 @@ __global__ void __launch_bounds__(64) dsa3d_sort_small_kernel(const uint32_t* st
             const uint4 r0 = grec[2 * ((uint64_t)s + i)], r1 = grec[2 * ((uint64_t)s + i) + 1];
             srec[2 * i] = r0;
             srec[2 * i + 1] = r1;
-            skey[i] = ((uint64_t)r1.z << 32) | i;
+            skey[i] = ((uint64_t)r1.y << 32) | i;
         }
         __syncthreads();
         bitonic_sort(n, threadIdx.x, 64, LdsKeySwap{skey}, BlockSync());
@@ -429,22 +430,56 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_key_kernel(BwdArgs a) {
 
     float ak[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float av[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const char* Qc = reinterpret_cast<const char*>(Qb);
+    const char* Gc = reinterpret_cast<const char*>(Gb);
 #pragma unroll 1
     for (int c = 0; c < 8; ++c) {
         const int ct = (c >> 2) & 1, ch = (c >> 1) & 1, cw = c & 1;
         const uint32_t cell = cell_index(a.g, bh, t - ct, h - ch, w - cw);
         const uint32_t e1 = a.start[cell + 1];
-        for (uint32_t e = a.start[cell]; e < e1; ++e) {
-            const uint4 r0 = rec[2 * (uint64_t)e];
-            const uint4 r1 = rec[2 * (uint64_t)e + 1];
-            const float ft = __uint_as_float(r0.z), fh = __uint_as_float(r0.w), fw = __uint_as_float(r1.x);
-            const float wt = (ct ? ft : 1.0f - ft) * (ch ? fh : 1.0f - fh) * (cw ? fw : 1.0f - fw);
-            const int64_t qrow = (int64_t)r1.y * C;
-            Frag8<T> qf, gf;
-            qf.load(Qb + qrow);
-            gf.load(Gb + qrow);
-            qf.axpy(__uint_as_float(r0.x) * wt, ak);
-            gf.axpy(__uint_as_float(r0.y) * wt, av);
+        uint32_t e = a.start[cell];
+        // Two records per step. The next pair's records are fetched while the
+        // current pair's rows load, so each step waits on one memory latency.
+        uint4 ra0 = make_uint4(0, 0, 0, 0), ra1 = ra0, rb0 = ra0, rb1 = ra0;
+        if (e + 1 < e1) {
+            ra0 = rec[2 * (uint64_t)e]; ra1 = rec[2 * (uint64_t)e + 1];
+            rb0 = rec[2 * (uint64_t)e + 2]; rb1 = rec[2 * (uint64_t)e + 3];
+        }
+        for (; e + 1 < e1; e += 2) {
+            const uint64_t oa = ((uint64_t)ra1.w << 32) | ra1.z, ob = ((uint64_t)rb1.w << 32) | rb1.z;
+            Frag8<T> qa, ga, qb, gb;
+            qa.load(reinterpret_cast<const T*>(Qc + oa));
+            ga.load(reinterpret_cast<const T*>(Gc + oa));
+            qb.load(reinterpret_cast<const T*>(Qc + ob));
+            gb.load(reinterpret_cast<const T*>(Gc + ob));
+            uint4 na0 = ra0, na1 = ra1, nb0 = rb0, nb1 = rb1;
+            if (e + 3 < e1) {
+                na0 = rec[2 * (uint64_t)e + 4]; na1 = rec[2 * (uint64_t)e + 5];
+                nb0 = rec[2 * (uint64_t)e + 6]; nb1 = rec[2 * (uint64_t)e + 7];
+            }
+            const float wa = (ct ? __uint_as_float(ra0.z) : 1.0f - __uint_as_float(ra0.z)) *
+                             (ch ? __uint_as_float(ra0.w) : 1.0f - __uint_as_float(ra0.w)) *
+                             (cw ? __uint_as_float(ra1.x) : 1.0f - __uint_as_float(ra1.x));
+            const float wb = (ct ? __uint_as_float(rb0.z) : 1.0f - __uint_as_float(rb0.z)) *
+                             (ch ? __uint_as_float(rb0.w) : 1.0f - __uint_as_float(rb0.w)) *
+                             (cw ? __uint_as_float(rb1.x) : 1.0f - __uint_as_float(rb1.x));
+            qa.axpy(__uint_as_float(ra0.x) * wa, ak);
+            ga.axpy(__uint_as_float(ra0.y) * wa, av);
+            qb.axpy(__uint_as_float(rb0.x) * wb, ak);
+            gb.axpy(__uint_as_float(rb0.y) * wb, av);
+            ra0 = na0; ra1 = na1; rb0 = nb0; rb1 = nb1;
+        }
+        if (e < e1) {
+            const uint4 r0 = rec[2 * (uint64_t)e], r1 = rec[2 * (uint64_t)e + 1];
+            const uint64_t oa = ((uint64_t)r1.w << 32) | r1.z;
+            const float wr = (ct ? __uint_as_float(r0.z) : 1.0f - __uint_as_float(r0.z)) *
+                             (ch ? __uint_as_float(r0.w) : 1.0f - __uint_as_float(r0.w)) *
+                             (cw ? __uint_as_float(r1.x) : 1.0f - __uint_as_float(r1.x));
+            Frag8<T> qr, gr;
+            qr.load(reinterpret_cast<const T*>(Qc + oa));
+            gr.load(reinterpret_cast<const T*>(Gc + oa));
+            qr.axpy(__uint_as_float(r0.x) * wr, ak);
+            gr.axpy(__uint_as_float(r0.y) * wr, av);
         }
     }
     Frag8<T> kf, vf;

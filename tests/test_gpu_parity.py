@@ -39,9 +39,11 @@ def _wl(name="case", B=1, T=3, H=4, W=5, heads=2, d=32, window=(3, 3, 3), dil=(1
 def _check(name, gpu, ref, dtype, tol_f32=F32_TOL, tol_bf16=BF16_TOL):
     if dtype == "f32":
         err = float(np.abs(gpu - ref).max()) if gpu.size else 0.0
+        say(f"    {name}: max abs err {err:.3e} (tolerance {tol_f32})")
         assert err <= tol_f32, f"{name}: max abs err {err:.3e} > {tol_f32}"
     else:
         err = rel_l2(gpu, ref)
+        say(f"    {name}: rel-L2 err {err:.3e} (tolerance {tol_bf16})")
         assert err <= tol_bf16, f"{name}: rel-L2 err {err:.3e} > {tol_bf16}"
     return err
 
