@@ -65,47 +65,53 @@ __global__ void __launch_bounds__(256) dsa3d_fwd_kernel(FwdArgs a) {
     Frag8<T> qf;
     qf.load(reinterpret_cast<const T*>(a.q) + tok * C + row_off);
 
+    // The group walks the samples in chunks of L: each lane computes the cell
+    // of one sample of the chunk and leaves it in LDS, then every lane reads
+    // each sample's cell from there (a broadcast read).
+    __shared__ SampleGeo s_geo[256];
+    SampleGeo* geo = s_geo + (threadIdx.x - li);
+
     float m = -INFINITY, z = 0.0f;
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    const Window& win = a.win;
-    for (int it = 0; it < win.kt; ++it) {
-        const float rt = (float)(t + win.dil_t * (it - win.rt));
-        for (int ih = 0; ih < win.kh; ++ih) {
-            const float rh = (float)(h + win.dil_h * (ih - win.rh));
-            for (int iw = 0; iw < win.kw; ++iw) {
-                const float rw = (float)(w + win.dil_w * (iw - win.rw));
-                float dt, dh, dw;
-                load_offsets<T>(offq, dt, dh, dw);
-                offq += 3;
-                int32_t t0 = 0, h0 = 0, w0c = 0;
-                float ft = 0.f, fh = 0.f, fw = 0.f;
-                const bool inside = sample_cell(rt, rh, rw, dt, dh, dw, t0, h0, w0c, ft, fh, fw);
-                CellCorners cc;
-                cell_corners(a.g, tok_b, inside, t0, h0, w0c, ft, fh, fw, cc);
-                CornerAddr ca;
-                corner_addresses(cc, Kb, Vb, cs, zero, __all(cc.all_in), ca);
-                Frag8<T> kf[8], vf[8];
+    for (int p0 = 0; p0 < a.P; p0 += L) {
+        const int n = min(L, a.P - p0);
+        wave_lds_sync();  // the previous chunk has been read
+        if (li < n) {
+            SampleGeo sg;
+            int32_t t0, h0, w0c;
+            sample_geo<T>(a.g, a.win, tok_b, t, h, w, p0 + li, offq + (p0 + li) * 3, sg, t0, h0, w0c);
+            geo[li] = sg;
+        }
+        wave_lds_sync();
+        for (int j = 0; j < n; ++j) {
+            const SampleGeo& sg = geo[j];
+            const uint32_t valid = sg.valid;
+            CornerAddr ca;
+            corner_addresses(sg.tok0, valid, Kb, Vb, cs, zero, __all((valid >> 8) & 1u), ca);
+            Frag8<T> kf[8], vf[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    kf[i].load(reinterpret_cast<const T*>(ca.a[i]));
-                    vf[i].load(reinterpret_cast<const T*>(ca.b[i]));
-                }
-                float acc = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc = fmaf(cc.w[i], kf[i].dot(qf, 0.0f), acc);
-                const float s = a.scale * group_sum<L>(acc);
-                const float m_new = fmaxf(m, s);
-                const float alpha = __expf(m - m_new);  // 0 for the first sample (m = -inf)
-                const float beta = __expf(s - m_new);
-                z = fmaf(z, alpha, beta);
-                if (!__all(m_new == m)) {  // the running max rarely moves after the first samples
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) o[e] *= alpha;
-                }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) vf[i].axpy(beta * cc.w[i], o);
-                m = m_new;
+            for (int i = 0; i < 8; ++i) {
+                kf[i].load(reinterpret_cast<const T*>(ca.a[i]));
+                vf[i].load(reinterpret_cast<const T*>(ca.b[i]));
             }
+            float wgt[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) wgt[i] = sg.w[i];
+            float acc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc = fmaf(wgt[i], kf[i].dot(qf, 0.0f), acc);
+            const float s = a.scale * group_sum<L>(acc);
+            const float m_new = fmaxf(m, s);
+            const float alpha = __expf(m - m_new);  // 0 for the first sample (m = -inf)
+            const float beta = __expf(s - m_new);
+            z = fmaf(z, alpha, beta);
+            if (!__all(m_new == m)) {  // the running max rarely moves after the first samples
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] *= alpha;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) vf[i].axpy(beta * wgt[i], o);
+            m = m_new;
         }
     }
     const float inv_z = 1.0f / z;

@@ -125,6 +125,57 @@ __device__ __forceinline__ void cell_corners(const TaskGrid& g, uint32_t tok_b, 
     cc.tok0 = tok_b + ((uint32_t)t0 * (uint32_t)g.H + (uint32_t)h0) * (uint32_t)g.W + (uint32_t)w0;
 }
 
+// The offset (dt, dh, dw) of one sample, widened to float32.
+template <typename T>
+__device__ __forceinline__ void load_offsets(const T* off, float& dt, float& dh, float& dw) {
+    dt = load_scalar<T>(off + 0);
+    dh = load_scalar<T>(off + 1);
+    dw = load_scalar<T>(off + 2);
+}
+
+// One sample's cell as computed by one lane and shared with its group through
+// LDS: corner weights with the grid bounds folded in, the token of corner 0,
+// the in-grid corner mask, the three fractions, and one spare word.
+struct __attribute__((aligned(16))) SampleGeo {
+    float w[8];
+    uint32_t tok0;
+    uint32_t valid;   // bit i: corner i in the grid; bit 8: all eight
+    float ft, fh, fw;
+    uint32_t extra;
+};
+
+// The geometry of window point p of query (t, h, w): reference point, cell
+// and corner data.
+template <typename T>
+__device__ __forceinline__ void sample_geo(const TaskGrid& g, const Window& win, uint32_t tok_b, int32_t t, int32_t h,
+                                           int32_t w, int32_t p, const T* off, SampleGeo& sg, int32_t& t0,
+                                           int32_t& h0, int32_t& w0) {
+    float dt, dh, dw;
+    load_offsets<T>(off, dt, dh, dw);
+    t0 = h0 = w0 = 0;
+    float ft = 0.f, fh = 0.f, fw = 0.f;
+    const bool inside = sample_geometry(win, t, h, w, p, dt, dh, dw, t0, h0, w0, ft, fh, fw);
+    CellCorners cc;
+    cell_corners(g, tok_b, inside, t0, h0, w0, ft, fh, fw, cc);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sg.w[i] = cc.w[i];
+    sg.tok0 = cc.tok0;
+    sg.valid = cc.valid | (cc.all_in ? 0x100u : 0u);
+    sg.ft = ft;
+    sg.fh = fh;
+    sg.fw = fw;
+    sg.extra = 0u;
+}
+
+// Ordering of LDS accesses between lanes of one wave: the wave executes in
+// lockstep and its LDS operations complete in order, so only the compiler
+// must be kept from moving accesses across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Strides of the corner rows of one tensor: tokens per frame and per row,
 // and the same in bytes (row_bytes = bytes per token).
 struct CornerStrides {
@@ -152,12 +203,12 @@ struct CornerAddr {
     const char* b[8];
 };
 
-__device__ __forceinline__ void corner_addresses(const CellCorners& cc, const char* base_a, const char* base_b,
-                                                 const CornerStrides& s, const char* zero, bool wave_all_in,
-                                                 CornerAddr& ca) {
+__device__ __forceinline__ void corner_addresses(uint32_t tok0, uint32_t valid, const char* base_a,
+                                                 const char* base_b, const CornerStrides& s, const char* zero,
+                                                 bool wave_all_in, CornerAddr& ca) {
     const int64_t b_minus_a = base_b - base_a;
     if (wave_all_in) {
-        const char* p0 = base_a + (int64_t)(int32_t)cc.tok0 * s.row_bytes;
+        const char* p0 = base_a + (int64_t)(int32_t)tok0 * s.row_bytes;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             ca.a[i] = p0 + (((i >> 2) & 1) ? s.dt_bytes : 0) + (((i >> 1) & 1) ? s.dh_bytes : 0) +
@@ -167,21 +218,14 @@ __device__ __forceinline__ void corner_addresses(const CellCorners& cc, const ch
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const uint32_t tok = cc.tok0 + (((i >> 2) & 1) ? s.hw_tok : 0u) + (((i >> 1) & 1) ? s.w_tok : 0u) +
+            const uint32_t tok = tok0 + (((i >> 2) & 1) ? s.hw_tok : 0u) + (((i >> 1) & 1) ? s.w_tok : 0u) +
                                  (uint32_t)(i & 1);
-            const bool ok = (cc.valid >> i) & 1u;
+            const bool ok = (valid >> i) & 1u;
             const int64_t off = (int64_t)(int32_t)tok * s.row_bytes;
             ca.a[i] = ok ? base_a + off : zero;
             ca.b[i] = ok ? base_b + off : zero;
         }
     }
-}
-
-template <typename T>
-__device__ __forceinline__ void load_offsets(const T* off, float& dt, float& dh, float& dw) {
-    dt = load_scalar<T>(off + 0);
-    dh = load_scalar<T>(off + 1);
-    dw = load_scalar<T>(off + 2);
 }
 
 // Zero row read in place of a corner outside the grid (256 floats: the widest

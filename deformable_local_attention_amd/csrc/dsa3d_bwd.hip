@@ -229,7 +229,7 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_query_kernel(BwdArgs a) {
                 CellCorners cc;
                 cell_corners(a.g, tok_b, inside, t0, h0, w0, ft, fh, fw, cc);
                 CornerAddr ca;
-                corner_addresses(cc, Kb, Vb, cs, zero, __all(cc.all_in), ca);
+                corner_addresses(cc.tok0, cc.valid, Kb, Vb, cs, zero, __all(cc.all_in), ca);
                 Frag8<T> kf[8], vf[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
