@@ -31,6 +31,7 @@
 
 namespace dsa3d {
 
+constexpr uint32_t kNoSlot = 0xffffffffu;  // a sample with no corner in the grid
 constexpr int kScanThreads = 256;
 constexpr int kScanItems = 16;
 constexpr uint32_t kScanChunk = kScanThreads * kScanItems;
@@ -204,7 +205,8 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_query_kernel(BwdArgs a) {
     const int64_t offrow = (tok * a.g.heads + eta) * (int64_t)a.P * 3;
     const T* offq = reinterpret_cast<const T*>(a.off) + offrow;
     T* doffq = reinterpret_cast<T*>(a.doff) + offrow;
-    uint32_t sid = (uint32_t)(task * a.P);
+    const uint32_t sid0 = (uint32_t)(task * a.P);
+    const uint64_t qrow_bytes = (uint64_t)tok * (uint64_t)cs.row_bytes;
 
     Frag8<T> qf, gf, of;
     qf.load(reinterpret_cast<const T*>(a.q) + tok * C + row_off);
@@ -213,80 +215,104 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_query_kernel(BwdArgs a) {
     const float Dsum = group_sum<L>(gf.dot(of, 0.0f));
     const float lse = a.lse[tok * a.g.heads + eta];
 
+    // Chunks of L samples: each lane computes one sample's cell and takes its
+    // slot in the cell's bucket (so a chunk's atomics issue together), the
+    // group then works through the chunk sample by sample, and finally each
+    // lane writes its own sample's doffsets and record.
+    __shared__ SampleGeo s_geo[256];
+    __shared__ float4 s_out[256];   // scale*ds_p, a_p, doff_t, doff_h
+    __shared__ float s_outw[256];   // doff_w
+    SampleGeo* geo = s_geo + (threadIdx.x - li);
+    float4* out = s_out + (threadIdx.x - li);
+    float* outw = s_outw + (threadIdx.x - li);
+
     float dq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    const Window& win = a.win;
-    for (int it = 0; it < win.kt; ++it) {
-        const float rt = (float)(t + win.dil_t * (it - win.rt));
-        for (int ih = 0; ih < win.kh; ++ih) {
-            const float rh = (float)(h + win.dil_h * (ih - win.rh));
-            for (int iw = 0; iw < win.kw; ++iw, offq += 3, doffq += 3, ++sid) {
-                const float rw = (float)(w + win.dil_w * (iw - win.rw));
-                float dt, dh, dw;
-                load_offsets<T>(offq, dt, dh, dw);
-                int32_t t0 = 0, h0 = 0, w0 = 0;
-                float ft = 0.f, fh = 0.f, fw = 0.f;
-                const bool inside = sample_cell(rt, rh, rw, dt, dh, dw, t0, h0, w0, ft, fh, fw);
-                CellCorners cc;
-                cell_corners(a.g, tok_b, inside, t0, h0, w0, ft, fh, fw, cc);
-                CornerAddr ca;
-                corner_addresses(cc.tok0, cc.valid, Kb, Vb, cs, zero, __all(cc.all_in), ca);
-                Frag8<T> kf[8], vf[8];
+    for (int p0 = 0; p0 < a.P; p0 += L) {
+        const int n = min(L, a.P - p0);
+        wave_lds_sync();  // the previous chunk has been read and flushed
+        if (li < n) {
+            SampleGeo sg;
+            int32_t t0, h0, w0;
+            sample_geo<T>(a.g, a.win, tok_b, t, h, w, p0 + li, offq + (p0 + li) * 3, sg, t0, h0, w0);
+            uint32_t slot = kNoSlot;
+            if ((sg.valid & 0xffu) != 0u) {
+                const uint32_t cell = cell_index(a.g, bh, t0, h0, w0);
+                const uint32_t sl = a.start[cell] + atomicAdd(a.cnt + cell, 1u);
+                // the count kernel filed exactly these samples in these cells;
+                // the bound only keeps a write inside its bucket
+                if (sl < a.start[cell + 1]) slot = sl;
+            }
+            sg.extra = slot;
+            geo[li] = sg;
+        }
+        wave_lds_sync();
+        for (int j = 0; j < n; ++j) {
+            const SampleGeo& sg = geo[j];
+            const uint32_t valid = sg.valid;
+            CornerAddr ca;
+            corner_addresses(sg.tok0, valid, Kb, Vb, cs, zero, __all((valid >> 8) & 1u), ca);
+            Frag8<T> kf[8], vf[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    kf[i].load(reinterpret_cast<const T*>(ca.a[i]));
-                    vf[i].load(reinterpret_cast<const T*>(ca.b[i]));
+            for (int i = 0; i < 8; ++i) {
+                kf[i].load(reinterpret_cast<const T*>(ca.a[i]));
+                vf[i].load(reinterpret_cast<const T*>(ca.b[i]));
+            }
+            float qk[8], dv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                qk[i] = kf[i].dot(qf, 0.0f);
+                dv[i] = vf[i].dot(gf, 0.0f);
+            }
+            // The logit, dL/da and the derivatives of both along t, h, w, in
+            // factored form over the cell's axes (w, then h, then t). The raw
+            // factors (1-f, f) serve every corner: a corner outside the grid
+            // read a zero row, so its dot products are exactly 0.
+            const float ft = sg.ft, fh = sg.fh, fw = sg.fw;
+            const float aw0 = 1.0f - fw, ah0 = 1.0f - fh, at0 = 1.0f - ft;
+            float r[8];
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const float* X = x == 0 ? qk : dv;
+                float A[4], dW[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {  // k = ct*2 + ch
+                    A[k] = fmaf(fw, X[2 * k + 1], aw0 * X[2 * k]);
+                    dW[k] = X[2 * k + 1] - X[2 * k];
                 }
-                float qk[8], dv[8];
+                const float B0 = fmaf(fh, A[1], ah0 * A[0]), B1 = fmaf(fh, A[3], ah0 * A[2]);
+                r[x] = fmaf(ft, B1, at0 * B0);                                        // value
+                r[2 + 3 * x] = B1 - B0;                                                // d/dt
+                r[3 + 3 * x] = fmaf(ft, A[3] - A[2], at0 * (A[1] - A[0]));            // d/dh
+                r[4 + 3 * x] = fmaf(ft, fmaf(fh, dW[3], ah0 * dW[2]), at0 * fmaf(fh, dW[1], ah0 * dW[0]));  // d/dw
+            }
+            // r = {value(qk), value(dv), d/dt(qk), d/dh(qk), d/dw(qk), d/dt(dv), d/dh(dv), d/dw(dv)}
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    qk[i] = kf[i].dot(qf, 0.0f);
-                    dv[i] = vf[i].dot(gf, 0.0f);
-                }
-                // weighted sums: logit, dL/da, and the offset-derivative sums per
-                // axis. The factors below carry the grid bounds: a corner outside
-                // the grid has a zero row, so its dot products are 0 anyway.
-                const float at[2] = {1.0f - ft, ft}, ah[2] = {1.0f - fh, fh}, aw[2] = {1.0f - fw, fw};
-                float r[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int k = 0; k < 8; ++k) r[k] = group_sum<L>(r[k]);
+            const float s = a.scale * r[0];
+            const float ap = __expf(s - lse);
+            const float ds = ap * (r[1] - Dsum);
+            const float ck = a.scale * ds;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int ct = (i >> 2) & 1, ch = (i >> 1) & 1, cw = i & 1;
-                    const float st = ct ? 1.f : -1.f, sh = ch ? 1.f : -1.f, sw = cw ? 1.f : -1.f;
-                    const float gt = st * ah[ch] * aw[cw], gh = at[ct] * sh * aw[cw], gw = at[ct] * ah[ch] * sw;
-                    r[0] = fmaf(cc.w[i], qk[i], r[0]);
-                    r[1] = fmaf(cc.w[i], dv[i], r[1]);
-                    r[2] = fmaf(gt, qk[i], r[2]);
-                    r[3] = fmaf(gh, qk[i], r[3]);
-                    r[4] = fmaf(gw, qk[i], r[4]);
-                    r[5] = fmaf(gt, dv[i], r[5]);
-                    r[6] = fmaf(gh, dv[i], r[6]);
-                    r[7] = fmaf(gw, dv[i], r[7]);
-                }
-#pragma unroll
-                for (int j = 0; j < 8; ++j) r[j] = group_sum<L>(r[j]);
-                const float s = a.scale * r[0];
-                const float ap = __expf(s - lse);
-                const float ds = ap * (r[1] - Dsum);
-                const float ck = a.scale * ds;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) kf[i].axpy(ck * cc.w[i], dq);
-                if (li == 0) {
-                    store_scalar<T>(doffq + 0, fmaf(ck, r[2], ap * r[5]));
-                    store_scalar<T>(doffq + 1, fmaf(ck, r[3], ap * r[6]));
-                    store_scalar<T>(doffq + 2, fmaf(ck, r[4], ap * r[7]));
-                    if (cc.valid != 0u) {
-                        const uint32_t cell = cell_index(a.g, bh, t0, h0, w0);
-                        const uint32_t slot = a.start[cell] + atomicAdd(a.cnt + cell, 1u);
-                        // the count kernel filed exactly these samples; the bound
-                        // only keeps a write inside its bucket should they ever differ
-                        if (slot < a.start[cell + 1]) {
-                            uint4* dst = reinterpret_cast<uint4*>(a.rec + slot);
-                            dst[0] = make_uint4(__float_as_uint(ck), __float_as_uint(ap), __float_as_uint(ft),
-                                                __float_as_uint(fh));
-                            const uint64_t row = (uint64_t)tok * (uint64_t)cs.row_bytes;
-                            dst[1] = make_uint4(__float_as_uint(fw), sid, (uint32_t)row, (uint32_t)(row >> 32));
-                        }
-                    }
-                }
+            for (int i = 0; i < 8; ++i) kf[i].axpy(ck * sg.w[i], dq);
+            if (li == 0) {
+                out[j] = make_float4(ck, ap, fmaf(ck, r[2], ap * r[5]), fmaf(ck, r[3], ap * r[6]));
+                outw[j] = fmaf(ck, r[4], ap * r[7]);
+            }
+        }
+        wave_lds_sync();
+        if (li < n) {
+            const int p = p0 + li;
+            const float4 ov = out[li];
+            store_scalar<T>(doffq + p * 3 + 0, ov.z);
+            store_scalar<T>(doffq + p * 3 + 1, ov.w);
+            store_scalar<T>(doffq + p * 3 + 2, outw[li]);
+            const SampleGeo& sg = geo[li];
+            if (sg.extra != kNoSlot) {
+                uint4* dst = reinterpret_cast<uint4*>(a.rec + sg.extra);
+                dst[0] = make_uint4(__float_as_uint(ov.x), __float_as_uint(ov.y), __float_as_uint(sg.ft),
+                                    __float_as_uint(sg.fh));
+                dst[1] = make_uint4(__float_as_uint(sg.fw), sid0 + (uint32_t)p, (uint32_t)qrow_bytes,
+                                    (uint32_t)(qrow_bytes >> 32));
             }
         }
     }
