@@ -454,58 +454,69 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_key_kernel(BwdArgs a) {
     const T* Gb = reinterpret_cast<const T*>(a.dout) + row_off;
     const uint4* rec = reinterpret_cast<const uint4*>(a.rec);
 
-    float ak[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float av[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // The key's samples are the records of its 8 buckets (base cells y - c),
+    // taken in the fixed order c = 0..7 and bucket order, as one list of N
+    // entries. The group walks the list in chunks of L: each lane loads one
+    // record (the chunk's loads are coalesced), computes its corner weight and
+    // both coefficients and leaves them in LDS; then every lane reads each
+    // entry from there and adds its query and output-gradient rows.
+    uint32_t bs[8], cum[8];
+    uint32_t N = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const uint32_t cell = cell_index(a.g, bh, t - ((c >> 2) & 1), h - ((c >> 1) & 1), w - (c & 1));
+        bs[c] = a.start[cell];
+        cum[c] = N;
+        N += a.start[cell + 1] - bs[c];
+    }
+    __shared__ float4 s_ent[256];  // scale*ds*w, a*w, row offset (lo, hi)
+    float4* ent = s_ent + (threadIdx.x - li);
     const char* Qc = reinterpret_cast<const char*>(Qb);
     const char* Gc = reinterpret_cast<const char*>(Gb);
-#pragma unroll 1
-    for (int c = 0; c < 8; ++c) {
-        const int ct = (c >> 2) & 1, ch = (c >> 1) & 1, cw = c & 1;
-        const uint32_t cell = cell_index(a.g, bh, t - ct, h - ch, w - cw);
-        const uint32_t e1 = a.start[cell + 1];
-        uint32_t e = a.start[cell];
-        // Two records per step. The next pair's records are fetched while the
-        // current pair's rows load, so each step waits on one memory latency.
-        uint4 ra0 = make_uint4(0, 0, 0, 0), ra1 = ra0, rb0 = ra0, rb1 = ra0;
-        if (e + 1 < e1) {
-            ra0 = rec[2 * (uint64_t)e]; ra1 = rec[2 * (uint64_t)e + 1];
-            rb0 = rec[2 * (uint64_t)e + 2]; rb1 = rec[2 * (uint64_t)e + 3];
+    float ak[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float av[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (uint32_t k0 = 0; k0 < N; k0 += L) {
+        const uint32_t n = min((uint32_t)L, N - k0);
+        wave_lds_sync();  // the previous chunk has been read
+        if ((uint32_t)li < n) {
+            const uint32_t k = k0 + li;
+            int c = 0;
+            uint32_t e = bs[0] + k;
+#pragma unroll
+            for (int cc = 1; cc < 8; ++cc) {  // the last bucket that starts at or before k holds it
+                if (k >= cum[cc]) { c = cc; e = bs[cc] + (k - cum[cc]); }
+            }
+            const uint4 r0 = rec[2 * (uint64_t)e], r1 = rec[2 * (uint64_t)e + 1];
+            const float ft = __uint_as_float(r0.z), fh = __uint_as_float(r0.w), fw = __uint_as_float(r1.x);
+            const float wt = (((c >> 2) & 1) ? ft : 1.0f - ft) * (((c >> 1) & 1) ? fh : 1.0f - fh) *
+                             ((c & 1) ? fw : 1.0f - fw);
+            ent[li] = make_float4(__uint_as_float(r0.x) * wt, __uint_as_float(r0.y) * wt, __uint_as_float(r1.z),
+                                  __uint_as_float(r1.w));
         }
-        for (; e + 1 < e1; e += 2) {
-            const uint64_t oa = ((uint64_t)ra1.w << 32) | ra1.z, ob = ((uint64_t)rb1.w << 32) | rb1.z;
+        wave_lds_sync();
+        uint32_t j = 0;
+        for (; j + 1 < n; j += 2) {  // two entries per step: four row loads in flight
+            const float4 ea = ent[j], eb = ent[j + 1];
+            const uint64_t oa = ((uint64_t)__float_as_uint(ea.w) << 32) | __float_as_uint(ea.z);
+            const uint64_t ob = ((uint64_t)__float_as_uint(eb.w) << 32) | __float_as_uint(eb.z);
             Frag8<T> qa, ga, qb, gb;
             qa.load(reinterpret_cast<const T*>(Qc + oa));
             ga.load(reinterpret_cast<const T*>(Gc + oa));
             qb.load(reinterpret_cast<const T*>(Qc + ob));
             gb.load(reinterpret_cast<const T*>(Gc + ob));
-            uint4 na0 = ra0, na1 = ra1, nb0 = rb0, nb1 = rb1;
-            if (e + 3 < e1) {
-                na0 = rec[2 * (uint64_t)e + 4]; na1 = rec[2 * (uint64_t)e + 5];
-                nb0 = rec[2 * (uint64_t)e + 6]; nb1 = rec[2 * (uint64_t)e + 7];
-            }
-            const float wa = (ct ? __uint_as_float(ra0.z) : 1.0f - __uint_as_float(ra0.z)) *
-                             (ch ? __uint_as_float(ra0.w) : 1.0f - __uint_as_float(ra0.w)) *
-                             (cw ? __uint_as_float(ra1.x) : 1.0f - __uint_as_float(ra1.x));
-            const float wb = (ct ? __uint_as_float(rb0.z) : 1.0f - __uint_as_float(rb0.z)) *
-                             (ch ? __uint_as_float(rb0.w) : 1.0f - __uint_as_float(rb0.w)) *
-                             (cw ? __uint_as_float(rb1.x) : 1.0f - __uint_as_float(rb1.x));
-            qa.axpy(__uint_as_float(ra0.x) * wa, ak);
-            ga.axpy(__uint_as_float(ra0.y) * wa, av);
-            qb.axpy(__uint_as_float(rb0.x) * wb, ak);
-            gb.axpy(__uint_as_float(rb0.y) * wb, av);
-            ra0 = na0; ra1 = na1; rb0 = nb0; rb1 = nb1;
+            qa.axpy(ea.x, ak);
+            ga.axpy(ea.y, av);
+            qb.axpy(eb.x, ak);
+            gb.axpy(eb.y, av);
         }
-        if (e < e1) {
-            const uint4 r0 = rec[2 * (uint64_t)e], r1 = rec[2 * (uint64_t)e + 1];
-            const uint64_t oa = ((uint64_t)r1.w << 32) | r1.z;
-            const float wr = (ct ? __uint_as_float(r0.z) : 1.0f - __uint_as_float(r0.z)) *
-                             (ch ? __uint_as_float(r0.w) : 1.0f - __uint_as_float(r0.w)) *
-                             (cw ? __uint_as_float(r1.x) : 1.0f - __uint_as_float(r1.x));
-            Frag8<T> qr, gr;
-            qr.load(reinterpret_cast<const T*>(Qc + oa));
-            gr.load(reinterpret_cast<const T*>(Gc + oa));
-            qr.axpy(__uint_as_float(r0.x) * wr, ak);
-            gr.axpy(__uint_as_float(r0.y) * wr, av);
+        if (j < n) {
+            const float4 ea = ent[j];
+            const uint64_t oa = ((uint64_t)__float_as_uint(ea.w) << 32) | __float_as_uint(ea.z);
+            Frag8<T> qa, ga;
+            qa.load(reinterpret_cast<const T*>(Qc + oa));
+            ga.load(reinterpret_cast<const T*>(Gc + oa));
+            qa.axpy(ea.x, ak);
+            ga.axpy(ea.y, av);
         }
     }
     Frag8<T> kf, vf;
