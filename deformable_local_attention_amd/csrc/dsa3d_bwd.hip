@@ -381,38 +381,53 @@ struct GlobalRecSwap {
 };
 
 // One wave per block; the block walks kSortBucketsPerBlock consecutive
-// buckets. A bucket of up to kWaveSortMax records is staged in LDS, its keys
-// sorted and the records written back in order; larger buckets are queued in
-// `large` ([0] = count, [1..cap] = bucket numbers) for the next kernel.
+// buckets. A bucket of up to kWaveSortMax records is held in registers (lane
+// l holds records l, l+64, ...), its (sample number, position) keys are
+// sorted in LDS, and each lane then writes the records it holds straight to
+// their sorted positions (all reads precede all writes, so the permutation is
+// done in place). Larger buckets are queued in `large` ([0] = count,
+// [1..cap] = bucket numbers) for the next kernel.
 __global__ void __launch_bounds__(64) dsa3d_sort_small_kernel(const uint32_t* start, uint32_t ncell, SampleRec* rec,
                                                               uint32_t* large, uint32_t large_cap) {
-    __shared__ uint4 srec[2 * kWaveSortMax];
+    constexpr int kPer = kWaveSortMax / 64;  // records per lane
     __shared__ uint64_t skey[kWaveSortMax];
+    __shared__ uint16_t srank[kWaveSortMax];
     const uint32_t c0 = blockIdx.x * kSortBucketsPerBlock;
     const uint32_t c1 = min(ncell, c0 + kSortBucketsPerBlock);
     uint4* grec = reinterpret_cast<uint4*>(rec);
+    const uint32_t lane = threadIdx.x;
     for (uint32_t c = c0; c < c1; ++c) {
         const uint32_t s = start[c], n = start[c + 1] - s;
         if (n < 2) continue;
         if (n > kWaveSortMax) {
-            if (threadIdx.x == 0) {
+            if (lane == 0) {
                 const uint32_t slot = atomicAdd(large, 1u);
                 if (slot < large_cap) large[1 + slot] = c;
             }
             continue;
         }
-        for (uint32_t i = threadIdx.x; i < n; i += 64) {
-            const uint4 r0 = grec[2 * ((uint64_t)s + i)], r1 = grec[2 * ((uint64_t)s + i) + 1];
-            srec[2 * i] = r0;
-            srec[2 * i + 1] = r1;
-            skey[i] = ((uint64_t)r1.y << 32) | i;
+        uint4 r0[kPer], r1[kPer];
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const uint32_t i = lane + 64u * k;
+            if (i < n) {
+                r0[k] = grec[2 * ((uint64_t)s + i)];
+                r1[k] = grec[2 * ((uint64_t)s + i) + 1];
+                skey[i] = ((uint64_t)r1[k].y << 32) | i;
+            }
         }
         __syncthreads();
-        bitonic_sort(n, threadIdx.x, 64, LdsKeySwap{skey}, BlockSync());
-        for (uint32_t i = threadIdx.x; i < n; i += 64) {
-            const uint32_t from = (uint32_t)skey[i];
-            grec[2 * ((uint64_t)s + i)] = srec[2 * from];
-            grec[2 * ((uint64_t)s + i) + 1] = srec[2 * from + 1];
+        bitonic_sort(n, lane, 64, LdsKeySwap{skey}, BlockSync());
+        for (uint32_t i = lane; i < n; i += 64) srank[(uint32_t)skey[i]] = (uint16_t)i;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const uint32_t i = lane + 64u * k;
+            if (i < n) {
+                const uint64_t dst = (uint64_t)s + srank[i];
+                grec[2 * dst] = r0[k];
+                grec[2 * dst + 1] = r1[k];
+            }
         }
         __syncthreads();
     }

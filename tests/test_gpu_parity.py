@@ -125,6 +125,27 @@ def test_special_offsets(fill):
     _check_geometry(wl, x["offsets"])
 
 
+def test_every_sample_in_one_cell_deterministic():
+    """Offsets that move every sample of every query to the same cell: one
+    bucket of T*H*W*P samples per head, which takes the large-bucket sort."""
+    wl = _wl("one-cell", T=3, H=4, W=5, heads=2, d=32, window=(3, 3, 3), dtype="f32", det=True)
+    x = synth.make_inputs(wl, "cpu", seed=23)
+    kt, kh, kw = wl.window
+    it, ih, iw = np.meshgrid(np.arange(kt), np.arange(kh), np.arange(kw), indexing="ij")
+    win = np.stack([it.ravel() - 1, ih.ravel() - 1, iw.ravel() - 1], 1)          # [P, 3]
+    grid = np.stack(np.meshgrid(np.arange(wl.T), np.arange(wl.H), np.arange(wl.W), indexing="ij"), -1)
+    ref = grid[:, :, :, None, :] + win[None, None, None]                           # [T,H,W,P,3]
+    target = np.array([1.25, 2.5, 2.75])
+    off = (target - ref).astype(np.float32)                                        # exact in f32
+    x["offsets"].copy_(torch.from_numpy(off)[None, :, :, :, None].expand(x["offsets"].shape))
+    say(f"[one-cell] {synth.describe(wl)}: {wl.T * wl.H * wl.W * wl.P} samples per head in one cell")
+    ch = _run_whole(wl, x, det=True)
+    first = [t.clone() for t in (ch.dk, ch.dv)]
+    ch.run()
+    torch.cuda.synchronize()
+    assert torch.equal(first[0], ch.dk) and torch.equal(first[1], ch.dv)
+
+
 def _check_geometry(wl, off_cpu):
     desc = dsa.desc_like(torch.empty((wl.B, wl.T, wl.H, wl.W, wl.heads, wl.head_dim), dtype=wl.torch_dtype),
                          wl.window, wl.dilation)
