@@ -197,6 +197,556 @@ __global__ void __launch_bounds__(256) dsa3d_gemm_kernel(GemmArgs g) {
             }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 path: 256x256 outputs per 256-thread workgroup, each of the four waves
+// a 128x128 quarter computed as 4x4 v_mfma_f32_32x32x16_bf16 tiles whose
+// float32 accumulators stay in registers for the whole K loop. K advances in
+// 64-deep slices through two LDS stages (2 x 64 KiB): while the waves multiply
+// one stage, the next slice is already in flight from memory into registers
+// and is written to the other stage afterwards, so one barrier per slice
+// suffices and the barrier waits for LDS traffic only.
+//
+// LDS holds every operand tile as 256 rows x 128 B (64 bf16 of K), the 16-byte
+// chunk c of row r at chunk c ^ ((r >> 1) & 7): eight (and sixteen)
+// consecutive rows read at the same logical chunk then fall on distinct banks.
+// A K-contiguous operand is copied chunk for chunk; an M/N-contiguous one is
+// loaded as 8x8 blocks (8 rows of K, 8 elements along M/N) and transposed in
+// registers with byte permutes before it is written.
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+constexpr int XM = 256, XN = 256, XK = 64;
+constexpr int X_ROW_BYTES = XK * 2;                 // one LDS row: 64 bf16 of K
+constexpr int X_TILE_BYTES = XM * X_ROW_BYTES;      // 32 KiB per operand and stage
+constexpr int X_LDS_BYTES = 4 * X_TILE_BYTES;       // A and B, two stages
+
+__device__ __forceinline__ uint32_t xswz(uint32_t r) { return (r >> 1) & 7u; }
+
+struct XSlice { uint4 v[8]; };
+
+// Rows [r0, r0+256) x k [k0, k0+64) of one operand, as one thread loads them:
+// a wave-uniform base pointer plus 32-bit element offsets that stay fixed
+// from slice to slice (only the base moves with k0).
+//
+// K-contiguous (element (r, k) at src[r*ld + k]): thread t takes chunk t%8 of
+// rows t/8 + 32j. Rows past the end are clamped (their products are never
+// stored); k past kend reads zero.
+template <bool KC> struct XOperand;
+template <> struct XOperand<true> {
+    const bf16_t* base;  // src + r0*ld
+    int64_t ld;
+    uint32_t off[8];
+    __device__ __forceinline__ void init(const bf16_t* src, int64_t ld_, int64_t rows, int64_t r0) {
+        const int tid = threadIdx.x;
+        ld = ld_;
+        base = src + r0 * ld_;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t r = std::min<int64_t>(r0 + (tid >> 3) + 32 * j, rows - 1) - r0;
+            off[j] = (uint32_t)(r * ld_ + (tid & 7) * 8);
+        }
+    }
+    template <bool FULL>
+    __device__ __forceinline__ void load(int64_t k0, int64_t kend, XSlice& s) const {
+        const bf16_t* p = base + k0;
+        if (FULL) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s.v[j] = *reinterpret_cast<const uint4*>(p + off[j]);
+        } else {
+            // read the last in-bounds chunk instead, then zero it
+            const int64_t gk = k0 + (threadIdx.x & 7) * 8;
+            const bool ok = gk < kend;
+            const uint32_t back = ok ? 0u : (uint32_t)(gk - (kend - 8));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint4 v = *reinterpret_cast<const uint4*>(p + (off[j] - back));
+                s.v[j] = make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+            }
+        }
+    }
+};
+
+// M/N-contiguous (element (r, k) at src[k*ld + r]; rows is a multiple of 8
+// here, so an 8-row group is wholly in or out): thread t takes the 8x8 block
+// of k-group t%8 and row group t/8, groups past the end clamped to the last.
+template <> struct XOperand<false> {
+    const bf16_t* base;  // src + r0
+    int64_t ld;
+    uint32_t off;
+    __device__ __forceinline__ void init(const bf16_t* src, int64_t ld_, int64_t rows, int64_t r0) {
+        const int tid = threadIdx.x;
+        ld = ld_;
+        base = src + r0;
+        const int64_t gr = std::min<int64_t>(r0 + (tid >> 3) * 8, rows - 8);
+        off = (uint32_t)((tid & 7) * 8 * ld_ + (gr - r0));
+    }
+    template <bool FULL>
+    __device__ __forceinline__ void load(int64_t k0, int64_t kend, XSlice& s) const {
+        const bf16_t* p = base + k0 * ld;
+        if (FULL) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s.v[i] = *reinterpret_cast<const uint4*>(p + i * ld + off);
+        } else {
+            const int64_t gk = k0 + (threadIdx.x & 7) * 8;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const bool ok = gk + i < kend;
+                const int64_t back = ok ? 0 : (gk + i - (kend - 1)) * ld;
+                const uint4 v = *reinterpret_cast<const uint4*>(p + i * ld + off - back);
+                s.v[i] = make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+            }
+        }
+    }
+};
+
+template <bool KC>
+__device__ __forceinline__ void x_load(const XOperand<KC>& op, int64_t k0, int64_t kend, XSlice& s) {
+    if (k0 + XK <= kend) op.template load<true>(k0, kend, s);
+    else op.template load<false>(k0, kend, s);
+}
+
+__device__ __forceinline__ void x_store_kc(const XSlice& s, char* lds) {
+    const int tid = threadIdx.x;
+    const uint32_t c = (uint32_t)(tid & 7) ^ xswz((uint32_t)(tid >> 3));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t r = (uint32_t)(tid >> 3) + 32u * j;
+        *reinterpret_cast<uint4*>(lds + r * X_ROW_BYTES + c * 16u) = s.v[j];
+    }
+}
+
+__device__ __forceinline__ uint32_t u4_word(const uint4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Transposes the 8x8 block in registers (byte permutes) and writes its 8 rows.
+__device__ __forceinline__ void x_store_mn(const XSlice& s, char* lds) {
+    const int tid = threadIdx.x;
+    const uint32_t kg = (uint32_t)(tid & 7);
+#pragma unroll
+    for (int mm = 0; mm < 8; ++mm) {
+        // row rg*8+mm holds, at k = kg*8 + i, element mm of s.v[i]
+        const uint32_t sel = (mm & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t w[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            w[jj] = __builtin_amdgcn_perm(u4_word(s.v[2 * jj + 1], mm >> 1), u4_word(s.v[2 * jj], mm >> 1), sel);
+        const uint32_t r = (uint32_t)(tid >> 3) * 8u + mm;
+        *reinterpret_cast<uint4*>(lds + r * X_ROW_BYTES + ((kg ^ xswz(r)) * 16u)) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+template <bool KC>
+__device__ __forceinline__ void x_store(const XSlice& s, char* lds) {
+    if constexpr (KC) x_store_kc(s, lds);
+    else x_store_mn(s, lds);
+}
+
+// LDS-only workgroup barrier: waits for this wave's LDS traffic, not for the
+// global loads of the next slice that are still in flight.
+__device__ __forceinline__ void x_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One k16 step (s = 0..3 of a 64-deep slice) of 4x4 MFMAs on this wave's
+// quarter. Lane l supplies row l%32 of each 32-row operand tile and 8
+// consecutive k (chunk 2s + l/32 of the slice); both operands use the same k
+// assignment, so the hardware's k order inside one MFMA does not matter.
+__device__ __forceinline__ void x_mma_step(const char* As, const char* Bs, uint32_t a_off, uint32_t b_off,
+                                           uint32_t sw, uint32_t kh, uint32_t s, f32x16_t acc[4][4]) {
+    const uint32_t c = ((2u * s + kh) ^ sw) * 16u;
+    bf16x8_t a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[i] = *reinterpret_cast<const bf16x8_t*>(As + a_off + i * 32 * X_ROW_BYTES + c);
+        b[i] = *reinterpret_cast<const bf16x8_t*>(Bs + b_off + i * 32 * X_ROW_BYTES + c);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+}
+
+// Accumulator element e of tile (i, j) is row 8*(e/4) + 4*(lane/32) + e%4,
+// column lane%32 of that 32x32 tile. EDGE: the tile crosses the end of M or N.
+template <int MODE, bool EDGE>
+__device__ __forceinline__ void x_epilogue(const GemmArgs& g, f32x16_t acc[4][4], int64_t m0, int64_t n0, int wm,
+                                           int wn, int lane) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
+        if (EDGE && n >= g.N) continue;
+        const float bb = (MODE == OUT_BIAS && g.bias) ? load_scalar<bf16_t>(reinterpret_cast<const bf16_t*>(g.bias) + n)
+                                                      : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t m = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                if (EDGE && m >= g.M) continue;
+                const float x = acc[i][j][e];
+                if (MODE == OUT_BIAS) {
+                    store_scalar<bf16_t>(reinterpret_cast<bf16_t*>(g.C) + m * g.ldc + n, x + bb);
+                } else if (MODE == OUT_ACCUM) {
+                    bf16_t* p = reinterpret_cast<bf16_t*>(g.C) + m * g.ldc + n;
+                    store_scalar<bf16_t>(p, load_scalar<bf16_t>(p) + x);
+                } else {
+                    reinterpret_cast<float*>(g.C)[(int64_t)blockIdx.z * g.M * g.ldc + m * g.ldc + n] = x;
+                }
+            }
+    }
+}
+
+template <bool AK, bool BKC, int MODE>
+__global__ void __launch_bounds__(256, 1) dsa3d_xgemm_kernel(GemmArgs g) {
+    __shared__ __attribute__((aligned(16))) char lds[X_LDS_BYTES];
+    const int lane = threadIdx.x % 64, wv = threadIdx.x / 64;
+    const int wm = wv / 2, wn = wv % 2;
+    const uint32_t ntn = (uint32_t)((g.N + XN - 1) / XN);
+    const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int64_t m0 = (int64_t)(lb / ntn) * XM, n0 = (int64_t)(lb % ntn) * XN;
+    const int64_t kb = (int64_t)blockIdx.z * g.k_split;
+    const int64_t ke = std::min<int64_t>(g.K, kb + g.k_split);
+    const bf16_t* A = reinterpret_cast<const bf16_t*>(g.A);
+    const bf16_t* B = reinterpret_cast<const bf16_t*>(g.B);
+    // stage z: A at lds + 2z tiles, B at lds + (2z+1) tiles
+#define XA(z) (lds + (z) * 2 * X_TILE_BYTES)
+#define XB(z) (lds + ((z) * 2 + 1) * X_TILE_BYTES)
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    const uint32_t r = (uint32_t)(lane & 31), kh = (uint32_t)(lane >> 5);
+    const uint32_t a_off = ((uint32_t)wm * 128u + r) * X_ROW_BYTES;
+    const uint32_t b_off = ((uint32_t)wn * 128u + r) * X_ROW_BYTES;
+    const uint32_t sw = xswz(r);
+
+    const int64_t nk = (ke - kb + XK - 1) / XK;
+    XOperand<AK> opa;
+    XOperand<BKC> opb;
+    opa.init(A, g.lda, g.M, m0);
+    opb.init(B, g.ldb, g.N, n0);
+    XSlice sa, sb;
+    if (nk > 0) {
+        x_load<AK>(opa, kb, ke, sa);
+        x_load<BKC>(opb, kb, ke, sb);
+        x_store<AK>(sa, XA(0));
+        x_store<BKC>(sb, XB(0));
+        if (nk > 1) {
+            x_load<AK>(opa, kb + XK, ke, sa);
+            x_load<BKC>(opb, kb + XK, ke, sb);
+        }
+        x_barrier();
+    }
+    for (int64_t t = 0; t < nk; ++t) {
+        const int cur = (int)(t & 1);
+        // First k16 step, then the hand-over of the next slice while those
+        // MFMAs run: its registers go to the other stage (last read in the
+        // previous slice, before the barrier) and the loads of the slice after
+        // it are issued, a whole slice ahead of their use.
+        x_mma_step(XA(cur), XB(cur), a_off, b_off, sw, kh, 0, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + 1 < nk) {
+            x_store<AK>(sa, XA(cur ^ 1));
+            x_store<BKC>(sb, XB(cur ^ 1));
+        }
+        if (t + 2 < nk) {
+            x_load<AK>(opa, kb + (t + 2) * XK, ke, sa);
+            x_load<BKC>(opb, kb + (t + 2) * XK, ke, sb);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (uint32_t ks = 1; ks < 4; ++ks) x_mma_step(XA(cur), XB(cur), a_off, b_off, sw, kh, ks, acc);
+        x_barrier();
+    }
+#undef XA
+#undef XB
+
+    if (m0 + XM <= g.M && n0 + XN <= g.N)
+        x_epilogue<MODE, false>(g, acc, m0, n0, wm, wn, lane);
+    else
+        x_epilogue<MODE, true>(g, acc, m0, n0, wm, wn, lane);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 products whose operands are both K-contiguous (the projection forward,
+// and dq with W transposed beforehand): the same 256x256 tile and 4 waves of
+// 128x128, but the operand tiles travel from memory straight into LDS
+// (global_load_lds_dwordx4: each lane's 16 bytes land at M0 + 16*lane) through
+// a ring of four 32-deep stages, so three slices are in flight while one is
+// multiplied and no register holds staged data. Each wave waits for its own
+// copies with an exact vmcnt, then one barrier per slice publishes the stage
+// and frees the oldest one for the next copy.
+//
+// LDS rows are 64 B (32 bf16 of K); chunk c of row r sits at c ^ ((r>>1)&3).
+// One copy instruction fills 1 KiB = rows 16q..16q+15, lane l taking row
+// 16q + l/4, stored chunk l%4 (so it reads the logical chunk that maps there).
+//
+// The products are formed transposed (D = B.A^T per 32x32 tile): a lane then
+// holds 4 consecutive output columns of one row, which the epilogue writes to
+// LDS as 8-byte pieces and streams out as whole 16-byte row chunks.
+// ---------------------------------------------------------------------------
+constexpr int YK = 32, Y_STAGES = 4;
+constexpr int Y_ROW = YK * 2;                 // 64 B
+constexpr int Y_TILE = 256 * Y_ROW;           // 16 KiB per operand
+constexpr int Y_STAGE = 2 * Y_TILE;           // A then B
+constexpr int Y_LDS = Y_STAGES * Y_STAGE;     // 128 KiB
+
+__device__ __forceinline__ uint32_t yswz(uint32_t r) { return (r >> 1) & 3u; }
+
+// This wave's four copy instructions of one operand tile: lane offsets (bytes,
+// from the tile's first row at k = 0) and the logical K chunk each lane reads.
+struct YOperand {
+    const char* base;  // src + r0*ld, in bytes
+    uint32_t off[4];
+    uint32_t kc;       // first k (elements) of this lane's chunk within a slice
+    __device__ __forceinline__ void init(const bf16_t* src, int64_t ld, int64_t rows, int64_t r0, int wave,
+                                         int lane) {
+        base = reinterpret_cast<const char*>(src + r0 * ld);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t r = 16u * (4u * wave + q) + (uint32_t)(lane >> 2);
+            const int64_t rr = std::min<int64_t>(r0 + r, rows - 1) - r0;
+            off[q] = (uint32_t)(rr * ld * 2);
+        }
+        // the row of instruction q differs by 16 rows, so its swizzle term is the same for all q
+        kc = (((uint32_t)(lane & 3)) ^ yswz((uint32_t)(lane >> 2))) * 8u;
+    }
+};
+
+// M0 carries the LDS address of the copy; it is saved and restored around it
+// (one wait state between setting M0 and the copy).
+__device__ __forceinline__ void y_copy(const char* gbase, uint32_t voff, uint32_t lds_addr) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_addr), "v"(voff), "s"(gbase)
+        : "memory");
+}
+
+// Issue this wave's copies of slice [k0, k0+32) of both operands into a stage.
+// On the last, partial slice a lane whose chunk starts at or past kend reads
+// the last in-bounds chunk instead; y_zero_tail clears it once it has landed.
+__device__ __forceinline__ void y_issue(const YOperand& a, const YOperand& b, int64_t k0, int64_t kend,
+                                        uint32_t stage_addr, int wave) {
+    const bool full = k0 + YK <= kend;
+    const int64_t gk = k0 + a.kc;
+    const uint32_t back = (full || gk < kend) ? 0u : (uint32_t)((gk - (kend - 8)) * 2);
+    const char* ga = a.base + k0 * 2;
+    const char* gb = b.base + k0 * 2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y_copy(ga, a.off[q] + a.kc * 2 - back, stage_addr + (4 * wave + q) * 1024);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y_copy(gb, b.off[q] + b.kc * 2 - back, stage_addr + Y_TILE + (4 * wave + q) * 1024);
+}
+
+__device__ __forceinline__ void y_zero_tail(char* stage, const YOperand& a, int64_t k0, int64_t kend, int wave,
+                                            int lane) {
+    if (k0 + a.kc < kend) return;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        *reinterpret_cast<uint4*>(stage + (4 * wave + q) * 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(stage + Y_TILE + (4 * wave + q) * 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void y_wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void y_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Operand fragments of one k16 step (s = 0, 1) of a stage: lane l holds row
+// l%32 of each 32-row tile and 8 consecutive k (chunk 2s + l/32).
+struct YFrag { bf16x8_t a[4], b[4]; };
+
+__device__ __forceinline__ void y_read(const char* stage, uint32_t a_off, uint32_t b_off, uint32_t sw, uint32_t kh,
+                                       uint32_t s, YFrag& f) {
+    const uint32_t c = ((2u * s + kh) ^ sw) * 16u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f.a[i] = *reinterpret_cast<const bf16x8_t*>(stage + a_off + i * 32 * Y_ROW + c);
+        f.b[i] = *reinterpret_cast<const bf16x8_t*>(stage + Y_TILE + b_off + i * 32 * Y_ROW + c);
+    }
+}
+
+// acc[i][j] = B_j . A_i^T (the transposed 32x32 product), for MFMA number
+// 4i + j of the step.
+__device__ __forceinline__ void y_mma(const YFrag& f, int i, int j, f32x16_t acc[4][4]) {
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+}
+
+// acc[i][j] element e: output row m = 32i + lane%32, columns n = 32j + 8*(e/4)
+// + 4*(lane/32) + e%4 (four consecutive per e/4), of this wave's quarter.
+template <int MODE>
+__device__ __forceinline__ void y_epilogue(const GemmArgs& g, f32x16_t acc[4][4], char* lds, int64_t m0, int64_t n0,
+                                           int wm, int wn, int lane, int wave) {
+    const int64_t mq = m0 + wm * 128, nq = n0 + wn * 128;  // this wave's quarter
+    char* tile = lds + wave * 32768;                        // 128 rows x 256 B, 16-byte chunk c of row m at c ^ (m & 15)
+    const bf16_t* bias = reinterpret_cast<const bf16_t*>(g.bias);
+    bf16_t* C = reinterpret_cast<bf16_t*>(g.C);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const int nl = 32 * j + 8 * e4 + 4 * (lane >> 5);  // first of 4 columns
+            float add[4] = {0.f, 0.f, 0.f, 0.f};
+            if (MODE == OUT_BIAS && bias) {
+                const int64_t n = nq + nl;
+                if (n + 4 <= g.N) {
+                    const uint2 bw = *reinterpret_cast<const uint2*>(bias + n);
+                    add[0] = bf16_lo(bw.x); add[1] = bf16_hi(bw.x); add[2] = bf16_lo(bw.y); add[3] = bf16_hi(bw.y);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ml = 32 * i + (lane & 31);
+                float x[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) x[u] = acc[i][j][4 * e4 + u] + add[u];
+                if (MODE == OUT_ACCUM) {
+                    const int64_t m = mq + ml, n = nq + nl;
+                    if (m < g.M && n + 4 <= g.N) {
+                        const uint2 o = *reinterpret_cast<const uint2*>(C + m * g.ldc + n);
+                        x[0] += bf16_lo(o.x); x[1] += bf16_hi(o.x); x[2] += bf16_lo(o.y); x[3] += bf16_hi(o.y);
+                    }
+                }
+                const uint2 w = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+                const uint32_t chunk = ((uint32_t)nl >> 3) ^ ((uint32_t)ml & 15u);
+                *reinterpret_cast<uint2*>(tile + ml * 256 + chunk * 16 + (nl & 4) * 2) = w;
+            }
+        }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    // 128 rows x 16 chunks: lane takes chunk lane%16 of rows 4*it + lane/16
+    const int cl = lane & 15;
+    const int64_t n = nq + cl * 8;
+    if (n + 8 > g.N) return;
+#pragma unroll 4
+    for (int it = 0; it < 32; ++it) {
+        const int ml = 4 * it + (lane >> 4);
+        const int64_t m = mq + ml;
+        if (m >= g.M) break;
+        const uint4 v = *reinterpret_cast<const uint4*>(tile + ml * 256 + (((uint32_t)cl ^ ((uint32_t)ml & 15u)) * 16));
+        *reinterpret_cast<uint4*>(C + m * g.ldc + n) = v;
+    }
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(256, 1) dsa3d_ntgemm_kernel(GemmArgs g) {
+    __shared__ __attribute__((aligned(1024))) char lds[Y_LDS];
+    const int lane = threadIdx.x % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int wm = wave / 2, wn = wave % 2;
+    const uint32_t ntn = (uint32_t)((g.N + XN - 1) / XN);
+    const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int64_t m0 = (int64_t)(lb / ntn) * XM, n0 = (int64_t)(lb % ntn) * XN;
+    const int64_t K = g.K;
+    YOperand opa, opb;
+    opa.init(reinterpret_cast<const bf16_t*>(g.A), g.lda, g.M, m0, wave, lane);
+    opb.init(reinterpret_cast<const bf16_t*>(g.B), g.ldb, g.N, n0, wave, lane);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    const uint32_t r = (uint32_t)(lane & 31), kh = (uint32_t)(lane >> 5);
+    const uint32_t a_off = ((uint32_t)wm * 128u + r) * Y_ROW;
+    const uint32_t b_off = ((uint32_t)wn * 128u + r) * Y_ROW;
+    const uint32_t sw = yswz(r);
+
+    // Slices 0..S-1 fill the ring. Iteration t multiplies slice t in two k16
+    // steps; between them every wave waits for its copies of slice t+1 and
+    // meets the others at the barrier, after which stage t (read completely
+    // into registers by then) takes slice t+S and the first fragments of
+    // slice t+1 are read. The copies and reads of the second step sit between
+    // its MFMAs, so the matrix pipe keeps running while they issue.
+    const int64_t nk = (K + YK - 1) / YK;
+#pragma unroll
+    for (int t = 0; t < Y_STAGES; ++t)
+        if (t < nk) y_issue(opa, opb, (int64_t)t * YK, K, lds0 + t * Y_STAGE, wave);
+    YFrag f0, f1;
+    if (nk > 0) {
+        const int64_t after = std::min<int64_t>(nk - 1, Y_STAGES - 1);  // slices issued after slice 0
+        if (after >= 3) y_wait_vm<24>();
+        else if (after == 2) y_wait_vm<16>();
+        else if (after == 1) y_wait_vm<8>();
+        else y_wait_vm<0>();
+        if (YK > K) y_zero_tail(lds, opa, 0, K, wave, lane);
+        y_barrier();
+        y_read(lds, a_off, b_off, sw, kh, 0, f0);
+    }
+    for (int64_t t = 0; t < nk; ++t) {
+        const char* stage = lds + (t % Y_STAGES) * Y_STAGE;
+        y_read(stage, a_off, b_off, sw, kh, 1, f1);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) y_mma(f0, q / 4, q % 4, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        const bool more = t + 1 < nk;
+        if (more) {
+            // copies issued after slice t+1's: min(nk-2-t, S-2) slices of 8
+            const int64_t after = std::min<int64_t>(nk - 2 - t, Y_STAGES - 2);
+            if (after >= 2) y_wait_vm<16>();
+            else if (after == 1) y_wait_vm<8>();
+            else y_wait_vm<0>();
+            char* next = lds + ((t + 1) % Y_STAGES) * Y_STAGE;
+            if ((t + 2) * YK > K) y_zero_tail(next, opa, (t + 1) * YK, K, wave, lane);
+        }
+        y_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            const bool refill = more && t + Y_STAGES < nk;
+            const int64_t k0 = (t + Y_STAGES) * YK;
+            const uint32_t st = lds0 + (t % Y_STAGES) * Y_STAGE;
+            const char* ga = opa.base + k0 * 2;
+            const char* gb = opb.base + k0 * 2;
+            const int64_t gk = k0 + opa.kc;
+            const uint32_t back = (k0 + YK <= K || gk < K) ? 0u : (uint32_t)((gk - (K - 8)) * 2);
+            const char* next = lds + ((t + 1) % Y_STAGES) * Y_STAGE;
+            const uint32_t c0 = ((0u + kh) ^ sw) * 16u;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                y_mma(f1, q / 4, q % 4, acc);
+                __builtin_amdgcn_sched_barrier(0);
+                if (q < 8) {
+                    if (refill) {
+                        const int qq = q & 3;
+                        if (q < 4) y_copy(ga, opa.off[qq] + opa.kc * 2 - back, st + (4 * wave + qq) * 1024);
+                        else y_copy(gb, opb.off[qq] + opb.kc * 2 - back, st + Y_TILE + (4 * wave + qq) * 1024);
+                    }
+                } else {
+                    const int i = q - 8;
+                    if (i < 4) f0.a[i] = *reinterpret_cast<const bf16x8_t*>(next + a_off + i * 32 * Y_ROW + c0);
+                    else f0.b[i - 4] = *reinterpret_cast<const bf16x8_t*>(next + Y_TILE + b_off + (i - 4) * 32 * Y_ROW + c0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    y_barrier();  // every wave is done with the stages before they hold the output tile
+    y_epilogue<MODE>(g, acc, lds, m0, n0, wm, wn, lane, wave);
+}
+
 // out[i] = sum_{z < nsplit} part[z*n + i], in order z = 0, 1, ...
 __global__ void __launch_bounds__(256) dsa3d_split_sum_kernel(const float* part, float* out, int64_t n, int nsplit) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
@@ -234,13 +784,74 @@ static hipError_t gemm(GemmArgs g, int splits, int kernel_id, hipStream_t s) {
 
 static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+// The bf16 256x256 path needs 16-byte vectors everywhere: leading dimensions
+// and the contiguous extent of each operand (K for a K-contiguous one, M or N
+// for the other) multiples of 8, and 16-byte aligned bases.
+static bool xgemm_ok(const GemmArgs& g, bool ak, bool bk) {
+    const bool a = (g.lda % 8 == 0) && aligned16(g.A) && ((ak ? g.K : g.M) % 8 == 0);
+    const bool b = (g.ldb % 8 == 0) && aligned16(g.B) && ((bk ? g.K : g.N) % 8 == 0);
+    return a && b && (g.k_split % XK == 0 || g.k_split >= g.K);
+}
+
+template <bool AK, bool BKC, int MODE>
+static hipError_t xgemm(GemmArgs g, int splits, int kernel_id, hipStream_t s) {
+    const int64_t tiles = ((g.M + XM - 1) / XM) * ((g.N + XN - 1) / XN);
+    if (tiles == 0) return hipSuccess;
+    LaunchScope ls(kernel_id, s);
+    hipLaunchKernelGGL((dsa3d_xgemm_kernel<AK, BKC, MODE>), dim3((unsigned)tiles, 1, splits), dim3(256), 0, s, g);
+    return hipGetLastError();
+}
+
+// out[c*F + f] = w[f*C + c]: 64x64 tiles through LDS (odd row stride, no bank conflicts).
+__global__ void __launch_bounds__(256) dsa3d_transpose_kernel(const bf16_t* w, bf16_t* out, int64_t F, int64_t C) {
+    __shared__ bf16_t t[64][65];
+    const int64_t f0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        const int r = i / 64, c = i % 64;
+        if (f0 + r < F && c0 + c < C) t[r][c] = w[(f0 + r) * C + c0 + c];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        const int r = i / 64, c = i % 64;
+        if (c0 + r < C && f0 + c < F) out[(c0 + r) * F + f0 + c] = t[c][r];
+    }
+}
+
+// The DMA-fed kernel needs both operands K-contiguous and everything in
+// 16-byte pieces: K, the leading dimensions and N multiples of 8, 16-byte
+// aligned bases (bias included), one K range.
+static bool ntgemm_ok(const GemmArgs& g) {
+    return g.lda % 8 == 0 && g.ldb % 8 == 0 && g.ldc % 8 == 0 && g.K % 8 == 0 && g.N % 8 == 0 && aligned16(g.A) &&
+           aligned16(g.B) && aligned16(g.C) && (g.bias == nullptr || aligned16(g.bias)) && g.k_split >= g.K;
+}
+
+template <int MODE>
+static hipError_t ntgemm(GemmArgs g, int kernel_id, hipStream_t s) {
+    const int64_t tiles = ((g.M + XM - 1) / XM) * ((g.N + XN - 1) / XN);
+    if (tiles == 0) return hipSuccess;
+    LaunchScope ls(kernel_id, s);
+    hipLaunchKernelGGL((dsa3d_ntgemm_kernel<MODE>), dim3((unsigned)tiles), dim3(256), 0, s, g);
+    return hipGetLastError();
+}
+
+// bf16 products go to the 256x256 kernel when its vector conditions hold,
+// everything else (float32, odd sizes) to the 128x128 one.
+template <typename T, bool AK, bool BKC, int MODE>
+static hipError_t gemm_any(GemmArgs g, int splits, int kernel_id, hipStream_t s) {
+    if constexpr (sizeof(T) == 2) {
+        if (xgemm_ok(g, AK, BKC)) return xgemm<AK, BKC, MODE>(g, splits, kernel_id, s);
+    }
+    return gemm<T, AK, BKC, MODE>(g, splits, kernel_id, s);
+}
+
 // Split counts of the two long reductions over the N_tok rows.
 void proj_bwd_splits(const dsa3d_desc& d, int& dw_splits, int& db_splits) {
     const int64_t ntok = d.B * d.T * d.H * d.W;
     const int64_t F = (int64_t)d.heads * d.P * 3, C = (int64_t)d.heads * d.head_dim;
-    const int64_t tiles = ((F + BM - 1) / BM) * ((C + BN - 1) / BN);
+    const int64_t tm = d.dtype == DSA3D_BF16 ? XM : BM, tn = d.dtype == DSA3D_BF16 ? XN : BN;
+    const int64_t tiles = ((F + tm - 1) / tm) * ((C + tn - 1) / tn);
     int64_t s = (1024 + tiles - 1) / std::max<int64_t>(tiles, 1);
-    s = std::max<int64_t>(1, std::min<int64_t>(s, std::max<int64_t>(1, ntok / (8 * BK))));
+    s = std::max<int64_t>(1, std::min<int64_t>(s, std::max<int64_t>(1, ntok / (4 * XK))));
     s = std::min<int64_t>(s, 64);
     dw_splits = (int)s;
     const int64_t fb = (F + 255) / 256;
@@ -253,7 +864,9 @@ size_t proj_bwd_workspace_bytes(const dsa3d_desc& d) {
     int sw, sb;
     proj_bwd_splits(d, sw, sb);
     const int64_t F = (int64_t)d.heads * d.P * 3, C = (int64_t)d.heads * d.head_dim;
-    return (size_t)sw * F * C * 4 + (size_t)sb * F * 4 + 256;
+    size_t bytes = (size_t)sw * F * C * 4 + (size_t)sb * F * 4;
+    if (d.dtype == DSA3D_BF16) bytes += 256 + (size_t)F * C * 2;  // w transposed, 256-aligned
+    return bytes + 256;
 }
 
 hipError_t launch_proj_forward(const dsa3d_desc& d, const void* q, const void* w, const void* bias, void* off,
@@ -268,7 +881,8 @@ hipError_t launch_proj_forward(const dsa3d_desc& d, const void* q, const void* w
     g.C = off; g.ldc = g.N;
     g.bias = bias;
     if (d.dtype == DSA3D_F32) return gemm<float, true, true, OUT_BIAS>(g, 1, DSA3D_K_PROJ_FORWARD, s);
-    return gemm<bf16_t, true, true, OUT_BIAS>(g, 1, DSA3D_K_PROJ_FORWARD, s);
+    if (ntgemm_ok(g)) return ntgemm<OUT_BIAS>(g, DSA3D_K_PROJ_FORWARD, s);
+    return gemm_any<bf16_t, true, true, OUT_BIAS>(g, 1, DSA3D_K_PROJ_FORWARD, s);
 }
 
 hipError_t launch_proj_backward(const dsa3d_desc& d, const void* q, const void* w, const void* doff, void* dq,
@@ -278,6 +892,8 @@ hipError_t launch_proj_backward(const dsa3d_desc& d, const void* q, const void* 
     if (ntok == 0) return hipSuccess;
     const bool f32 = d.dtype == DSA3D_F32;
     hipError_t e;
+    int sw, sb;
+    proj_bwd_splits(d, sw, sb);
     // dq[ntok, C] += doff[ntok, F] . W[F, C]
     GemmArgs g{};
     g.A = doff; g.lda = F;
@@ -285,22 +901,38 @@ hipError_t launch_proj_backward(const dsa3d_desc& d, const void* q, const void* 
     g.M = ntok; g.N = C; g.K = F;
     g.k_split = round_up(F, BK);
     g.C = dq; g.ldc = C;
-    e = f32 ? gemm<float, true, false, OUT_ACCUM>(g, 1, DSA3D_K_PROJ_BWD_DQ, s)
-              : gemm<bf16_t, true, false, OUT_ACCUM>(g, 1, DSA3D_K_PROJ_BWD_DQ, s);
+    // bf16: with W transposed into the workspace ([C, F], K-contiguous) the
+    // product takes the DMA-fed kernel
+    const uintptr_t wt_at = round_up((int64_t)(reinterpret_cast<uintptr_t>(ws) + (size_t)sw * F * C * 4 +
+                                               (size_t)sb * F * 4), 256);
+    GemmArgs gt = g;
+    gt.B = reinterpret_cast<const void*>(wt_at);
+    gt.ldb = F;
+    if (!f32 && ntgemm_ok(gt)) {
+        {
+            LaunchScope ls(DSA3D_K_TRANSPOSE, s);
+            hipLaunchKernelGGL(dsa3d_transpose_kernel, dim3((unsigned)((C + 63) / 64), (unsigned)((F + 63) / 64)),
+                               dim3(256), 0, s, reinterpret_cast<const bf16_t*>(w), reinterpret_cast<bf16_t*>(wt_at),
+                               F, C);
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        e = ntgemm<OUT_ACCUM>(gt, DSA3D_K_PROJ_BWD_DQ, s);
+    } else {
+        e = f32 ? gemm<float, true, false, OUT_ACCUM>(g, 1, DSA3D_K_PROJ_BWD_DQ, s)
+                : gemm_any<bf16_t, true, false, OUT_ACCUM>(g, 1, DSA3D_K_PROJ_BWD_DQ, s);
+    }
     if (e != hipSuccess) return e;
     // dW[F, C] = doff^T . q, split over the token rows, then a fixed-order sum
-    int sw, sb;
-    proj_bwd_splits(d, sw, sb);
     float* part = reinterpret_cast<float*>(ws);
     GemmArgs h{};
     h.A = doff; h.lda = F;   // a(m=f, k=n) = doff[n*F + f]: M-contiguous
     h.B = q; h.ldb = C;      // b(k=n, n=c) = q[n*C + c]: N-contiguous
     h.M = F; h.N = C; h.K = ntok;
-    h.k_split = round_up((ntok + sw - 1) / sw, BK);
+    h.k_split = round_up((ntok + sw - 1) / sw, XK);  // a multiple of both kernels' K slice
     const int splits = (int)((ntok + h.k_split - 1) / h.k_split);
     h.C = part; h.ldc = C;
     e = f32 ? gemm<float, false, false, OUT_PARTIAL>(h, splits, DSA3D_K_PROJ_BWD_DW, s)
-              : gemm<bf16_t, false, false, OUT_PARTIAL>(h, splits, DSA3D_K_PROJ_BWD_DW, s);
+              : gemm_any<bf16_t, false, false, OUT_PARTIAL>(h, splits, DSA3D_K_PROJ_BWD_DW, s);
     if (e != hipSuccess) return e;
     const int64_t nw = F * C;
     {

@@ -146,7 +146,8 @@ int dsa3d_backward(const dsa3d_desc* desc, const void* q, const void* k, const v
  *   dw[f, c]  = sum_n doffsets[n, f] * q[n, c]          (float32, overwritten)
  *   dbias[f]  = sum_n doffsets[n, f]                    (float32, overwritten; may be NULL)
  * dw and dbias are summed in a fixed order (bitwise reproducible). The
- * workspace (DSA3D_WS_PROJ_BACKWARD) holds split-sum partials. */
+ * workspace (DSA3D_WS_PROJ_BACKWARD) holds split-sum partials and, for bf16,
+ * a transposed copy of w. */
 int dsa3d_offset_proj_backward(const dsa3d_desc* desc, const void* q, const void* w,
                                const void* doffsets, void* dq_accum, float* dw, float* dbias,
                                void* workspace, size_t workspace_bytes, void* stream);
@@ -173,7 +174,8 @@ typedef enum {
     DSA3D_K_GEOMETRY = 10,      /* test hook */
     DSA3D_K_BWD_SCAN = 11,      /* backward: bucket starts (3 small kernels, one entry) */
     DSA3D_K_BWD_COUNT = 12,     /* backward: samples per base cell */
-    DSA3D_K_BWD_SORT = 13       /* backward, deterministic: bucket sort (2 kernels, one entry) */
+    DSA3D_K_BWD_SORT = 13,      /* backward, deterministic: bucket sort (2 kernels, one entry) */
+    DSA3D_K_TRANSPOSE = 14      /* projection backward: W transposed for the dq product */
 } dsa3d_kernel;
 
 typedef struct dsa3d_launch_log {

@@ -194,9 +194,15 @@ def test_deterministic_mode_is_bitwise_reproducible_across_runs_and_pass_splits(
 # offset projection
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_projection_forward_and_backward(dtype):
-    wl = synth.Workload("proj-" + dtype, 1, 3, 10, 13, 3, 32, (3, 3, 3), (1, 1, 1), dtype, "proj", backward=True)
+# (heads, head_dim, grid): 3 heads give F = 243, which takes the 128x128 kernel
+# for every product; 8 heads (F = 648, C = 512) take the bf16 256x256 kernel
+# for all three, with ragged M, N and K tiles (1,380 tokens; 648 = 2.5 tiles;
+# K = 648 = 10.1 slices for dq; a short last split for dW).
+@pytest.mark.parametrize("dtype,shape", [("bf16", (3, 32, (3, 10, 13))), ("f32", (3, 32, (3, 10, 13))),
+                                         ("bf16", (8, 64, (3, 20, 23)))])
+def test_projection_forward_and_backward(dtype, shape):
+    heads, hd, (T, H, W) = shape
+    wl = synth.Workload("proj-" + dtype, 1, T, H, W, heads, hd, (3, 3, 3), (1, 1, 1), dtype, "proj", backward=True)
     say(f"[projection] {synth.describe(wl)}")
     x = synth.make_inputs(wl, "cpu", seed=19)
     x["proj_b"].normal_(0, 0.1, generator=torch.Generator().manual_seed(2))
