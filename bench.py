@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 VALU_F32_PEAK_TFLOPS = 157.3   # MI355X vector fp32, published (dual-issue/packed)
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
 METRIC = "3D-DSA fwd+bwd tokens/sec at 256×68×120 tokens; achieved HBM GB/s vs peak"
 
 
@@ -330,6 +331,19 @@ def main():
                     "unit": "TFLOP/s", "frac": round(step_flops / (ms_per_step / 1e3) / 1e12 / VALU_F32_PEAK_TFLOPS, 5),
                     "flops_per_token": step_flops // wl.tokens}
 
+    # the projection GEMMs (workloads whose offsets come from the Linear): MFMA-bound
+    roofline_proj = None
+    if wl.offsets == "proj":
+        gemm_flops = 2.0 * wl.tokens * wl.C * wl.F  # one product of the projection
+        roofline_proj = {}
+        for k in ("proj_forward", "proj_bwd_dq", "proj_bwd_dw"):
+            if k in per_kernel:
+                tf = gemm_flops / (per_kernel[k]["mean_ms"] / 1e3) / 1e12
+                roofline_proj[k] = {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                                    "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                                    "launch_ms": round(per_kernel[k]["mean_ms"], 3),
+                                    "flops_per_launch": gemm_flops}
+
     result = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
@@ -341,6 +355,7 @@ def main():
                    "chain": ("proj+" if wl.offsets == "proj" else "") + ("fwd+bwd" if wl.backward else "fwd"),
                    "deterministic": wl.deterministic},
         "roofline": roofline, "roofline_alu": roofline_alu,
+        **({"roofline_proj": roofline_proj} if roofline_proj else {}),
         "kernels": {k: {"launches": v["launches"], "mean_ms": round(v["mean_ms"], 3)} for k, v in per_kernel.items()},
     }
     if args.cpu_baseline == "on":

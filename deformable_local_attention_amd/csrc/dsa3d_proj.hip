@@ -568,6 +568,19 @@ __device__ __forceinline__ void y_wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Wait until at most `slices` slices of this wave's copies (8 each) are in flight.
+__device__ __forceinline__ void y_wait_slices(int64_t slices) {
+    static_assert(Y_STAGES <= 6, "vmcnt holds at most 63 outstanding copies");
+    switch (slices) {
+        case 0: y_wait_vm<0>(); break;
+        case 1: y_wait_vm<8>(); break;
+        case 2: y_wait_vm<16>(); break;
+        case 3: y_wait_vm<24>(); break;
+        case 4: y_wait_vm<32>(); break;
+        default: y_wait_vm<40>(); break;
+    }
+}
+
 __device__ __forceinline__ void y_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Operand fragments of one k16 step (s = 0, 1) of a stage: lane l holds row
@@ -688,10 +701,7 @@ __global__ void __launch_bounds__(256, 1) dsa3d_ntgemm_kernel(GemmArgs g) {
     YFrag f0, f1;
     if (nk > 0) {
         const int64_t after = std::min<int64_t>(nk - 1, Y_STAGES - 1);  // slices issued after slice 0
-        if (after >= 3) y_wait_vm<24>();
-        else if (after == 2) y_wait_vm<16>();
-        else if (after == 1) y_wait_vm<8>();
-        else y_wait_vm<0>();
+        y_wait_slices(after);
         if (YK > K) y_zero_tail(lds, opa, 0, K, wave, lane);
         y_barrier();
         y_read(lds, a_off, b_off, sw, kh, 0, f0);
@@ -706,9 +716,7 @@ __global__ void __launch_bounds__(256, 1) dsa3d_ntgemm_kernel(GemmArgs g) {
         if (more) {
             // copies issued after slice t+1's: min(nk-2-t, S-2) slices of 8
             const int64_t after = std::min<int64_t>(nk - 2 - t, Y_STAGES - 2);
-            if (after >= 2) y_wait_vm<16>();
-            else if (after == 1) y_wait_vm<8>();
-            else y_wait_vm<0>();
+            y_wait_slices(after);
             char* next = lds + ((t + 1) % Y_STAGES) * Y_STAGE;
             if ((t + 2) * YK > K) y_zero_tail(next, opa, (t + 1) * YK, K, wave, lane);
         }
@@ -767,6 +775,49 @@ __global__ void __launch_bounds__(256) dsa3d_colsum_kernel(const T* g, float* pa
     float s = 0.0f;
     for (int64_t r = r0; r < r1; ++r) s += load_scalar<T>(g + r * F + f);
     part[(int64_t)blockIdx.y * F + f] = s;
+}
+
+// bf16 with F % 8 == 0: a thread owns 8 consecutive columns (16-byte loads)
+// and keeps four running sums per column, over rows r = 0, 1, 2, 3 (mod 4) of
+// its split, joined as (s0 + s1) + (s2 + s3): a fixed order, four loads in flight.
+__global__ void __launch_bounds__(256) dsa3d_colsum8_kernel(const bf16_t* g, float* part, int64_t rows, int64_t F,
+                                                            int64_t rows_per_split) {
+    const int64_t c = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+    if (c >= F) return;
+    const int64_t r0 = (int64_t)blockIdx.y * rows_per_split;
+    const int64_t r1 = std::min<int64_t>(rows, r0 + rows_per_split);
+    float acc[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[u][e] = 0.0f;
+    int64_t r = r0;
+    for (; r + 4 <= r1; r += 4) {
+        Frag8<bf16_t> v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u].load(g + (r + u) * F + c);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float x[8];
+            v[u].to_f32(x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[u][e] += x[e];
+        }
+    }
+    for (; r < r1; ++r) {
+        Frag8<bf16_t> v;
+        v.load(g + r * F + c);
+        float x[8];
+        v.to_f32(x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[0][e] += x[e];
+    }
+    float out[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (acc[0][e] + acc[1][e]) + (acc[2][e] + acc[3][e]);
+    Frag8<float> o;
+    o.from_f32(out);
+    o.store(part + (int64_t)blockIdx.y * F + c);
 }
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -854,10 +905,8 @@ void proj_bwd_splits(const dsa3d_desc& d, int& dw_splits, int& db_splits) {
     s = std::max<int64_t>(1, std::min<int64_t>(s, std::max<int64_t>(1, ntok / (4 * XK))));
     s = std::min<int64_t>(s, 64);
     dw_splits = (int)s;
-    const int64_t fb = (F + 255) / 256;
-    int64_t sb = (1024 + fb - 1) / fb;
-    sb = std::max<int64_t>(1, std::min<int64_t>(sb, std::max<int64_t>(1, ntok / 64)));
-    db_splits = (int)std::min<int64_t>(sb, 256);
+    // column sums: up to 1024 splits of at least 256 rows
+    db_splits = (int)std::max<int64_t>(1, std::min<int64_t>(1024, ntok / 256));
 }
 
 size_t proj_bwd_workspace_bytes(const dsa3d_desc& d) {
@@ -945,14 +994,21 @@ hipError_t launch_proj_backward(const dsa3d_desc& d, const void* q, const void* 
         float* bpart = part + (size_t)sw * F * C;
         const int64_t rps = (ntok + sb - 1) / sb;
         const int bsplits = (int)((ntok + rps - 1) / rps);
-        dim3 grid((unsigned)((F + 255) / 256), (unsigned)bsplits);
         {
-        LaunchScope ls(DSA3D_K_COLSUM, s);
-        if (f32)
-            hipLaunchKernelGGL((dsa3d_colsum_kernel<float>), grid, dim3(256), 0, s, (const float*)doff, bpart, ntok, F, rps);
-        else
-            hipLaunchKernelGGL((dsa3d_colsum_kernel<bf16_t>), grid, dim3(256), 0, s, (const bf16_t*)doff, bpart, ntok, F,
-                               rps);
+            LaunchScope ls(DSA3D_K_COLSUM, s);
+            if (!f32 && F % 8 == 0 && aligned16(doff) && aligned16(bpart)) {
+                dim3 grid((unsigned)((F / 8 + 255) / 256), (unsigned)bsplits);
+                hipLaunchKernelGGL(dsa3d_colsum8_kernel, grid, dim3(256), 0, s, (const bf16_t*)doff, bpart, ntok, F,
+                                   rps);
+            } else {
+                dim3 grid((unsigned)((F + 255) / 256), (unsigned)bsplits);
+                if (f32)
+                    hipLaunchKernelGGL((dsa3d_colsum_kernel<float>), grid, dim3(256), 0, s, (const float*)doff, bpart,
+                                       ntok, F, rps);
+                else
+                    hipLaunchKernelGGL((dsa3d_colsum_kernel<bf16_t>), grid, dim3(256), 0, s, (const bf16_t*)doff,
+                                       bpart, ntok, F, rps);
+            }
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
         LaunchScope ls(DSA3D_K_SPLIT_SUM, s);
