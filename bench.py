@@ -128,13 +128,17 @@ def cpu_baseline(wl, budget_s: float = 20.0):
                        f"whole tokens ({wl.heads} heads)")}
 
 
+# the sources the attention kernels (forward, backward per query and per key)
+# are compiled from
+ATTN_SOURCES = ("dsa3d_attn.hip", "dsa3d_bwd.hip", "dsa3d_attn_common.h", "dsa3d_device.h")
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the kernel sources and the C ABI header: counter readings
-    taken on other sources no longer describe the kernels."""
-    import glob
+    """sha256 over the attention kernels' sources: counter readings taken on
+    other sources no longer describe the kernels."""
     import hashlib
     pkg = os.path.join(ROOT, "deformable_local_attention_amd", "csrc")
-    files = sorted(glob.glob(os.path.join(pkg, "*"))) + [os.path.join(ROOT, "include", "dsa3d.h")]
+    files = [os.path.join(pkg, f) for f in ATTN_SOURCES]
     h = hashlib.sha256()
     for f in files:
         h.update(os.path.basename(f).encode())
