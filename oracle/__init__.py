@@ -316,3 +316,61 @@ def offset_proj_backward(q2d, w, doff2d) -> Tuple[np.ndarray, np.ndarray, np.nda
     dW = doff^T @ q, db = column sums of doff)."""
     g = _f64(doff2d)
     return g @ _f64(w), g.T @ _f64(q2d), g.sum(axis=0)
+
+
+# ----------------------------------------------------------------------------
+# Depthwise 3-D convolution of the offset network, before the pointwise layer
+# [MegaSlide-DiT, §5.3 Implementation considerations: nn.Conv3d with groups equal
+# to the hidden size, followed by pointwise convolutions; Dutch and French
+# summaries, "3D Deformable Slide Attention", Implementation: a lightweight
+# depthwise 3-D convolution and a linear layer]. The pages give no kernel size;
+# the reading here is 3x3x3, stride 1, zero padding 1 (output the size of the
+# input), with a bias, applied to the query tensor [B,T,H,W,C] channel by
+# channel, C = heads*head_dim, weight [C, 3, 3, 3] (torch's Conv3d weight
+# [C, 1, 3, 3, 3] without its unit axis). Conv3d is a cross-correlation: tap
+# (i, j, k) reads the input at offset (i-1, j-1, k-1).
+# ----------------------------------------------------------------------------
+
+def _pad1(x: np.ndarray) -> np.ndarray:
+    B, T, H, W, C = x.shape
+    xp = np.zeros((B, T + 2, H + 2, W + 2, C))
+    xp[:, 1:-1, 1:-1, 1:-1] = x
+    return xp
+
+
+def dwconv3d(q, w, b=None) -> np.ndarray:
+    """y[b,t,h,x,c] = bias[c] + sum over taps (i,j,k) in {0,1,2}^3 of
+    w[c,i,j,k] * q[b, t+i-1, h+j-1, x+k-1, c], zero outside the grid; float64."""
+    x = _f64(q)
+    wt = _f64(w)
+    B, T, H, W, C = x.shape
+    xp = _pad1(x)
+    y = np.zeros_like(x)
+    for i in range(3):
+        for j in range(3):
+            for k in range(3):
+                y += wt[:, i, j, k] * xp[:, i:i + T, j:j + H, k:k + W]
+    if b is not None:
+        y += _f64(b)
+    return y
+
+
+def dwconv3d_backward(q, w, dy) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of dwconv3d for an output gradient dy, float64:
+    dq[b,t,h,x,c] = sum over taps of w[c,i,j,k] * dy[b, t-i+1, h-j+1, x-k+1, c]
+    (zero outside), dw[c,i,j,k] = sum over all tokens of dy * q shifted by the
+    tap, db[c] = sum over all tokens of dy."""
+    g = _f64(dy)
+    x = _f64(q)
+    wt = _f64(w)
+    B, T, H, W, C = g.shape
+    gp = _pad1(g)
+    xp = _pad1(x)
+    dq = np.zeros_like(g)
+    dw = np.zeros((C, 3, 3, 3))
+    for i in range(3):
+        for j in range(3):
+            for k in range(3):
+                dq += wt[:, i, j, k] * gp[:, 2 - i:2 - i + T, 2 - j:2 - j + H, 2 - k:2 - k + W]
+                dw[:, i, j, k] = (g * xp[:, i:i + T, j:j + H, k:k + W]).sum(axis=(0, 1, 2, 3))
+    return dq, dw, g.sum(axis=(0, 1, 2, 3))

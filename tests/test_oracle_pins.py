@@ -472,3 +472,76 @@ def test_projection_matches_explicit_loops():
     # a basis-vector weight picks single query columns (catches a transposed operand)
     w1 = np.zeros((F, C)); w1[np.arange(F), np.arange(F)] = 1
     assert np.array_equal(oracle.offset_proj(q, w1), q[:, :F])
+
+
+# ---------------------------------------------------------------------------
+# 12. Depthwise 3-D convolution of the offset network: explicit loops, a
+# library correlation, shifted deltas, the adjoint identity and finite
+# differences pin the forward and all three gradients.
+# ---------------------------------------------------------------------------
+
+def _dwconv_loops(q, w, b):
+    B, T, H, W, C = q.shape
+    y = np.zeros_like(q)
+    for bb in range(B):
+        for t in range(T):
+            for h in range(H):
+                for x in range(W):
+                    for c in range(C):
+                        s = b[c]
+                        for i in range(3):
+                            for j in range(3):
+                                for k in range(3):
+                                    tt, hh, xx = t + i - 1, h + j - 1, x + k - 1
+                                    if 0 <= tt < T and 0 <= hh < H and 0 <= xx < W:
+                                        s += w[c, i, j, k] * q[bb, tt, hh, xx, c]
+                        y[bb, t, h, x, c] = s
+    return y
+
+
+def test_dwconv_matches_explicit_loops():
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((2, 3, 4, 5, 3)); w = rng.standard_normal((3, 3, 3, 3)); b = rng.standard_normal(3)
+    assert np.abs(oracle.dwconv3d(q, w, b) - _dwconv_loops(q, w, b)).max() < 1e-12
+
+
+def test_dwconv_matches_library_correlation():
+    from scipy.ndimage import correlate
+    rng = np.random.default_rng(22)
+    q = rng.standard_normal((1, 5, 6, 7, 4)); w = rng.standard_normal((4, 3, 3, 3))
+    y = oracle.dwconv3d(q, w)
+    for c in range(4):
+        ref = correlate(q[0, ..., c], w[c], mode="constant", cval=0.0)
+        assert np.abs(y[0, ..., c] - ref).max() < 1e-12
+
+
+def test_dwconv_deltas_identity_and_shift():
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal((1, 4, 5, 6, 2))
+    w = np.zeros((2, 3, 3, 3)); w[:, 1, 1, 1] = 1.0
+    assert np.array_equal(oracle.dwconv3d(q, w), q)
+    # tap (2, 1, 0) reads the input one frame later and one token to the left
+    w = np.zeros((2, 3, 3, 3)); w[:, 2, 1, 0] = 1.0
+    y = oracle.dwconv3d(q, w)
+    assert np.array_equal(y[0, :-1, :, 1:], q[0, 1:, :, :-1])
+    assert np.all(y[0, -1] == 0) and np.all(y[0, :, :, 0] == 0)
+
+
+def test_dwconv_backward_adjoint_and_finite_differences():
+    rng = np.random.default_rng(24)
+    q = rng.standard_normal((1, 3, 3, 4, 2)); w = rng.standard_normal((2, 3, 3, 3)); b = rng.standard_normal(2)
+    g = rng.standard_normal(q.shape)
+    dq, dw, db = oracle.dwconv3d_backward(q, w, g)
+    # <conv(q), g> = <q, conv^T(g)> for the linear part
+    assert abs(np.sum(oracle.dwconv3d(q, w) * g) - np.sum(q * dq)) < 1e-10
+    L = lambda q_, w_, b_: float(np.sum(oracle.dwconv3d(q_, w_, b_) * g))
+    eps = 1e-6
+    for idx in [(0, 0, 0, 0, 0), (0, 1, 2, 3, 1), (0, 2, 1, 0, 0)]:
+        e = np.zeros_like(q); e[idx] = eps
+        assert abs((L(q + e, w, b) - L(q - e, w, b)) / (2 * eps) - dq[idx]) < 1e-6
+    for idx in [(0, 0, 0, 0), (1, 2, 1, 0), (0, 1, 1, 1), (1, 0, 2, 2)]:
+        e = np.zeros_like(w); e[idx] = eps
+        assert abs((L(q, w + e, b) - L(q, w - e, b)) / (2 * eps) - dw[idx]) < 1e-6
+    for c in range(2):
+        e = np.zeros_like(b); e[c] = eps
+        assert abs((L(q, w, b + e) - L(q, w, b - e)) / (2 * eps) - db[c]) < 1e-6
