@@ -24,19 +24,21 @@ __all__ = [
     "dsa3d_version", "dsa3d_status_string", "dsa3d_validate", "dsa3d_workspace_size", "dsa3d_workspace_min",
     "dsa3d_offset_proj_forward", "dsa3d_forward", "dsa3d_backward", "dsa3d_offset_proj_backward",
     "dsa3d_debug_geometry", "forward", "backward", "offset_proj", "offset_proj_backward",
-    "DSA3D_F32", "DSA3D_BF16", "WS_FORWARD", "WS_BACKWARD", "WS_PROJ_BACKWARD",
+    "DSA3D_F32", "DSA3D_BF16", "WS_FORWARD", "WS_BACKWARD", "WS_PROJ_BACKWARD", "WS_DWCONV_BACKWARD",
+    "dsa3d_dwconv_forward", "dsa3d_dwconv_backward", "dwconv", "dwconv_backward",
     "dsa3d_set_launch_log", "LaunchLog", "launch_timer", "KERNELS",
 ]
 
 DSA3D_F32, DSA3D_BF16 = 0, 1
-WS_FORWARD, WS_BACKWARD, WS_PROJ_BACKWARD = 0, 1, 2
+WS_FORWARD, WS_BACKWARD, WS_PROJ_BACKWARD, WS_DWCONV_BACKWARD = 0, 1, 2, 3
 EXPORTS = ("dsa3d_version", "dsa3d_status_string", "dsa3d_validate", "dsa3d_workspace_size",
            "dsa3d_workspace_min", "dsa3d_offset_proj_forward", "dsa3d_forward", "dsa3d_backward",
-           "dsa3d_offset_proj_backward", "dsa3d_debug_geometry", "dsa3d_set_launch_log")
+           "dsa3d_offset_proj_backward", "dsa3d_debug_geometry", "dsa3d_dwconv_forward", "dsa3d_dwconv_backward",
+           "dsa3d_set_launch_log")
 # kernel ids of the launch log (dsa3d_kernel)
 KERNELS = {1: "proj_forward", 2: "forward", 3: "bwd_query", 4: "bwd_key", 5: "fill", 6: "proj_bwd_dq",
            7: "proj_bwd_dw", 8: "split_sum", 9: "colsum", 10: "geometry", 11: "bwd_scan", 12: "bwd_count",
-           13: "bwd_sort", 14: "transpose"}
+           13: "bwd_sort", 14: "transpose", 15: "dwconv", 16: "dwconv_wgrad"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -94,6 +96,8 @@ def lib() -> ctypes.CDLL:
                 "dsa3d_backward": ([dp] + [vp] * 11 + [vp, sz, vp], ctypes.c_int),
                 "dsa3d_offset_proj_backward": ([dp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
                 "dsa3d_debug_geometry": ([dp, vp, vp, vp, vp], ctypes.c_int),
+                "dsa3d_dwconv_forward": ([dp, vp, vp, vp, vp, vp], ctypes.c_int),
+                "dsa3d_dwconv_backward": ([dp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
                 "dsa3d_set_launch_log": ([ctypes.POINTER(LaunchLog)], ctypes.c_int),
             }
             for name, (args, res) in sig.items():
@@ -193,6 +197,18 @@ def dsa3d_offset_proj_backward(desc: Desc, q, w, doffsets, dq_accum, dw, dbias, 
                                             _ptr(dw), _ptr(dbias), _ptr(workspace), nbytes, _stream(stream)))
 
 
+def dsa3d_dwconv_forward(desc: Desc, q, wt, bias, y, stream=None):
+    _check("dsa3d_dwconv_forward",
+           lib().dsa3d_dwconv_forward(ctypes.byref(desc), _ptr(q), _ptr(wt), _ptr(bias), _ptr(y), _stream(stream)))
+
+
+def dsa3d_dwconv_backward(desc: Desc, q, wt, dy, dq_accum, dwt, dbias, workspace, stream=None):
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dsa3d_dwconv_backward",
+           lib().dsa3d_dwconv_backward(ctypes.byref(desc), _ptr(q), _ptr(wt), _ptr(dy), _ptr(dq_accum), _ptr(dwt),
+                                       _ptr(dbias), _ptr(workspace), nbytes, _stream(stream)))
+
+
 def dsa3d_set_launch_log(log: Optional[LaunchLog]):
     _check("dsa3d_set_launch_log", lib().dsa3d_set_launch_log(None if log is None else ctypes.byref(log)))
 
@@ -282,6 +298,24 @@ def offset_proj(q, w, bias, window, stream=None):
     off = torch.empty((B, T, H, W, nh, P, 3), dtype=q.dtype, device=q.device)
     dsa3d_offset_proj_forward(desc, q, w, bias, off, stream)
     return off
+
+
+def dwconv(q, wt, bias, stream=None):
+    """Depthwise 3x3x3 convolution of q [B,T,H,W,heads,d] (channels = heads*d) with wt [C,3,3,3]."""
+    desc = desc_like(q, (1, 1, 1))
+    y = torch.empty_like(q)
+    dsa3d_dwconv_forward(desc, q, wt, bias, y, stream)
+    return y
+
+
+def dwconv_backward(q, wt, dy, dq_accum, with_bias: bool = True, stream=None):
+    """Adds the convolution's input gradient into dq_accum; returns (dwt, dbias) in float32."""
+    desc = desc_like(q, (1, 1, 1))
+    dwt = torch.empty(wt.shape, dtype=torch.float32, device=q.device)
+    db = torch.empty(wt.shape[0], dtype=torch.float32, device=q.device) if with_bias else None
+    ws = _workspace(desc, WS_DWCONV_BACKWARD, q.device)
+    dsa3d_dwconv_backward(desc, q, wt, dy, dq_accum, dwt, db, ws, stream)
+    return dwt, db
 
 
 def offset_proj_backward(q, w, doffsets, dq_accum, window, with_bias: bool = True, stream=None):

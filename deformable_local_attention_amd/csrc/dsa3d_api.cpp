@@ -90,6 +90,7 @@ size_t dsa3d_workspace_min(const dsa3d_desc* d, int kind) {
     switch (kind) {
         case DSA3D_WS_BACKWARD: return dsa3d::bwd_workspace_bytes(*d, 1);
         case DSA3D_WS_PROJ_BACKWARD: return dsa3d::proj_bwd_workspace_bytes(*d);
+        case DSA3D_WS_DWCONV_BACKWARD: return dsa3d::dwconv_bwd_workspace_bytes(*d);
         default: return 0;
     }
 }
@@ -148,6 +149,27 @@ int dsa3d_offset_proj_backward(const dsa3d_desc* d, const void* q, const void* w
     if (!aligned16(workspace)) return DSA3D_ERR_MISALIGNED;
     return hip_status(dsa3d::launch_proj_backward(*d, q, w, doffsets, dq_accum, dw, dbias, workspace,
                                                   static_cast<hipStream_t>(stream)));
+}
+
+int dsa3d_dwconv_forward(const dsa3d_desc* d, const void* q, const void* wt, const void* bias, void* y, void* stream) {
+    int rc = dsa3d_validate(d);
+    if (rc != DSA3D_OK) return rc;
+    if ((rc = check_ptrs({q, wt, y})) != DSA3D_OK) return rc;
+    if (bias != nullptr && !aligned16(bias)) return DSA3D_ERR_MISALIGNED;
+    return hip_status(dsa3d::launch_dwconv_forward(*d, q, wt, bias, y, static_cast<hipStream_t>(stream)));
+}
+
+int dsa3d_dwconv_backward(const dsa3d_desc* d, const void* q, const void* wt, const void* dy, void* dq_accum,
+                          float* dwt, float* dbias, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = dsa3d_validate(d);
+    if (rc != DSA3D_OK) return rc;
+    if ((rc = check_ptrs({q, wt, dy, dq_accum, dwt})) != DSA3D_OK) return rc;
+    if (dbias != nullptr && !aligned16(dbias)) return DSA3D_ERR_MISALIGNED;
+    const size_t need = dsa3d::dwconv_bwd_workspace_bytes(*d);
+    if (workspace == nullptr || workspace_bytes < need) return DSA3D_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return DSA3D_ERR_MISALIGNED;
+    return hip_status(dsa3d::launch_dwconv_backward(*d, q, wt, dy, dq_accum, dwt, dbias, workspace,
+                                                    static_cast<hipStream_t>(stream)));
 }
 
 int dsa3d_debug_geometry(const dsa3d_desc* d, const void* offsets, int32_t* base, float* frac, void* stream) {

@@ -1,0 +1,283 @@
+// dsa3d_conv.hip -- depthwise 3x3x3 convolution of the offset network (gfx950).
+//
+// The offset network convolves the query tensor [B,T,H,W,C] channel by channel
+// with a 3x3x3 kernel (stride 1, zero padding 1, bias) before its pointwise
+// layer [MegaSlide-DiT, §5.3 Implementation considerations: nn.Conv3d with
+// groups equal to the hidden size; the kernel size is not given there, 3x3x3
+// is the reading taken]. Tap (i, j, k) of channel c multiplies the input at
+// offset (i-1, j-1, k-1): a cross-correlation, as torch's Conv3d.
+//
+// The work is bound by memory traffic and plain ALU work, not by a contraction,
+// so it runs on the vector units. A lane owns two adjacent channels of one row
+// (b, t, h) of the grid and walks a run of tokens along w; the 9 input rows at
+// (t+-1, h+-1) are read coalesced across the wave (64 lanes x 2 channels) and a
+// 3-column window of them, widened to float32 once, slides along w in
+// registers, so each input element is loaded once per (row, run) and reused
+// for the three outputs it touches along w. The rows a block's neighbours need
+// are consecutive blocks (rows are the fastest grid axis), so they meet in L2.
+//
+//   forward:   y  = bias + conv(q, w)                       (one rounding)
+//   dq:        dq += conv(dy, w mirrored through its centre)  (one rounding)
+//   dw, db:    per tap, sums over tokens of dy * shifted q, split over groups
+//              of rows and then summed over the groups in a fixed order.
+#include "dsa3d_device.h"
+#include "dsa3d_internal.h"
+
+namespace dsa3d {
+
+namespace {
+
+constexpr int kRun = 12;  // tokens along w per lane
+
+// Two adjacent channels as float32.
+template <typename T> struct Pair;
+template <> struct Pair<bf16_t> {
+    static __device__ __forceinline__ float2 load(const bf16_t* p) {
+        const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+        return make_float2(bf16_lo(u), bf16_hi(u));
+    }
+    static __device__ __forceinline__ void store(bf16_t* p, float2 v) {
+        *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(v.x, v.y);
+    }
+};
+template <> struct Pair<float> {
+    static __device__ __forceinline__ float2 load(const float* p) { return *reinterpret_cast<const float2*>(p); }
+    static __device__ __forceinline__ void store(float* p, float2 v) { *reinterpret_cast<float2*>(p) = v; }
+};
+
+struct ConvGrid {
+    int32_t B, T, H, W;
+    int64_t C;
+};
+
+// The 9 input rows (t+dt, h+dh), dt, dh in {-1, 0, 1}, of the lane's channel
+// pair, or null where the row is outside the grid (zero padding).
+template <typename T>
+__device__ __forceinline__ void neighbour_rows(const T* x, const ConvGrid& g, int64_t row, int64_t c,
+                                               const T* rows[9]) {
+    const int32_t h = (int32_t)(row % g.H);
+    const int64_t bt = row / g.H;
+    const int32_t t = (int32_t)(bt % g.T);
+#pragma unroll
+    for (int dt = -1; dt <= 1; ++dt)
+#pragma unroll
+        for (int dh = -1; dh <= 1; ++dh) {
+            const bool in = (unsigned)(t + dt) < (unsigned)g.T && (unsigned)(h + dh) < (unsigned)g.H;
+            rows[(dt + 1) * 3 + (dh + 1)] = in ? x + ((row + (int64_t)dt * g.H + dh) * g.W) * g.C + c : nullptr;
+        }
+}
+
+// Column w of the 9 rows (zero outside the grid).
+template <typename T>
+__device__ __forceinline__ void load_column(const T* const rows[9], const ConvGrid& g, int32_t w, float2 col[9]) {
+    const bool win = (unsigned)w < (unsigned)g.W;
+#pragma unroll
+    for (int r = 0; r < 9; ++r)
+        col[r] = (win && rows[r]) ? Pair<T>::load(rows[r] + (int64_t)w * g.C) : make_float2(0.f, 0.f);
+}
+
+}  // namespace
+
+// y[row, w, c] = bias[c] + sum_tap wt[c, tap] * x[row + (dt, dh), w + dk, c] (MIRROR: tap 26 - tap),
+// or (ACCUM) out[...] += the sum without bias. Grid: x = rows (B*T*H), y = channel groups of 512,
+// z = runs of kRun tokens along w.
+template <typename T, bool MIRROR, bool ACCUM>
+__global__ void __launch_bounds__(256) dsa3d_dwconv_kernel(const T* x, const T* wt, const T* bias, T* out, ConvGrid g) {
+    const int64_t row = blockIdx.x;
+    const int64_t c = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 2;
+    if (c >= g.C) return;
+    const int32_t w0 = (int32_t)blockIdx.z * kRun;
+    float wa[27], wb[27];
+#pragma unroll
+    for (int tap = 0; tap < 27; ++tap) {
+        const int src = MIRROR ? 26 - tap : tap;
+        wa[tap] = load_scalar<T>(wt + c * 27 + src);
+        wb[tap] = load_scalar<T>(wt + (c + 1) * 27 + src);
+    }
+    float2 bb = make_float2(0.f, 0.f);
+    if (!ACCUM && bias) bb = Pair<T>::load(bias + c);
+    const T* rows[9];
+    neighbour_rows(x, g, row, c, rows);
+    float2 cm[9], c0[9], cp[9];  // columns w-1, w, w+1
+    load_column(rows, g, w0 - 1, cm);
+    load_column(rows, g, w0, c0);
+    T* orow = out + row * g.W * g.C + c;
+#pragma unroll
+    for (int u = 0; u < kRun; ++u) {
+        const int32_t w = w0 + u;
+        if (w >= g.W) break;
+        load_column(rows, g, w + 1, cp);
+        float2 acc = bb;
+#pragma unroll
+        for (int r = 0; r < 9; ++r) {
+            acc.x = fmaf(wa[r * 3 + 0], cm[r].x, acc.x);
+            acc.y = fmaf(wb[r * 3 + 0], cm[r].y, acc.y);
+            acc.x = fmaf(wa[r * 3 + 1], c0[r].x, acc.x);
+            acc.y = fmaf(wb[r * 3 + 1], c0[r].y, acc.y);
+            acc.x = fmaf(wa[r * 3 + 2], cp[r].x, acc.x);
+            acc.y = fmaf(wb[r * 3 + 2], cp[r].y, acc.y);
+        }
+        T* o = orow + (int64_t)w * g.C;
+        if (ACCUM) {
+            const float2 old = Pair<T>::load(o);
+            acc.x += old.x;
+            acc.y += old.y;
+        }
+        Pair<T>::store(o, acc);
+#pragma unroll
+        for (int r = 0; r < 9; ++r) {
+            cm[r] = c0[r];
+            c0[r] = cp[r];
+        }
+    }
+}
+
+// Per group of `rows_per_group` rows: part[group][c][tap] = sum over the
+// group's tokens of dy[tok, c] * x[tok + tap offset, c], partb[group][c] =
+// sum of dy[tok, c]; rows in increasing order, w in increasing order.
+// Grid: x = groups, y = channel groups of 512.
+template <typename T>
+__global__ void __launch_bounds__(256) dsa3d_dwconv_wgrad_kernel(const T* x, const T* dy, float* part, float* partb,
+                                                                 ConvGrid g, int64_t rows_per_group) {
+    const int64_t c = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 2;
+    if (c >= g.C) return;
+    const int64_t nrows = (int64_t)g.B * g.T * g.H;
+    const int64_t r0 = (int64_t)blockIdx.x * rows_per_group;
+    const int64_t r1 = min(nrows, r0 + rows_per_group);
+    float aa[27], ab[27];
+#pragma unroll
+    for (int tap = 0; tap < 27; ++tap) aa[tap] = ab[tap] = 0.f;
+    float2 sb = make_float2(0.f, 0.f);
+    for (int64_t row = r0; row < r1; ++row) {
+        const T* rows[9];
+        neighbour_rows(x, g, row, c, rows);
+        const T* grow = dy + row * g.W * g.C + c;
+        float2 cm[9], c0[9], cp[9];
+        load_column(rows, g, -1, cm);
+        load_column(rows, g, 0, c0);
+        for (int32_t w = 0; w < g.W; ++w) {
+            load_column(rows, g, w + 1, cp);
+            const float2 d = Pair<T>::load(grow + (int64_t)w * g.C);
+            sb.x += d.x;
+            sb.y += d.y;
+#pragma unroll
+            for (int r = 0; r < 9; ++r) {
+                aa[r * 3 + 0] = fmaf(d.x, cm[r].x, aa[r * 3 + 0]);
+                ab[r * 3 + 0] = fmaf(d.y, cm[r].y, ab[r * 3 + 0]);
+                aa[r * 3 + 1] = fmaf(d.x, c0[r].x, aa[r * 3 + 1]);
+                ab[r * 3 + 1] = fmaf(d.y, c0[r].y, ab[r * 3 + 1]);
+                aa[r * 3 + 2] = fmaf(d.x, cp[r].x, aa[r * 3 + 2]);
+                ab[r * 3 + 2] = fmaf(d.y, cp[r].y, ab[r * 3 + 2]);
+            }
+#pragma unroll
+            for (int r = 0; r < 9; ++r) {
+                cm[r] = c0[r];
+                c0[r] = cp[r];
+            }
+        }
+    }
+    float* pa = part + ((int64_t)blockIdx.x * g.C + c) * 27;
+#pragma unroll
+    for (int tap = 0; tap < 27; ++tap) {
+        pa[tap] = aa[tap];
+        pa[27 + tap] = ab[tap];
+    }
+    partb[(int64_t)blockIdx.x * g.C + c] = sb.x;
+    partb[(int64_t)blockIdx.x * g.C + c + 1] = sb.y;
+}
+
+// out[i] = sum_{z < nsplit} part[z*n + i], z in increasing order.
+__global__ void __launch_bounds__(256) dsa3d_conv_split_sum_kernel(const float* part, float* out, int64_t n,
+                                                                   int64_t nsplit) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        float s = 0.0f;
+        for (int64_t z = 0; z < nsplit; ++z) s += part[z * n + i];
+        out[i] = s;
+    }
+}
+
+namespace {
+
+ConvGrid conv_grid(const dsa3d_desc& d) {
+    return ConvGrid{(int32_t)d.B, (int32_t)d.T, (int32_t)d.H, (int32_t)d.W, (int64_t)d.heads * d.head_dim};
+}
+
+// Rows per group of the weight gradient: enough groups for about 8192 waves.
+int64_t wgrad_rows_per_group(const dsa3d_desc& d) {
+    const int64_t rows = d.B * d.T * d.H;
+    const int64_t C = (int64_t)d.heads * d.head_dim;
+    const int64_t waves_per_group = (C / 2 + 63) / 64;
+    const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(rows, 8192 / std::max<int64_t>(1, waves_per_group)));
+    return (rows + groups - 1) / groups;
+}
+
+template <typename T, bool MIRROR, bool ACCUM>
+hipError_t conv_launch(const dsa3d_desc& d, const void* x, const void* w, const void* bias, void* out, int kernel_id,
+                       hipStream_t s) {
+    const ConvGrid g = conv_grid(d);
+    const int64_t rows = (int64_t)g.B * g.T * g.H;
+    if (rows == 0 || g.W == 0) return hipSuccess;
+    dim3 grid((unsigned)rows, (unsigned)((g.C / 2 + 255) / 256), (unsigned)((g.W + kRun - 1) / kRun));
+    LaunchScope ls(kernel_id, s);
+    hipLaunchKernelGGL((dsa3d_dwconv_kernel<T, MIRROR, ACCUM>), grid, dim3(256), 0, s, reinterpret_cast<const T*>(x),
+                       reinterpret_cast<const T*>(w), reinterpret_cast<const T*>(bias), reinterpret_cast<T*>(out), g);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t dwconv_bwd_workspace_bytes(const dsa3d_desc& d) {
+    const int64_t rows = d.B * d.T * d.H;
+    const int64_t C = (int64_t)d.heads * d.head_dim;
+    const int64_t rpg = wgrad_rows_per_group(d);
+    const int64_t groups = (rows + rpg - 1) / rpg;
+    return (size_t)groups * C * 27 * 4 + 256 + (size_t)groups * C * 4 + 256;
+}
+
+hipError_t launch_dwconv_forward(const dsa3d_desc& d, const void* q, const void* w, const void* bias, void* y,
+                                 hipStream_t s) {
+    if (d.dtype == DSA3D_F32) return conv_launch<float, false, false>(d, q, w, bias, y, DSA3D_K_DWCONV, s);
+    return conv_launch<bf16_t, false, false>(d, q, w, bias, y, DSA3D_K_DWCONV, s);
+}
+
+hipError_t launch_dwconv_backward(const dsa3d_desc& d, const void* q, const void* w, const void* dy, void* dq,
+                                  float* dw, float* db, void* ws, hipStream_t s) {
+    const ConvGrid g = conv_grid(d);
+    const int64_t rows = (int64_t)g.B * g.T * g.H;
+    if (rows == 0 || g.W == 0) return hipSuccess;
+    const bool f32 = d.dtype == DSA3D_F32;
+    hipError_t e = f32 ? conv_launch<float, true, true>(d, dy, w, nullptr, dq, DSA3D_K_DWCONV, s)
+                       : conv_launch<bf16_t, true, true>(d, dy, w, nullptr, dq, DSA3D_K_DWCONV, s);
+    if (e != hipSuccess) return e;
+    const int64_t rpg = wgrad_rows_per_group(d);
+    const int64_t groups = (rows + rpg - 1) / rpg;
+    float* part = reinterpret_cast<float*>(ws);
+    float* partb = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
+                                            (((size_t)groups * g.C * 27 * 4 + 255) & ~size_t(255)));
+    {
+        LaunchScope ls(DSA3D_K_DWCONV_WGRAD, s);
+        dim3 grid((unsigned)groups, (unsigned)((g.C / 2 + 255) / 256));
+        if (f32)
+            hipLaunchKernelGGL((dsa3d_dwconv_wgrad_kernel<float>), grid, dim3(256), 0, s,
+                               reinterpret_cast<const float*>(q), reinterpret_cast<const float*>(dy), part, partb, g,
+                               rpg);
+        else
+            hipLaunchKernelGGL((dsa3d_dwconv_wgrad_kernel<bf16_t>), grid, dim3(256), 0, s,
+                               reinterpret_cast<const bf16_t*>(q), reinterpret_cast<const bf16_t*>(dy), part, partb, g,
+                               rpg);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    LaunchScope ls(DSA3D_K_SPLIT_SUM, s);
+    const int64_t nw = g.C * 27;
+    hipLaunchKernelGGL(dsa3d_conv_split_sum_kernel, dim3((unsigned)std::min<int64_t>((nw + 255) / 256, 65536)),
+                       dim3(256), 0, s, part, dw, nw, groups);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (db) {
+        hipLaunchKernelGGL(dsa3d_conv_split_sum_kernel, dim3((unsigned)std::min<int64_t>((g.C + 255) / 256, 65536)),
+                           dim3(256), 0, s, partb, db, g.C, groups);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace dsa3d

@@ -90,5 +90,10 @@ hipError_t launch_proj_forward(const dsa3d_desc& d, const void* q, const void* w
                                hipStream_t s);
 hipError_t launch_proj_backward(const dsa3d_desc& d, const void* q, const void* w, const void* doff, void* dq,
                                 float* dw, float* db, void* ws, hipStream_t s);
+size_t dwconv_bwd_workspace_bytes(const dsa3d_desc& d);
+hipError_t launch_dwconv_forward(const dsa3d_desc& d, const void* q, const void* w, const void* bias, void* y,
+                                 hipStream_t s);
+hipError_t launch_dwconv_backward(const dsa3d_desc& d, const void* q, const void* w, const void* dy, void* dq,
+                                  float* dw, float* db, void* ws, hipStream_t s);
 
 }  // namespace dsa3d

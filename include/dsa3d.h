@@ -84,7 +84,8 @@ typedef struct dsa3d_desc {
 typedef enum {
     DSA3D_WS_FORWARD = 0,
     DSA3D_WS_BACKWARD = 1,
-    DSA3D_WS_PROJ_BACKWARD = 2
+    DSA3D_WS_PROJ_BACKWARD = 2,
+    DSA3D_WS_DWCONV_BACKWARD = 3
 } dsa3d_ws_kind;
 
 /* Library version (major*10000 + minor*100 + patch). */
@@ -152,6 +153,30 @@ int dsa3d_offset_proj_backward(const dsa3d_desc* desc, const void* q, const void
                                const void* doffsets, void* dq_accum, float* dw, float* dbias,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Depthwise 3-D convolution of the offset network, before its pointwise layer
+ * [MegaSlide-DiT, §5.3 Implementation considerations: nn.Conv3d with groups
+ * equal to the hidden size; Dutch and French summaries, Implementation: a
+ * lightweight depthwise 3-D convolution]. The pages give no kernel size; this
+ * is 3x3x3, stride 1, zero padding 1, per channel c of q [B,T,H,W,C]
+ * (C = heads*head_dim), as a cross-correlation:
+ *   y[b,t,h,w,c] = bias[c] + sum_{i,j,k in 0..2} wt[c,i,j,k] * q[b,t+i-1,h+j-1,w+k-1,c]
+ * with q read as zero outside the grid. wt is [C,3,3,3] (torch's [C,1,3,3,3])
+ * in the run dtype, bias [C] in the run dtype or NULL; y [B,T,H,W,C] in the run
+ * dtype, accumulated in float32 and rounded once. All device pointers, 16-byte
+ * aligned; asynchronous on `stream`. */
+int dsa3d_dwconv_forward(const dsa3d_desc* desc, const void* q, const void* wt, const void* bias,
+                         void* y, void* stream);
+
+/* Backward of dsa3d_dwconv_forward for dy = dL/dy [B,T,H,W,C]:
+ *   dq_accum[b,t,h,w,c] += sum_{i,j,k} wt[c,i,j,k] * dy[b,t-i+1,h-j+1,w-k+1,c]  (one rounding)
+ *   dwt[c,i,j,k] = sum over all tokens of dy[tok,c] * q[tok + (i-1,j-1,k-1), c]  (float32, overwritten)
+ *   dbias[c]     = sum over all tokens of dy[tok,c]                            (float32, overwritten; may be NULL)
+ * dwt and dbias are summed in a fixed order (bitwise reproducible); the
+ * workspace (DSA3D_WS_DWCONV_BACKWARD) holds their split partials. */
+int dsa3d_dwconv_backward(const dsa3d_desc* desc, const void* q, const void* wt, const void* dy,
+                          void* dq_accum, float* dwt, float* dbias,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Test hook: the integer base corner floor(pos) and the float32 fraction f of
  * every sample, both [B,T,H,W,heads,P,3] (int32, float32). A sample whose
  * position is NaN, infinite or |pos| >= 2^30 reports base INT32_MIN and f 0. */
@@ -175,7 +200,9 @@ typedef enum {
     DSA3D_K_BWD_SCAN = 11,      /* backward: bucket starts (3 small kernels, one entry) */
     DSA3D_K_BWD_COUNT = 12,     /* backward: samples per base cell */
     DSA3D_K_BWD_SORT = 13,      /* backward, deterministic: bucket sort (2 kernels, one entry) */
-    DSA3D_K_TRANSPOSE = 14      /* projection backward: W transposed for the dq product */
+    DSA3D_K_TRANSPOSE = 14,     /* projection backward: W transposed for the dq product */
+    DSA3D_K_DWCONV = 15,        /* depthwise convolution: forward, and dq of its backward */
+    DSA3D_K_DWCONV_WGRAD = 16   /* depthwise convolution backward: split weight and bias sums */
 } dsa3d_kernel;
 
 typedef struct dsa3d_launch_log {

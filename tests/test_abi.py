@@ -23,7 +23,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     declared = _declared_functions()
-    assert len(declared) == 11, declared
+    assert len(declared) == 13, declared
     out = subprocess.run(["nm", "-D", "--defined-only", dsa.library_path()], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT (dsa3d_\w+)", out))
@@ -125,6 +125,11 @@ def test_workspace_sizes():
     assert rec <= (16 << 30) < rec + ph
     assert dsa.dsa3d_workspace_size(dsa.make_desc(1, 1, 1, 1, 1, 8, (1, 1, 1), dtype=torch.bfloat16),
                                     dsa.WS_PROJ_BACKWARD) > 0
+    # depthwise convolution backward: float32 partials of 27 taps plus the bias per channel and row group
+    conv = dsa.make_desc(1, 256, 68, 120, 24, 128, (3, 3, 3), dtype=torch.bfloat16)
+    cw = dsa.dsa3d_workspace_size(conv, dsa.WS_DWCONV_BACKWARD)
+    assert 28 * 3072 * 4 <= cw <= 28 * 3072 * 4 * (256 * 68) + 1024
+    assert dsa.dsa3d_workspace_size(conv, 7) == 0
     bad = _desc(window=(2, 2, 2))
     assert dsa.dsa3d_workspace_size(bad, dsa.WS_BACKWARD) == 0
     # one head with 2^30 tokens x 27 samples cannot be numbered in 32 bits

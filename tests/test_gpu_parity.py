@@ -227,6 +227,43 @@ def test_projection_forward_and_backward(dtype, shape):
 
 
 # ---------------------------------------------------------------------------
+# depthwise convolution of the offset network
+# ---------------------------------------------------------------------------
+
+# (B, T, H, W, heads, head_dim): 24 channels (part of one wave), W under one
+# run; 512 channels with ragged runs along w (30 = 12 + 12 + 6); 640 channels
+# (a second, partial block of channels), single-token rows and frames.
+@pytest.mark.parametrize("dtype,shape", [("f32", (2, 3, 5, 7, 3, 8)), ("bf16", (2, 3, 5, 7, 3, 8)),
+                                         ("bf16", (1, 4, 6, 30, 8, 64)), ("f32", (1, 1, 1, 5, 5, 128)),
+                                         ("bf16", (1, 3, 2, 1, 5, 128))])
+def test_dwconv_forward_and_backward(dtype, shape):
+    B, T, H, W, heads, hd = shape
+    C = heads * hd
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    say(f"[dwconv] {dtype} B={B} T={T} H={H} W={W} C={C}")
+    gen = torch.Generator().manual_seed(31)
+    q = torch.randn((B, T, H, W, heads, hd), generator=gen).to(tdt)
+    wt = (torch.randn((C, 3, 3, 3), generator=gen) * 0.2).to(tdt)
+    bias = (torch.randn(C, generator=gen) * 0.1).to(tdt)
+    dy = torch.randn(q.shape, generator=gen).to(tdt)
+    dq0 = torch.randn(q.shape, generator=gen).to(tdt)
+    qd, wd, bd, gd = q.to(DEV), wt.to(DEV), bias.to(DEV), dy.to(DEV)
+    y = dsa.dwconv(qd, wd, bd)
+    dq = dq0.to(DEV).clone()
+    dwt, db = dsa.dwconv_backward(qd, wd, gd, dq)
+    torch.cuda.synchronize()
+    q5, g5 = to_np(q).reshape(B, T, H, W, C), to_np(dy).reshape(B, T, H, W, C)
+    ref = oracle.dwconv3d(q5, to_np(wt), to_np(bias))
+    _check("dwconv y", to_np(y).reshape(-1, C), ref.reshape(-1, C), dtype)
+    dq_ref, dw_ref, db_ref = oracle.dwconv3d_backward(q5, to_np(wt), g5)
+    _check("dwconv dq_accum", to_np(dq).reshape(-1, C), (to_np(dq0).reshape(B, T, H, W, C) + dq_ref).reshape(-1, C),
+           dtype)
+    # dwt and dbias are float32 sums of exactly widened inputs: tight for both dtypes
+    assert rel_l2(to_np(dwt), dw_ref) <= 1e-5, rel_l2(to_np(dwt), dw_ref)
+    assert rel_l2(to_np(db), db_ref) <= 1e-5
+
+
+# ---------------------------------------------------------------------------
 # the named workloads: small one whole, full-size ones sampled
 # ---------------------------------------------------------------------------
 
