@@ -83,8 +83,11 @@ def cpu_baseline(wl, budget_s: float = 20.0):
     cores = max(1, min(cores, 16, wl.heads))
     crop = wl.with_grid(B=1, T=min(wl.T, 16), H=min(wl.H, 24), W=min(wl.W, 24), heads=cores, name=wl.name + "-crop")
     x = synth.make_inputs(crop, "cpu", seed=0, with_grad=True)
-    if crop.offsets == "proj":
+    if crop.offsets in ("proj", "conv"):
         q2 = x["q"].double().numpy().reshape(crop.tokens, crop.C)
+        if crop.offsets == "conv":
+            q5 = q2.reshape(crop.B, crop.T, crop.H, crop.W, crop.C)
+            q2 = oracle.dwconv3d(q5, x["conv_w"].double().numpy(), None).reshape(crop.tokens, crop.C)
         off = oracle.offset_proj(q2, x["proj_w"].double().numpy(), None).astype(np.float32)
         off = off.reshape(crop.B, crop.T, crop.H, crop.W, crop.heads, crop.P, 3)
     else:
@@ -337,7 +340,7 @@ def main():
 
     # the projection GEMMs (workloads whose offsets come from the Linear): MFMA-bound
     roofline_proj = None
-    if wl.offsets == "proj":
+    if wl.offsets in ("proj", "conv"):
         gemm_flops = 2.0 * wl.tokens * wl.C * wl.F  # one product of the projection
         roofline_proj = {}
         for k in ("proj_forward", "proj_bwd_dq", "proj_bwd_dw"):
@@ -348,18 +351,34 @@ def main():
                                     "launch_ms": round(per_kernel[k]["mean_ms"], 3),
                                     "flops_per_launch": gemm_flops}
 
+    # the depthwise convolution of the "conv" offset network: HBM-bound, algorithmic bytes per token
+    # forward 2Cs (q read, y written), dq 3Cs (dy read, dq read and written), weight sums 2Cs (q, dy read)
+    roofline_conv = None
+    if wl.offsets == "conv":
+        s_el = 4 if wl.dtype == "f32" else 2
+        conv_bytes = {"dwconv": 2, "dwconv_dq": 3, "dwconv_wgrad": 2}
+        roofline_conv = {}
+        for k, m in conv_bytes.items():
+            if k in per_kernel:
+                gbs = m * wl.C * s_el * wl.tokens / (per_kernel[k]["mean_ms"] / 1e3) / 1e9
+                roofline_conv[k] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                    "frac": round(gbs / HBM_PEAK_GBS, 4), "launch_ms": round(per_kernel[k]["mean_ms"], 3),
+                                    "bytes_per_launch": m * wl.C * s_el * wl.tokens}
+
     result = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == "bf16" else "f32", "data": "synthetic (seeded N(0,1) q/k/v/dO; offsets "
-        + (f"N(0,{wl.offset_sigma})" if wl.offsets == "direct" else "from a Linear with N(0,0.02) weights") + ")",
+        + (f"N(0,{wl.offset_sigma})" if wl.offsets == "direct" else "from a Linear with N(0,0.02) weights"
+           + (" of a depthwise 3x3x3 conv with N(0,0.2) weights" if wl.offsets == "conv" else "")) + ")",
         "config": {"workload": wl.name, "grid": [wl.B, wl.T, wl.H, wl.W], "heads": wl.heads, "head_dim": wl.head_dim,
                    "window": list(wl.window), "P": wl.P, "dilation": list(wl.dilation), "offsets": wl.offsets,
-                   "chain": ("proj+" if wl.offsets == "proj" else "") + ("fwd+bwd" if wl.backward else "fwd"),
+                   "chain": {"proj": "proj+", "conv": "dwconv+proj+"}.get(wl.offsets, "") + ("fwd+bwd" if wl.backward else "fwd"),
                    "deterministic": wl.deterministic},
         "roofline": roofline, "roofline_alu": roofline_alu,
         **({"roofline_proj": roofline_proj} if roofline_proj else {}),
+        **({"roofline_conv": roofline_conv} if roofline_conv else {}),
         "kernels": {k: {"launches": v["launches"], "mean_ms": round(v["mean_ms"], 3)} for k, v in per_kernel.items()},
     }
     if args.cpu_baseline == "on":

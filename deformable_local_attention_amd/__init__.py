@@ -38,7 +38,7 @@ EXPORTS = ("dsa3d_version", "dsa3d_status_string", "dsa3d_validate", "dsa3d_work
 # kernel ids of the launch log (dsa3d_kernel)
 KERNELS = {1: "proj_forward", 2: "forward", 3: "bwd_query", 4: "bwd_key", 5: "fill", 6: "proj_bwd_dq",
            7: "proj_bwd_dw", 8: "split_sum", 9: "colsum", 10: "geometry", 11: "bwd_scan", 12: "bwd_count",
-           13: "bwd_sort", 14: "transpose", 15: "dwconv", 16: "dwconv_wgrad"}
+           13: "bwd_sort", 14: "transpose", 15: "dwconv", 16: "dwconv_wgrad", 17: "dwconv_dq"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None

@@ -8,10 +8,10 @@
 // offset (i-1, j-1, k-1): a cross-correlation, as torch's Conv3d.
 //
 // The work is bound by memory traffic and plain ALU work, not by a contraction,
-// so it runs on the vector units. A lane owns two adjacent channels of one row
-// (b, t, h) of the grid and walks a run of tokens along w; the 9 input rows at
-// (t+-1, h+-1) are read coalesced across the wave (64 lanes x 2 channels) and a
-// 3-column window of them, widened to float32 once, slides along w in
+// so it runs on the vector units. A lane owns one channel of one row (b, t, h)
+// of the grid and walks a run of tokens along w; the 9 input rows at
+// (t+-1, h+-1) are read coalesced across the wave (64 consecutive channels)
+// and a 3-column window of them, widened to float32 once, slides along w in
 // registers, so each input element is loaded once per (row, run) and reused
 // for the three outputs it touches along w. The rows a block's neighbours need
 // are consecutive blocks (rows are the fastest grid axis), so they meet in L2.
@@ -27,103 +27,73 @@ namespace dsa3d {
 
 namespace {
 
-constexpr int kRun = 12;  // tokens along w per lane
-
-// Two adjacent channels as float32.
-template <typename T> struct Pair;
-template <> struct Pair<bf16_t> {
-    static __device__ __forceinline__ float2 load(const bf16_t* p) {
-        const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
-        return make_float2(bf16_lo(u), bf16_hi(u));
-    }
-    static __device__ __forceinline__ void store(bf16_t* p, float2 v) {
-        *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(v.x, v.y);
-    }
-};
-template <> struct Pair<float> {
-    static __device__ __forceinline__ float2 load(const float* p) { return *reinterpret_cast<const float2*>(p); }
-    static __device__ __forceinline__ void store(float* p, float2 v) { *reinterpret_cast<float2*>(p) = v; }
-};
-
 struct ConvGrid {
     int32_t B, T, H, W;
     int64_t C;
 };
 
 // The 9 input rows (t+dt, h+dh), dt, dh in {-1, 0, 1}, of the lane's channel
-// pair, or null where the row is outside the grid (zero padding).
+// pair. A row outside the grid points at the lane's own row and is flagged in
+// `outside` (bit r), so its loads stay in bounds and their values are replaced
+// by zero (padding) before use.
 template <typename T>
-__device__ __forceinline__ void neighbour_rows(const T* x, const ConvGrid& g, int64_t row, int64_t c,
-                                               const T* rows[9]) {
+__device__ __forceinline__ uint32_t neighbour_rows(const T* x, const ConvGrid& g, int64_t row, int64_t c,
+                                                   const T* rows[9]) {
     const int32_t h = (int32_t)(row % g.H);
-    const int64_t bt = row / g.H;
-    const int32_t t = (int32_t)(bt % g.T);
+    const int32_t t = (int32_t)((row / g.H) % g.T);
+    uint32_t outside = 0;
 #pragma unroll
     for (int dt = -1; dt <= 1; ++dt)
 #pragma unroll
         for (int dh = -1; dh <= 1; ++dh) {
+            const int r = (dt + 1) * 3 + (dh + 1);
             const bool in = (unsigned)(t + dt) < (unsigned)g.T && (unsigned)(h + dh) < (unsigned)g.H;
-            rows[(dt + 1) * 3 + (dh + 1)] = in ? x + ((row + (int64_t)dt * g.H + dh) * g.W) * g.C + c : nullptr;
+            rows[r] = x + ((in ? row + (int64_t)dt * g.H + dh : row) * g.W) * g.C + c;
+            if (!in) outside |= 1u << r;
         }
+    return outside;
 }
 
-// Column w of the 9 rows (zero outside the grid).
-template <typename T>
-__device__ __forceinline__ void load_column(const T* const rows[9], const ConvGrid& g, int32_t w, float2 col[9]) {
+// Column w (clamped into the grid; zero for a column outside it) of the 9 rows.
+template <typename T, bool EDGE>
+__device__ __forceinline__ void load_column(const T* const rows[9], uint32_t outside, const ConvGrid& g, int32_t w,
+                                            float col[9]) {
     const bool win = (unsigned)w < (unsigned)g.W;
+    const int64_t off = (int64_t)min(max(w, 0), g.W - 1) * g.C;
 #pragma unroll
-    for (int r = 0; r < 9; ++r)
-        col[r] = (win && rows[r]) ? Pair<T>::load(rows[r] + (int64_t)w * g.C) : make_float2(0.f, 0.f);
+    for (int r = 0; r < 9; ++r) {
+        const float v = load_scalar<T>(rows[r] + off);
+        const bool keep = win && (!EDGE || !((outside >> r) & 1u));
+        col[r] = keep ? v : 0.0f;
+    }
 }
 
-}  // namespace
+// The lane's weights of channel c (MIRROR: tap 26 - tap), float32.
+template <typename T, bool MIRROR>
+__device__ __forceinline__ void load_weights(const T* wt, int64_t c, float wa[27]) {
+#pragma unroll
+    for (int tap = 0; tap < 27; ++tap) wa[tap] = load_scalar<T>(wt + c * 27 + (MIRROR ? 26 - tap : tap));
+}
 
-// y[row, w, c] = bias[c] + sum_tap wt[c, tap] * x[row + (dt, dh), w + dk, c] (MIRROR: tap 26 - tap),
-// or (ACCUM) out[...] += the sum without bias. Grid: x = rows (B*T*H), y = channel groups of 512,
-// z = runs of kRun tokens along w.
-template <typename T, bool MIRROR, bool ACCUM>
-__global__ void __launch_bounds__(256) dsa3d_dwconv_kernel(const T* x, const T* wt, const T* bias, T* out, ConvGrid g) {
-    const int64_t row = blockIdx.x;
-    const int64_t c = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 2;
-    if (c >= g.C) return;
-    const int32_t w0 = (int32_t)blockIdx.z * kRun;
-    float wa[27], wb[27];
-#pragma unroll
-    for (int tap = 0; tap < 27; ++tap) {
-        const int src = MIRROR ? 26 - tap : tap;
-        wa[tap] = load_scalar<T>(wt + c * 27 + src);
-        wb[tap] = load_scalar<T>(wt + (c + 1) * 27 + src);
-    }
-    float2 bb = make_float2(0.f, 0.f);
-    if (!ACCUM && bias) bb = Pair<T>::load(bias + c);
-    const T* rows[9];
-    neighbour_rows(x, g, row, c, rows);
-    float2 cm[9], c0[9], cp[9];  // columns w-1, w, w+1
-    load_column(rows, g, w0 - 1, cm);
-    load_column(rows, g, w0, c0);
-    T* orow = out + row * g.W * g.C + c;
-#pragma unroll
-    for (int u = 0; u < kRun; ++u) {
-        const int32_t w = w0 + u;
-        if (w >= g.W) break;
-        load_column(rows, g, w + 1, cp);
-        float2 acc = bb;
+// One row run [w0, w1) of outputs; EDGE: some of the 9 rows are outside the grid.
+template <typename T, bool ACCUM, bool EDGE>
+__device__ __forceinline__ void conv_run(const T* const rows[9], uint32_t outside, const ConvGrid& g, int32_t w0,
+                                         int32_t w1, const float wa[27], float bb, T* orow) {
+    float cm[9], c0[9], cp[9];  // columns w-1, w, w+1
+    load_column<T, EDGE>(rows, outside, g, w0 - 1, cm);
+    load_column<T, EDGE>(rows, outside, g, w0, c0);
+    for (int32_t w = w0; w < w1; ++w) {
+        load_column<T, EDGE>(rows, outside, g, w + 1, cp);
+        float acc = bb;
 #pragma unroll
         for (int r = 0; r < 9; ++r) {
-            acc.x = fmaf(wa[r * 3 + 0], cm[r].x, acc.x);
-            acc.y = fmaf(wb[r * 3 + 0], cm[r].y, acc.y);
-            acc.x = fmaf(wa[r * 3 + 1], c0[r].x, acc.x);
-            acc.y = fmaf(wb[r * 3 + 1], c0[r].y, acc.y);
-            acc.x = fmaf(wa[r * 3 + 2], cp[r].x, acc.x);
-            acc.y = fmaf(wb[r * 3 + 2], cp[r].y, acc.y);
+            acc = fmaf(wa[r * 3 + 0], cm[r], acc);
+            acc = fmaf(wa[r * 3 + 1], c0[r], acc);
+            acc = fmaf(wa[r * 3 + 2], cp[r], acc);
         }
         T* o = orow + (int64_t)w * g.C;
-        if (ACCUM) {
-            const float2 old = Pair<T>::load(o);
-            acc.x += old.x;
-            acc.y += old.y;
-        }
-        Pair<T>::store(o, acc);
+        if (ACCUM) acc += load_scalar<T>(o);
+        store_scalar<T>(o, acc);
 #pragma unroll
         for (int r = 0; r < 9; ++r) {
             cm[r] = c0[r];
@@ -132,58 +102,85 @@ __global__ void __launch_bounds__(256) dsa3d_dwconv_kernel(const T* x, const T* 
     }
 }
 
+}  // namespace
+
+// y[row, w, c] = bias[c] + sum_tap wt[c, tap] * x[row + (dt, dh), w + dk, c] (MIRROR: tap 26 - tap),
+// or (ACCUM) out[...] += the sum without bias. Grid: x = rows (B*T*H), y = channel groups of 256,
+// z = runs of `run` tokens along w.
+template <typename T, bool MIRROR, bool ACCUM>
+__global__ void __launch_bounds__(256) dsa3d_dwconv_kernel(const T* x, const T* wt, const T* bias, T* out, ConvGrid g,
+                                                           int32_t run) {
+    const int64_t row = blockIdx.x;
+    const int64_t c = (int64_t)blockIdx.y * 256 + threadIdx.x;
+    if (c >= g.C) return;
+    const int32_t w0 = (int32_t)blockIdx.z * run;
+    const int32_t w1 = min(g.W, w0 + run);
+    float wa[27];
+    load_weights<T, MIRROR>(wt, c, wa);
+    const float bb = (!ACCUM && bias) ? load_scalar<T>(bias + c) : 0.0f;
+    const T* rows[9];
+    const uint32_t outside = neighbour_rows(x, g, row, c, rows);
+    T* orow = out + row * g.W * g.C + c;
+    if (outside) conv_run<T, ACCUM, true>(rows, outside, g, w0, w1, wa, bb, orow);
+    else conv_run<T, ACCUM, false>(rows, outside, g, w0, w1, wa, bb, orow);
+}
+
+namespace {
+
+// The weight-gradient sums of one row: acc[tap] += dy[w] * x[row + (dt, dh), w + dk].
+template <typename T, bool EDGE>
+__device__ __forceinline__ void wgrad_row(const T* const rows[9], uint32_t outside, const T* grow, const ConvGrid& g,
+                                          float aa[27], float& sb) {
+    float cm[9], c0[9], cp[9];
+    load_column<T, EDGE>(rows, outside, g, -1, cm);
+    load_column<T, EDGE>(rows, outside, g, 0, c0);
+    for (int32_t w = 0; w < g.W; ++w) {
+        load_column<T, EDGE>(rows, outside, g, w + 1, cp);
+        const float d = load_scalar<T>(grow + (int64_t)w * g.C);
+        sb += d;
+#pragma unroll
+        for (int r = 0; r < 9; ++r) {
+            aa[r * 3 + 0] = fmaf(d, cm[r], aa[r * 3 + 0]);
+            aa[r * 3 + 1] = fmaf(d, c0[r], aa[r * 3 + 1]);
+            aa[r * 3 + 2] = fmaf(d, cp[r], aa[r * 3 + 2]);
+        }
+#pragma unroll
+        for (int r = 0; r < 9; ++r) {
+            cm[r] = c0[r];
+            c0[r] = cp[r];
+        }
+    }
+}
+
+}  // namespace
+
 // Per group of `rows_per_group` rows: part[group][c][tap] = sum over the
 // group's tokens of dy[tok, c] * x[tok + tap offset, c], partb[group][c] =
 // sum of dy[tok, c]; rows in increasing order, w in increasing order.
-// Grid: x = groups, y = channel groups of 512.
+// Grid: x = groups, y = channel groups of 256.
 template <typename T>
 __global__ void __launch_bounds__(256) dsa3d_dwconv_wgrad_kernel(const T* x, const T* dy, float* part, float* partb,
                                                                  ConvGrid g, int64_t rows_per_group) {
-    const int64_t c = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 2;
+    const int64_t c = (int64_t)blockIdx.y * 256 + threadIdx.x;
     if (c >= g.C) return;
     const int64_t nrows = (int64_t)g.B * g.T * g.H;
     const int64_t r0 = (int64_t)blockIdx.x * rows_per_group;
     const int64_t r1 = min(nrows, r0 + rows_per_group);
-    float aa[27], ab[27];
+    float aa[27];
 #pragma unroll
-    for (int tap = 0; tap < 27; ++tap) aa[tap] = ab[tap] = 0.f;
-    float2 sb = make_float2(0.f, 0.f);
+    for (int tap = 0; tap < 27; ++tap) aa[tap] = 0.f;
+    float sb = 0.f;
     for (int64_t row = r0; row < r1; ++row) {
         const T* rows[9];
-        neighbour_rows(x, g, row, c, rows);
+        const uint32_t outside = neighbour_rows(x, g, row, c, rows);
         const T* grow = dy + row * g.W * g.C + c;
-        float2 cm[9], c0[9], cp[9];
-        load_column(rows, g, -1, cm);
-        load_column(rows, g, 0, c0);
-        for (int32_t w = 0; w < g.W; ++w) {
-            load_column(rows, g, w + 1, cp);
-            const float2 d = Pair<T>::load(grow + (int64_t)w * g.C);
-            sb.x += d.x;
-            sb.y += d.y;
-#pragma unroll
-            for (int r = 0; r < 9; ++r) {
-                aa[r * 3 + 0] = fmaf(d.x, cm[r].x, aa[r * 3 + 0]);
-                ab[r * 3 + 0] = fmaf(d.y, cm[r].y, ab[r * 3 + 0]);
-                aa[r * 3 + 1] = fmaf(d.x, c0[r].x, aa[r * 3 + 1]);
-                ab[r * 3 + 1] = fmaf(d.y, c0[r].y, ab[r * 3 + 1]);
-                aa[r * 3 + 2] = fmaf(d.x, cp[r].x, aa[r * 3 + 2]);
-                ab[r * 3 + 2] = fmaf(d.y, cp[r].y, ab[r * 3 + 2]);
-            }
-#pragma unroll
-            for (int r = 0; r < 9; ++r) {
-                cm[r] = c0[r];
-                c0[r] = cp[r];
-            }
-        }
+        if (outside) wgrad_row<T, true>(rows, outside, grow, g, aa, sb);
+        else wgrad_row<T, false>(rows, outside, grow, g, aa, sb);
     }
     float* pa = part + ((int64_t)blockIdx.x * g.C + c) * 27;
 #pragma unroll
-    for (int tap = 0; tap < 27; ++tap) {
-        pa[tap] = aa[tap];
-        pa[27 + tap] = ab[tap];
-    }
-    partb[(int64_t)blockIdx.x * g.C + c] = sb.x;
-    partb[(int64_t)blockIdx.x * g.C + c + 1] = sb.y;
+    for (int tap = 0; tap < 27; ++tap) pa[tap] = aa[tap];
+    partb[(int64_t)blockIdx.x * g.C + c] = sb;
 }
 
 // out[i] = sum_{z < nsplit} part[z*n + i], z in increasing order.
@@ -202,12 +199,14 @@ ConvGrid conv_grid(const dsa3d_desc& d) {
     return ConvGrid{(int32_t)d.B, (int32_t)d.T, (int32_t)d.H, (int32_t)d.W, (int64_t)d.heads * d.head_dim};
 }
 
-// Rows per group of the weight gradient: enough groups for about 8192 waves.
+// Rows per group of the weight gradient: enough groups for about 8192 waves,
+// at most 512 (each output of the split sum adds the groups one by one).
 int64_t wgrad_rows_per_group(const dsa3d_desc& d) {
     const int64_t rows = d.B * d.T * d.H;
     const int64_t C = (int64_t)d.heads * d.head_dim;
-    const int64_t waves_per_group = (C / 2 + 63) / 64;
-    const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(rows, 8192 / std::max<int64_t>(1, waves_per_group)));
+    const int64_t waves_per_group = (C + 63) / 64;
+    const int64_t groups = std::max<int64_t>(
+        1, std::min<int64_t>({rows, (int64_t)512, 8192 / std::max<int64_t>(1, waves_per_group)}));
     return (rows + groups - 1) / groups;
 }
 
@@ -217,10 +216,14 @@ hipError_t conv_launch(const dsa3d_desc& d, const void* x, const void* w, const 
     const ConvGrid g = conv_grid(d);
     const int64_t rows = (int64_t)g.B * g.T * g.H;
     if (rows == 0 || g.W == 0) return hipSuccess;
-    dim3 grid((unsigned)rows, (unsigned)((g.C / 2 + 255) / 256), (unsigned)((g.W + kRun - 1) / kRun));
+    // runs of at most 64 tokens along w, of equal length
+    const int32_t nrun = (g.W + 63) / 64;
+    const int32_t run = (g.W + nrun - 1) / nrun;
+    dim3 grid((unsigned)rows, (unsigned)((g.C + 255) / 256), (unsigned)nrun);
     LaunchScope ls(kernel_id, s);
     hipLaunchKernelGGL((dsa3d_dwconv_kernel<T, MIRROR, ACCUM>), grid, dim3(256), 0, s, reinterpret_cast<const T*>(x),
-                       reinterpret_cast<const T*>(w), reinterpret_cast<const T*>(bias), reinterpret_cast<T*>(out), g);
+                       reinterpret_cast<const T*>(w), reinterpret_cast<const T*>(bias), reinterpret_cast<T*>(out), g,
+                       run);
     return hipGetLastError();
 }
 
@@ -246,8 +249,8 @@ hipError_t launch_dwconv_backward(const dsa3d_desc& d, const void* q, const void
     const int64_t rows = (int64_t)g.B * g.T * g.H;
     if (rows == 0 || g.W == 0) return hipSuccess;
     const bool f32 = d.dtype == DSA3D_F32;
-    hipError_t e = f32 ? conv_launch<float, true, true>(d, dy, w, nullptr, dq, DSA3D_K_DWCONV, s)
-                       : conv_launch<bf16_t, true, true>(d, dy, w, nullptr, dq, DSA3D_K_DWCONV, s);
+    hipError_t e = f32 ? conv_launch<float, true, true>(d, dy, w, nullptr, dq, DSA3D_K_DWCONV_DQ, s)
+                       : conv_launch<bf16_t, true, true>(d, dy, w, nullptr, dq, DSA3D_K_DWCONV_DQ, s);
     if (e != hipSuccess) return e;
     const int64_t rpg = wgrad_rows_per_group(d);
     const int64_t groups = (rows + rpg - 1) / rpg;
@@ -256,7 +259,7 @@ hipError_t launch_dwconv_backward(const dsa3d_desc& d, const void* q, const void
                                             (((size_t)groups * g.C * 27 * 4 + 255) & ~size_t(255)));
     {
         LaunchScope ls(DSA3D_K_DWCONV_WGRAD, s);
-        dim3 grid((unsigned)groups, (unsigned)((g.C / 2 + 255) / 256));
+        dim3 grid((unsigned)groups, (unsigned)((g.C + 255) / 256));
         if (f32)
             hipLaunchKernelGGL((dsa3d_dwconv_wgrad_kernel<float>), grid, dim3(256), 0, s,
                                reinterpret_cast<const float*>(q), reinterpret_cast<const float*>(dy), part, partb, g,

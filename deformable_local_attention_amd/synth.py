@@ -37,7 +37,7 @@ class Workload:
     window: Tuple[int, int, int]          # (k_t, k_h, k_w)
     dilation: Tuple[int, int, int]        # (dil_t, dil_h, dil_w)
     dtype: str                            # "f32" or "bf16"
-    offsets: str                          # "direct" or "proj"
+    offsets: str                          # "direct", "proj" (Linear of q) or "conv" (Linear of dwconv(q))
     offset_sigma: float = 0.0             # std of direct offsets (token units)
     weight_sigma: float = 0.02            # std of projection weights
     backward: bool = False                # chain includes the backward pass
@@ -86,6 +86,10 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("720p-bf16-proj-dil2", 1, 64, 45, 80, 16, 64, (3, 3, 3), (1, 2, 2), "bf16", "proj",
                  backward=True,
                  description="bf16 projection + fwd + bwd, 64x45x80 tokens, 16x64 heads, dilation (1,2,2)"),
+        Workload("720p-bf16-conv-dil2", 1, 64, 45, 80, 16, 64, (3, 3, 3), (1, 2, 2), "bf16", "conv",
+                 backward=True,
+                 description="bf16 depthwise 3x3x3 conv + projection + fwd + bwd, 64x45x80 tokens, 16x64 heads, "
+                             "dilation (1,2,2)"),
         Workload("1080p-bf16-proj", 1, 256, 68, 120, 24, 128, (3, 3, 3), (1, 1, 1), "bf16", "proj",
                  description="bf16 projection + fwd, 256x68x120 tokens, 24x128 heads"),
         Workload("1080p-bf16-p75-det", 1, 256, 68, 120, 24, 128, (3, 5, 5), (1, 1, 1), "bf16", "direct",
@@ -94,6 +98,10 @@ WORKLOADS: Dict[str, Workload] = {
                              "offsets N(0,2), deterministic K/V gradients"),
     ]
 }
+
+# Depthwise-convolution weights of the "conv" offset network: N(0, 0.2^2), so
+# that the 27-tap sums keep the scale of q (0.2 * sqrt(27) ~ 1).
+CONV_SIGMA = 0.2
 
 # The headline workload: fwd+bwd on the 256x68x120 grid.
 HEADLINE = "1080p-bf16-p75-det"
@@ -132,7 +140,10 @@ def make_inputs(wl: Workload, device="cpu", seed: int = 0,
     out["q"] = _randn(shp, 1.0, dt, gen, dev)
     out["k"] = _randn(shp, 1.0, dt, gen, dev)
     out["v"] = _randn(shp, 1.0, dt, gen, dev)
-    if wl.offsets == "proj":
+    if wl.offsets == "conv":
+        out["conv_w"] = _randn((wl.C, 3, 3, 3), CONV_SIGMA, dt, gen, dev)
+        out["conv_b"] = torch.zeros(wl.C, dtype=dt, device=dev)
+    if wl.offsets in ("proj", "conv"):
         out["proj_w"] = _randn((wl.F, wl.C), wl.weight_sigma, dt, gen, dev)
         out["proj_b"] = torch.zeros(wl.F, dtype=dt, device=dev)
     else:

@@ -201,8 +201,9 @@ typedef enum {
     DSA3D_K_BWD_COUNT = 12,     /* backward: samples per base cell */
     DSA3D_K_BWD_SORT = 13,      /* backward, deterministic: bucket sort (2 kernels, one entry) */
     DSA3D_K_TRANSPOSE = 14,     /* projection backward: W transposed for the dq product */
-    DSA3D_K_DWCONV = 15,        /* depthwise convolution: forward, and dq of its backward */
-    DSA3D_K_DWCONV_WGRAD = 16   /* depthwise convolution backward: split weight and bias sums */
+    DSA3D_K_DWCONV = 15,        /* depthwise convolution forward */
+    DSA3D_K_DWCONV_WGRAD = 16,  /* depthwise convolution backward: split weight and bias sums */
+    DSA3D_K_DWCONV_DQ = 17      /* depthwise convolution backward: dq += conv with the mirrored kernel */
 } dsa3d_kernel;
 
 typedef struct dsa3d_launch_log {

@@ -263,6 +263,51 @@ def test_dwconv_forward_and_backward(dtype, shape):
     assert rel_l2(to_np(db), db_ref) <= 1e-5
 
 
+def test_conv_offset_network_chain():
+    """The whole chain with the depthwise convolution in the offset network:
+    offsets = Linear(dwconv(q)), then attention forward and backward, then the
+    projection and convolution backward into dq."""
+    wl = synth.Workload("conv-chain", 1, 4, 6, 10, 8, 32, (3, 3, 3), (1, 2, 2), "bf16", "conv", backward=True)
+    say(f"[conv chain] {synth.describe(wl)}")
+    x = synth.make_inputs(wl, "cpu", seed=5)
+    xd = {k: v.to(DEV) for k, v in x.items()}
+    ch = Chain(wl, xd)
+    desc = ch.desc
+    dsa.dsa3d_dwconv_forward(desc, xd["q"], xd["conv_w"], xd["conv_b"], ch.pin)
+    dsa.dsa3d_offset_proj_forward(desc, ch.pin, xd["proj_w"], xd["proj_b"], ch.offsets)
+    dsa.dsa3d_forward(desc, xd["q"], xd["k"], xd["v"], ch.offsets, ch.out, ch.lse)
+    dsa.dsa3d_backward(desc, xd["q"], xd["k"], xd["v"], ch.offsets, ch.out, ch.lse, xd["dout"], ch.dq, ch.dk, ch.dv,
+                       ch.doff, ch.ws)
+    torch.cuda.synchronize()
+    dq_attn = ch.dq.clone()
+    ch.dpin.zero_()
+    dsa.dsa3d_offset_proj_backward(desc, ch.pin, xd["proj_w"], ch.doff, ch.dpin, ch.dw, ch.db, ch.pws)
+    dsa.dsa3d_dwconv_backward(desc, xd["q"], xd["conv_w"], ch.dpin, ch.dq, ch.dcw, ch.dcb, ch.cws)
+    torch.cuda.synchronize()
+    N, C, F = wl.tokens, wl.C, wl.F
+    q5 = to_np(x["q"]).reshape(1, wl.T, wl.H, wl.W, C)
+    y_ref = oracle.dwconv3d(q5, to_np(x["conv_w"]), to_np(x["conv_b"]))
+    _check("conv output", to_np(ch.pin).reshape(N, C), y_ref.reshape(N, C), "bf16")
+    off_ref = oracle.offset_proj(to_np(ch.pin).reshape(N, C), to_np(x["proj_w"]), to_np(x["proj_b"]))
+    _check("offsets", to_np(ch.offsets).reshape(N, F), off_ref, "bf16")
+    # the attention on the GPU's offsets
+    ref = oracle.forward(to_np(x["q"]), to_np(x["k"]), to_np(x["v"]), to_np(ch.offsets), wl.window, wl.dilation)
+    _check("out", to_np(ch.out), ref[0], "bf16")
+    # projection and convolution backward on the GPU's doffsets and convolution-output gradient
+    g = to_np(ch.doff).reshape(N, F)
+    _check("d(conv output)", to_np(ch.dpin).reshape(N, C), g @ to_np(x["proj_w"]), "bf16")
+    dq_conv, dcw_ref, dcb_ref = oracle.dwconv3d_backward(q5, to_np(x["conv_w"]), to_np(ch.dpin).reshape(q5.shape))
+    _check("dq total", to_np(ch.dq).reshape(N, C), to_np(dq_attn).reshape(N, C) + dq_conv.reshape(N, C), "bf16")
+    assert rel_l2(to_np(ch.dcw), dcw_ref) <= 1e-5
+    assert rel_l2(to_np(ch.dcb), dcb_ref) <= 1e-5
+    assert rel_l2(to_np(ch.dw), g.T @ to_np(ch.pin).reshape(N, C)) <= 1e-5
+    # the chain's own run() gives the same bits
+    dq_once = ch.dq.clone()
+    ch.run()
+    torch.cuda.synchronize()
+    assert torch.equal(ch.dq.view(torch.int16), dq_once.view(torch.int16))
+
+
 # ---------------------------------------------------------------------------
 # the named workloads: small one whole, full-size ones sampled
 # ---------------------------------------------------------------------------
