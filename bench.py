@@ -57,6 +57,21 @@ def algorithmic(wl):
     """
     s = 4 if wl.dtype == "f32" else 2
     d, P = wl.head_dim, wl.P
+    if wl.offsets == "none":
+        # fixed window (no offsets): forward reads q, k, v, writes o and lse;
+        # flops 4*d*P (one dot product and one row update per sample). Backward
+        # per query reads q, k, v, o, dO and lse, writes dq and <dO,o> (4 B);
+        # per key reads k, v, lse and <dO,o> of its queries (8 B), writes dk, dv;
+        # flops 10*d*P (logit, dL/da, dq, dk and dv per sample).
+        return {
+            "forward": 4 * d * s + 4,
+            "bwd_query": 6 * d * s + 8,
+            "bwd_key": 4 * d * s + 8,
+            "fwd_bytes": 4 * d * s + 4,
+            "bwd_bytes": 8 * d * s + 8,
+            "fwd_flops": 4 * d * P,
+            "bwd_flops": 10 * d * P,
+        }
     return {
         "forward": 4 * d * s + 3 * P * s + 4,
         "bwd_query": 6 * d * s + 6 * P * s + 4,
@@ -91,7 +106,8 @@ def cpu_baseline(wl, budget_s: float = 20.0):
         off = oracle.offset_proj(q2, x["proj_w"].double().numpy(), None).astype(np.float32)
         off = off.reshape(crop.B, crop.T, crop.H, crop.W, crop.heads, crop.P, 3)
     else:
-        off = x["offsets"].float().numpy()
+        off = (x["offsets"].float().numpy() if crop.offsets == "direct"
+               else np.zeros((crop.B, crop.T, crop.H, crop.W, crop.heads, crop.P, 3), dtype=np.float32))
     np64 = lambda t: t.double().numpy()
     q, k, v, g = np64(x["q"]), np64(x["k"]), np64(x["v"]), np64(x["dout"])
     T, H, W = crop.T, crop.H, crop.W
@@ -370,7 +386,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == "bf16" else "f32", "data": "synthetic (seeded N(0,1) q/k/v/dO; offsets "
-        + (f"N(0,{wl.offset_sigma})" if wl.offsets == "direct" else "from a Linear with N(0,0.02) weights"
+        + (f"N(0,{wl.offset_sigma})" if wl.offsets == "direct" else "none: fixed window, every offset zero"
+           if wl.offsets == "none" else "from a Linear with N(0,0.02) weights"
            + (" of a depthwise 3x3x3 conv with N(0,0.2) weights" if wl.offsets == "conv" else "")) + ")",
         "config": {"workload": wl.name, "grid": [wl.B, wl.T, wl.H, wl.W], "heads": wl.heads, "head_dim": wl.head_dim,
                    "window": list(wl.window), "P": wl.P, "dilation": list(wl.dilation), "offsets": wl.offsets,

@@ -25,12 +25,13 @@ __all__ = [
     "dsa3d_offset_proj_forward", "dsa3d_forward", "dsa3d_backward", "dsa3d_offset_proj_backward",
     "dsa3d_debug_geometry", "forward", "backward", "offset_proj", "offset_proj_backward",
     "DSA3D_F32", "DSA3D_BF16", "WS_FORWARD", "WS_BACKWARD", "WS_PROJ_BACKWARD", "WS_DWCONV_BACKWARD",
+    "WS_BACKWARD_FIXED",
     "dsa3d_dwconv_forward", "dsa3d_dwconv_backward", "dwconv", "dwconv_backward",
     "dsa3d_set_launch_log", "LaunchLog", "launch_timer", "KERNELS",
 ]
 
 DSA3D_F32, DSA3D_BF16 = 0, 1
-WS_FORWARD, WS_BACKWARD, WS_PROJ_BACKWARD, WS_DWCONV_BACKWARD = 0, 1, 2, 3
+WS_FORWARD, WS_BACKWARD, WS_PROJ_BACKWARD, WS_DWCONV_BACKWARD, WS_BACKWARD_FIXED = 0, 1, 2, 3, 4
 EXPORTS = ("dsa3d_version", "dsa3d_status_string", "dsa3d_validate", "dsa3d_workspace_size",
            "dsa3d_workspace_min", "dsa3d_offset_proj_forward", "dsa3d_forward", "dsa3d_backward",
            "dsa3d_offset_proj_backward", "dsa3d_debug_geometry", "dsa3d_dwconv_forward", "dsa3d_dwconv_backward",
@@ -270,7 +271,7 @@ def _workspace(desc: Desc, kind: int, device, nbytes: Optional[int] = None) -> O
 
 
 def forward(q, k, v, offsets, window, dilation=(1, 1, 1), scale: float = 0.0, stream=None):
-    """Returns (out, lse)."""
+    """Returns (out, lse); offsets None is the fixed window (every offset zero)."""
     desc = desc_like(q, window, dilation, scale)
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:5], dtype=torch.float32, device=q.device)
@@ -280,12 +281,12 @@ def forward(q, k, v, offsets, window, dilation=(1, 1, 1), scale: float = 0.0, st
 
 def backward(q, k, v, offsets, out, lse, dout, window, dilation=(1, 1, 1), scale: float = 0.0,
              deterministic: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
-    """Returns (dq, dk, dv, doffsets)."""
+    """Returns (dq, dk, dv, doffsets); offsets None is the fixed window (doffsets None)."""
     desc = desc_like(q, window, dilation, scale, deterministic)
     if workspace is None:
-        workspace = _workspace(desc, WS_BACKWARD, q.device)
+        workspace = _workspace(desc, WS_BACKWARD if offsets is not None else WS_BACKWARD_FIXED, q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    doff = torch.empty_like(offsets)
+    doff = torch.empty_like(offsets) if offsets is not None else None
     dsa3d_backward(desc, q, k, v, offsets, out, lse, dout, dq, dk, dv, doff, workspace, stream)
     return dq, dk, dv, doff
 

@@ -12,7 +12,7 @@ from typing import Dict, Optional
 
 import torch
 
-from . import (WS_BACKWARD, WS_DWCONV_BACKWARD, WS_PROJ_BACKWARD, desc_like, dsa3d_backward,
+from . import (WS_BACKWARD, WS_BACKWARD_FIXED, WS_DWCONV_BACKWARD, WS_PROJ_BACKWARD, desc_like, dsa3d_backward,
                dsa3d_dwconv_backward, dsa3d_dwconv_forward, dsa3d_forward, dsa3d_offset_proj_backward,
                dsa3d_offset_proj_forward, dsa3d_workspace_size)
 from .synth import Workload
@@ -31,10 +31,11 @@ class Chain:
         self.proj = wl.offsets in ("proj", "conv")
         # the projection's input: q itself, or its depthwise convolution
         self.pin = torch.empty_like(q) if self.conv else q
+        self.fixed = wl.offsets == "none"  # fixed window: no offsets tensor
         if self.proj:
             self.offsets = torch.empty(q.shape[:5] + (wl.P, 3), dtype=q.dtype, device=dev)
         else:
-            self.offsets = inputs["offsets"]
+            self.offsets = None if self.fixed else inputs["offsets"]
         self.out = torch.empty_like(q)
         self.lse = torch.empty(q.shape[:5], dtype=torch.float32, device=dev)
         self.backward = wl.backward
@@ -42,8 +43,9 @@ class Chain:
             self.dq = torch.empty_like(q)
             self.dk = torch.empty_like(q)
             self.dv = torch.empty_like(q)
-            self.doff = torch.empty_like(self.offsets)
-            n = dsa3d_workspace_size(self.desc, WS_BACKWARD) if bwd_workspace_bytes is None else bwd_workspace_bytes
+            self.doff = None if self.fixed else torch.empty_like(self.offsets)
+            kind = WS_BACKWARD_FIXED if self.fixed else WS_BACKWARD
+            n = dsa3d_workspace_size(self.desc, kind) if bwd_workspace_bytes is None else bwd_workspace_bytes
             self.ws = torch.empty(max(16, (n + 15) // 16 * 16), dtype=torch.uint8, device=dev) if n else None
             if self.proj:
                 self.dw = torch.empty(inputs["proj_w"].shape, dtype=torch.float32, device=dev)

@@ -91,6 +91,7 @@ size_t dsa3d_workspace_min(const dsa3d_desc* d, int kind) {
         case DSA3D_WS_BACKWARD: return dsa3d::bwd_workspace_bytes(*d, 1);
         case DSA3D_WS_PROJ_BACKWARD: return dsa3d::proj_bwd_workspace_bytes(*d);
         case DSA3D_WS_DWCONV_BACKWARD: return dsa3d::dwconv_bwd_workspace_bytes(*d);
+        case DSA3D_WS_BACKWARD_FIXED: return dsa3d::fixed_bwd_workspace_bytes(*d);
         default: return 0;
     }
 }
@@ -119,7 +120,10 @@ int dsa3d_forward(const dsa3d_desc* d, const void* q, const void* k, const void*
                   float* lse, void* stream) {
     int rc = dsa3d_validate(d);
     if (rc != DSA3D_OK) return rc;
-    if ((rc = check_ptrs({q, k, v, offsets, out, lse})) != DSA3D_OK) return rc;
+    if ((rc = check_ptrs({q, k, v, out, lse})) != DSA3D_OK) return rc;
+    if (offsets == nullptr)  // fixed window: every offset zero
+        return hip_status(dsa3d::launch_fixed_forward(*d, q, k, v, out, lse, static_cast<hipStream_t>(stream)));
+    if (!aligned16(offsets)) return DSA3D_ERR_MISALIGNED;
     return hip_status(dsa3d::launch_forward(*d, q, k, v, offsets, out, lse, static_cast<hipStream_t>(stream)));
 }
 
@@ -128,7 +132,16 @@ int dsa3d_backward(const dsa3d_desc* d, const void* q, const void* k, const void
                    void* workspace, size_t workspace_bytes, void* stream) {
     int rc = dsa3d_validate(d);
     if (rc != DSA3D_OK) return rc;
-    if ((rc = check_ptrs({q, k, v, offsets, out, lse, dout, dq, dk, dv, doffsets})) != DSA3D_OK) return rc;
+    if ((rc = check_ptrs({q, k, v, out, lse, dout, dq, dk, dv})) != DSA3D_OK) return rc;
+    if ((offsets == nullptr) != (doffsets == nullptr)) return DSA3D_ERR_INVALID_ARG;
+    if (offsets == nullptr) {  // fixed window: every offset zero, no offset gradient
+        if (workspace == nullptr || workspace_bytes < dsa3d::fixed_bwd_workspace_bytes(*d))
+            return DSA3D_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return DSA3D_ERR_MISALIGNED;
+        return hip_status(dsa3d::launch_fixed_backward(*d, q, k, v, out, lse, dout, dq, dk, dv, workspace,
+                                                       static_cast<hipStream_t>(stream)));
+    }
+    if (!aligned16(offsets) || !aligned16(doffsets)) return DSA3D_ERR_MISALIGNED;
     const size_t need = dsa3d::bwd_workspace_bytes(*d, 1);
     if (need == 0) return DSA3D_ERR_UNSUPPORTED;  // sample or cell numbers of one head exceed 32 bits
     if (workspace == nullptr || workspace_bytes < need) return DSA3D_ERR_WORKSPACE;

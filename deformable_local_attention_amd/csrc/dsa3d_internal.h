@@ -91,6 +91,12 @@ hipError_t launch_proj_forward(const dsa3d_desc& d, const void* q, const void* w
 hipError_t launch_proj_backward(const dsa3d_desc& d, const void* q, const void* w, const void* doff, void* dq,
                                 float* dw, float* db, void* ws, hipStream_t s);
 size_t dwconv_bwd_workspace_bytes(const dsa3d_desc& d);
+size_t fixed_bwd_workspace_bytes(const dsa3d_desc& d);
+hipError_t launch_fixed_forward(const dsa3d_desc& d, const void* q, const void* k, const void* v, void* out,
+                                float* lse, hipStream_t s);
+hipError_t launch_fixed_backward(const dsa3d_desc& d, const void* q, const void* k, const void* v, const void* o,
+                                 const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws,
+                                 hipStream_t s);
 hipError_t launch_dwconv_forward(const dsa3d_desc& d, const void* q, const void* w, const void* bias, void* y,
                                  hipStream_t s);
 hipError_t launch_dwconv_backward(const dsa3d_desc& d, const void* q, const void* w, const void* dy, void* dq,

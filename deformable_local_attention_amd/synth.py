@@ -37,7 +37,8 @@ class Workload:
     window: Tuple[int, int, int]          # (k_t, k_h, k_w)
     dilation: Tuple[int, int, int]        # (dil_t, dil_h, dil_w)
     dtype: str                            # "f32" or "bf16"
-    offsets: str                          # "direct", "proj" (Linear of q) or "conv" (Linear of dwconv(q))
+    offsets: str                          # "direct", "proj" (Linear of q), "conv" (Linear of dwconv(q))
+                                          # or "none" (fixed window: every offset zero, none stored)
     offset_sigma: float = 0.0             # std of direct offsets (token units)
     weight_sigma: float = 0.02            # std of projection weights
     backward: bool = False                # chain includes the backward pass
@@ -92,6 +93,10 @@ WORKLOADS: Dict[str, Workload] = {
                              "dilation (1,2,2)"),
         Workload("1080p-bf16-proj", 1, 256, 68, 120, 24, 128, (3, 3, 3), (1, 1, 1), "bf16", "proj",
                  description="bf16 projection + fwd, 256x68x120 tokens, 24x128 heads"),
+        Workload("1080p-bf16-fixed377", 1, 256, 68, 120, 24, 128, (3, 7, 7), (1, 1, 1), "bf16", "none",
+                 backward=True,
+                 description="bf16 fwd + bwd of the fixed 3x7x7 window (every offset zero), 256x68x120 tokens, "
+                             "24x128 heads"),
         Workload("1080p-bf16-p75-det", 1, 256, 68, 120, 24, 128, (3, 5, 5), (1, 1, 1), "bf16", "direct",
                  offset_sigma=2.0, backward=True, deterministic=True,
                  description="bf16 fwd + bwd, 256x68x120 tokens, 24x128 heads, 3x5x5 window, "
@@ -146,7 +151,7 @@ def make_inputs(wl: Workload, device="cpu", seed: int = 0,
     if wl.offsets in ("proj", "conv"):
         out["proj_w"] = _randn((wl.F, wl.C), wl.weight_sigma, dt, gen, dev)
         out["proj_b"] = torch.zeros(wl.F, dtype=dt, device=dev)
-    else:
+    elif wl.offsets == "direct":
         out["offsets"] = _randn(shp[:5] + (wl.P, 3), wl.offset_sigma, dt, gen, dev)
     if with_grad if with_grad is not None else wl.backward:
         out["dout"] = _randn(shp, 1.0, dt, gen, dev)

@@ -85,7 +85,8 @@ typedef enum {
     DSA3D_WS_FORWARD = 0,
     DSA3D_WS_BACKWARD = 1,
     DSA3D_WS_PROJ_BACKWARD = 2,
-    DSA3D_WS_DWCONV_BACKWARD = 3
+    DSA3D_WS_DWCONV_BACKWARD = 3,
+    DSA3D_WS_BACKWARD_FIXED = 4    /* dsa3d_backward with offsets == NULL */
 } dsa3d_ws_kind;
 
 /* Library version (major*10000 + minor*100 + patch). */
@@ -115,7 +116,12 @@ int dsa3d_offset_proj_forward(const dsa3d_desc* desc, const void* q, const void*
                               const void* bias, void* offsets, void* stream);
 
 /* Forward. Writes out and lse (log of the softmax denominator, float32, used
- * by the backward). No workspace is needed. */
+ * by the backward). No workspace is needed.
+ * offsets == NULL selects the fixed window: every offset is zero, so each
+ * sample is the reference token itself and the operator is fixed local
+ * attention over the dilated window [MegaSlide-DiT, §9.1: offsets frozen at
+ * zero, a fixed (3,7,7) window]; the result equals the general path with a
+ * zero offsets tensor, without reading offsets or interpolating. */
 int dsa3d_forward(const dsa3d_desc* desc, const void* q, const void* k, const void* v,
                   const void* offsets, void* out, float* lse, void* stream);
 
@@ -135,7 +141,12 @@ int dsa3d_forward(const dsa3d_desc* desc, const void* q, const void* k, const vo
  * The workspace (at least dsa3d_workspace_min(desc, DSA3D_WS_BACKWARD), the
  * size of a pass over one head) holds the index; a larger one lets one pass
  * cover more heads. A single head whose B*T*H*W*P samples, or whose
- * B*(T+1)*(H+1)*(W+1) cells, reach 2^32 gives DSA3D_ERR_UNSUPPORTED. */
+ * B*(T+1)*(H+1)*(W+1) cells, reach 2^32 gives DSA3D_ERR_UNSUPPORTED.
+ * offsets == NULL (and doffsets == NULL; one without the other is
+ * DSA3D_ERR_INVALID_ARG) is the fixed window of dsa3d_forward: no offset
+ * gradient; each key walks the queries whose window contains it, so dk and dv
+ * are summed in a fixed order for either value of `deterministic`; the
+ * workspace (DSA3D_WS_BACKWARD_FIXED) holds one float per (token, head). */
 int dsa3d_backward(const dsa3d_desc* desc, const void* q, const void* k, const void* v,
                    const void* offsets, const void* out, const float* lse, const void* dout,
                    void* dq, void* dk, void* dv, void* doffsets,

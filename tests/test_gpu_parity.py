@@ -55,7 +55,8 @@ def _run_whole(wl, x, det=None, ws_bytes=None):
     ch = Chain(wl, xd, bwd_workspace_bytes=ws_bytes, deterministic=det)
     ch.run()
     torch.cuda.synchronize()
-    off = to_np32(ch.offsets)
+    off = (to_np32(ch.offsets) if ch.offsets is not None
+           else np.zeros(tuple(x["q"].shape[:5]) + (wl.P, 3), dtype=np.float32))  # fixed window
     o, lse = oracle.forward(to_np(x["q"]), to_np(x["k"]), to_np(x["v"]), off, wl.window, wl.dilation)
     _check("o", to_np(ch.out), o, wl.dtype)
     lerr = float(np.abs(to_np(ch.lse) - lse).max())
@@ -66,7 +67,8 @@ def _run_whole(wl, x, det=None, ws_bytes=None):
         _check("dq", to_np(ch.dq), dq, wl.dtype)
         _check("dk", to_np(ch.dk), dk, wl.dtype)
         _check("dv", to_np(ch.dv), dv, wl.dtype)
-        _check("doff", to_np(ch.doff), doff, wl.dtype)
+        if ch.doff is not None:
+            _check("doff", to_np(ch.doff), doff, wl.dtype)
     return ch
 
 
@@ -188,6 +190,45 @@ def test_deterministic_mode_is_bitwise_reproducible_across_runs_and_pass_splits(
         for a, b in zip(outs[0], other):
             assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
+# ---------------------------------------------------------------------------
+# fixed window (offsets NULL: every offset zero)
+# ---------------------------------------------------------------------------
+
+# (dtype, B, T, H, W, heads, d, window, dilation): the pages' 3x7x7 window on
+# ragged grids, a dilated 3x3x3 window, a window wider than the grid.
+@pytest.mark.parametrize("case", [("f32", 2, 3, 5, 11, 2, 32, (3, 7, 7), (1, 1, 1)),
+                                  ("bf16", 1, 4, 9, 13, 3, 128, (3, 7, 7), (1, 1, 1)),
+                                  ("bf16", 1, 5, 8, 10, 2, 64, (3, 3, 3), (1, 2, 2)),
+                                  ("f32", 1, 2, 3, 4, 1, 8, (3, 7, 7), (2, 1, 1))])
+def test_fixed_window_whole(case):
+    dt, B, T, H, W, nh, d, win, dil = case
+    wl = synth.Workload("fixed", B, T, H, W, nh, d, win, dil, dt, "none", backward=True)
+    _run_whole(wl, synth.make_inputs(wl, "cpu", seed=41))
+
+
+def test_fixed_window_equals_general_path_at_zero_offsets():
+    """offsets NULL and a zero offsets tensor: the same forward and dq bits;
+    dk/dv are summed in another order (per key window instead of per cell)."""
+    wl = synth.Workload("fixed", 1, 4, 6, 9, 2, 64, (3, 7, 7), (1, 1, 1), "bf16", "none", backward=True)
+    x = {k: v.to(DEV) for k, v in synth.make_inputs(wl, "cpu", seed=43).items()}
+    zeros = torch.zeros(tuple(x["q"].shape[:5]) + (wl.P, 3), dtype=x["q"].dtype, device=DEV)
+    o_f, lse_f = dsa.forward(x["q"], x["k"], x["v"], None, wl.window)
+    o_g, lse_g = dsa.forward(x["q"], x["k"], x["v"], zeros, wl.window)
+    dq_f, dk_f, dv_f, doff_f = dsa.backward(x["q"], x["k"], x["v"], None, o_f, lse_f, x["dout"], wl.window)
+    dq_g, dk_g, dv_g, _ = dsa.backward(x["q"], x["k"], x["v"], zeros, o_g, lse_g, x["dout"], wl.window)
+    torch.cuda.synchronize()
+    assert doff_f is None
+    assert torch.equal(o_f.view(torch.int16), o_g.view(torch.int16))
+    assert torch.equal(lse_f, lse_g)
+    assert torch.equal(dq_f.view(torch.int16), dq_g.view(torch.int16))
+    assert rel_l2(to_np(dk_f), to_np(dk_g)) <= 1e-2 and rel_l2(to_np(dv_f), to_np(dv_g)) <= 1e-2
+    # NULL offsets need NULL doffsets
+    desc = dsa.desc_like(x["q"], wl.window)
+    ws = dsa._workspace(desc, dsa.WS_BACKWARD_FIXED, DEV)
+    with pytest.raises(dsa.DSA3DError):
+        dsa.dsa3d_backward(desc, x["q"], x["k"], x["v"], None, o_f, lse_f, x["dout"], dq_f, dk_f, dv_f, zeros, ws)
 
 
 # ---------------------------------------------------------------------------
@@ -392,6 +433,31 @@ def test_1080p_projection_workload_full_size_sampled():
     ref = oracle.offset_proj(to_np(xd["q"].view(N, C)[rows]), to_np(xd["proj_w"]), to_np(xd["proj_b"]))
     _check("offsets rows", to_np(ch.offsets.view(N, F)[rows]), ref, "bf16")
     _sampled_attention_checks(wl, ch, xd, n_random=64, seed=3)
+    del ch, xd
+    _free()
+
+
+@pytest.mark.slow
+def test_1080p_fixed_377_workload_full_size_sampled():
+    """The fixed 3x7x7 window at 1080p, in the bench's launch configuration."""
+    wl = synth.WORKLOADS["1080p-bf16-fixed377"]
+    say(f"[full] {synth.describe(wl)}")
+    xd = synth.make_inputs(wl, DEV)
+    ch = Chain(wl, xd)
+    ch.run()
+    torch.cuda.synchronize()
+    # a zero offsets tensor as a broadcast view (no memory) for the oracle helpers
+    zeros = torch.zeros((), dtype=xd["q"].dtype, device=DEV).expand(tuple(xd["q"].shape[:5]) + (wl.P, 3))
+    qs = sample_queries(wl, heads=[0, wl.heads - 1], n_random=48, seed=7)
+    say(f"[sampled] {len(qs)} queries")
+    r = oracle_queries(wl, xd, zeros, qs, dout=xd["dout"])
+    _check("o (sampled)", gather(ch.out, qs), r["o"], "bf16")
+    assert float(np.abs(gather(ch.lse.unsqueeze(-1), qs)[:, 0] - r["lse"]).max()) <= 1e-3
+    _check("dq (sampled)", gather(ch.dq, qs), r["dq"], "bf16")
+    keys = sample_queries(wl, heads=[0, wl.heads - 1], n_random=3, seed=8, faces=0)[:8]
+    kk, vv = oracle_dkdv_at_keys(wl, xd, zeros, xd["dout"], keys)
+    _check("dk (keys)", gather(ch.dk, keys), kk, "bf16")
+    _check("dv (keys)", gather(ch.dv, keys), vv, "bf16")
     del ch, xd
     _free()
 
