@@ -105,15 +105,21 @@ __device__ __forceinline__ void conv_run(const T* const rows[9], uint32_t outsid
 }  // namespace
 
 // y[row, w, c] = bias[c] + sum_tap wt[c, tap] * x[row + (dt, dh), w + dk, c] (MIRROR: tap 26 - tap),
-// or (ACCUM) out[...] += the sum without bias. Grid: x = rows (B*T*H), y = channel groups of 256,
-// z = runs of `run` tokens along w.
+// or (ACCUM) out[...] += the sum without bias. One block per (row (b,t,h), group of 256 channels,
+// run of `run` tokens along w).
 template <typename T, bool MIRROR, bool ACCUM>
 __global__ void __launch_bounds__(256) dsa3d_dwconv_kernel(const T* x, const T* wt, const T* bias, T* out, ConvGrid g,
-                                                           int32_t run) {
-    const int64_t row = blockIdx.x;
-    const int64_t c = (int64_t)blockIdx.y * 256 + threadIdx.x;
+                                                           int32_t run, int64_t ngroups) {
+    // 1-D grid, XCD-contiguous: each XCD walks a range of (run, channel group, row) with the row
+    // fastest, so the blocks of neighbouring rows, which read the same input rows, share its L2
+    const int64_t nrows = (int64_t)g.B * g.T * g.H;
+    const int64_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int64_t row = lb % nrows;
+    const int64_t cg = (lb / nrows) % ngroups;
+    const int32_t ri = (int32_t)(lb / nrows / ngroups);
+    const int64_t c = cg * 256 + threadIdx.x;
     if (c >= g.C) return;
-    const int32_t w0 = (int32_t)blockIdx.z * run;
+    const int32_t w0 = ri * run;
     const int32_t w1 = min(g.W, w0 + run);
     float wa[27];
     load_weights<T, MIRROR>(wt, c, wa);
@@ -157,14 +163,18 @@ __device__ __forceinline__ void wgrad_row(const T* const rows[9], uint32_t outsi
 // Per group of `rows_per_group` rows: part[group][c][tap] = sum over the
 // group's tokens of dy[tok, c] * x[tok + tap offset, c], partb[group][c] =
 // sum of dy[tok, c]; rows in increasing order, w in increasing order.
-// Grid: x = groups, y = channel groups of 256.
+// One block per (group of rows, group of 256 channels).
 template <typename T>
 __global__ void __launch_bounds__(256) dsa3d_dwconv_wgrad_kernel(const T* x, const T* dy, float* part, float* partb,
                                                                  ConvGrid g, int64_t rows_per_group) {
-    const int64_t c = (int64_t)blockIdx.y * 256 + threadIdx.x;
-    if (c >= g.C) return;
+    // 1-D grid, XCD-contiguous, row groups fastest (neighbouring groups share input rows)
     const int64_t nrows = (int64_t)g.B * g.T * g.H;
-    const int64_t r0 = (int64_t)blockIdx.x * rows_per_group;
+    const int64_t ngrp = (nrows + rows_per_group - 1) / rows_per_group;
+    const int64_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int64_t grp = lb % ngrp;
+    const int64_t c = (lb / ngrp) * 256 + threadIdx.x;
+    if (c >= g.C) return;
+    const int64_t r0 = grp * rows_per_group;
     const int64_t r1 = min(nrows, r0 + rows_per_group);
     float aa[27];
 #pragma unroll
@@ -177,10 +187,10 @@ __global__ void __launch_bounds__(256) dsa3d_dwconv_wgrad_kernel(const T* x, con
         if (outside) wgrad_row<T, true>(rows, outside, grow, g, aa, sb);
         else wgrad_row<T, false>(rows, outside, grow, g, aa, sb);
     }
-    float* pa = part + ((int64_t)blockIdx.x * g.C + c) * 27;
+    float* pa = part + (grp * g.C + c) * 27;
 #pragma unroll
     for (int tap = 0; tap < 27; ++tap) pa[tap] = aa[tap];
-    partb[(int64_t)blockIdx.x * g.C + c] = sb;
+    partb[grp * g.C + c] = sb;
 }
 
 // out[i] = sum_{z < nsplit} part[z*n + i], z in increasing order.
@@ -219,11 +229,12 @@ hipError_t conv_launch(const dsa3d_desc& d, const void* x, const void* w, const 
     // runs of at most 64 tokens along w, of equal length
     const int32_t nrun = (g.W + 63) / 64;
     const int32_t run = (g.W + nrun - 1) / nrun;
-    dim3 grid((unsigned)rows, (unsigned)((g.C + 255) / 256), (unsigned)nrun);
+    const int64_t ngroups = (g.C + 255) / 256;
+    const int64_t nblocks = rows * ngroups * nrun;
     LaunchScope ls(kernel_id, s);
-    hipLaunchKernelGGL((dsa3d_dwconv_kernel<T, MIRROR, ACCUM>), grid, dim3(256), 0, s, reinterpret_cast<const T*>(x),
-                       reinterpret_cast<const T*>(w), reinterpret_cast<const T*>(bias), reinterpret_cast<T*>(out), g,
-                       run);
+    hipLaunchKernelGGL((dsa3d_dwconv_kernel<T, MIRROR, ACCUM>), dim3((unsigned)nblocks), dim3(256), 0, s,
+                       reinterpret_cast<const T*>(x), reinterpret_cast<const T*>(w), reinterpret_cast<const T*>(bias),
+                       reinterpret_cast<T*>(out), g, run, ngroups);
     return hipGetLastError();
 }
 
@@ -259,7 +270,7 @@ hipError_t launch_dwconv_backward(const dsa3d_desc& d, const void* q, const void
                                             (((size_t)groups * g.C * 27 * 4 + 255) & ~size_t(255)));
     {
         LaunchScope ls(DSA3D_K_DWCONV_WGRAD, s);
-        dim3 grid((unsigned)groups, (unsigned)((g.C + 255) / 256));
+        dim3 grid((unsigned)(groups * ((g.C + 255) / 256)));
         if (f32)
             hipLaunchKernelGGL((dsa3d_dwconv_wgrad_kernel<float>), grid, dim3(256), 0, s,
                                reinterpret_cast<const float*>(q), reinterpret_cast<const float*>(dy), part, partb, g,
