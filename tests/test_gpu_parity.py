@@ -421,6 +421,51 @@ def test_720p_dil2_workload_full_size_sampled():
 
 
 @pytest.mark.slow
+def test_720p_conv_workload_full_size_sampled():
+    """The 720p chain with the depthwise convolution in the offset network, at full size:
+    the convolution and its gradients on a subset of channels over the whole grid, the
+    offsets and attention on sampled tokens."""
+    wl = synth.WORKLOADS["720p-bf16-conv-dil2"]
+    say(f"[full] {synth.describe(wl)}")
+    xd = synth.make_inputs(wl, DEV)
+    ch = Chain(wl, xd)
+    desc = ch.desc
+    dsa.dsa3d_dwconv_forward(desc, xd["q"], xd["conv_w"], xd["conv_b"], ch.pin)
+    dsa.dsa3d_offset_proj_forward(desc, ch.pin, xd["proj_w"], xd["proj_b"], ch.offsets)
+    dsa.dsa3d_forward(desc, xd["q"], xd["k"], xd["v"], ch.offsets, ch.out, ch.lse)
+    dsa.dsa3d_backward(desc, xd["q"], xd["k"], xd["v"], ch.offsets, ch.out, ch.lse, xd["dout"], ch.dq, ch.dk, ch.dv,
+                       ch.doff, ch.ws)
+    torch.cuda.synchronize()
+    dq_attn = ch.dq.clone()
+    ch.dpin.zero_()
+    dsa.dsa3d_offset_proj_backward(desc, ch.pin, xd["proj_w"], ch.doff, ch.dpin, ch.dw, ch.db, ch.pws)
+    dsa.dsa3d_dwconv_backward(desc, xd["q"], xd["conv_w"], ch.dpin, ch.dq, ch.dcw, ch.dcb, ch.cws)
+    torch.cuda.synchronize()
+    N, C, F = wl.tokens, wl.C, wl.F
+    g5 = (1, wl.T, wl.H, wl.W, C)
+    cols = torch.tensor(np.sort(np.random.default_rng(3).choice(C, 16, replace=False)), device=DEV)
+    sub = lambda t: to_np(t.view(g5).index_select(4, cols))
+    cw = to_np(xd["conv_w"].index_select(0, cols))
+    q_c = sub(xd["q"])
+    _check("conv output (16 channels)", sub(ch.pin).reshape(-1, 16),
+           oracle.dwconv3d(q_c, cw, to_np(xd["conv_b"].index_select(0, cols))).reshape(-1, 16), "bf16")
+    rows = np.random.default_rng(0).choice(N, 512, replace=False)
+    pin2 = ch.pin.view(N, C)
+    ref = oracle.offset_proj(to_np(pin2[rows]), to_np(xd["proj_w"]), to_np(xd["proj_b"]))
+    _check("offsets rows", to_np(ch.offsets.view(N, F)[rows]), ref, "bf16")
+    qs, r = _sampled_attention_checks(wl, ch, xd, n_random=64, seed=9)
+    _check("dq_attn (sampled)", gather(dq_attn, qs), r["dq"], "bf16")
+    g = to_np(ch.doff.view(N, F)[rows])
+    _check("d(conv output) rows", to_np(ch.dpin.view(N, C)[rows]), g @ to_np(xd["proj_w"]), "bf16")
+    dq_c, dcw_ref, dcb_ref = oracle.dwconv3d_backward(q_c, cw, sub(ch.dpin))
+    _check("dq total (16 channels)", sub(ch.dq).reshape(-1, 16), (sub(dq_attn) + dq_c).reshape(-1, 16), "bf16")
+    assert rel_l2(to_np(ch.dcw.index_select(0, cols)), dcw_ref) <= 1e-5
+    assert rel_l2(to_np(ch.dcb.index_select(0, cols)), dcb_ref) <= 1e-5
+    del ch, xd
+    _free()
+
+
+@pytest.mark.slow
 def test_1080p_projection_workload_full_size_sampled():
     wl = synth.WORKLOADS["1080p-bf16-proj"]
     say(f"[full] {synth.describe(wl)}")
