@@ -5,12 +5,18 @@
 //           dW[F, C]          = doff^T . q                        (split over N_tok, fixed-order sum)
 //           db[F]             = column sums of doff               (split over N_tok, fixed-order sum)
 //
-// One kernel template covers all three products: a 128x128 output tile per
-// 256-thread workgroup, four waves of 64x64, staged through LDS in 32-deep K
-// slices stored K-contiguous (padded rows), consumed by
-// v_mfma_f32_16x16x32_bf16 (bf16) or v_mfma_f32_16x16x4_f32 (float32) with
-// float32 accumulation. Operands stored M/N-contiguous are transposed while
-// they are written to LDS.
+// Three kernels, by operand layout and dtype:
+//  - dsa3d_ntgemm_kernel (bf16, both operands K-contiguous: the forward, and dq
+//    once W is transposed into the workspace): 256x256 tiles, operands copied
+//    from memory straight into a 4-stage LDS ring;
+//  - dsa3d_xgemm_kernel (bf16, any layout, used for dW): 256x256 tiles, two
+//    register-staged LDS stages, M/N-contiguous operands transposed in
+//    registers;
+//  - dsa3d_gemm_kernel (float32 runs, and bf16 shapes the others cannot
+//    take): 128x128 tiles, four waves of 64x64, 32-deep K slices in padded LDS
+//    rows, v_mfma_f32_16x16x32_bf16 or v_mfma_f32_16x16x4_f32.
+// All accumulate in float32; dW and db are split over the tokens and summed in
+// a fixed order.
 #include "dsa3d_device.h"
 #include "dsa3d_internal.h"
 
