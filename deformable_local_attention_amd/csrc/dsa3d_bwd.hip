@@ -99,6 +99,65 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_count_kernel(BwdArgs a) {
     }
 }
 
+// The same counts, tile by tile: a block takes 4 frames x 8 rows x 16 tokens
+// of one (batch, head) and counts its samples' cells in an LDS histogram over
+// the tile's cells widened by the window's reach plus a margin, then adds the
+// histogram's non-zero entries to the global counts (one atomic per cell
+// instead of one per sample); a sample whose cell lies outside the histogram
+// counts in global memory directly. Counts are integers, so the result does
+// not depend on the order.
+constexpr int kCtT = 4, kCtH = 8, kCtW = 16;
+constexpr int kCountLdsCells = 12288;  // 48 KiB
+
+struct CountTile {
+    int32_t mt, mh, mw;     // reach of a sample beyond its token, in cells, per axis
+    int32_t RT, RH, RW;     // histogram extent: tile + 2*reach + 1 (cells start one below a token)
+    int32_t ntt, nth, ntw;  // tiles per axis
+};
+
+template <typename T>
+__global__ void __launch_bounds__(256) dsa3d_bwd_count_tiled_kernel(BwdArgs a, CountTile ct) {
+    __shared__ uint32_t hist[kCountLdsCells];
+    const int ncell = ct.RT * ct.RH * ct.RW;
+    for (int i = threadIdx.x; i < ncell; i += 256) hist[i] = 0u;
+    __syncthreads();
+    const int64_t per_bh = (int64_t)ct.ntt * ct.nth * ct.ntw;
+    const int64_t bh = blockIdx.x / per_bh;
+    const int32_t r = (int32_t)(blockIdx.x - bh * per_bh);
+    const int32_t it = r / (ct.nth * ct.ntw), ih = (r / ct.ntw) % ct.nth, iw = r % ct.ntw;
+    const int32_t tt0 = it * kCtT, th0 = ih * kCtH, tw0 = iw * kCtW;
+    const int32_t ot = tt0 - ct.mt - 1, oh = th0 - ct.mh - 1, ow = tw0 - ct.mw - 1;  // histogram origin
+    const int32_t b = (int32_t)(bh / a.g.nheads);
+    const int32_t eta = a.g.head0 + (int32_t)(bh - (int64_t)b * a.g.nheads);
+    const uint32_t tok_b = (uint32_t)b * (uint32_t)a.g.T * (uint32_t)a.g.H * (uint32_t)a.g.W;
+    const int nsamp = kCtT * kCtH * kCtW * a.P;
+    for (int i = threadIdx.x; i < nsamp; i += 256) {
+        const int lt = i / a.P, p = i - lt * a.P;
+        const int32_t t = tt0 + lt / (kCtH * kCtW), h = th0 + (lt / kCtW) % kCtH, w = tw0 + lt % kCtW;
+        if (t >= a.g.T || h >= a.g.H || w >= a.g.W) continue;
+        const int64_t tok = (int64_t)tok_b + ((int64_t)t * a.g.H + h) * a.g.W + w;
+        float dt, dh, dw;
+        load_offsets<T>(reinterpret_cast<const T*>(a.off) + ((tok * a.g.heads + eta) * (int64_t)a.P + p) * 3, dt, dh,
+                        dw);
+        int32_t t0, h0, w0;
+        float ft, fh, fw;
+        if (!sample_geometry(a.win, t, h, w, p, dt, dh, dw, t0, h0, w0, ft, fh, fw)) continue;
+        if (t0 < -1 || t0 >= a.g.T || h0 < -1 || h0 >= a.g.H || w0 < -1 || w0 >= a.g.W) continue;
+        const uint32_t lt0 = (uint32_t)(t0 - ot), lh0 = (uint32_t)(h0 - oh), lw0 = (uint32_t)(w0 - ow);
+        if (lt0 < (uint32_t)ct.RT && lh0 < (uint32_t)ct.RH && lw0 < (uint32_t)ct.RW)
+            atomicAdd(&hist[(lt0 * ct.RH + lh0) * ct.RW + lw0], 1u);
+        else
+            atomicAdd(a.cnt + cell_index(a.g, bh, t0, h0, w0), 1u);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < ncell; i += 256) {
+        const uint32_t c = hist[i];
+        if (c == 0u) continue;  // only cells that samples counted, all inside the grid's cell range
+        const int32_t lw0 = i % ct.RW, lh0 = (i / ct.RW) % ct.RH, lt0 = i / (ct.RW * ct.RH);
+        atomicAdd(a.cnt + cell_index(a.g, bh, ot + lt0, oh + lh0, ow + lw0), c);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // 2. exclusive scan of the bucket counts: start[i] = sum_{j<i} cnt[j],
 //    start[n] = total. Three kernels: chunk sums, a one-block scan of the chunk
@@ -553,6 +612,27 @@ struct BwdLayout {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// The tiled count's histogram: the window's reach per axis plus up to 4 cells
+// of offset margin, as much as fits in the LDS histogram (none: the untiled
+// count kernel is used).
+bool count_tile(const dsa3d_desc& d, CountTile& ct) {
+    const int64_t reach_t = (int64_t)(d.kt - 1) / 2 * d.dil_t, reach_h = (int64_t)(d.kh - 1) / 2 * d.dil_h,
+                  reach_w = (int64_t)(d.kw - 1) / 2 * d.dil_w;
+    for (int extra = 4; extra >= 0; --extra) {
+        const int64_t mt = reach_t + extra, mh = reach_h + extra, mw = reach_w + extra;
+        const int64_t RT = kCtT + 2 * mt + 1, RH = kCtH + 2 * mh + 1, RW = kCtW + 2 * mw + 1;
+        if (RT * RH * RW <= kCountLdsCells) {
+            ct.mt = (int32_t)mt; ct.mh = (int32_t)mh; ct.mw = (int32_t)mw;
+            ct.RT = (int32_t)RT; ct.RH = (int32_t)RH; ct.RW = (int32_t)RW;
+            ct.ntt = (int32_t)((d.T + kCtT - 1) / kCtT);
+            ct.nth = (int32_t)((d.H + kCtH - 1) / kCtH);
+            ct.ntw = (int32_t)((d.W + kCtW - 1) / kCtW);
+            return true;
+        }
+    }
+    return false;
+}
+
 bool bwd_layout(const dsa3d_desc& d, int64_t nh, BwdLayout& L) {
     const uint64_t ntok = (uint64_t)(d.B * d.T * d.H * d.W);
     const uint64_t cells_per_bh = (uint64_t)(d.T + 1) * (uint64_t)(d.H + 1) * (uint64_t)(d.W + 1);
@@ -643,9 +723,16 @@ hipError_t launch_backward(const dsa3d_desc& d, const void* q, const void* k, co
         if ((e = fill_zero(large, 4, s)) != hipSuccess) return e;
         {
             LaunchScope ls(DSA3D_K_BWD_COUNT, s);
-            const unsigned gb = grid_for((int64_t)L.nsamp, 256, 1 << 16);
-            if (f32) hipLaunchKernelGGL(dsa3d_bwd_count_kernel<float>, dim3(gb), dim3(256), 0, s, a);
-            else hipLaunchKernelGGL(dsa3d_bwd_count_kernel<bf16_t>, dim3(gb), dim3(256), 0, s, a);
+            CountTile ct;
+            if (count_tile(d, ct)) {
+                const int64_t nb = (int64_t)d.B * nh * ct.ntt * ct.nth * ct.ntw;
+                if (f32) hipLaunchKernelGGL(dsa3d_bwd_count_tiled_kernel<float>, dim3((unsigned)nb), dim3(256), 0, s, a, ct);
+                else hipLaunchKernelGGL(dsa3d_bwd_count_tiled_kernel<bf16_t>, dim3((unsigned)nb), dim3(256), 0, s, a, ct);
+            } else {
+                const unsigned gb = grid_for((int64_t)L.nsamp, 256, 1 << 16);
+                if (f32) hipLaunchKernelGGL(dsa3d_bwd_count_kernel<float>, dim3(gb), dim3(256), 0, s, a);
+                else hipLaunchKernelGGL(dsa3d_bwd_count_kernel<bf16_t>, dim3(gb), dim3(256), 0, s, a);
+            }
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
         // 2. bucket starts; the counts become fill cursors
