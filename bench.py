@@ -10,11 +10,14 @@ included. Inputs are drawn on the GPU (seed 0) and are resident in HBM before
 the timed region starts. Prints one JSON line on stdout; progress goes to
 stderr.
 
-`roofline` is taken for the kernel with the largest share of the timed
-region, timed per launch with HIP events that libdsa3d records around each of
-its launches (dsa3d_set_launch_log) on the launch stream. Its achieved rate
-is the algorithmic bytes (each tensor read or written once; sampled K/V rows
-are never counted) of one launch over its mean launch duration.
+`roofline` is taken for the attention kernel with the largest share of the
+timed region, timed per launch with HIP events that libdsa3d records around
+each of its launches (dsa3d_set_launch_log) on the launch stream. That kernel
+is bound by vector-ALU work, so `roofline` is its algorithmic flops of one
+launch over its mean launch duration against the vector fp32 peak;
+`roofline_hbm` is the same launch's algorithmic bytes (each tensor read or
+written once; sampled K/V rows are never counted) against the HBM peak, and
+`roofline_step` the whole step's flops against the vector peak.
 
 `--copy-calibration` instead runs a plain device copy of a known size, whose
 rocprofv3 FETCH_SIZE / WRITE_SIZE readings scale the counters of the kernels.
@@ -33,7 +36,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
-VALU_F32_PEAK_TFLOPS = 157.3   # MI355X vector fp32, published (dual-issue/packed)
+VALU_F32_PEAK_TFLOPS = 157.3   # MI355X vector fp32: 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2 (packed) x 2.4 GHz
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
 METRIC = "3D-DSA fwd+bwd tokens/sec at 256×68×120 tokens; achieved HBM GB/s vs peak"
 
@@ -53,7 +56,10 @@ def algorithmic(wl):
     bwd_query: reads q, k, v, o, dO (5d), offsets (3P) and lse (4 B), writes
                dq (d) and doffsets (3P).
     bwd_key:   reads q and dO (2d), writes dk and dv (2d).
-    The whole backward is then 8d + 6P elements + 4 B, flops 80*d*P.
+    The whole backward is then 8d + 6P elements + 4 B, flops 80*d*P: per
+    sample 48*d in the query kernel (logit, <dO, V[c]> and the dq update over
+    8 corners) and 32*d in the key kernel (the dK and dV updates of 8 corners).
+    Keys "<kernel>_flops" give the flops per (token, head) of each kernel.
     """
     s = 4 if wl.dtype == "f32" else 2
     d, P = wl.head_dim, wl.P
@@ -71,6 +77,9 @@ def algorithmic(wl):
             "bwd_bytes": 8 * d * s + 8,
             "fwd_flops": 4 * d * P,
             "bwd_flops": 10 * d * P,
+            "forward_flops": 4 * d * P,
+            "bwd_query_flops": 6 * d * P,
+            "bwd_key_flops": 4 * d * P,
         }
     return {
         "forward": 4 * d * s + 3 * P * s + 4,
@@ -80,6 +89,9 @@ def algorithmic(wl):
         "bwd_bytes": 8 * d * s + 6 * P * s + 4,
         "fwd_flops": 32 * d * P,
         "bwd_flops": 80 * d * P,
+        "forward_flops": 32 * d * P,
+        "bwd_query_flops": 48 * d * P,
+        "bwd_key_flops": 32 * d * P,
     }
 
 
@@ -343,16 +355,23 @@ def main():
     if wl.dtype == "f32":
         kname = kname.replace("unsigned short", "float")
     traffic = recorded_traffic(kname, wl.name)
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved_gbs, 2), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 5),
+    unit_flops = alg[dom + "_flops"]
+    achieved_tf = unit_flops * units / mean_s / 1e12
+    roofline = {"bound": "alu", "kernel": dom, "achieved": round(achieved_tf, 3), "peak": VALU_F32_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved_tf / VALU_F32_PEAK_TFLOPS, 5),
                 "traffic": None if traffic is None else round(traffic),
                 "launch_ms": round(per_kernel[dom]["mean_ms"], 3), "units_per_launch": units,
-                "bytes_per_unit": unit_bytes}
+                "flops_per_unit": unit_flops}
+    roofline_hbm = {"bound": "hbm", "kernel": dom, "achieved": round(achieved_gbs, 2), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 5),
+                    "traffic": None if traffic is None else round(traffic),
+                    "launch_ms": round(per_kernel[dom]["mean_ms"], 3), "units_per_launch": units,
+                    "bytes_per_unit": unit_bytes}
     step_flops = wl.tokens * wl.heads * (alg["fwd_flops"] + (alg["bwd_flops"] if wl.backward else 0))
-    roofline_alu = {"bound": "alu", "scope": "whole step",
-                    "achieved": round(step_flops / (ms_per_step / 1e3) / 1e12, 3), "peak": VALU_F32_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(step_flops / (ms_per_step / 1e3) / 1e12 / VALU_F32_PEAK_TFLOPS, 5),
-                    "flops_per_token": step_flops // wl.tokens}
+    roofline_step = {"bound": "alu", "scope": "whole step",
+                     "achieved": round(step_flops / (ms_per_step / 1e3) / 1e12, 3), "peak": VALU_F32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(step_flops / (ms_per_step / 1e3) / 1e12 / VALU_F32_PEAK_TFLOPS, 5),
+                     "flops_per_token": step_flops // wl.tokens}
 
     # the projection GEMMs (workloads whose offsets come from the Linear): MFMA-bound
     roofline_proj = None
@@ -393,7 +412,7 @@ def main():
                    "window": list(wl.window), "P": wl.P, "dilation": list(wl.dilation), "offsets": wl.offsets,
                    "chain": {"proj": "proj+", "conv": "dwconv+proj+"}.get(wl.offsets, "") + ("fwd+bwd" if wl.backward else "fwd"),
                    "deterministic": wl.deterministic},
-        "roofline": roofline, "roofline_alu": roofline_alu,
+        "roofline": roofline, "roofline_hbm": roofline_hbm, "roofline_step": roofline_step,
         **({"roofline_proj": roofline_proj} if roofline_proj else {}),
         **({"roofline_conv": roofline_conv} if roofline_conv else {}),
         "kernels": {k: {"launches": v["launches"], "mean_ms": round(v["mean_ms"], 3)} for k, v in per_kernel.items()},
