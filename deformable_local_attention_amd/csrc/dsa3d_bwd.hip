@@ -569,6 +569,30 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_key_kernel(BwdArgs a) {
         }
         wave_lds_sync();
         uint32_t j = 0;
+        for (; j + 3 < n; j += 4) {
+            const float4 ea = ent[j], eb = ent[j + 1], ec = ent[j + 2], ed = ent[j + 3];
+            const uint64_t oa = ((uint64_t)__float_as_uint(ea.w) << 32) | __float_as_uint(ea.z);
+            const uint64_t ob = ((uint64_t)__float_as_uint(eb.w) << 32) | __float_as_uint(eb.z);
+            const uint64_t oc = ((uint64_t)__float_as_uint(ec.w) << 32) | __float_as_uint(ec.z);
+            const uint64_t od = ((uint64_t)__float_as_uint(ed.w) << 32) | __float_as_uint(ed.z);
+            Frag8<T> qa, ga, qb, gb, qc, gc, qd, gd;
+            qa.load(reinterpret_cast<const T*>(Qc + oa));
+            ga.load(reinterpret_cast<const T*>(Gc + oa));
+            qb.load(reinterpret_cast<const T*>(Qc + ob));
+            gb.load(reinterpret_cast<const T*>(Gc + ob));
+            qc.load(reinterpret_cast<const T*>(Qc + oc));
+            gc.load(reinterpret_cast<const T*>(Gc + oc));
+            qd.load(reinterpret_cast<const T*>(Qc + od));
+            gd.load(reinterpret_cast<const T*>(Gc + od));
+            qa.axpy(ea.x, ak);
+            ga.axpy(ea.y, av);
+            qb.axpy(eb.x, ak);
+            gb.axpy(eb.y, av);
+            qc.axpy(ec.x, ak);
+            gc.axpy(ec.y, av);
+            qd.axpy(ed.x, ak);
+            gd.axpy(ed.y, av);
+        }
         for (; j + 1 < n; j += 2) {  // two entries per step: four row loads in flight
             const float4 ea = ent[j], eb = ent[j + 1];
             const uint64_t oa = ((uint64_t)__float_as_uint(ea.w) << 32) | __float_as_uint(ea.z);
