@@ -18,6 +18,8 @@ launch over its mean launch duration against the vector fp32 peak;
 `roofline_hbm` is the same launch's algorithmic bytes (each tensor read or
 written once; sampled K/V rows are never counted) against the HBM peak, and
 `roofline_step` the whole step's flops against the vector peak.
+`roofline_gather` gives each attention kernel's gathered corner-row bytes
+against the vector-L1 load rate, the limit those kernels actually meet.
 
 `--copy-calibration` instead runs a plain device copy of a known size, whose
 rocprofv3 FETCH_SIZE / WRITE_SIZE readings scale the counters of the kernels.
@@ -38,6 +40,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 VALU_F32_PEAK_TFLOPS = 157.3   # MI355X vector fp32: 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2 (packed) x 2.4 GHz
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
+L1_LOAD_PEAK_TBS = 39.3        # vector L1 loads, measured: 64 B/clock/CU x 256 CUs x 2.4 GHz
 METRIC = "3D-DSA fwd+bwd tokens/sec at 256×68×120 tokens; achieved HBM GB/s vs peak"
 
 
@@ -373,6 +376,20 @@ def main():
                      "unit": "TFLOP/s", "frac": round(step_flops / (ms_per_step / 1e3) / 1e12 / VALU_F32_PEAK_TFLOPS, 5),
                      "flops_per_token": step_flops // wl.tokens}
 
+    # The gathers: every sample reads the head's rows of 8 corner tokens in two tensors (keys and values
+    # in the forward and the query kernel, queries and output gradients in the key kernel), 16*d*s*P bytes
+    # per (token, head), or 2*d*s*P for the fixed window. These pass through each CU's vector L1 and its
+    # texture-data path, which rocprofv3 shows 97-98% busy in all three kernels; the ceiling is the L1
+    # load rate measured with a probe kernel streaming 16-byte loads from an L1-resident buffer,
+    # 64 B per clock per CU (256 CUs at 2.4 GHz).
+    gather_unit = (2 if wl.offsets == "none" else 16) * wl.head_dim * (4 if wl.dtype == "f32" else 2) * wl.P
+    roofline_gather = {}
+    for k in attn:
+        u = wl.tokens * wl.heads * args.steps / per_kernel[k]["launches"]
+        tbs = gather_unit * u / (per_kernel[k]["mean_ms"] / 1e3) / 1e12
+        roofline_gather[k] = {"bound": "l1", "achieved": round(tbs, 2), "peak": L1_LOAD_PEAK_TBS, "unit": "TB/s",
+                              "frac": round(tbs / L1_LOAD_PEAK_TBS, 4), "bytes_per_unit": gather_unit}
+
     # the projection GEMMs (workloads whose offsets come from the Linear): MFMA-bound
     roofline_proj = None
     if wl.offsets in ("proj", "conv"):
@@ -413,6 +430,7 @@ def main():
                    "chain": {"proj": "proj+", "conv": "dwconv+proj+"}.get(wl.offsets, "") + ("fwd+bwd" if wl.backward else "fwd"),
                    "deterministic": wl.deterministic},
         "roofline": roofline, "roofline_hbm": roofline_hbm, "roofline_step": roofline_step,
+        "roofline_gather": roofline_gather,
         **({"roofline_proj": roofline_proj} if roofline_proj else {}),
         **({"roofline_conv": roofline_conv} if roofline_conv else {}),
         "kernels": {k: {"launches": v["launches"], "mean_ms": round(v["mean_ms"], 3)} for k, v in per_kernel.items()},
