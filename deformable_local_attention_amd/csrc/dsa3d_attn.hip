@@ -181,24 +181,20 @@ unsigned grid_for(int64_t n, int threads, int64_t cap) {
     return (unsigned)b;
 }
 
-BlockOrder make_block_order(const dsa3d_desc& d, int G) {
+BlockOrder make_block_order(const dsa3d_desc& d, int G, Supertile st, const char* tuning_env) {
     BlockOrder o;
     o.G = G;
     o.BW = (int32_t)((d.W + G - 1) / G);
-    // Supertile of (at most) 16 frames x 32 rows x 16 tokens, and the XCDs
-    // take one supertile each in turn: the eight supertiles in flight are
-    // neighbours, so the rows their samples gather are shared through the
-    // memory-side cache. Measured on the 256x68x120 grid (3x5x5 window,
-    // offsets N(0,2)) this order runs the step 15% faster than one contiguous
-    // range of 4 x 8 x 64 supertiles per XCD.
-    int st = 16, sh = 32, sw_tok = 16, chunk = -1;
+    int frames = st.frames, rows = st.rows, tokens = st.tokens, chunk = -1;
 #ifdef DSA3D_TUNING
-    // tuning builds only: DSA3D_ORDER="frames,rows,tokens,chunk"
-    if (const char* e = getenv("DSA3D_ORDER")) sscanf(e, "%d,%d,%d,%d", &st, &sh, &sw_tok, &chunk);
+    // tuning builds only: <tuning_env>="frames,rows,tokens,chunk"
+    if (const char* e = getenv(tuning_env)) sscanf(e, "%d,%d,%d,%d", &frames, &rows, &tokens, &chunk);
+#else
+    (void)tuning_env;
 #endif
-    o.ST = std::max(1, st);
-    o.SH = std::max(1, sh);
-    o.SW = std::max(1, sw_tok / G);
+    o.ST = std::max(1, frames);
+    o.SH = std::max(1, rows);
+    o.SW = std::max(1, tokens / G);
     o.chunk = chunk < 0 ? o.ST * o.SH * o.SW : chunk;
     o.nblk_bh = d.T * d.H * (int64_t)o.BW;
     return o;
@@ -226,7 +222,7 @@ hipError_t launch_forward(const dsa3d_desc& d, const void* q, const void* k, con
     a.P = d.P;
     a.scale = logit_scale(d);
     a.win = make_window(d);
-    a.ord = make_block_order(d, attn_tokens_per_block(d.head_dim));
+    a.ord = make_block_order(d, attn_tokens_per_block(d.head_dim), kGatherSupertile, "DSA3D_ORDER");
     const int64_t nb = a.ord.nblk_bh * d.B * d.heads;
     if (nb == 0) return hipSuccess;
     if (d.dtype == DSA3D_F32) { DSA3D_DISPATCH_D(d.head_dim, fwd_f32, a, nb, s); }

@@ -17,11 +17,13 @@
 //     slot of its bucket (one more atomic on the cursor);
 //  4. deterministic mode only: sort every bucket by sample number, so that the
 //     summation order below does not depend on the order the slots were taken;
-//  5. key kernel (one task = one (key token, head)): the samples whose cell
-//     has key y as corner c are exactly those with base cell y - c, so the key
-//     streams the records of the 8 buckets y - c and accumulates
+//  5. key kernel (one task = two neighbouring keys of one head): the samples
+//     whose cell has key y as corner c are exactly those with base cell
+//     y - c, so a key streams the records of the 8 buckets y - c and
+//     accumulates
 //        dK[y] += w_c * scale * ds_p * q_x,   dV[y] += w_c * a_p * dO_x
-//     in float32 registers, then writes its rows once.
+//     in float32 registers, then writes its rows once; two keys side by side
+//     along w share 4 of their buckets and read those records and rows once.
 // Base cells run over the grid extended by one cell on the low side of each
 // axis (a cell with base -1 still has its upper corner at 0), per (batch,
 // head). A pass covers a range of heads whose index fits in the workspace;
@@ -507,8 +509,20 @@ __global__ void __launch_bounds__(1024) dsa3d_sort_large_kernel(const uint32_t* 
 }
 
 // ---------------------------------------------------------------------------
-// 5. key kernel
+// 5. key kernel: one task = two keys side by side along w (w even, w + 1)
+//
+// Key y takes the records of the buckets of base cells y - c. For the pair
+// (w, w+1) those are the cells of the columns w-1, w and w+1 (two frames by
+// two rows each): column w-1 reaches only the left key, column w+1 only the
+// right key, and column w both, with the corner of its upper w side for the
+// right key and of its lower side for the left one. The pair walks these 12
+// buckets as one list (column, then frame, then row, then bucket order), so
+// the records of the shared column and their query and output-gradient rows
+// are read once for both keys; each entry updates both keys, a key that the
+// entry's cell does not reach taking a zero coefficient.
 // ---------------------------------------------------------------------------
+constexpr int kPairBuckets = 12;
+
 template <typename T, int D>
 __global__ void __launch_bounds__(256) dsa3d_bwd_key_kernel(BwdArgs a) {
     constexpr int L = D / 8;
@@ -517,111 +531,99 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_key_kernel(BwdArgs a) {
     int64_t bh;
     int32_t t, h, wb;
     block_coords(a.g, a.ord, logical_block(blockIdx.x, gridDim.x, a.ord.chunk), bh, t, h, wb);
-    const int32_t w = wb + g;
-    if (w >= a.g.W) return;
+    const int32_t w = wb + 2 * g;  // left key; the right key is w + 1
+    if (w >= a.g.W) return;        // no block-wide barrier below
+    const bool right = w + 1 < a.g.W;
     const int32_t b = (int32_t)(bh / a.g.nheads);
     const int32_t eta = a.g.head0 + (int32_t)(bh - (int64_t)b * a.g.nheads);
     const int64_t tok = (((int64_t)b * a.g.T + t) * a.g.H + h) * a.g.W + w;
     const int64_t C = (int64_t)a.g.heads * D;
     const int64_t row_off = (int64_t)eta * D + li * 8;
-    const T* Qb = reinterpret_cast<const T*>(a.q) + row_off;
-    const T* Gb = reinterpret_cast<const T*>(a.dout) + row_off;
     const uint4* rec = reinterpret_cast<const uint4*>(a.rec);
 
-    // The key's samples are the records of its 8 buckets (base cells y - c),
-    // taken in the fixed order c = 0..7 and bucket order, as one list of N
-    // entries. The group walks the list in chunks of L: each lane loads one
-    // record (the chunk's loads are coalesced), computes its corner weight and
-    // both coefficients and leaves them in LDS; then every lane reads each
-    // entry from there and adds its query and output-gradient rows.
-    uint32_t bs[8], cum[8];
+    // The pair's buckets: start and position in the joint list of N entries,
+    // kept in LDS (one lane per bucket writes them).
+    __shared__ uint32_t s_bs[256 / L][kPairBuckets], s_cum[256 / L][kPairBuckets];
+    __shared__ float4 s_coef[256];  // left (scale*ds*w, a*w), right (scale*ds*w, a*w)
+    __shared__ uint2 s_row[256];    // byte offset of the query's row
+    uint32_t* bs = s_bs[g];
+    uint32_t* cum = s_cum[g];
+    float4* coef = s_coef + (threadIdx.x - li);
+    uint2* row = s_row + (threadIdx.x - li);
     uint32_t N = 0;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const uint32_t cell = cell_index(a.g, bh, t - ((c >> 2) & 1), h - ((c >> 1) & 1), w - (c & 1));
-        bs[c] = a.start[cell];
-        cum[c] = N;
-        N += a.start[cell + 1] - bs[c];
+    for (int i = 0; i < kPairBuckets; ++i) {
+        const int j = i >> 2, ct = (i >> 1) & 1, ch = i & 1;
+        uint32_t s0 = 0u, n = 0u;
+        if (j < 2 || right) {  // column w+1 exists only with the right key
+            const uint32_t cell = cell_index(a.g, bh, t - ct, h - ch, w - 1 + j);
+            s0 = a.start[cell];
+            n = a.start[cell + 1] - s0;
+        }
+        if (li == 0) { bs[i] = s0; cum[i] = N; }
+        N += n;
     }
-    __shared__ float4 s_ent[256];  // scale*ds*w, a*w, row offset (lo, hi)
-    float4* ent = s_ent + (threadIdx.x - li);
-    const char* Qc = reinterpret_cast<const char*>(Qb);
-    const char* Gc = reinterpret_cast<const char*>(Gb);
-    float ak[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float av[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const char* Qc = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.q) + row_off);
+    const char* Gc = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.dout) + row_off);
+    float akl[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, avl[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float akr[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, avr[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (uint32_t k0 = 0; k0 < N; k0 += L) {
         const uint32_t n = min((uint32_t)L, N - k0);
-        wave_lds_sync();  // the previous chunk has been read
+        wave_lds_sync();  // the bucket table is written; the previous chunk has been read
         if ((uint32_t)li < n) {
             const uint32_t k = k0 + li;
-            int c = 0;
-            uint32_t e = bs[0] + k;
+            int i = 0;
 #pragma unroll
-            for (int cc = 1; cc < 8; ++cc) {  // the last bucket that starts at or before k holds it
-                if (k >= cum[cc]) { c = cc; e = bs[cc] + (k - cum[cc]); }
-            }
+            for (int ii = 1; ii < kPairBuckets; ++ii)  // the last bucket that starts at or before k holds it
+                if (k >= cum[ii]) i = ii;
+            const uint32_t e = bs[i] + (k - cum[i]);
             const uint4 r0 = rec[2 * (uint64_t)e], r1 = rec[2 * (uint64_t)e + 1];
             const float ft = __uint_as_float(r0.z), fh = __uint_as_float(r0.w), fw = __uint_as_float(r1.x);
-            const float wt = (((c >> 2) & 1) ? ft : 1.0f - ft) * (((c >> 1) & 1) ? fh : 1.0f - fh) *
-                             ((c & 1) ? fw : 1.0f - fw);
-            ent[li] = make_float4(__uint_as_float(r0.x) * wt, __uint_as_float(r0.y) * wt, __uint_as_float(r1.z),
-                                  __uint_as_float(r1.w));
+            const int j = i >> 2, ct = (i >> 1) & 1, ch = i & 1;
+            const float wth = (ct ? ft : 1.0f - ft) * (ch ? fh : 1.0f - fh);
+            // left key: corner w offset 1 - j (column w-1: upper side, column w: lower side)
+            const float wl = j == 0 ? wth * fw : j == 1 ? wth * (1.0f - fw) : 0.0f;
+            // right key: corner w offset 2 - j (column w: upper side, column w+1: lower side)
+            const float wr = j == 1 ? wth * fw : j == 2 ? wth * (1.0f - fw) : 0.0f;
+            const float ck = __uint_as_float(r0.x), cv = __uint_as_float(r0.y);
+            coef[li] = make_float4(ck * wl, cv * wl, ck * wr, cv * wr);
+            row[li] = make_uint2(r1.z, r1.w);
         }
         wave_lds_sync();
         uint32_t j = 0;
-        for (; j + 3 < n; j += 4) {
-            const float4 ea = ent[j], eb = ent[j + 1], ec = ent[j + 2], ed = ent[j + 3];
-            const uint64_t oa = ((uint64_t)__float_as_uint(ea.w) << 32) | __float_as_uint(ea.z);
-            const uint64_t ob = ((uint64_t)__float_as_uint(eb.w) << 32) | __float_as_uint(eb.z);
-            const uint64_t oc = ((uint64_t)__float_as_uint(ec.w) << 32) | __float_as_uint(ec.z);
-            const uint64_t od = ((uint64_t)__float_as_uint(ed.w) << 32) | __float_as_uint(ed.z);
-            Frag8<T> qa, ga, qb, gb, qc, gc, qd, gd;
-            qa.load(reinterpret_cast<const T*>(Qc + oa));
-            ga.load(reinterpret_cast<const T*>(Gc + oa));
-            qb.load(reinterpret_cast<const T*>(Qc + ob));
-            gb.load(reinterpret_cast<const T*>(Gc + ob));
-            qc.load(reinterpret_cast<const T*>(Qc + oc));
-            gc.load(reinterpret_cast<const T*>(Gc + oc));
-            qd.load(reinterpret_cast<const T*>(Qc + od));
-            gd.load(reinterpret_cast<const T*>(Gc + od));
-            qa.axpy(ea.x, ak);
-            ga.axpy(ea.y, av);
-            qb.axpy(eb.x, ak);
-            gb.axpy(eb.y, av);
-            qc.axpy(ec.x, ak);
-            gc.axpy(ec.y, av);
-            qd.axpy(ed.x, ak);
-            gd.axpy(ed.y, av);
-        }
         for (; j + 1 < n; j += 2) {  // two entries per step: four row loads in flight
-            const float4 ea = ent[j], eb = ent[j + 1];
-            const uint64_t oa = ((uint64_t)__float_as_uint(ea.w) << 32) | __float_as_uint(ea.z);
-            const uint64_t ob = ((uint64_t)__float_as_uint(eb.w) << 32) | __float_as_uint(eb.z);
+            const float4 ca = coef[j], cb = coef[j + 1];
+            const uint2 ra = row[j], rb = row[j + 1];
+            const uint64_t oa = ((uint64_t)ra.y << 32) | ra.x, ob = ((uint64_t)rb.y << 32) | rb.x;
             Frag8<T> qa, ga, qb, gb;
             qa.load(reinterpret_cast<const T*>(Qc + oa));
             ga.load(reinterpret_cast<const T*>(Gc + oa));
             qb.load(reinterpret_cast<const T*>(Qc + ob));
             gb.load(reinterpret_cast<const T*>(Gc + ob));
-            qa.axpy(ea.x, ak);
-            ga.axpy(ea.y, av);
-            qb.axpy(eb.x, ak);
-            gb.axpy(eb.y, av);
+            qa.axpy(ca.x, akl); ga.axpy(ca.y, avl); qa.axpy(ca.z, akr); ga.axpy(ca.w, avr);
+            qb.axpy(cb.x, akl); gb.axpy(cb.y, avl); qb.axpy(cb.z, akr); gb.axpy(cb.w, avr);
         }
         if (j < n) {
-            const float4 ea = ent[j];
-            const uint64_t oa = ((uint64_t)__float_as_uint(ea.w) << 32) | __float_as_uint(ea.z);
+            const float4 ca = coef[j];
+            const uint2 ra = row[j];
+            const uint64_t oa = ((uint64_t)ra.y << 32) | ra.x;
             Frag8<T> qa, ga;
             qa.load(reinterpret_cast<const T*>(Qc + oa));
             ga.load(reinterpret_cast<const T*>(Gc + oa));
-            qa.axpy(ea.x, ak);
-            ga.axpy(ea.y, av);
+            qa.axpy(ca.x, akl); ga.axpy(ca.y, avl); qa.axpy(ca.z, akr); ga.axpy(ca.w, avr);
         }
     }
-    Frag8<T> kf, vf;
-    kf.from_f32(ak);
-    vf.from_f32(av);
-    kf.store(reinterpret_cast<T*>(a.dk) + tok * C + row_off);
-    vf.store(reinterpret_cast<T*>(a.dv) + tok * C + row_off);
+    Frag8<T> f;
+    f.from_f32(akl);
+    f.store(reinterpret_cast<T*>(a.dk) + tok * C + row_off);
+    f.from_f32(avl);
+    f.store(reinterpret_cast<T*>(a.dv) + tok * C + row_off);
+    if (right) {
+        f.from_f32(akr);
+        f.store(reinterpret_cast<T*>(a.dk) + (tok + 1) * C + row_off);
+        f.from_f32(avr);
+        f.store(reinterpret_cast<T*>(a.dv) + (tok + 1) * C + row_off);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -719,7 +721,9 @@ hipError_t launch_backward(const dsa3d_desc& d, const void* q, const void* k, co
     const int64_t chunk = bwd_heads_per_pass(d, ws_bytes);
     if (chunk < 1) return hipErrorInvalidValue;
     const bool f32 = d.dtype == DSA3D_F32;
-    const BlockOrder ord = make_block_order(d, attn_tokens_per_block(d.head_dim));
+    const BlockOrder ord = make_block_order(d, attn_tokens_per_block(d.head_dim), kGatherSupertile, "DSA3D_ORDER_Q");
+    const BlockOrder kord = make_block_order(d, 2 * attn_tokens_per_block(d.head_dim), kKeySupertile,
+                                             "DSA3D_ORDER_KEY");
     hipError_t e;
     for (int64_t h0 = 0; h0 < d.heads; h0 += chunk) {
         const int32_t nh = (int32_t)std::min<int64_t>(chunk, d.heads - h0);
@@ -784,9 +788,11 @@ hipError_t launch_backward(const dsa3d_desc& d, const void* q, const void* k, co
                                (uint32_t)L.large_cap);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        // 5. dk, dv
-        if (f32) { DSA3D_DISPATCH_D_E(d.head_dim, bwd_key_f32, e, a, nblocks, s); }
-        else { DSA3D_DISPATCH_D_E(d.head_dim, bwd_key_bf16, e, a, nblocks, s); }
+        // 5. dk, dv (two keys per task)
+        a.ord = kord;
+        const int64_t kblocks = kord.nblk_bh * d.B * nh;
+        if (f32) { DSA3D_DISPATCH_D_E(d.head_dim, bwd_key_f32, e, a, kblocks, s); }
+        else { DSA3D_DISPATCH_D_E(d.head_dim, bwd_key_bf16, e, a, kblocks, s); }
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

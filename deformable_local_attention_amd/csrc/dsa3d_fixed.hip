@@ -230,7 +230,7 @@ FixedArgs fixed_args(const dsa3d_desc& d) {
     a.P = d.P;
     a.scale = logit_scale(d);
     a.win = make_window(d);
-    a.ord = make_block_order(d, attn_tokens_per_block(d.head_dim));
+    a.ord = make_block_order(d, attn_tokens_per_block(d.head_dim), kGatherSupertile, "DSA3D_ORDER_FIXED");
     return a;
 }
 

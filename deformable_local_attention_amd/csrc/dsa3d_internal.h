@@ -63,7 +63,23 @@ private:
 struct Window;
 struct TaskGrid;
 struct BlockOrder;
-BlockOrder make_block_order(const dsa3d_desc& d, int G);
+// Supertile of the attention kernels' block order: the XCDs take one
+// supertile of (at most) frames x rows x tokens each in turn, so the eight
+// supertiles in flight are neighbours and the rows their samples gather are
+// shared through the memory-side cache.
+struct Supertile {
+    int frames, rows, tokens;
+};
+// Forward, query and fixed-window kernels (one token per task). Measured on
+// the 256x68x120 grid (3x5x5 window, offsets N(0,2)): the step runs 15% faster
+// than with one contiguous range of 4 x 8 x 64 supertiles per XCD.
+constexpr Supertile kGatherSupertile = {16, 32, 16};
+// Key kernel (two tokens per task): deeper in t and shallower in h; on the
+// same grid 76 ms per 3-head pass against 91 ms with the 16 x 32 x 32 shape.
+constexpr Supertile kKeySupertile = {32, 16, 32};
+// Block order for tasks of G tokens along w; `tuning_env` names the variable
+// that overrides the supertile in tuning builds.
+BlockOrder make_block_order(const dsa3d_desc& d, int G, Supertile st, const char* tuning_env);
 int attn_tokens_per_block(int head_dim);
 Window make_window(const dsa3d_desc& d);
 TaskGrid make_task_grid(const dsa3d_desc& d, int32_t head0, int32_t nheads);
