@@ -441,8 +441,90 @@ struct GlobalRecSwap {
     }
 };
 
-// One wave per block; the block walks kSortBucketsPerBlock consecutive
-// buckets. A bucket of up to kWaveSortMax records is held in registers (lane
+// Buckets of 2 to kRankSortMax records (nearly all of them: a bucket holds P
+// records on average): one wave per block walks kSortBucketsPerBlock
+// consecutive buckets. Lane l holds records l and l + 64 in registers and puts
+// their sample numbers in LDS; the rank of a record is the number of sample
+// numbers in the bucket below its own (they are distinct), and each lane
+// writes its records to their ranks (all reads precede all writes, so the
+// permutation is done in place). The next bucket's records are requested
+// before the current bucket is ranked.
+constexpr uint32_t kRankSortMax = 128;
+
+struct RankPair {
+    uint4 a0, a1, b0, b1;  // records lane and lane + 64 (word 5 = a1.y / b1.y is the sample number)
+};
+
+__device__ __forceinline__ void rank_fetch(const uint4* grec, uint32_t s, uint32_t n, uint32_t lane, RankPair& r) {
+    if (n < 2 || n > kRankSortMax) return;
+    if (lane < n) {
+        r.a0 = grec[2 * ((uint64_t)s + lane)];
+        r.a1 = grec[2 * ((uint64_t)s + lane) + 1];
+    }
+    if (lane + 64 < n) {
+        r.b0 = grec[2 * ((uint64_t)s + lane + 64)];
+        r.b1 = grec[2 * ((uint64_t)s + lane + 64) + 1];
+    }
+}
+
+__global__ void __launch_bounds__(64) dsa3d_sort_rank_kernel(const uint32_t* start, uint32_t ncell, SampleRec* rec) {
+    __shared__ __attribute__((aligned(16))) uint32_t skey[kRankSortMax];
+    const uint32_t c0 = blockIdx.x * kSortBucketsPerBlock;
+    const uint32_t nb = min(ncell - c0, (uint32_t)kSortBucketsPerBlock);
+    uint4* grec = reinterpret_cast<uint4*>(rec);
+    const uint32_t lane = threadIdx.x;
+    // bucket starts of the block: lane l holds start[c0 + l], and one more at the end
+    const uint32_t my_start = lane <= nb ? start[c0 + lane] : 0u;
+    const uint32_t end_start = start[c0 + nb];
+    auto bucket = [&](uint32_t i, uint32_t& s0, uint32_t& n) {
+        s0 = (uint32_t)__shfl((int)my_start, (int)i, 64);
+        const uint32_t s1 = i + 1 < 64 ? (uint32_t)__shfl((int)my_start, (int)(i + 1), 64) : end_start;
+        n = (i + 1 == nb ? end_start : s1) - s0;
+    };
+    RankPair cur{}, nxt{};
+    uint32_t s, n;
+    bucket(0, s, n);
+    rank_fetch(grec, s, n, lane, cur);
+    for (uint32_t i = 0; i < nb; ++i) {
+        uint32_t sn = 0, nn = 0;
+        if (i + 1 < nb) {
+            bucket(i + 1, sn, nn);
+            rank_fetch(grec, sn, nn, lane, nxt);
+        }
+        if (n >= 2 && n <= kRankSortMax) {
+            const bool ha = lane < n, hb = lane + 64 < n;
+            // slots past the bucket hold the largest key, which no sample number reaches
+            skey[lane] = ha ? cur.a1.y : 0xffffffffu;
+            skey[lane + 64] = hb ? cur.b1.y : 0xffffffffu;
+            wave_lds_sync();
+            uint32_t ra = 0, rb = 0;
+            const uint4* k4 = reinterpret_cast<const uint4*>(skey);
+            for (uint32_t k = 0; k < (n + 3) / 4; ++k) {
+                const uint4 q = k4[k];
+                ra += (q.x < cur.a1.y ? 1u : 0u) + (q.y < cur.a1.y ? 1u : 0u) + (q.z < cur.a1.y ? 1u : 0u) +
+                      (q.w < cur.a1.y ? 1u : 0u);
+                rb += (q.x < cur.b1.y ? 1u : 0u) + (q.y < cur.b1.y ? 1u : 0u) + (q.z < cur.b1.y ? 1u : 0u) +
+                      (q.w < cur.b1.y ? 1u : 0u);
+            }
+            if (ha) {
+                grec[2 * ((uint64_t)s + ra)] = cur.a0;
+                grec[2 * ((uint64_t)s + ra) + 1] = cur.a1;
+            }
+            if (hb) {
+                grec[2 * ((uint64_t)s + rb)] = cur.b0;
+                grec[2 * ((uint64_t)s + rb) + 1] = cur.b1;
+            }
+            wave_lds_sync();  // every lane has read the keys before the next bucket writes them
+        }
+        cur = nxt;
+        s = sn;
+        n = nn;
+    }
+}
+
+// Buckets of kRankSortMax + 1 to kWaveSortMax records: one wave per block;
+// the block walks kSortBucketsPerBlock consecutive buckets (skipping the
+// smaller ones). A bucket is held in registers (lane
 // l holds records l, l+64, ...), its (sample number, position) keys are
 // sorted in LDS, and each lane then writes the records it holds straight to
 // their sorted positions (all reads precede all writes, so the permutation is
@@ -459,7 +541,7 @@ __global__ void __launch_bounds__(64) dsa3d_sort_small_kernel(const uint32_t* st
     const uint32_t lane = threadIdx.x;
     for (uint32_t c = c0; c < c1; ++c) {
         const uint32_t s = start[c], n = start[c + 1] - s;
-        if (n < 2) continue;
+        if (n <= kRankSortMax) continue;
         if (n > kWaveSortMax) {
             if (lane == 0) {
                 const uint32_t slot = atomicAdd(large, 1u);
@@ -782,6 +864,7 @@ hipError_t launch_backward(const dsa3d_desc& d, const void* q, const void* k, co
         if (d.deterministic) {
             LaunchScope ls(DSA3D_K_BWD_SORT, s);
             const unsigned nblk = (unsigned)((L.ncell + kSortBucketsPerBlock - 1) / kSortBucketsPerBlock);
+            hipLaunchKernelGGL(dsa3d_sort_rank_kernel, dim3(nblk), dim3(64), 0, s, a.start, ncell, a.rec);
             hipLaunchKernelGGL(dsa3d_sort_small_kernel, dim3(nblk), dim3(64), 0, s, a.start, ncell, a.rec, large,
                                (uint32_t)L.large_cap);
             hipLaunchKernelGGL(dsa3d_sort_large_kernel, dim3(256), dim3(1024), 0, s, a.start, a.rec, large,

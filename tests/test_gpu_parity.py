@@ -148,6 +148,38 @@ def test_every_sample_in_one_cell_deterministic():
     assert torch.equal(first[0], ch.dk) and torch.equal(first[1], ch.dv)
 
 
+def test_bucket_sizes_across_the_sort_paths():
+    """Buckets of chosen sizes on both sides of each sort path's limit (128
+    records: ranked by one wave; 512: bitonic network of one wave; beyond:
+    one block per bucket), in deterministic mode, against the oracle and
+    bitwise reproducible."""
+    wl = _wl("bucket-sizes", T=4, H=5, W=6, heads=1, d=32, window=(3, 3, 3), dtype="f32", det=True)
+    x = synth.make_inputs(wl, "cpu", seed=29)
+    sizes = [2, 64, 127, 128, 129, 200, 512, 513]
+    cells = [(0, 0, 0), (1, 1, 1), (2, 2, 2), (3, 3, 3), (0, 4, 5), (1, 0, 4), (2, 3, 1), (3, 1, 4)]
+    kt, kh, kw = wl.window
+    it, ih, iw = np.meshgrid(np.arange(kt), np.arange(kh), np.arange(kw), indexing="ij")
+    win = np.stack([it.ravel() - 1, ih.ravel() - 1, iw.ravel() - 1], 1)          # [P, 3]
+    grid = np.stack(np.meshgrid(np.arange(wl.T), np.arange(wl.H), np.arange(wl.W), indexing="ij"), -1)
+    ref = (grid[:, :, :, None, :] + win[None, None, None]).reshape(-1, 3)          # samples in flat order
+    off = x["offsets"][0, :, :, :, 0].reshape(-1, 3).numpy().copy()
+    s = 0
+    for n, cell in zip(sizes, cells):
+        for j in range(s, s + n):
+            frac = np.array([((j * 37 + a * 11) % 7 + 1) / 8.0 for a in range(3)])
+            off[j] = (np.array(cell) + frac - ref[j]).astype(np.float32)           # exact in f32
+        s += n
+    assert s <= len(off)
+    off[s:] = 1.0e6  # the other samples fall outside the grid: the buckets hold exactly these sizes
+    x["offsets"][0, :, :, :, 0] = torch.from_numpy(off).reshape(wl.T, wl.H, wl.W, wl.P, 3)
+    say(f"[bucket-sizes] {synth.describe(wl)}: buckets of {sizes} samples")
+    ch = _run_whole(wl, x, det=True)
+    first = [t.clone() for t in (ch.dk, ch.dv)]
+    ch.run()
+    torch.cuda.synchronize()
+    assert torch.equal(first[0], ch.dk) and torch.equal(first[1], ch.dv)
+
+
 def _check_geometry(wl, off_cpu):
     desc = dsa.desc_like(torch.empty((wl.B, wl.T, wl.H, wl.W, wl.heads, wl.head_dim), dtype=wl.torch_dtype),
                          wl.window, wl.dilation)
