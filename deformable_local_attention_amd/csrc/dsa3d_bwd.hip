@@ -33,7 +33,6 @@
 
 namespace dsa3d {
 
-constexpr uint32_t kNoSlot = 0xffffffffu;  // a sample with no corner in the grid
 constexpr int kScanThreads = 256;
 constexpr int kScanItems = 16;
 constexpr uint32_t kScanChunk = kScanThreads * kScanItems;
@@ -276,10 +275,11 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_query_kernel(BwdArgs a) {
     const float Dsum = group_sum<L>(gf.dot(of, 0.0f));
     const float lse = a.lse[tok * a.g.heads + eta];
 
-    // Chunks of L samples: each lane computes one sample's cell and takes its
-    // slot in the cell's bucket (so a chunk's atomics issue together), the
-    // group then works through the chunk sample by sample, and finally each
-    // lane writes its own sample's doffsets and record.
+    // Chunks of L samples: each lane computes one sample's cell and requests
+    // a slot in the cell's bucket (so a chunk's atomics issue together), the
+    // group then works through the chunk sample by sample while the slots
+    // return, and finally each lane writes its own sample's doffsets and
+    // record.
     __shared__ SampleGeo s_geo[256];
     __shared__ float4 s_out[256];   // scale*ds_p, a_p, doff_t, doff_h
     __shared__ float s_outw[256];   // doff_w
@@ -291,19 +291,19 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_query_kernel(BwdArgs a) {
     for (int p0 = 0; p0 < a.P; p0 += L) {
         const int n = min(L, a.P - p0);
         wave_lds_sync();  // the previous chunk has been read and flushed
+        bool has_rec = false;
+        uint32_t taken = 0u, b0 = 0u, b1 = 0u;  // cursor value taken, bucket start and end
         if (li < n) {
             SampleGeo sg;
             int32_t t0, h0, w0;
             sample_geo<T>(a.g, a.win, tok_b, t, h, w, p0 + li, offq + (p0 + li) * 3, sg, t0, h0, w0);
-            uint32_t slot = kNoSlot;
             if ((sg.valid & 0xffu) != 0u) {
                 const uint32_t cell = cell_index(a.g, bh, t0, h0, w0);
-                const uint32_t sl = a.start[cell] + atomicAdd(a.cnt + cell, 1u);
-                // the count kernel filed exactly these samples in these cells;
-                // the bound only keeps a write inside its bucket
-                if (sl < a.start[cell + 1]) slot = sl;
+                taken = atomicAdd(a.cnt + cell, 1u);
+                b0 = a.start[cell];
+                b1 = a.start[cell + 1];
+                has_rec = true;
             }
-            sg.extra = slot;
             geo[li] = sg;
         }
         wave_lds_sync();
@@ -368,8 +368,10 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_query_kernel(BwdArgs a) {
             store_scalar<T>(doffq + p * 3 + 1, ov.w);
             store_scalar<T>(doffq + p * 3 + 2, outw[li]);
             const SampleGeo& sg = geo[li];
-            if (sg.extra != kNoSlot) {
-                uint4* dst = reinterpret_cast<uint4*>(a.rec + sg.extra);
+            // the count kernel filed exactly these samples in these cells; the
+            // bound only keeps a write inside its bucket
+            if (has_rec && b0 + taken < b1) {
+                uint4* dst = reinterpret_cast<uint4*>(a.rec + (b0 + taken));
                 dst[0] = make_uint4(__float_as_uint(ov.x), __float_as_uint(ov.y), __float_as_uint(sg.ft),
                                     __float_as_uint(sg.fh));
                 dst[1] = make_uint4(__float_as_uint(sg.fw), sid0 + (uint32_t)p, (uint32_t)qrow_bytes,
