@@ -17,13 +17,13 @@
 //     slot of its bucket (one more atomic on the cursor);
 //  4. deterministic mode only: sort every bucket by sample number, so that the
 //     summation order below does not depend on the order the slots were taken;
-//  5. key kernel (one task = two neighbouring keys of one head): the samples
-//     whose cell has key y as corner c are exactly those with base cell
-//     y - c, so a key streams the records of the 8 buckets y - c and
-//     accumulates
+//  5. key kernel (one task = a 2 x 2 group of keys of one head, in t and w):
+//     the samples whose cell has key y as corner c are exactly those with
+//     base cell y - c, so a key streams the records of the 8 buckets y - c
+//     and accumulates
 //        dK[y] += w_c * scale * ds_p * q_x,   dV[y] += w_c * a_p * dO_x
-//     in float32 registers, then writes its rows once; two keys side by side
-//     along w share 4 of their buckets and read those records and rows once.
+//     in float32 registers, then writes its rows once; the four keys of a
+//     group share buckets and read each shared record and row once.
 // Base cells run over the grid extended by one cell on the low side of each
 // axis (a cell with base -1 still has its upper corner at 0), per (batch,
 // head). A pass covers a range of heads whose index fits in the workspace;
@@ -593,19 +593,21 @@ __global__ void __launch_bounds__(1024) dsa3d_sort_large_kernel(const uint32_t* 
 }
 
 // ---------------------------------------------------------------------------
-// 5. key kernel: one task = two keys side by side along w (w even, w + 1)
+// 5. key kernel: one task = four keys, two frames by two tokens along w
+//    ((t, w), (t, w+1), (t+1, w), (t+1, w+1), with t and w even)
 //
-// Key y takes the records of the buckets of base cells y - c. For the pair
-// (w, w+1) those are the cells of the columns w-1, w and w+1 (two frames by
-// two rows each): column w-1 reaches only the left key, column w+1 only the
-// right key, and column w both, with the corner of its upper w side for the
-// right key and of its lower side for the left one. The pair walks these 12
-// buckets as one list (column, then frame, then row, then bucket order), so
-// the records of the shared column and their query and output-gradient rows
-// are read once for both keys; each entry updates both keys, a key that the
-// entry's cell does not reach taking a zero coefficient.
+// Key y takes the records of the buckets of base cells y - c. For the group
+// those are the cells of frames t-1 .. t+1, rows h-1 and h, and columns
+// w-1 .. w+1: 18 buckets, against 32 for four keys taken one by one. A cell
+// reaches the keys whose offset from it is a corner (0 or 1 on each axis):
+// frame t-1 only the keys of frame t, frame t+1 only those of frame t+1, and
+// frame t both; likewise along w. The group walks its 18 buckets as one list
+// (frame, then row, then column, then bucket order), so each record and its
+// query and output-gradient rows are read once for every key they reach; each
+// entry updates all four keys, a key the entry's cell does not reach taking a
+// zero coefficient.
 // ---------------------------------------------------------------------------
-constexpr int kPairBuckets = 12;
+constexpr int kQuadBuckets = 18;
 
 template <typename T, int D>
 __global__ void __launch_bounds__(256) dsa3d_bwd_key_kernel(BwdArgs a) {
@@ -613,11 +615,14 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_key_kernel(BwdArgs a) {
     const int g = threadIdx.x / L;
     const int li = threadIdx.x % L;
     int64_t bh;
-    int32_t t, h, wb;
-    block_coords(a.g, a.ord, logical_block(blockIdx.x, gridDim.x, a.ord.chunk), bh, t, h, wb);
-    const int32_t w = wb + 2 * g;  // left key; the right key is w + 1
-    if (w >= a.g.W) return;        // no block-wide barrier below
-    const bool right = w + 1 < a.g.W;
+    int32_t tp, h, wb;
+    TaskGrid gp = a.g;
+    gp.T = (a.g.T + 1) / 2;  // the block order walks pairs of frames
+    block_coords(gp, a.ord, logical_block(blockIdx.x, gridDim.x, a.ord.chunk), bh, tp, h, wb);
+    const int32_t t = 2 * tp;
+    const int32_t w = wb + 2 * g;
+    if (w >= a.g.W) return;  // no block-wide barrier below
+    const bool right = w + 1 < a.g.W, late = t + 1 < a.g.T;  // the group's second token along w / in t exists
     const int32_t b = (int32_t)(bh / a.g.nheads);
     const int32_t eta = a.g.head0 + (int32_t)(bh - (int64_t)b * a.g.nheads);
     const int64_t tok = (((int64_t)b * a.g.T + t) * a.g.H + h) * a.g.W + w;
@@ -625,22 +630,22 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_key_kernel(BwdArgs a) {
     const int64_t row_off = (int64_t)eta * D + li * 8;
     const uint4* rec = reinterpret_cast<const uint4*>(a.rec);
 
-    // The pair's buckets: start and position in the joint list of N entries,
+    // The group's buckets: start and position in the joint list of N entries,
     // kept in LDS (one lane per bucket writes them).
-    __shared__ uint32_t s_bs[256 / L][kPairBuckets], s_cum[256 / L][kPairBuckets];
-    __shared__ float4 s_coef[256];  // left (scale*ds*w, a*w), right (scale*ds*w, a*w)
-    __shared__ uint2 s_row[256];    // byte offset of the query's row
+    __shared__ uint32_t s_bs[256 / L][kQuadBuckets], s_cum[256 / L][kQuadBuckets];
+    __shared__ float4 s_coef[256][2];  // keys (t, w), (t, w+1) | (t+1, w), (t+1, w+1): (scale*ds*w, a*w) each
+    __shared__ uint2 s_row[256];     // byte offset of the query's row
     uint32_t* bs = s_bs[g];
     uint32_t* cum = s_cum[g];
-    float4* coef = s_coef + (threadIdx.x - li);
+    float4 (*coef)[2] = s_coef + (threadIdx.x - li);
     uint2* row = s_row + (threadIdx.x - li);
     uint32_t N = 0;
 #pragma unroll
-    for (int i = 0; i < kPairBuckets; ++i) {
-        const int j = i >> 2, ct = (i >> 1) & 1, ch = i & 1;
+    for (int i = 0; i < kQuadBuckets; ++i) {
+        const int it = i / 6, ch = (i / 3) & 1, j = i % 3;  // cell frame t-1+it, row h-ch, column w-1+j
         uint32_t s0 = 0u, n = 0u;
-        if (j < 2 || right) {  // column w+1 exists only with the right key
-            const uint32_t cell = cell_index(a.g, bh, t - ct, h - ch, w - 1 + j);
+        if ((it < 2 || late) && (j < 2 || right)) {
+            const uint32_t cell = cell_index(a.g, bh, t - 1 + it, h - ch, w - 1 + j);
             s0 = a.start[cell];
             n = a.start[cell + 1] - s0;
         }
@@ -649,8 +654,11 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_key_kernel(BwdArgs a) {
     }
     const char* Qc = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.q) + row_off);
     const char* Gc = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.dout) + row_off);
-    float akl[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, avl[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float akr[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, avr[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float ak[4][8], av[4][8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { ak[k][e] = 0.f; av[k][e] = 0.f; }
     for (uint32_t k0 = 0; k0 < N; k0 += L) {
         const uint32_t n = min((uint32_t)L, N - k0);
         wave_lds_sync();  // the bucket table is written; the previous chunk has been read
@@ -658,25 +666,32 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_key_kernel(BwdArgs a) {
             const uint32_t k = k0 + li;
             int i = 0;
 #pragma unroll
-            for (int ii = 1; ii < kPairBuckets; ++ii)  // the last bucket that starts at or before k holds it
+            for (int ii = 1; ii < kQuadBuckets; ++ii)  // the last bucket that starts at or before k holds it
                 if (k >= cum[ii]) i = ii;
             const uint32_t e = bs[i] + (k - cum[i]);
             const uint4 r0 = rec[2 * (uint64_t)e], r1 = rec[2 * (uint64_t)e + 1];
             const float ft = __uint_as_float(r0.z), fh = __uint_as_float(r0.w), fw = __uint_as_float(r1.x);
-            const int j = i >> 2, ct = (i >> 1) & 1, ch = i & 1;
-            const float wth = (ct ? ft : 1.0f - ft) * (ch ? fh : 1.0f - fh);
-            // left key: corner w offset 1 - j (column w-1: upper side, column w: lower side)
-            const float wl = j == 0 ? wth * fw : j == 1 ? wth * (1.0f - fw) : 0.0f;
-            // right key: corner w offset 2 - j (column w: upper side, column w+1: lower side)
-            const float wr = j == 1 ? wth * fw : j == 2 ? wth * (1.0f - fw) : 0.0f;
+            const int it = i / 6, ch = (i / 3) & 1, j = i % 3;
             const float ck = __uint_as_float(r0.x), cv = __uint_as_float(r0.y);
-            coef[li] = make_float4(ck * wl, cv * wl, ck * wr, cv * wr);
+            float c8[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {  // key (t + dt, w + dw): corner (dt + 1 - it, ch, dw + 1 - j)
+                const int dt = q >> 1, dw = q & 1;
+                const int ct = dt + 1 - it, cw = dw + 1 - j;
+                float wt = 0.0f;
+                if (ct >= 0 && ct <= 1 && cw >= 0 && cw <= 1)
+                    wt = ((ct ? ft : 1.0f - ft) * (ch ? fh : 1.0f - fh)) * (cw ? fw : 1.0f - fw);
+                c8[2 * q] = ck * wt;
+                c8[2 * q + 1] = cv * wt;
+            }
+            coef[li][0] = make_float4(c8[0], c8[1], c8[2], c8[3]);
+            coef[li][1] = make_float4(c8[4], c8[5], c8[6], c8[7]);
             row[li] = make_uint2(r1.z, r1.w);
         }
         wave_lds_sync();
         uint32_t j = 0;
         for (; j + 1 < n; j += 2) {  // two entries per step: four row loads in flight
-            const float4 ca = coef[j], cb = coef[j + 1];
+            const float4 ca0 = coef[j][0], ca1 = coef[j][1], cb0 = coef[j + 1][0], cb1 = coef[j + 1][1];
             const uint2 ra = row[j], rb = row[j + 1];
             const uint64_t oa = ((uint64_t)ra.y << 32) | ra.x, ob = ((uint64_t)rb.y << 32) | rb.x;
             Frag8<T> qa, ga, qb, gb;
@@ -684,29 +699,33 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_key_kernel(BwdArgs a) {
             ga.load(reinterpret_cast<const T*>(Gc + oa));
             qb.load(reinterpret_cast<const T*>(Qc + ob));
             gb.load(reinterpret_cast<const T*>(Gc + ob));
-            qa.axpy(ca.x, akl); ga.axpy(ca.y, avl); qa.axpy(ca.z, akr); ga.axpy(ca.w, avr);
-            qb.axpy(cb.x, akl); gb.axpy(cb.y, avl); qb.axpy(cb.z, akr); gb.axpy(cb.w, avr);
+            qa.axpy(ca0.x, ak[0]); ga.axpy(ca0.y, av[0]); qa.axpy(ca0.z, ak[1]); ga.axpy(ca0.w, av[1]);
+            qa.axpy(ca1.x, ak[2]); ga.axpy(ca1.y, av[2]); qa.axpy(ca1.z, ak[3]); ga.axpy(ca1.w, av[3]);
+            qb.axpy(cb0.x, ak[0]); gb.axpy(cb0.y, av[0]); qb.axpy(cb0.z, ak[1]); gb.axpy(cb0.w, av[1]);
+            qb.axpy(cb1.x, ak[2]); gb.axpy(cb1.y, av[2]); qb.axpy(cb1.z, ak[3]); gb.axpy(cb1.w, av[3]);
         }
         if (j < n) {
-            const float4 ca = coef[j];
+            const float4 ca0 = coef[j][0], ca1 = coef[j][1];
             const uint2 ra = row[j];
             const uint64_t oa = ((uint64_t)ra.y << 32) | ra.x;
             Frag8<T> qa, ga;
             qa.load(reinterpret_cast<const T*>(Qc + oa));
             ga.load(reinterpret_cast<const T*>(Gc + oa));
-            qa.axpy(ca.x, akl); ga.axpy(ca.y, avl); qa.axpy(ca.z, akr); ga.axpy(ca.w, avr);
+            qa.axpy(ca0.x, ak[0]); ga.axpy(ca0.y, av[0]); qa.axpy(ca0.z, ak[1]); ga.axpy(ca0.w, av[1]);
+            qa.axpy(ca1.x, ak[2]); ga.axpy(ca1.y, av[2]); qa.axpy(ca1.z, ak[3]); ga.axpy(ca1.w, av[3]);
         }
     }
+    const int64_t HW = (int64_t)a.g.H * a.g.W;
     Frag8<T> f;
-    f.from_f32(akl);
-    f.store(reinterpret_cast<T*>(a.dk) + tok * C + row_off);
-    f.from_f32(avl);
-    f.store(reinterpret_cast<T*>(a.dv) + tok * C + row_off);
-    if (right) {
-        f.from_f32(akr);
-        f.store(reinterpret_cast<T*>(a.dk) + (tok + 1) * C + row_off);
-        f.from_f32(avr);
-        f.store(reinterpret_cast<T*>(a.dv) + (tok + 1) * C + row_off);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int dt = q >> 1, dw = q & 1;
+        if ((dt && !late) || (dw && !right)) continue;
+        const int64_t tq = tok + dt * HW + dw;
+        f.from_f32(ak[q]);
+        f.store(reinterpret_cast<T*>(a.dk) + tq * C + row_off);
+        f.from_f32(av[q]);
+        f.store(reinterpret_cast<T*>(a.dv) + tq * C + row_off);
     }
 }
 
@@ -806,7 +825,9 @@ hipError_t launch_backward(const dsa3d_desc& d, const void* q, const void* k, co
     if (chunk < 1) return hipErrorInvalidValue;
     const bool f32 = d.dtype == DSA3D_F32;
     const BlockOrder ord = make_block_order(d, attn_tokens_per_block(d.head_dim), kGatherSupertile, "DSA3D_ORDER_Q");
-    const BlockOrder kord = make_block_order(d, 2 * attn_tokens_per_block(d.head_dim), kKeySupertile,
+    dsa3d_desc dpair = d;
+    dpair.T = (d.T + 1) / 2;
+    const BlockOrder kord = make_block_order(dpair, 2 * attn_tokens_per_block(d.head_dim), kKeySupertile,
                                              "DSA3D_ORDER_KEY");
     hipError_t e;
     for (int64_t h0 = 0; h0 < d.heads; h0 += chunk) {

@@ -74,9 +74,11 @@ struct Supertile {
 // the 256x68x120 grid (3x5x5 window, offsets N(0,2)): the step runs 15% faster
 // than with one contiguous range of 4 x 8 x 64 supertiles per XCD.
 constexpr Supertile kGatherSupertile = {16, 32, 16};
-// Key kernel (two tokens per task): deeper in t and shallower in h; on the
-// same grid 76 ms per 3-head pass against 91 ms with the 16 x 32 x 32 shape.
-constexpr Supertile kKeySupertile = {32, 16, 32};
+// Key kernel (tasks of 2 frames x 2 tokens; its frames count pairs of frames):
+// 32 frames x 16 rows x 32 tokens, deeper in t and shallower in h than the
+// others; on the same grid 72 ms per 3-head pass, against 76 ms with tasks of
+// one frame and 91 ms with those at 16 x 32 x 32.
+constexpr Supertile kKeySupertile = {16, 16, 32};
 // Block order for tasks of G tokens along w; `tuning_env` names the variable
 // that overrides the supertile in tuning builds.
 BlockOrder make_block_order(const dsa3d_desc& d, int G, Supertile st, const char* tuning_env);
