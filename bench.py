@@ -376,15 +376,19 @@ def main():
                      "unit": "TFLOP/s", "frac": round(step_flops / (ms_per_step / 1e3) / 1e12 / VALU_F32_PEAK_TFLOPS, 5),
                      "flops_per_token": step_flops // wl.tokens}
 
-    # The gathers: every sample reads the head's rows of 8 corner tokens in two tensors (keys and values
-    # in the forward and the query kernel, queries and output gradients in the key kernel), 16*d*s*P bytes
-    # per (token, head), or 2*d*s*P for the fixed window. These pass through each CU's vector L1 and its
-    # texture-data path, which rocprofv3 shows 97-98% busy in all three kernels; the ceiling is the L1
+    # The gathers: in the forward and the query kernel every sample reads the head's rows of its 8 corner
+    # tokens in two tensors (keys and values), 16*d*s*P bytes per (token, head). The key kernel reads the
+    # query and output-gradient rows of each record once per 2x2 group of keys it reaches, 4.5 groups per
+    # sample on average (18 buckets per group of 4 keys instead of 8 per key): 9*d*s*P. The fixed window
+    # reads 2 rows per sample in every kernel. These bytes pass through each CU's vector L1 and its
+    # texture-data path, which rocprofv3 shows 98-99% busy in all three kernels; the ceiling is the L1
     # load rate measured with a probe kernel streaming 16-byte loads from an L1-resident buffer,
     # 64 B per clock per CU (256 CUs at 2.4 GHz).
-    gather_unit = (2 if wl.offsets == "none" else 16) * wl.head_dim * (4 if wl.dtype == "f32" else 2) * wl.P
+    s_el = 4 if wl.dtype == "f32" else 2
+    rows_per_sample = {"forward": 16, "bwd_query": 16, "bwd_key": 9}
     roofline_gather = {}
     for k in attn:
+        gather_unit = (2 if wl.offsets == "none" else rows_per_sample[k]) * wl.head_dim * s_el * wl.P
         u = wl.tokens * wl.heads * args.steps / per_kernel[k]["launches"]
         tbs = gather_unit * u / (per_kernel[k]["mean_ms"] / 1e3) / 1e12
         roofline_gather[k] = {"bound": "l1", "achieved": round(tbs, 2), "peak": L1_LOAD_PEAK_TBS, "unit": "TB/s",
