@@ -380,7 +380,8 @@ def main():
     # tokens in two tensors (keys and values), 16*d*s*P bytes per (token, head). The key kernel reads the
     # query and output-gradient rows of each record once per 2x2 group of keys it reaches, 4.5 groups per
     # sample on average (18 buckets per group of 4 keys instead of 8 per key): 9*d*s*P. The fixed window
-    # reads 2 rows per sample in every kernel. These bytes pass through each CU's vector L1 and its
+    # reads 2 rows per window column, shared by the 4 tokens of a task along w when w is not dilated:
+    # 2 * (4 + k_w - 1) / (4 * k_w) rows per sample. These bytes pass through each CU's vector L1 and its
     # texture-data path, which rocprofv3 shows 98-99% busy in all three kernels; the ceiling is the L1
     # load rate measured with a probe kernel streaming 16-byte loads from an L1-resident buffer,
     # 64 B per clock per CU (256 CUs at 2.4 GHz).
@@ -388,7 +389,12 @@ def main():
     rows_per_sample = {"forward": 16, "bwd_query": 16, "bwd_key": 9}
     roofline_gather = {}
     for k in attn:
-        gather_unit = (2 if wl.offsets == "none" else rows_per_sample[k]) * wl.head_dim * s_el * wl.P
+        if wl.offsets == "none":
+            kw = wl.window[2]
+            rows = 2.0 * (4 + kw - 1) / (4 * kw) if wl.dilation[2] == 1 else 2.0
+        else:
+            rows = rows_per_sample[k]
+        gather_unit = rows * wl.head_dim * s_el * wl.P
         u = wl.tokens * wl.heads * args.steps / per_kernel[k]["launches"]
         tbs = gather_unit * u / (per_kernel[k]["mean_ms"] / 1e3) / 1e12
         roofline_gather[k] = {"bound": "l1", "achieved": round(tbs, 2), "peak": L1_LOAD_PEAK_TBS, "unit": "TB/s",
