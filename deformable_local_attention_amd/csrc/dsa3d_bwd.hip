@@ -5,8 +5,9 @@
 // cell. Pushing those corner contributions with atomics costs 16*head_dim
 // atomic adds per sample; instead the backward pulls them per key:
 //
-//  1. count kernel: the base cell floor(pos) of every sample (geometry only)
-//     and one 32-bit atomic increment of that cell's bucket count;
+//  1. count kernel: the base cell floor(pos) of every sample (geometry only),
+//     counted per tile of tokens in an LDS histogram whose non-zero cells are
+//     then added to the buckets' 32-bit counts;
 //  2. an exclusive scan turns the counts into bucket starts (the counts are
 //     then cleared to serve as fill cursors);
 //  3. query kernel (one task = one (query, head), as in the forward):
@@ -16,7 +17,9 @@
 //     the fraction f, the query token, the sample number) straight into a free
 //     slot of its bucket (one more atomic on the cursor);
 //  4. deterministic mode only: sort every bucket by sample number, so that the
-//     summation order below does not depend on the order the slots were taken;
+//     summation order below does not depend on the order the slots were taken
+//     (a bucket holds P records on average; one wave ranks a bucket of up to
+//     128 in registers);
 //  5. key kernel (one task = a 2 x 2 group of keys of one head, in t and w):
 //     the samples whose cell has key y as corner c are exactly those with
 //     base cell y - c, so a key streams the records of the 8 buckets y - c
