@@ -167,17 +167,26 @@ def cpu_baseline(wl, budget_s: float = 20.0):
 ATTN_SOURCES = ("dsa3d_attn.hip", "dsa3d_bwd.hip", "dsa3d_attn_common.h", "dsa3d_device.h")
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the attention kernels' sources: counter readings taken on
-    other sources no longer describe the kernels."""
+def code_text(src: str) -> str:
+    """A source's code without its comments and with whitespace collapsed."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
+def kernel_source_hash(read=None) -> str:
+    """sha256 over the attention kernels' code (comments and layout do not
+    count): counter readings taken on other code no longer describe the
+    kernels."""
     import hashlib
     pkg = os.path.join(ROOT, "deformable_local_attention_amd", "csrc")
-    files = [os.path.join(pkg, f) for f in ATTN_SOURCES]
+    if read is None:
+        read = lambda name: open(os.path.join(pkg, name)).read()
     h = hashlib.sha256()
-    for f in files:
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+    for f in ATTN_SOURCES:
+        h.update(f.encode())
+        h.update(code_text(read(f)).encode())
     return h.hexdigest()[:16]
 
 
