@@ -617,11 +617,15 @@ constexpr int kQuadBuckets = 18;
 template <int N>
 using IntC = std::integral_constant<int, N>;
 
-// bf16 rows of 64 channels or more: at most 128 registers, so that four waves
-// share each SIMD (65 ms per 3-head pass at 1080p against 69 ms with the 138
-// the compiler takes unbounded); the other instantiations are left unbounded.
+// Rows of 128 channels or more take four entries per step (eight row loads in
+// flight) at three waves per SIMD: a 3-head pass at 1080p runs in 60 ms, against
+// 65 ms with two entries at four waves and 67 ms with eight at two. Narrower
+// rows take two entries per step, bf16 rows of 64 channels at four waves (the
+// 720p pass: 8.5 ms, against 9.1 ms with four entries and 11.9 ms at two waves).
+template <int D>
+constexpr int key_entries_per_step() { return D >= 128 ? 4 : 2; }
 template <typename T, int D>
-constexpr int key_kernel_waves() { return std::is_same<T, bf16_t>::value && D >= 64 ? 4 : 1; }
+constexpr int key_kernel_waves() { return D >= 128 ? 3 : std::is_same<T, bf16_t>::value && D == 64 ? 4 : 1; }
 
 template <typename T, int D>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(key_kernel_waves<T, D>())))
@@ -722,6 +726,24 @@ dsa3d_bwd_key_kernel(BwdArgs a) {
                 }
             };
             uint32_t j = 0;
+            for (; key_entries_per_step<D>() == 4 && j + 3 < n; j += 4) {  // eight row loads in flight
+                const uint2 ra = row[j], rb = row[j + 1], rc = row[j + 2], rd = row[j + 3];
+                const uint64_t oa = ((uint64_t)ra.y << 32) | ra.x, ob = ((uint64_t)rb.y << 32) | rb.x;
+                const uint64_t oc = ((uint64_t)rc.y << 32) | rc.x, od = ((uint64_t)rd.y << 32) | rd.x;
+                Frag8<T> qa, ga, qb, gb, qc, gc, qd, gd;
+                qa.load(reinterpret_cast<const T*>(Qc + oa));
+                ga.load(reinterpret_cast<const T*>(Gc + oa));
+                qb.load(reinterpret_cast<const T*>(Qc + ob));
+                gb.load(reinterpret_cast<const T*>(Gc + ob));
+                qc.load(reinterpret_cast<const T*>(Qc + oc));
+                gc.load(reinterpret_cast<const T*>(Gc + oc));
+                qd.load(reinterpret_cast<const T*>(Qc + od));
+                gd.load(reinterpret_cast<const T*>(Gc + od));
+                add(qa, ga, coef[j][0], coef[j][1]);
+                add(qb, gb, coef[j + 1][0], coef[j + 1][1]);
+                add(qc, gc, coef[j + 2][0], coef[j + 2][1]);
+                add(qd, gd, coef[j + 3][0], coef[j + 3][1]);
+            }
             for (; j + 1 < n; j += 2) {  // two entries per step: four row loads in flight
                 const uint2 ra = row[j], rb = row[j + 1];
                 const uint64_t oa = ((uint64_t)ra.y << 32) | ra.x, ob = ((uint64_t)rb.y << 32) | rb.x;
