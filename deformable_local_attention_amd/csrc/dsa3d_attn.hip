@@ -192,6 +192,10 @@ BlockOrder make_block_order(const dsa3d_desc& d, int G, Supertile st, const char
 #else
     (void)tuning_env;
 #endif
+    if (rows < 0) {  // bands of about -rows rows, of equal height
+        const int64_t bands = std::max<int64_t>(1, (d.H + (-rows) / 2) / (-rows));
+        rows = (int)((d.H + bands - 1) / bands);
+    }
     o.ST = std::max(1, frames);
     o.SH = std::max(1, rows);
     o.SW = std::max(1, tokens / G);
@@ -222,7 +226,7 @@ hipError_t launch_forward(const dsa3d_desc& d, const void* q, const void* k, con
     a.P = d.P;
     a.scale = logit_scale(d);
     a.win = make_window(d);
-    a.ord = make_block_order(d, attn_tokens_per_block(d.head_dim), kGatherSupertile, "DSA3D_ORDER");
+    a.ord = make_block_order(d, attn_tokens_per_block(d.head_dim), kForwardSupertile, "DSA3D_ORDER");
     const int64_t nb = a.ord.nblk_bh * d.B * d.heads;
     if (nb == 0) return hipSuccess;
     if (d.dtype == DSA3D_F32) { DSA3D_DISPATCH_D(d.head_dim, fwd_f32, a, nb, s); }

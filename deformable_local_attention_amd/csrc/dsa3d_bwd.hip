@@ -878,7 +878,7 @@ hipError_t launch_backward(const dsa3d_desc& d, const void* q, const void* k, co
     const int64_t chunk = bwd_heads_per_pass(d, ws_bytes);
     if (chunk < 1) return hipErrorInvalidValue;
     const bool f32 = d.dtype == DSA3D_F32;
-    const BlockOrder ord = make_block_order(d, attn_tokens_per_block(d.head_dim), kGatherSupertile, "DSA3D_ORDER_Q");
+    const BlockOrder ord = make_block_order(d, attn_tokens_per_block(d.head_dim), kQuerySupertile, "DSA3D_ORDER_Q");
     dsa3d_desc dpair = d;
     dpair.T = (d.T + 1) / 2;
     const BlockOrder kord = make_block_order(dpair, 2 * attn_tokens_per_block(d.head_dim), kKeySupertile,
