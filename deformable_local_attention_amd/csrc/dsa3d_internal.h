@@ -67,7 +67,7 @@ struct BlockOrder;
 // supertile of (at most) frames x rows x tokens each in turn, so the eight
 // supertiles in flight are neighbours and the rows their samples gather are
 // shared through the memory-side cache. A negative `rows` asks for bands of
-// about -rows rows of equal height (68 rows: three bands of 23 or 22).
+// about -rows rows of equal height (68 rows and -14: five bands of 14 or 13).
 struct Supertile {
     int frames, rows, tokens;
 };
@@ -75,12 +75,13 @@ struct Supertile {
 // (3x5x5 window, offsets N(0,2)) for the deformable kernels: the step runs 15%
 // faster than with one contiguous range of 4 x 8 x 64 supertiles per XCD.
 constexpr Supertile kGatherSupertile = {16, 32, 16};
-// Forward: 64 frames x bands of ~23 rows x 16 tokens, 533-537 ms on that grid
-// against 558-562 ms with 16 x 32 x 16.
-constexpr Supertile kForwardSupertile = {64, -23, 16};
-// Backward query kernel: 32 frames x bands of ~23 rows x 16 tokens, 90.4 ms per
-// 3-head pass against 91.9 ms with 16 x 32 x 16.
-constexpr Supertile kQuerySupertile = {32, -23, 16};
+// Forward: 64 frames x bands of ~14 rows x 16 tokens, 520-524 ms on that grid,
+// against 529-539 ms with bands of ~23 rows, 551-554 with ~12 or ~17, and
+// 558-562 ms with 16 x 32 x 16.
+constexpr Supertile kForwardSupertile = {64, -14, 16};
+// Backward query kernel: 32 frames x bands of ~14 rows x 16 tokens, 1-2% faster
+// per pass than 32 x ~23 x 16 or 16 x 32 x 16.
+constexpr Supertile kQuerySupertile = {32, -14, 16};
 // Key kernel (tasks of 2 frames x 2 tokens; its frames count pairs of frames):
 // 32 frames x 16 rows x 32 tokens, deeper in t and shallower in h than the
 // others; on the same grid 72 ms per 3-head pass, against 76 ms with tasks of
