@@ -8,8 +8,8 @@
 //  1. count kernel: the base cell floor(pos) of every sample (geometry only),
 //     counted per tile of tokens in an LDS histogram whose non-zero cells are
 //     then added to the buckets' 32-bit counts;
-//  2. an exclusive scan turns the counts into bucket starts (the counts are
-//     then cleared to serve as fill cursors);
+//  2. an exclusive scan turns the counts into bucket starts, which also
+//     replace the counts as the buckets' fill cursors;
 //  3. query kernel (one task = one (query, head), as in the forward):
 //     recompute the logits, a_p = exp(s_p - lse), da_p = sum_c w_c <dO, V[c]>,
 //     ds_p = a_p (da_p - <dO, o>); write dq = scale sum_p ds_p sum_c w_c K[c]
@@ -43,6 +43,7 @@ constexpr int kScanItems = 16;
 constexpr uint32_t kScanChunk = kScanThreads * kScanItems;
 constexpr uint32_t kWaveSortMax = 512;  // buckets up to this size: one wave, in LDS
 constexpr int kSortBucketsPerBlock = 64;
+constexpr uint32_t kNoSlot = 0xffffffffu;  // a sample with no record
 
 // Per-sample record, written by the query kernel into its bucket and read by
 // the key kernel.
@@ -67,9 +68,10 @@ struct BwdArgs {
     void* doff;
     void* dk;
     void* dv;
-    uint32_t* cnt;    // [ncell] bucket counts, then fill cursors
+    uint32_t* cnt;    // [ncell] bucket counts, then fill cursors (the next free record of each bucket)
     uint32_t* start;  // [ncell + 1] bucket starts
     SampleRec* rec;   // [nsamp] records, bucket by bucket
+    uint32_t nsamp;   // records in this pass
     TaskGrid g;
     BlockOrder ord;
     int32_t P;
@@ -223,7 +225,9 @@ __global__ void __launch_bounds__(1024) dsa3d_scan_top_kernel(uint32_t* bsum, ui
     if (threadIdx.x == 0) start[n] = carry;
 }
 
-__global__ void __launch_bounds__(kScanThreads) dsa3d_scan_apply_kernel(const uint32_t* cnt, uint32_t n,
+// The chunk-local scans write each bucket's start twice: into `start`, and
+// over its count, which from then on is the bucket's fill cursor.
+__global__ void __launch_bounds__(kScanThreads) dsa3d_scan_apply_kernel(uint32_t* cnt, uint32_t n,
                                                                         const uint32_t* bsum, uint32_t* start) {
     __shared__ uint32_t lds[kScanThreads / 64 + 1];
     const uint64_t i0 = (uint64_t)blockIdx.x * kScanChunk + (uint64_t)threadIdx.x * kScanItems;
@@ -238,7 +242,7 @@ __global__ void __launch_bounds__(kScanThreads) dsa3d_scan_apply_kernel(const ui
     uint32_t run = block_exclusive_scan(s, lds, total) + bsum[blockIdx.x];
 #pragma unroll
     for (int j = 0; j < kScanItems; ++j) {
-        if (i0 + j < n) start[i0 + j] = run;
+        if (i0 + j < n) { start[i0 + j] = run; cnt[i0 + j] = run; }
         run += x[j];
     }
 }
@@ -280,14 +284,17 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_query_kernel(BwdArgs a) {
     const float Dsum = group_sum<L>(gf.dot(of, 0.0f));
     const float lse = a.lse[tok * a.g.heads + eta];
 
-    // Chunks of L samples: each lane computes one sample's cell and requests
-    // a slot in the cell's bucket (so a chunk's atomics issue together), the
+    // Chunks of L samples: each lane computes one sample's cell and takes the
+    // next record of the cell's bucket from its cursor (so a chunk's atomics
+    // issue together), the
     // group then works through the chunk sample by sample while the slots
     // return, and finally each lane writes its own sample's doffsets and
     // record.
     __shared__ SampleGeo s_geo[256];
     __shared__ float4 s_out[256];   // scale*ds_p, a_p, doff_t, doff_h
     __shared__ float s_outw[256];   // doff_w
+    __shared__ uint4 s_rec[256][2]; // the chunk's records, staged for paired stores
+    __shared__ uint32_t s_slot[256]; // their slots (kNoSlot: none)
     SampleGeo* geo = s_geo + (threadIdx.x - li);
     float4* out = s_out + (threadIdx.x - li);
     float* outw = s_outw + (threadIdx.x - li);
@@ -297,16 +304,14 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_query_kernel(BwdArgs a) {
         const int n = min(L, a.P - p0);
         wave_lds_sync();  // the previous chunk has been read and flushed
         bool has_rec = false;
-        uint32_t taken = 0u, b0 = 0u, b1 = 0u;  // cursor value taken, bucket start and end
+        uint32_t slot = 0u;  // the record taken from the bucket's cursor
         if (li < n) {
             SampleGeo sg;
             int32_t t0, h0, w0;
             sample_geo<T>(a.g, a.win, tok_b, t, h, w, p0 + li, offq + (p0 + li) * 3, sg, t0, h0, w0);
             if ((sg.valid & 0xffu) != 0u) {
                 const uint32_t cell = cell_index(a.g, bh, t0, h0, w0);
-                taken = atomicAdd(a.cnt + cell, 1u);
-                b0 = a.start[cell];
-                b1 = a.start[cell + 1];
+                slot = atomicAdd(a.cnt + cell, 1u);
                 has_rec = true;
             }
             geo[li] = sg;
@@ -366,6 +371,7 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_query_kernel(BwdArgs a) {
             }
         }
         wave_lds_sync();
+        uint32_t my_slot = kNoSlot;
         if (li < n) {
             const int p = p0 + li;
             const float4 ov = out[li];
@@ -373,15 +379,34 @@ __global__ void __launch_bounds__(256) dsa3d_bwd_query_kernel(BwdArgs a) {
             store_scalar<T>(doffq + p * 3 + 1, ov.w);
             store_scalar<T>(doffq + p * 3 + 2, outw[li]);
             const SampleGeo& sg = geo[li];
-            // the count kernel filed exactly these samples in these cells; the
-            // bound only keeps a write inside its bucket
-            if (has_rec && b0 + taken < b1) {
-                uint4* dst = reinterpret_cast<uint4*>(a.rec + (b0 + taken));
-                dst[0] = make_uint4(__float_as_uint(ov.x), __float_as_uint(ov.y), __float_as_uint(sg.ft),
-                                    __float_as_uint(sg.fh));
-                dst[1] = make_uint4(__float_as_uint(sg.fw), sid0 + (uint32_t)p, (uint32_t)qrow_bytes,
-                                    (uint32_t)(qrow_bytes >> 32));
+            // the count kernel filed exactly these samples in these cells, so
+            // the slot lies in the sample's bucket; the bound only keeps a
+            // write inside the records
+            if (has_rec && slot < a.nsamp) {
+                s_rec[threadIdx.x][0] = make_uint4(__float_as_uint(ov.x), __float_as_uint(ov.y),
+                                                   __float_as_uint(sg.ft), __float_as_uint(sg.fh));
+                s_rec[threadIdx.x][1] = make_uint4(__float_as_uint(sg.fw), sid0 + (uint32_t)p,
+                                                   (uint32_t)qrow_bytes, (uint32_t)(qrow_bytes >> 32));
+                my_slot = slot;
             }
+        }
+        s_slot[threadIdx.x] = my_slot;
+        wave_lds_sync();
+        // Each record is written by a pair of neighbouring lanes of its group,
+        // one 16-byte half each, so that a record costs one 32-byte write
+        // request rather than two: in two rounds, lanes (2i, 2i+1) write the
+        // record of the group's lane (L/2)*round + i. (With one lane per
+        // group, that lane writes both halves.)
+        if constexpr (L >= 2) {
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int src = (int)threadIdx.x - li + r * (L / 2) + (li >> 1);
+                const uint32_t sl = s_slot[src];
+                if (sl != kNoSlot) reinterpret_cast<uint4*>(a.rec + sl)[li & 1] = s_rec[src][li & 1];
+            }
+        } else if (my_slot != kNoSlot) {
+            reinterpret_cast<uint4*>(a.rec + my_slot)[0] = s_rec[threadIdx.x][0];
+            reinterpret_cast<uint4*>(a.rec + my_slot)[1] = s_rec[threadIdx.x][1];
         }
     }
     Frag8<T> dqf;
@@ -895,6 +920,7 @@ hipError_t launch_backward(const dsa3d_desc& d, const void* q, const void* k, co
         a.cnt = reinterpret_cast<uint32_t*>(base + L.off_cnt);
         a.start = reinterpret_cast<uint32_t*>(base + L.off_start);
         a.rec = reinterpret_cast<SampleRec*>(base + L.off_rec);
+        a.nsamp = (uint32_t)L.nsamp;
         a.g = make_task_grid(d, (int32_t)h0, nh);
         a.ord = ord;
         a.P = d.P;
@@ -922,7 +948,7 @@ hipError_t launch_backward(const dsa3d_desc& d, const void* q, const void* k, co
             }
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        // 2. bucket starts; the counts become fill cursors
+        // 2. bucket starts, which also become the fill cursors
         {
             LaunchScope ls(DSA3D_K_BWD_SCAN, s);
             hipLaunchKernelGGL(dsa3d_scan_sums_kernel, dim3((unsigned)L.nscan), dim3(kScanThreads), 0, s, a.cnt, ncell,
@@ -932,7 +958,6 @@ hipError_t launch_backward(const dsa3d_desc& d, const void* q, const void* k, co
                                ncell, bsum, a.start);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = fill_zero(a.cnt, L.ncell * 4, s)) != hipSuccess) return e;
         // 3. dq, doffsets and the sample records
         if (f32) { DSA3D_DISPATCH_D_E(d.head_dim, bwd_query_f32, e, a, nblocks, s); }
         else { DSA3D_DISPATCH_D_E(d.head_dim, bwd_query_bf16, e, a, nblocks, s); }
