@@ -164,7 +164,7 @@ def cpu_baseline(wl, budget_s: float = 20.0):
 
 # the sources the attention kernels (forward, backward per query and per key)
 # are compiled from
-ATTN_SOURCES = ("dsa3d_attn.hip", "dsa3d_bwd.hip", "dsa3d_attn_common.h", "dsa3d_device.h")
+ATTN_SOURCES = ("dsa3d_attn.hip", "dsa3d_bwd.hip", "dsa3d_attn_common.h", "dsa3d_device.h", "dsa3d_internal.h")
 
 
 def code_text(src: str) -> str:
