@@ -157,6 +157,213 @@ __global__ void __launch_bounds__(256) dsa3d_fixed_fwd_kernel(FixedArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Forward on the matrix cores: bf16, head_dim a multiple of 32 (up to 256),
+// no dilation along w and k_w <= 17.
+//
+// The 16 tokens w0 .. w0+15 of one row (t, h) of one head share, for each
+// (frame, row) of the window, one segment of 15 + k_w consecutive key tokens
+// (columns w0 - r_w ...): query c uses segment keys c .. c + k_w - 1, a band.
+// A wave takes these 16 queries through the window segment by segment:
+//   S^T = K_seg Q^T         two 16-key tiles, head_dim/32 steps of
+//                           v_mfma_f32_16x16x32_bf16,
+//   logits outside the band -> -inf, online softmax per query,
+//   O^T += V_seg^T P^T      one 16-channel tile per product; the weights are
+//                           split into a bf16 part and a bf16 remainder (two
+//                           products), so they enter at about 2^-17 relative
+//                           precision, and everything accumulates in f32.
+// The product layouts: lane l holds row l%16 and k-slice 8*(l/16) .. +7 of
+// each operand, and D[4*(l/16) + r][l%16] of the result. The k-slice of lane
+// group g in the second product is the key set {4g..4g+3, 16+4g..16+4g+3},
+// which is where the first product left group g's logits, so the weights
+// need no data movement; the segment's value rows pass through LDS, from
+// which each lane reads its eight (key, channel) elements. Keys outside the
+// grid are zero rows (logit 0, value 0), as in the gathering kernels; keys past
+// the segment lie outside every band.
+typedef __attribute__((ext_vector_type(8))) __bf16 mf_bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 mf_bf16x2;
+typedef __attribute__((ext_vector_type(4))) float mf_f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t mf_u32x4;
+
+constexpr int kMfmaTokens = 16;  // queries per wave
+constexpr int kMfmaMaxKw = 17;   // 15 + k_w keys fit two 16-key tiles
+// The running maximum is raised only when a logit exceeds it by more than
+// this, so most segments skip the rescale; weights stay below e^8.
+constexpr float kMfmaLazyMax = 8.0f;
+
+__device__ __forceinline__ uint32_t mf_pack(float lo, float hi) {  // two RNE bf16 in one word
+    const mf_bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// One window segment's operands: the two 16-key tiles of keys for the first
+// product (key 16*T + l%16, channels 32j + 8*(l/16) .. +7) and this lane's
+// part of the value rows (half l%2 of key l/2) on their way to LDS.
+template <int D>
+struct MfmaSeg {
+    mf_bf16x8 k[2][D / 32];
+    uint4 v[D / 16];
+};
+
+template <int D>
+__global__ void __launch_bounds__(256) dsa3d_fixed_fwd_mfma_kernel(FixedArgs a) {
+    constexpr int RS = D + 8;  // LDS row stride (elements): the four lane groups' rows fall in distinct banks
+    __shared__ __attribute__((aligned(16))) bf16_t s_v[4][32 * RS];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int c = lane & 15, g = lane >> 4;
+    int64_t bh;
+    int32_t t, h, bw0;
+    block_coords(a.g, a.ord, logical_block(blockIdx.x, gridDim.x, a.ord.chunk), bh, t, h, bw0);
+    const int32_t w0 = bw0 + wv * kMfmaTokens;
+    if (w0 >= a.g.W) return;  // no block-wide barrier below
+    const int32_t b = (int32_t)(bh / a.g.nheads);
+    const int32_t eta = a.g.head0 + (int32_t)(bh - (int64_t)b * a.g.nheads);
+    const uint32_t tok_b = (uint32_t)b * (uint32_t)a.g.T * (uint32_t)a.g.H * (uint32_t)a.g.W;
+    const int64_t C = (int64_t)a.g.heads * D;
+    const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + (int64_t)eta * D;
+    const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + (int64_t)eta * D;
+    const bf16_t* zero = reinterpret_cast<const bf16_t*>(g_zero_row);  // 512 zero elements
+    bf16_t* vs = s_v[wv];
+    const bool qin = w0 + c < a.g.W;
+    const int64_t qtok = (int64_t)tok_b + ((int64_t)t * a.g.H + h) * a.g.W + (w0 + c);
+
+    // This lane's key columns (the same in every segment) and whether they lie
+    // in the grid and the segment: keys c and 16 + c of the first product,
+    // key l/2 of the value staging.
+    const int span = kMfmaTokens - 1 + a.win.kw;
+    const int kv = lane >> 1, half = lane & 1;
+    const int32_t wk0 = w0 - a.win.rw + c, wk1 = wk0 + 16, wkv = w0 - a.win.rw + kv;
+    const bool ok0 = c < span && (uint32_t)wk0 < (uint32_t)a.g.W;
+    const bool ok1 = 16 + c < span && (uint32_t)wk1 < (uint32_t)a.g.W;
+    const bool okv = kv < span && (uint32_t)wkv < (uint32_t)a.g.W;
+    const int64_t ko0 = (int64_t)wk0 * C + 8 * g, ko1 = (int64_t)wk1 * C + 8 * g;
+    const int64_t kov = (int64_t)wkv * C + half * (D / 2);
+    const int nseg = a.win.kt * a.win.kh;
+
+    auto load_seg = [&](int sg, MfmaSeg<D>& x) {
+        const int it = sg / a.win.kh, ih = sg - it * a.win.kh;
+        const int32_t tt = t + a.win.dil_t * (it - a.win.rt), hh = h + a.win.dil_h * (ih - a.win.rh);
+        const bool rin = (uint32_t)tt < (uint32_t)a.g.T && (uint32_t)hh < (uint32_t)a.g.H;
+        const int64_t rb = rin ? ((int64_t)tok_b + ((int64_t)tt * a.g.H + hh) * a.g.W) * C : 0;
+        // a key outside the grid reads the zero row (offsets below stay within its 512 elements)
+        const bf16_t* p0 = rin && ok0 ? K + rb + ko0 : zero;
+        const bf16_t* p1 = rin && ok1 ? K + rb + ko1 : zero;
+        const bf16_t* pv = rin && okv ? V + rb + kov : zero;
+#pragma unroll
+        for (int j = 0; j < D / 32; ++j) {
+            x.k[0][j] = *reinterpret_cast<const mf_bf16x8*>(p0 + 32 * j);
+            x.k[1][j] = *reinterpret_cast<const mf_bf16x8*>(p1 + 32 * j);
+        }
+#pragma unroll
+        for (int pc = 0; pc < D / 16; ++pc) x.v[pc] = *reinterpret_cast<const uint4*>(pv + 8 * pc);
+    };
+
+    // Q as the second operand of the first product: query c, channels 32j + 8g .. +7
+    mf_bf16x8 qb[D / 32];
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j)
+        qb[j] = *reinterpret_cast<const mf_bf16x8*>(
+            qin ? reinterpret_cast<const bf16_t*>(a.q) + qtok * C + (int64_t)eta * D + 32 * j + 8 * g : zero);
+    mf_f32x4 oacc[D / 32][2];  // O^T rows 4g + r of tile (tau, par): channel 32*tau + 8g + 2r + par, query c
+#pragma unroll
+    for (int tau = 0; tau < D / 32; ++tau) oacc[tau][0] = oacc[tau][1] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, lsum = 0.0f;  // maximum in use (query c) and this lane's share of the denominator
+
+    for (int sg = 0; sg < nseg; ++sg) {
+        MfmaSeg<D> cur;
+        load_seg(sg, cur);
+        wave_lds_sync();  // the previous segment's values have been read
+#pragma unroll
+        for (int pc = 0; pc < D / 16; ++pc)
+            *reinterpret_cast<uint4*>(vs + kv * RS + half * (D / 2) + 8 * pc) = cur.v[pc];
+        // S^T for keys 16*T + 4g + r of the segment, query c
+        mf_f32x4 sacc[2];
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+            sacc[T] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < D / 32; ++j)
+                sacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[T][j], qb[j], sacc[T], 0, 0, 0);
+        }
+        // softmax of query c over its band: keys c .. c + k_w - 1
+        float sv[8];
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int kc = 16 * (i >> 2) + 4 * g + (i & 3);
+            sv[i] = (uint32_t)(kc - c) < (uint32_t)a.win.kw ? a.scale * sacc[i >> 2][i & 3] : -INFINITY;
+            mloc = fmaxf(mloc, sv[i]);
+        }
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+        if (!__all(mloc <= m + kMfmaLazyMax)) {  // always on the first segment (m = -inf)
+            const float m_new = fmaxf(m, mloc);
+            const float alpha = __expf(m - m_new);
+#pragma unroll
+            for (int tau = 0; tau < D / 32; ++tau) {
+                oacc[tau][0] *= alpha;
+                oacc[tau][1] *= alpha;
+            }
+            lsum *= alpha;
+            m = m_new;
+        }
+        // weights as a bf16 part and a bf16 remainder, in the second product's k order
+        mf_u32x4 phi, plo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float p0 = __expf(sv[2 * i] - m), p1 = __expf(sv[2 * i + 1] - m);
+            lsum += p0 + p1;
+            const uint32_t hw = mf_pack(p0, p1);
+            phi[i] = hw;
+            plo[i] = mf_pack(p0 - bf16_lo(hw), p1 - bf16_hi(hw));
+        }
+        const mf_bf16x8 pb_hi = __builtin_bit_cast(mf_bf16x8, phi);
+        const mf_bf16x8 pb_lo = __builtin_bit_cast(mf_bf16x8, plo);
+        wave_lds_sync();  // the segment's values are in LDS
+        // O^T += V^T P^T over tiles of 16 channels 32*tau + 2m + par (m = 0..15):
+        // one 32-bit LDS read gives a key's channel pair for the tiles
+        // (tau, 0) and (tau, 1). Element 8g + i of the k-slice is key 4g + i
+        // (i < 4) or 16 + 4g + i - 4.
+#pragma unroll
+        for (int tau = 0; tau < D / 32; ++tau) {
+            const bf16_t* col = vs + 32 * tau + 2 * c;
+            uint32_t d[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int key = i < 4 ? 4 * g + i : 12 + 4 * g + i;
+                d[i] = *reinterpret_cast<const uint32_t*>(col + key * RS);
+            }
+            mf_u32x4 ve, vo;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ve[i] = __builtin_amdgcn_perm(d[2 * i + 1], d[2 * i], 0x05040100u);  // even channels of keys 2i, 2i+1
+                vo[i] = __builtin_amdgcn_perm(d[2 * i + 1], d[2 * i], 0x07060302u);  // odd channels
+            }
+            const mf_bf16x8 vE = __builtin_bit_cast(mf_bf16x8, ve), vO = __builtin_bit_cast(mf_bf16x8, vo);
+            oacc[tau][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vE, pb_hi, oacc[tau][0], 0, 0, 0);
+            oacc[tau][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vE, pb_lo, oacc[tau][0], 0, 0, 0);
+            oacc[tau][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vO, pb_hi, oacc[tau][1], 0, 0, 0);
+            oacc[tau][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vO, pb_lo, oacc[tau][1], 0, 0, 0);
+        }
+    }
+
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    if (!qin) return;
+    const float inv = 1.0f / lsum;
+    bf16_t* orow = reinterpret_cast<bf16_t*>(a.out) + qtok * C + (int64_t)eta * D;
+#pragma unroll
+    for (int tau = 0; tau < D / 32; ++tau) {  // channels 32*tau + 8g .. +7 of query c
+        uint4 w;
+        w.x = mf_pack(oacc[tau][0][0] * inv, oacc[tau][1][0] * inv);
+        w.y = mf_pack(oacc[tau][0][1] * inv, oacc[tau][1][1] * inv);
+        w.z = mf_pack(oacc[tau][0][2] * inv, oacc[tau][1][2] * inv);
+        w.w = mf_pack(oacc[tau][0][3] * inv, oacc[tau][1][3] * inv);
+        *reinterpret_cast<uint4*>(orow + 32 * tau + 8 * g) = w;
+    }
+    if (g == 0) a.lse[qtok * a.g.heads + eta] = m + __logf(lsum);
+}
+
 // Backward per query: a_p = exp(s_p - lse), ds_p = a_p (<dO, V[p]> - <dO, o>),
 // dq = scale * sum_p ds_p K[p]; <dO, o> is kept for the key kernel.
 template <typename T, int D, int Q>
@@ -338,10 +545,34 @@ size_t fixed_bwd_workspace_bytes(const dsa3d_desc& d) {
     return (size_t)(d.B * d.T * d.H * d.W) * (size_t)d.heads * sizeof(float) + 256;
 }
 
+bool fixed_fwd_on_mfma(const dsa3d_desc& d) {
+    return d.dtype == DSA3D_BF16 && (d.head_dim == 32 || d.head_dim == 64 || d.head_dim == 128 || d.head_dim == 256) &&
+           d.dil_w == 1 && d.kw <= kMfmaMaxKw;
+}
+
+template <int D>
+hipError_t fixed_fwd_mfma(const FixedArgs& a, int64_t nb, hipStream_t s) {
+    LaunchScope ls(DSA3D_K_FORWARD, s);
+    hipLaunchKernelGGL((dsa3d_fixed_fwd_mfma_kernel<D>), dim3((unsigned)nb), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_fixed_forward(const dsa3d_desc& d, const void* q, const void* k, const void* v, void* out,
                                 float* lse, hipStream_t s) {
     FixedArgs a = fixed_args(d);
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
+    if (fixed_fwd_on_mfma(d)) {
+        // four waves of 16 tokens along w per block
+        a.ord = make_block_order(d, 4 * kMfmaTokens, kGatherSupertile, "DSA3D_ORDER_FIXED_MFMA");
+        const int64_t nb = a.ord.nblk_bh * d.B * d.heads;
+        if (nb == 0) return hipSuccess;
+        switch (d.head_dim) {
+            case 32: return fixed_fwd_mfma<32>(a, nb, s);
+            case 64: return fixed_fwd_mfma<64>(a, nb, s);
+            case 128: return fixed_fwd_mfma<128>(a, nb, s);
+            default: return fixed_fwd_mfma<256>(a, nb, s);
+        }
+    }
     const int64_t nb = a.ord.nblk_bh * d.B * d.heads;
     if (nb == 0) return hipSuccess;
     if (d.dtype == DSA3D_F32) { DSA3D_DISPATCH_D(d.head_dim, fixed_fwd_f32, a, nb, s); }
