@@ -187,6 +187,7 @@ typedef __attribute__((ext_vector_type(4))) uint32_t mf_u32x4;
 
 constexpr int kMfmaTokens = 16;  // queries per wave
 constexpr int kMfmaMaxKw = 17;   // 15 + k_w keys fit two 16-key tiles
+constexpr int kMfmaPairMaxD = 128;  // rows of up to this many channels go two to a wave
 // The running maximum is raised only when a logit exceeds it by more than
 // this, so most segments skip the rescale; weights stay below e^8.
 constexpr float kMfmaLazyMax = 8.0f;
@@ -205,15 +206,24 @@ struct MfmaSeg {
     uint4 v[D / 16];
 };
 
-template <int D>
-__global__ void __launch_bounds__(256) dsa3d_fixed_fwd_mfma_kernel(FixedArgs a) {
+// A wave takes R rows h .. h+R-1 of 16 tokens (R = 2 when the window is not
+// dilated along h and rows have at most 128 channels, else 1). The rows' windows share all but R - 1 of their
+// (frame, row) segments, so the wave walks the union once: each segment's
+// keys and values are loaded once, and the value fragments read from LDS once,
+// for every row whose window holds the segment.
+template <int D, int R>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+dsa3d_fixed_fwd_mfma_kernel(FixedArgs a) {
     constexpr int RS = D + 8;  // LDS row stride (elements): the four lane groups' rows fall in distinct banks
     __shared__ __attribute__((aligned(16))) bf16_t s_v[4][32 * RS];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int c = lane & 15, g = lane >> 4;
     int64_t bh;
-    int32_t t, h, bw0;
-    block_coords(a.g, a.ord, logical_block(blockIdx.x, gridDim.x, a.ord.chunk), bh, t, h, bw0);
+    int32_t t, hr, bw0;
+    TaskGrid gr = a.g;
+    gr.H = (a.g.H + R - 1) / R;  // the block order walks groups of R rows
+    block_coords(gr, a.ord, logical_block(blockIdx.x, gridDim.x, a.ord.chunk), bh, t, hr, bw0);
+    const int32_t h = R * hr;
     const int32_t w0 = bw0 + wv * kMfmaTokens;
     if (w0 >= a.g.W) return;  // no block-wide barrier below
     const int32_t b = (int32_t)(bh / a.g.nheads);
@@ -224,8 +234,13 @@ __global__ void __launch_bounds__(256) dsa3d_fixed_fwd_mfma_kernel(FixedArgs a) 
     const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + (int64_t)eta * D;
     const bf16_t* zero = reinterpret_cast<const bf16_t*>(g_zero_row);  // 512 zero elements
     bf16_t* vs = s_v[wv];
-    const bool qin = w0 + c < a.g.W;
-    const int64_t qtok = (int64_t)tok_b + ((int64_t)t * a.g.H + h) * a.g.W + (w0 + c);
+    bool qin[R];
+    int64_t qtok[R];
+#pragma unroll
+    for (int rho = 0; rho < R; ++rho) {
+        qin[rho] = w0 + c < a.g.W && h + rho < a.g.H;
+        qtok[rho] = (int64_t)tok_b + ((int64_t)t * a.g.H + h + rho) * a.g.W + (w0 + c);
+    }
 
     // This lane's key columns (the same in every segment) and whether they lie
     // in the grid and the segment: keys c and 16 + c of the first product,
@@ -238,130 +253,152 @@ __global__ void __launch_bounds__(256) dsa3d_fixed_fwd_mfma_kernel(FixedArgs a) 
     const bool okv = kv < span && (uint32_t)wkv < (uint32_t)a.g.W;
     const int64_t ko0 = (int64_t)wk0 * C + 8 * g, ko1 = (int64_t)wk1 * C + 8 * g;
     const int64_t kov = (int64_t)wkv * C + half * (D / 2);
-    const int nseg = a.win.kt * a.win.kh;
-
-    auto load_seg = [&](int sg, MfmaSeg<D>& x) {
-        const int it = sg / a.win.kh, ih = sg - it * a.win.kh;
-        const int32_t tt = t + a.win.dil_t * (it - a.win.rt), hh = h + a.win.dil_h * (ih - a.win.rh);
-        const bool rin = (uint32_t)tt < (uint32_t)a.g.T && (uint32_t)hh < (uint32_t)a.g.H;
-        const int64_t rb = rin ? ((int64_t)tok_b + ((int64_t)tt * a.g.H + hh) * a.g.W) * C : 0;
-        // a key outside the grid reads the zero row (offsets below stay within its 512 elements)
-        const bf16_t* p0 = rin && ok0 ? K + rb + ko0 : zero;
-        const bf16_t* p1 = rin && ok1 ? K + rb + ko1 : zero;
-        const bf16_t* pv = rin && okv ? V + rb + kov : zero;
-#pragma unroll
-        for (int j = 0; j < D / 32; ++j) {
-            x.k[0][j] = *reinterpret_cast<const mf_bf16x8*>(p0 + 32 * j);
-            x.k[1][j] = *reinterpret_cast<const mf_bf16x8*>(p1 + 32 * j);
-        }
-#pragma unroll
-        for (int pc = 0; pc < D / 16; ++pc) x.v[pc] = *reinterpret_cast<const uint4*>(pv + 8 * pc);
-    };
+    const int nu = a.win.kh + R - 1;  // segment rows of the union per frame
 
     // Q as the second operand of the first product: query c, channels 32j + 8g .. +7
-    mf_bf16x8 qb[D / 32];
+    mf_bf16x8 qb[R][D / 32];
+    mf_f32x4 oacc[R][D / 32][2];  // O^T rows 4g + r of tile (tau, par): channel 32*tau + 8g + 2r + par, query c
+    float m[R], lsum[R];          // maximum in use (query c) and this lane's share of the denominator
 #pragma unroll
-    for (int j = 0; j < D / 32; ++j)
-        qb[j] = *reinterpret_cast<const mf_bf16x8*>(
-            qin ? reinterpret_cast<const bf16_t*>(a.q) + qtok * C + (int64_t)eta * D + 32 * j + 8 * g : zero);
-    mf_f32x4 oacc[D / 32][2];  // O^T rows 4g + r of tile (tau, par): channel 32*tau + 8g + 2r + par, query c
+    for (int rho = 0; rho < R; ++rho) {
 #pragma unroll
-    for (int tau = 0; tau < D / 32; ++tau) oacc[tau][0] = oacc[tau][1] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, lsum = 0.0f;  // maximum in use (query c) and this lane's share of the denominator
+        for (int j = 0; j < D / 32; ++j)
+            qb[rho][j] = *reinterpret_cast<const mf_bf16x8*>(
+                qin[rho] ? reinterpret_cast<const bf16_t*>(a.q) + qtok[rho] * C + (int64_t)eta * D + 32 * j + 8 * g
+                         : zero);
+#pragma unroll
+        for (int tau = 0; tau < D / 32; ++tau) oacc[rho][tau][0] = oacc[rho][tau][1] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
+        m[rho] = -INFINITY;
+        lsum[rho] = 0.0f;
+    }
 
-    for (int sg = 0; sg < nseg; ++sg) {
-        MfmaSeg<D> cur;
-        load_seg(sg, cur);
-        wave_lds_sync();  // the previous segment's values have been read
+    for (int it = 0; it < a.win.kt; ++it) {
+        const int32_t tt = t + a.win.dil_t * (it - a.win.rt);
+        for (int u = 0; u < nu; ++u) {
+            // segment row: window row u - rho of row rho
+            const int32_t hh = R == 1 ? h + a.win.dil_h * (u - a.win.rh) : h - a.win.rh + u;
+            const bool rin = (uint32_t)tt < (uint32_t)a.g.T && (uint32_t)hh < (uint32_t)a.g.H;
+            const int64_t rb = rin ? ((int64_t)tok_b + ((int64_t)tt * a.g.H + hh) * a.g.W) * C : 0;
+            // a key outside the grid reads the zero row (offsets below stay within its 512 elements)
+            const bf16_t* p0 = rin && ok0 ? K + rb + ko0 : zero;
+            const bf16_t* p1 = rin && ok1 ? K + rb + ko1 : zero;
+            const bf16_t* pv = rin && okv ? V + rb + kov : zero;
+            MfmaSeg<D> cur;
 #pragma unroll
-        for (int pc = 0; pc < D / 16; ++pc)
-            *reinterpret_cast<uint4*>(vs + kv * RS + half * (D / 2) + 8 * pc) = cur.v[pc];
-        // S^T for keys 16*T + 4g + r of the segment, query c
-        mf_f32x4 sacc[2];
+            for (int j = 0; j < D / 32; ++j) {
+                cur.k[0][j] = *reinterpret_cast<const mf_bf16x8*>(p0 + 32 * j);
+                cur.k[1][j] = *reinterpret_cast<const mf_bf16x8*>(p1 + 32 * j);
+            }
 #pragma unroll
-        for (int T = 0; T < 2; ++T) {
-            sacc[T] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int pc = 0; pc < D / 16; ++pc) cur.v[pc] = *reinterpret_cast<const uint4*>(pv + 8 * pc);
+            wave_lds_sync();  // the previous segment's values have been read
 #pragma unroll
-            for (int j = 0; j < D / 32; ++j)
-                sacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[T][j], qb[j], sacc[T], 0, 0, 0);
-        }
-        // softmax of query c over its band: keys c .. c + k_w - 1
-        float sv[8];
-        float mloc = -INFINITY;
+            for (int pc = 0; pc < D / 16; ++pc)
+                *reinterpret_cast<uint4*>(vs + kv * RS + half * (D / 2) + 8 * pc) = cur.v[pc];
+            bool use[R];
+            mf_bf16x8 pb_hi[R], pb_lo[R];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int kc = 16 * (i >> 2) + 4 * g + (i & 3);
-            sv[i] = (uint32_t)(kc - c) < (uint32_t)a.win.kw ? a.scale * sacc[i >> 2][i & 3] : -INFINITY;
-            mloc = fmaxf(mloc, sv[i]);
-        }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-        if (!__all(mloc <= m + kMfmaLazyMax)) {  // always on the first segment (m = -inf)
-            const float m_new = fmaxf(m, mloc);
-            const float alpha = __expf(m - m_new);
+            for (int rho = 0; rho < R; ++rho) {
+                use[rho] = u - rho >= 0 && u - rho < a.win.kh;  // wave-uniform
+                if (!use[rho]) continue;
+                // S^T for keys 16*T + 4g + r of the segment, query c of row rho
+                mf_f32x4 sacc[2];
+#pragma unroll
+                for (int T = 0; T < 2; ++T) {
+                    sacc[T] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int j = 0; j < D / 32; ++j)
+                        sacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[T][j], qb[rho][j], sacc[T], 0, 0, 0);
+                }
+                // softmax of query c over its band: keys c .. c + k_w - 1
+                float sv[8];
+                float mloc = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int kc = 16 * (i >> 2) + 4 * g + (i & 3);
+                    sv[i] = (uint32_t)(kc - c) < (uint32_t)a.win.kw ? a.scale * sacc[i >> 2][i & 3] : -INFINITY;
+                    mloc = fmaxf(mloc, sv[i]);
+                }
+                mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+                mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+                if (!__all(mloc <= m[rho] + kMfmaLazyMax)) {  // always on the row's first segment (m = -inf)
+                    const float m_new = fmaxf(m[rho], mloc);
+                    const float alpha = __expf(m[rho] - m_new);
+#pragma unroll
+                    for (int tau = 0; tau < D / 32; ++tau) {
+                        oacc[rho][tau][0] *= alpha;
+                        oacc[rho][tau][1] *= alpha;
+                    }
+                    lsum[rho] *= alpha;
+                    m[rho] = m_new;
+                }
+                // weights as a bf16 part and a bf16 remainder, in the second product's k order
+                mf_u32x4 phi, plo;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float q0 = __expf(sv[2 * i] - m[rho]), q1 = __expf(sv[2 * i + 1] - m[rho]);
+                    lsum[rho] += q0 + q1;
+                    const uint32_t hw = mf_pack(q0, q1);
+                    phi[i] = hw;
+                    plo[i] = mf_pack(q0 - bf16_lo(hw), q1 - bf16_hi(hw));
+                }
+                pb_hi[rho] = __builtin_bit_cast(mf_bf16x8, phi);
+                pb_lo[rho] = __builtin_bit_cast(mf_bf16x8, plo);
+            }
+            wave_lds_sync();  // the segment's values are in LDS
+            // O^T += V^T P^T over tiles of 16 channels 32*tau + 2m + par (m = 0..15):
+            // one 32-bit LDS read gives a key's channel pair for the tiles
+            // (tau, 0) and (tau, 1). Element 8g + i of the k-slice is key 4g + i
+            // (i < 4) or 16 + 4g + i - 4.
 #pragma unroll
             for (int tau = 0; tau < D / 32; ++tau) {
-                oacc[tau][0] *= alpha;
-                oacc[tau][1] *= alpha;
+                const bf16_t* col = vs + 32 * tau + 2 * c;
+                uint32_t d[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int key = i < 4 ? 4 * g + i : 12 + 4 * g + i;
+                    d[i] = *reinterpret_cast<const uint32_t*>(col + key * RS);
+                }
+                mf_u32x4 ve, vo;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    ve[i] = __builtin_amdgcn_perm(d[2 * i + 1], d[2 * i], 0x05040100u);  // even channels of keys 2i, 2i+1
+                    vo[i] = __builtin_amdgcn_perm(d[2 * i + 1], d[2 * i], 0x07060302u);  // odd channels
+                }
+                const mf_bf16x8 vE = __builtin_bit_cast(mf_bf16x8, ve), vO = __builtin_bit_cast(mf_bf16x8, vo);
+#pragma unroll
+                for (int rho = 0; rho < R; ++rho) {
+                    if (!use[rho]) continue;
+                    oacc[rho][tau][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vE, pb_hi[rho], oacc[rho][tau][0], 0, 0, 0);
+                    oacc[rho][tau][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vE, pb_lo[rho], oacc[rho][tau][0], 0, 0, 0);
+                    oacc[rho][tau][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vO, pb_hi[rho], oacc[rho][tau][1], 0, 0, 0);
+                    oacc[rho][tau][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vO, pb_lo[rho], oacc[rho][tau][1], 0, 0, 0);
+                }
             }
-            lsum *= alpha;
-            m = m_new;
-        }
-        // weights as a bf16 part and a bf16 remainder, in the second product's k order
-        mf_u32x4 phi, plo;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float p0 = __expf(sv[2 * i] - m), p1 = __expf(sv[2 * i + 1] - m);
-            lsum += p0 + p1;
-            const uint32_t hw = mf_pack(p0, p1);
-            phi[i] = hw;
-            plo[i] = mf_pack(p0 - bf16_lo(hw), p1 - bf16_hi(hw));
-        }
-        const mf_bf16x8 pb_hi = __builtin_bit_cast(mf_bf16x8, phi);
-        const mf_bf16x8 pb_lo = __builtin_bit_cast(mf_bf16x8, plo);
-        wave_lds_sync();  // the segment's values are in LDS
-        // O^T += V^T P^T over tiles of 16 channels 32*tau + 2m + par (m = 0..15):
-        // one 32-bit LDS read gives a key's channel pair for the tiles
-        // (tau, 0) and (tau, 1). Element 8g + i of the k-slice is key 4g + i
-        // (i < 4) or 16 + 4g + i - 4.
-#pragma unroll
-        for (int tau = 0; tau < D / 32; ++tau) {
-            const bf16_t* col = vs + 32 * tau + 2 * c;
-            uint32_t d[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int key = i < 4 ? 4 * g + i : 12 + 4 * g + i;
-                d[i] = *reinterpret_cast<const uint32_t*>(col + key * RS);
-            }
-            mf_u32x4 ve, vo;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ve[i] = __builtin_amdgcn_perm(d[2 * i + 1], d[2 * i], 0x05040100u);  // even channels of keys 2i, 2i+1
-                vo[i] = __builtin_amdgcn_perm(d[2 * i + 1], d[2 * i], 0x07060302u);  // odd channels
-            }
-            const mf_bf16x8 vE = __builtin_bit_cast(mf_bf16x8, ve), vO = __builtin_bit_cast(mf_bf16x8, vo);
-            oacc[tau][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vE, pb_hi, oacc[tau][0], 0, 0, 0);
-            oacc[tau][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vE, pb_lo, oacc[tau][0], 0, 0, 0);
-            oacc[tau][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vO, pb_hi, oacc[tau][1], 0, 0, 0);
-            oacc[tau][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vO, pb_lo, oacc[tau][1], 0, 0, 0);
         }
     }
 
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
-    if (!qin) return;
-    const float inv = 1.0f / lsum;
-    bf16_t* orow = reinterpret_cast<bf16_t*>(a.out) + qtok * C + (int64_t)eta * D;
 #pragma unroll
-    for (int tau = 0; tau < D / 32; ++tau) {  // channels 32*tau + 8g .. +7 of query c
-        uint4 w;
-        w.x = mf_pack(oacc[tau][0][0] * inv, oacc[tau][1][0] * inv);
-        w.y = mf_pack(oacc[tau][0][1] * inv, oacc[tau][1][1] * inv);
-        w.z = mf_pack(oacc[tau][0][2] * inv, oacc[tau][1][2] * inv);
-        w.w = mf_pack(oacc[tau][0][3] * inv, oacc[tau][1][3] * inv);
-        *reinterpret_cast<uint4*>(orow + 32 * tau + 8 * g) = w;
+    for (int rho = 0; rho < R; ++rho) {
+        float l = lsum[rho];
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        if (!qin[rho]) continue;
+        const float inv = 1.0f / l;
+        bf16_t* orow = reinterpret_cast<bf16_t*>(a.out) + qtok[rho] * C + (int64_t)eta * D;
+#pragma unroll
+        for (int tau = 0; tau < D / 32; ++tau) {  // channels 32*tau + 8g .. +7 of query c
+            const mf_f32x4& e = oacc[rho][tau][0];
+            const mf_f32x4& o = oacc[rho][tau][1];
+            uint4 w;
+            w.x = mf_pack(e[0] * inv, o[0] * inv);
+            w.y = mf_pack(e[1] * inv, o[1] * inv);
+            w.z = mf_pack(e[2] * inv, o[2] * inv);
+            w.w = mf_pack(e[3] * inv, o[3] * inv);
+            *reinterpret_cast<uint4*>(orow + 32 * tau + 8 * g) = w;
+        }
+        if (g == 0) a.lse[qtok[rho] * a.g.heads + eta] = m[rho] + __logf(l);
     }
-    if (g == 0) a.lse[qtok * a.g.heads + eta] = m + __logf(lsum);
 }
 
 // Backward per query: a_p = exp(s_p - lse), ds_p = a_p (<dO, V[p]> - <dO, o>),
@@ -553,7 +590,13 @@ bool fixed_fwd_on_mfma(const dsa3d_desc& d) {
 template <int D>
 hipError_t fixed_fwd_mfma(const FixedArgs& a, int64_t nb, hipStream_t s) {
     LaunchScope ls(DSA3D_K_FORWARD, s);
-    hipLaunchKernelGGL((dsa3d_fixed_fwd_mfma_kernel<D>), dim3((unsigned)nb), dim3(256), 0, s, a);
+    if constexpr (D <= kMfmaPairMaxD) {
+        if (a.win.dil_h == 1) {
+            hipLaunchKernelGGL((dsa3d_fixed_fwd_mfma_kernel<D, 2>), dim3((unsigned)nb), dim3(256), 0, s, a);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((dsa3d_fixed_fwd_mfma_kernel<D, 1>), dim3((unsigned)nb), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -562,8 +605,10 @@ hipError_t launch_fixed_forward(const dsa3d_desc& d, const void* q, const void* 
     FixedArgs a = fixed_args(d);
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
     if (fixed_fwd_on_mfma(d)) {
-        // four waves of 16 tokens along w per block
-        a.ord = make_block_order(d, 4 * kMfmaTokens, kGatherSupertile, "DSA3D_ORDER_FIXED_MFMA");
+        // four waves of 16 tokens along w per block, each on R rows (2 when the h axis is not dilated)
+        dsa3d_desc dr = d;
+        dr.H = d.dil_h == 1 && d.head_dim <= kMfmaPairMaxD ? (d.H + 1) / 2 : d.H;
+        a.ord = make_block_order(dr, 4 * kMfmaTokens, kGatherSupertile, "DSA3D_ORDER_FIXED_MFMA");
         const int64_t nb = a.ord.nblk_bh * d.B * d.heads;
         if (nb == 0) return hipSuccess;
         switch (d.head_dim) {
