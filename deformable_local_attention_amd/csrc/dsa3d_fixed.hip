@@ -17,6 +17,9 @@
 //
 // Lane groups (L = head_dim/8 lanes, 8 channels each) and the block order are
 // those of the general kernels; a task owns a few neighbouring tokens along w.
+// For bf16 rows of 32-256 channels with an undilated w axis and k_w <= 17 the
+// forward runs on the matrix cores instead (dsa3d_fixed_fwd_mfma_kernel): the
+// queries of a row and their keys form a banded dense product there.
 #include "dsa3d_attn_common.h"
 #include "dsa3d_internal.h"
 

@@ -121,7 +121,9 @@ int dsa3d_offset_proj_forward(const dsa3d_desc* desc, const void* q, const void*
  * sample is the reference token itself and the operator is fixed local
  * attention over the dilated window [MegaSlide-DiT, §9.1: offsets frozen at
  * zero, a fixed (3,7,7) window]; the result equals the general path with a
- * zero offsets tensor, without reading offsets or interpolating. */
+ * zero offsets tensor (bf16 rows of 32-256 channels with k_w <= 17 and no
+ * dilation along w are summed on the matrix cores, in another order, so they
+ * agree to rounding), without reading offsets or interpolating. */
 int dsa3d_forward(const dsa3d_desc* desc, const void* q, const void* k, const void* v,
                   const void* offsets, void* out, float* lse, void* stream);
 
