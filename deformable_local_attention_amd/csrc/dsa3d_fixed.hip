@@ -23,6 +23,8 @@
 #include "dsa3d_attn_common.h"
 #include "dsa3d_internal.h"
 
+#include <type_traits>
+
 namespace dsa3d {
 
 struct FixedArgs {
@@ -404,6 +406,195 @@ dsa3d_fixed_fwd_mfma_kernel(FixedArgs a) {
     }
 }
 
+// Backward per query on the matrix cores (same shapes and layout as the
+// forward above): for each segment of the union of the R rows' windows,
+//   S^T  = K_seg Q^T,  dP^T = V_seg dO^T      (keys x queries, as in the forward)
+//   P    = exp(scale*S - lse),  dS = P (dP - <dO, o>)   (band keys only)
+//   dq^T += K_seg^T (scale*dS)^T              (weights split into a bf16 part
+//                                              and a bf16 remainder)
+// The segment's keys pass through LDS once and serve both as the first
+// product's operand (16-byte reads) and, read a channel pair at a time, as
+// the third's; the values are the second product's operand, loaded directly.
+// <dO, o> is left in the workspace for the key kernel, as by the vector kernel.
+template <int D, int R>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+dsa3d_fixed_bwd_query_mfma_kernel(FixedArgs a) {
+    constexpr int RS = D + 8;  // LDS row stride (elements), as in the forward
+    __shared__ __attribute__((aligned(16))) bf16_t s_k[4][32 * RS];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int c = lane & 15, g = lane >> 4;
+    int64_t bh;
+    int32_t t, hr, bw0;
+    TaskGrid gr = a.g;
+    gr.H = (a.g.H + R - 1) / R;
+    block_coords(gr, a.ord, logical_block(blockIdx.x, gridDim.x, a.ord.chunk), bh, t, hr, bw0);
+    const int32_t h = R * hr;
+    const int32_t w0 = bw0 + wv * kMfmaTokens;
+    if (w0 >= a.g.W) return;  // no block-wide barrier below
+    const int32_t b = (int32_t)(bh / a.g.nheads);
+    const int32_t eta = a.g.head0 + (int32_t)(bh - (int64_t)b * a.g.nheads);
+    const uint32_t tok_b = (uint32_t)b * (uint32_t)a.g.T * (uint32_t)a.g.H * (uint32_t)a.g.W;
+    const int64_t C = (int64_t)a.g.heads * D;
+    const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + (int64_t)eta * D;
+    const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + (int64_t)eta * D;
+    const bf16_t* zero = reinterpret_cast<const bf16_t*>(g_zero_row);  // 512 zero elements
+    bf16_t* ks = s_k[wv];
+
+    const int span = kMfmaTokens - 1 + a.win.kw;
+    const int kv = lane >> 1, half = lane & 1;
+    const int32_t wk0 = w0 - a.win.rw + c, wk1 = wk0 + 16, wkv = w0 - a.win.rw + kv;
+    const bool ok0 = c < span && (uint32_t)wk0 < (uint32_t)a.g.W;
+    const bool ok1 = 16 + c < span && (uint32_t)wk1 < (uint32_t)a.g.W;
+    const bool okv = kv < span && (uint32_t)wkv < (uint32_t)a.g.W;
+    const int64_t ko0 = (int64_t)wk0 * C + 8 * g, ko1 = (int64_t)wk1 * C + 8 * g;
+    const int64_t kov = (int64_t)wkv * C + half * (D / 2);
+    const int nu = a.win.kh + R - 1;
+
+    bool qin[R];
+    int64_t qtok[R];
+    mf_bf16x8 qb[R][D / 32], gb[R][D / 32];  // Q and dO as second operands: query c, channels 32j + 8g .. +7
+    mf_f32x4 dacc[R][D / 32][2];             // dq^T rows 4g + r of tile (tau, par): channel 32*tau + 8g + 2r + par
+    float lse[R], dsum[R];
+#pragma unroll
+    for (int rho = 0; rho < R; ++rho) {
+        qin[rho] = w0 + c < a.g.W && h + rho < a.g.H;
+        qtok[rho] = (int64_t)tok_b + ((int64_t)t * a.g.H + h + rho) * a.g.W + (w0 + c);
+        const int64_t ro = qtok[rho] * C + (int64_t)eta * D + 8 * g;
+        float part = 0.0f;
+#pragma unroll
+        for (int j = 0; j < D / 32; ++j) {
+            const bf16_t* qp = qin[rho] ? reinterpret_cast<const bf16_t*>(a.q) + ro + 32 * j : zero;
+            const bf16_t* gp = qin[rho] ? reinterpret_cast<const bf16_t*>(a.dout) + ro + 32 * j : zero;
+            const bf16_t* op = qin[rho] ? reinterpret_cast<const bf16_t*>(a.o) + ro + 32 * j : zero;
+            qb[rho][j] = *reinterpret_cast<const mf_bf16x8*>(qp);
+            gb[rho][j] = *reinterpret_cast<const mf_bf16x8*>(gp);
+            const uint4 gw = *reinterpret_cast<const uint4*>(gp), ow = *reinterpret_cast<const uint4*>(op);
+            part = dot2_bf16(gw.x, ow.x, part);
+            part = dot2_bf16(gw.y, ow.y, part);
+            part = dot2_bf16(gw.z, ow.z, part);
+            part = dot2_bf16(gw.w, ow.w, part);
+        }
+        part += __shfl_xor(part, 16, 64);
+        part += __shfl_xor(part, 32, 64);
+        dsum[rho] = part;
+        const int64_t ti = qtok[rho] * a.g.heads + eta;
+        lse[rho] = qin[rho] ? a.lse[ti] : 0.0f;
+        if (qin[rho] && g == 0) a.dsum[ti] = part;
+#pragma unroll
+        for (int tau = 0; tau < D / 32; ++tau) dacc[rho][tau][0] = dacc[rho][tau][1] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    for (int it = 0; it < a.win.kt; ++it) {
+        const int32_t tt = t + a.win.dil_t * (it - a.win.rt);
+        for (int u = 0; u < nu; ++u) {
+            const int32_t hh = R == 1 ? h + a.win.dil_h * (u - a.win.rh) : h - a.win.rh + u;
+            const bool rin = (uint32_t)tt < (uint32_t)a.g.T && (uint32_t)hh < (uint32_t)a.g.H;
+            const int64_t rb = rin ? ((int64_t)tok_b + ((int64_t)tt * a.g.H + hh) * a.g.W) * C : 0;
+            const bf16_t* p0 = rin && ok0 ? V + rb + ko0 : zero;
+            const bf16_t* p1 = rin && ok1 ? V + rb + ko1 : zero;
+            const bf16_t* pk = rin && okv ? K + rb + kov : zero;
+            mf_bf16x8 va[2][D / 32];  // values as the second product's first operand
+            uint4 kst[D / 16];        // this lane's part of the key rows, on their way to LDS
+#pragma unroll
+            for (int j = 0; j < D / 32; ++j) {
+                va[0][j] = *reinterpret_cast<const mf_bf16x8*>(p0 + 32 * j);
+                va[1][j] = *reinterpret_cast<const mf_bf16x8*>(p1 + 32 * j);
+            }
+#pragma unroll
+            for (int pc = 0; pc < D / 16; ++pc) kst[pc] = *reinterpret_cast<const uint4*>(pk + 8 * pc);
+#pragma unroll
+            for (int pc = 0; pc < D / 16; ++pc)
+                *reinterpret_cast<uint4*>(ks + kv * RS + half * (D / 2) + 8 * pc) = kst[pc];
+            wave_lds_sync();  // the segment's keys are in LDS
+            mf_bf16x8 ka[2][D / 32];  // keys as the first product's first operand: key 16T + c, channels 32j + 8g
+#pragma unroll
+            for (int T = 0; T < 2; ++T)
+#pragma unroll
+                for (int j = 0; j < D / 32; ++j)
+                    ka[T][j] = *reinterpret_cast<const mf_bf16x8*>(ks + (16 * T + c) * RS + 32 * j + 8 * g);
+            bool use[R];
+            mf_bf16x8 ds_hi[R], ds_lo[R];
+#pragma unroll
+            for (int rho = 0; rho < R; ++rho) {
+                use[rho] = u - rho >= 0 && u - rho < a.win.kh;  // wave-uniform
+                if (!use[rho]) continue;
+                mf_f32x4 sacc[2], pacc[2];
+#pragma unroll
+                for (int T = 0; T < 2; ++T) {
+                    sacc[T] = pacc[T] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int j = 0; j < D / 32; ++j) {
+                        sacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[T][j], qb[rho][j], sacc[T], 0, 0, 0);
+                        pacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[T][j], gb[rho][j], pacc[T], 0, 0, 0);
+                    }
+                }
+                mf_u32x4 hi, lo;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int ii = 2 * i + e;
+                        const int kc = 16 * (ii >> 2) + 4 * g + (ii & 3);
+                        const bool band = (uint32_t)(kc - c) < (uint32_t)a.win.kw;
+                        const float p = __expf(a.scale * sacc[ii >> 2][ii & 3] - lse[rho]);
+                        x[e] = band ? a.scale * p * (pacc[ii >> 2][ii & 3] - dsum[rho]) : 0.0f;
+                    }
+                    const uint32_t hw = mf_pack(x[0], x[1]);
+                    hi[i] = hw;
+                    lo[i] = mf_pack(x[0] - bf16_lo(hw), x[1] - bf16_hi(hw));
+                }
+                ds_hi[rho] = __builtin_bit_cast(mf_bf16x8, hi);
+                ds_lo[rho] = __builtin_bit_cast(mf_bf16x8, lo);
+            }
+            // dq^T += K^T (scale dS)^T, the keys read a channel pair at a time (as the forward's values)
+#pragma unroll
+            for (int tau = 0; tau < D / 32; ++tau) {
+                const bf16_t* col = ks + 32 * tau + 2 * c;
+                uint32_t d[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int key = i < 4 ? 4 * g + i : 12 + 4 * g + i;
+                    d[i] = *reinterpret_cast<const uint32_t*>(col + key * RS);
+                }
+                mf_u32x4 ke, ko;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    ke[i] = __builtin_amdgcn_perm(d[2 * i + 1], d[2 * i], 0x05040100u);
+                    ko[i] = __builtin_amdgcn_perm(d[2 * i + 1], d[2 * i], 0x07060302u);
+                }
+                const mf_bf16x8 kE = __builtin_bit_cast(mf_bf16x8, ke), kO = __builtin_bit_cast(mf_bf16x8, ko);
+#pragma unroll
+                for (int rho = 0; rho < R; ++rho) {
+                    if (!use[rho]) continue;
+                    dacc[rho][tau][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kE, ds_hi[rho], dacc[rho][tau][0], 0, 0, 0);
+                    dacc[rho][tau][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kE, ds_lo[rho], dacc[rho][tau][0], 0, 0, 0);
+                    dacc[rho][tau][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kO, ds_hi[rho], dacc[rho][tau][1], 0, 0, 0);
+                    dacc[rho][tau][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kO, ds_lo[rho], dacc[rho][tau][1], 0, 0, 0);
+                }
+            }
+            wave_lds_sync();  // the segment's keys have been read before the next segment writes them
+        }
+    }
+
+#pragma unroll
+    for (int rho = 0; rho < R; ++rho) {
+        if (!qin[rho]) continue;
+        bf16_t* drow = reinterpret_cast<bf16_t*>(a.dq) + qtok[rho] * C + (int64_t)eta * D;
+#pragma unroll
+        for (int tau = 0; tau < D / 32; ++tau) {  // channels 32*tau + 8g .. +7 of query c
+            const mf_f32x4& e = dacc[rho][tau][0];
+            const mf_f32x4& o = dacc[rho][tau][1];
+            uint4 w;
+            w.x = mf_pack(e[0], o[0]);
+            w.y = mf_pack(e[1], o[1]);
+            w.z = mf_pack(e[2], o[2]);
+            w.w = mf_pack(e[3], o[3]);
+            *reinterpret_cast<uint4*>(drow + 32 * tau + 8 * g) = w;
+        }
+    }
+}
+
 // Backward per query: a_p = exp(s_p - lse), ds_p = a_p (<dO, V[p]> - <dO, o>),
 // dq = scale * sum_p ds_p K[p]; <dO, o> is kept for the key kernel.
 template <typename T, int D, int Q>
@@ -558,14 +749,37 @@ hipError_t fixed_fwd_t(const FixedArgs& a, int64_t nb, hipStream_t s) {
 template <int D> hipError_t fixed_fwd_f32(const FixedArgs& a, int64_t nb, hipStream_t s) { return fixed_fwd_t<float, D>(a, nb, s); }
 template <int D> hipError_t fixed_fwd_bf16(const FixedArgs& a, int64_t nb, hipStream_t s) { return fixed_fwd_t<bf16_t, D>(a, nb, s); }
 
+// am (the matrix-core query kernel's arguments and block count) is null
+// where that kernel does not apply; rows of 256 channels keep the vector
+// kernel (the matrix-core one would not fit its registers).
 template <typename T, int D>
-hipError_t fixed_bwd_t(const FixedArgs& a, int64_t nb, hipStream_t s) {
+hipError_t fixed_bwd_t(const FixedArgs& a, int64_t nb, const FixedArgs* am, int64_t nbm, hipStream_t s) {
     {
         LaunchScope ls(DSA3D_K_BWD_QUERY, s);
-        if (a.group == kFixedGroup)
-            hipLaunchKernelGGL((dsa3d_fixed_bwd_query_kernel<T, D, kFixedGroup>), dim3((unsigned)nb), dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((dsa3d_fixed_bwd_query_kernel<T, D, 1>), dim3((unsigned)nb), dim3(256), 0, s, a);
+        bool done = false;
+        if constexpr (std::is_same<T, bf16_t>::value && D >= 32 && D <= kMfmaPairMaxD) {
+            if (am != nullptr) {
+                if constexpr (D <= kMfmaPairMaxD) {
+                    if (am->win.dil_h == 1) {
+                        hipLaunchKernelGGL((dsa3d_fixed_bwd_query_mfma_kernel<D, 2>), dim3((unsigned)nbm), dim3(256), 0,
+                                           s, *am);
+                        done = true;
+                    }
+                }
+                if (!done) {
+                    hipLaunchKernelGGL((dsa3d_fixed_bwd_query_mfma_kernel<D, 1>), dim3((unsigned)nbm), dim3(256), 0, s,
+                                       *am);
+                    done = true;
+                }
+            }
+        }
+        if (!done) {
+            if (a.group == kFixedGroup)
+                hipLaunchKernelGGL((dsa3d_fixed_bwd_query_kernel<T, D, kFixedGroup>), dim3((unsigned)nb), dim3(256), 0,
+                                   s, a);
+            else
+                hipLaunchKernelGGL((dsa3d_fixed_bwd_query_kernel<T, D, 1>), dim3((unsigned)nb), dim3(256), 0, s, a);
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -576,8 +790,14 @@ hipError_t fixed_bwd_t(const FixedArgs& a, int64_t nb, hipStream_t s) {
         hipLaunchKernelGGL((dsa3d_fixed_bwd_key_kernel<T, D, 1>), dim3((unsigned)nb), dim3(256), 0, s, a);
     return hipGetLastError();
 }
-template <int D> hipError_t fixed_bwd_f32(const FixedArgs& a, int64_t nb, hipStream_t s) { return fixed_bwd_t<float, D>(a, nb, s); }
-template <int D> hipError_t fixed_bwd_bf16(const FixedArgs& a, int64_t nb, hipStream_t s) { return fixed_bwd_t<bf16_t, D>(a, nb, s); }
+template <int D>
+hipError_t fixed_bwd_f32(const FixedArgs& a, int64_t nb, const FixedArgs* am, int64_t nbm, hipStream_t s) {
+    return fixed_bwd_t<float, D>(a, nb, am, nbm, s);
+}
+template <int D>
+hipError_t fixed_bwd_bf16(const FixedArgs& a, int64_t nb, const FixedArgs* am, int64_t nbm, hipStream_t s) {
+    return fixed_bwd_t<bf16_t, D>(a, nb, am, nbm, s);
+}
 
 }  // namespace
 
@@ -603,15 +823,21 @@ hipError_t fixed_fwd_mfma(const FixedArgs& a, int64_t nb, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Block order of the matrix-core kernels: four waves of 16 tokens along w per
+// block, each on R rows (2 when the h axis is not dilated and rows have at
+// most kMfmaPairMaxD channels).
+BlockOrder fixed_mfma_order(const dsa3d_desc& d) {
+    dsa3d_desc dr = d;
+    dr.H = d.dil_h == 1 && d.head_dim <= kMfmaPairMaxD ? (d.H + 1) / 2 : d.H;
+    return make_block_order(dr, 4 * kMfmaTokens, kGatherSupertile, "DSA3D_ORDER_FIXED_MFMA");
+}
+
 hipError_t launch_fixed_forward(const dsa3d_desc& d, const void* q, const void* k, const void* v, void* out,
                                 float* lse, hipStream_t s) {
     FixedArgs a = fixed_args(d);
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
     if (fixed_fwd_on_mfma(d)) {
-        // four waves of 16 tokens along w per block, each on R rows (2 when the h axis is not dilated)
-        dsa3d_desc dr = d;
-        dr.H = d.dil_h == 1 && d.head_dim <= kMfmaPairMaxD ? (d.H + 1) / 2 : d.H;
-        a.ord = make_block_order(dr, 4 * kMfmaTokens, kGatherSupertile, "DSA3D_ORDER_FIXED_MFMA");
+        a.ord = fixed_mfma_order(d);
         const int64_t nb = a.ord.nblk_bh * d.B * d.heads;
         if (nb == 0) return hipSuccess;
         switch (d.head_dim) {
@@ -636,8 +862,12 @@ hipError_t launch_fixed_backward(const dsa3d_desc& d, const void* q, const void*
     a.dsum = reinterpret_cast<float*>(ws);
     const int64_t nb = a.ord.nblk_bh * d.B * d.heads;
     if (nb == 0) return hipSuccess;
-    if (d.dtype == DSA3D_F32) { DSA3D_DISPATCH_D(d.head_dim, fixed_bwd_f32, a, nb, s); }
-    DSA3D_DISPATCH_D(d.head_dim, fixed_bwd_bf16, a, nb, s);
+    FixedArgs am = a;
+    am.ord = fixed_mfma_order(d);
+    const int64_t nbm = am.ord.nblk_bh * d.B * d.heads;
+    const FixedArgs* pm = fixed_fwd_on_mfma(d) ? &am : nullptr;
+    if (d.dtype == DSA3D_F32) { DSA3D_DISPATCH_D(d.head_dim, fixed_bwd_f32, a, nb, nullptr, 0, s); }
+    DSA3D_DISPATCH_D(d.head_dim, fixed_bwd_bf16, a, nb, pm, nbm, s);
 }
 
 }  // namespace dsa3d
