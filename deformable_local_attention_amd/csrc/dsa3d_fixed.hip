@@ -193,6 +193,7 @@ typedef __attribute__((ext_vector_type(4))) uint32_t mf_u32x4;
 constexpr int kMfmaTokens = 16;  // queries per wave
 constexpr int kMfmaMaxKw = 17;   // 15 + k_w keys fit two 16-key tiles
 constexpr int kMfmaPairMaxD = 128;  // rows of up to this many channels go two to a wave
+constexpr int kMfmaKeyPairMaxD = 64;  // the same for the backward per key (more accumulators)
 // The running maximum is raised only when a logit exceeds it by more than
 // this, so most segments skip the rescale; weights stay below e^8.
 constexpr float kMfmaLazyMax = 8.0f;
@@ -595,6 +596,227 @@ dsa3d_fixed_bwd_query_mfma_kernel(FixedArgs a) {
     }
 }
 
+// Backward per key on the matrix cores (bf16 rows of 32-128 channels, an
+// undilated w axis, k_w <= 17). The window is symmetric, so the queries
+// that sample the 16 keys w0 .. w0+15 of a row lie, frame by frame and row by
+// row, in the same segments of 15 + k_w tokens as the forward's keys, with
+// the same band: query slot j of a segment samples key c when 0 <= j - c < k_w.
+// A wave takes R rows of 16 keys (R = 2 when h is not dilated) and walks the
+// union of their segments; with the segment's queries and output gradients
+// staged in LDS:
+//   S^T  = Q_seg K^T,  dP^T = dO_seg V^T     (queries x keys)
+//   P    = exp(scale*S - lse_q),  dS = P (dP - <dO, o>_q)  (band, queries in the grid)
+//   dv^T += dO_seg^T P^T,  dk^T += Q_seg^T (scale*dS)^T   (weights split into a
+//                                                          bf16 part and remainder)
+// A query outside the grid does not exist, so it contributes nothing (its
+// weights are zero); a key's sums run over its window in a fixed order.
+template <int D, int R>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+dsa3d_fixed_bwd_key_mfma_kernel(FixedArgs a) {
+    constexpr int RS = D + 8;  // LDS row stride (elements), as in the forward
+    __shared__ __attribute__((aligned(16))) bf16_t s_q[4][32 * RS];
+    __shared__ __attribute__((aligned(16))) bf16_t s_g[4][32 * RS];
+    __shared__ float s_st[4][2][32];  // lse and <dO, o> of the segment's queries (0 outside the grid)
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int c = lane & 15, g = lane >> 4;
+    int64_t bh;
+    int32_t t, hr, bw0;
+    TaskGrid gr = a.g;
+    gr.H = (a.g.H + R - 1) / R;
+    block_coords(gr, a.ord, logical_block(blockIdx.x, gridDim.x, a.ord.chunk), bh, t, hr, bw0);
+    const int32_t h = R * hr;
+    const int32_t w0 = bw0 + wv * kMfmaTokens;
+    if (w0 >= a.g.W) return;  // no block-wide barrier below
+    const int32_t b = (int32_t)(bh / a.g.nheads);
+    const int32_t eta = a.g.head0 + (int32_t)(bh - (int64_t)b * a.g.nheads);
+    const uint32_t tok_b = (uint32_t)b * (uint32_t)a.g.T * (uint32_t)a.g.H * (uint32_t)a.g.W;
+    const int64_t C = (int64_t)a.g.heads * D;
+    const bf16_t* Qp = reinterpret_cast<const bf16_t*>(a.q) + (int64_t)eta * D;
+    const bf16_t* Gp = reinterpret_cast<const bf16_t*>(a.dout) + (int64_t)eta * D;
+    const bf16_t* zero = reinterpret_cast<const bf16_t*>(g_zero_row);  // 512 zero elements
+    bf16_t* qs = s_q[wv];
+    bf16_t* gs = s_g[wv];
+    float* st_lse = s_st[wv][0];
+    float* st_ds = s_st[wv][1];
+
+    const int span = kMfmaTokens - 1 + a.win.kw;
+    const int kv = lane >> 1, half = lane & 1;
+    const int32_t wkv = w0 - a.win.rw + kv;  // query column staged by this lane
+    const bool okv = kv < span && (uint32_t)wkv < (uint32_t)a.g.W;
+    const int64_t kov = (int64_t)wkv * C + half * (D / 2);
+    const int32_t wst = w0 - a.win.rw + (lane & 31);  // query column whose statistics this lane stages
+    const bool okst = (lane & 31) < span && (uint32_t)wst < (uint32_t)a.g.W;
+    const int nu = a.win.kh + R - 1;
+
+    bool kin[R];
+    int64_t ktok[R];
+    mf_bf16x8 kb[R][D / 32], vb[R][D / 32];  // own keys and values as second operands: key c, channels 32j + 8g
+    mf_f32x4 dk[R][D / 32][2], dv[R][D / 32][2];  // rows 4g + r of tile (tau, par): channel 32*tau + 8g + 2r + par
+#pragma unroll
+    for (int rho = 0; rho < R; ++rho) {
+        kin[rho] = w0 + c < a.g.W && h + rho < a.g.H;
+        ktok[rho] = (int64_t)tok_b + ((int64_t)t * a.g.H + h + rho) * a.g.W + (w0 + c);
+        const int64_t ro = ktok[rho] * C + (int64_t)eta * D + 8 * g;
+#pragma unroll
+        for (int j = 0; j < D / 32; ++j) {
+            kb[rho][j] = *reinterpret_cast<const mf_bf16x8*>(
+                kin[rho] ? reinterpret_cast<const bf16_t*>(a.k) + ro + 32 * j : zero);
+            vb[rho][j] = *reinterpret_cast<const mf_bf16x8*>(
+                kin[rho] ? reinterpret_cast<const bf16_t*>(a.v) + ro + 32 * j : zero);
+        }
+#pragma unroll
+        for (int tau = 0; tau < D / 32; ++tau)
+            dk[rho][tau][0] = dk[rho][tau][1] = dv[rho][tau][0] = dv[rho][tau][1] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    for (int it = 0; it < a.win.kt; ++it) {
+        const int32_t tt = t + a.win.dil_t * (it - a.win.rt);
+        for (int u = 0; u < nu; ++u) {
+            const int32_t hh = R == 1 ? h + a.win.dil_h * (u - a.win.rh) : h - a.win.rh + u;
+            const bool rin = (uint32_t)tt < (uint32_t)a.g.T && (uint32_t)hh < (uint32_t)a.g.H;
+            const int64_t rtok = (int64_t)tok_b + ((int64_t)tt * a.g.H + hh) * a.g.W;
+            const int64_t rb = rin ? rtok * C : 0;
+            const bf16_t* pq = rin && okv ? Qp + rb + kov : zero;
+            const bf16_t* pg = rin && okv ? Gp + rb + kov : zero;
+            uint4 qst[D / 16], gst[D / 16];
+#pragma unroll
+            for (int pc = 0; pc < D / 16; ++pc) {
+                qst[pc] = *reinterpret_cast<const uint4*>(pq + 8 * pc);
+                gst[pc] = *reinterpret_cast<const uint4*>(pg + 8 * pc);
+            }
+            const bool sin = rin && okst;
+            const float lq = sin ? a.lse[(rtok + wst) * a.g.heads + eta] : 0.0f;
+            const float dq = sin ? a.dsum[(rtok + wst) * a.g.heads + eta] : 0.0f;
+#pragma unroll
+            for (int pc = 0; pc < D / 16; ++pc) {
+                *reinterpret_cast<uint4*>(qs + kv * RS + half * (D / 2) + 8 * pc) = qst[pc];
+                *reinterpret_cast<uint4*>(gs + kv * RS + half * (D / 2) + 8 * pc) = gst[pc];
+            }
+            if (lane < 32) {
+                st_lse[lane] = lq;
+                st_ds[lane] = sin ? dq : 0.0f;
+            }
+            wave_lds_sync();  // the segment's queries are in LDS
+            // first operands: query 16T + c, channels 32j + 8g
+            mf_bf16x8 qa[2][D / 32], ga[2][D / 32];
+#pragma unroll
+            for (int T = 0; T < 2; ++T)
+#pragma unroll
+                for (int j = 0; j < D / 32; ++j) {
+                    qa[T][j] = *reinterpret_cast<const mf_bf16x8*>(qs + (16 * T + c) * RS + 32 * j + 8 * g);
+                    ga[T][j] = *reinterpret_cast<const mf_bf16x8*>(gs + (16 * T + c) * RS + 32 * j + 8 * g);
+                }
+            // statistics of this lane's queries 16T + 4g + r, and whether they lie in the grid
+            float ql[8], qd[8];
+            bool qok[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int qc = 16 * (i >> 2) + 4 * g + (i & 3);
+                ql[i] = st_lse[qc];
+                qd[i] = st_ds[qc];
+                qok[i] = rin && qc < span && (uint32_t)(w0 - a.win.rw + qc) < (uint32_t)a.g.W;
+            }
+            bool use[R];
+            mf_bf16x8 p_hi[R], p_lo[R], s_hi[R], s_lo[R];
+#pragma unroll
+            for (int rho = 0; rho < R; ++rho) {
+                use[rho] = u - rho >= 0 && u - rho < a.win.kh;  // wave-uniform
+                if (!use[rho]) continue;
+                mf_f32x4 sacc[2], pacc[2];
+#pragma unroll
+                for (int T = 0; T < 2; ++T) {
+                    sacc[T] = pacc[T] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int j = 0; j < D / 32; ++j) {
+                        sacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[T][j], kb[rho][j], sacc[T], 0, 0, 0);
+                        pacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga[T][j], vb[rho][j], pacc[T], 0, 0, 0);
+                    }
+                }
+                mf_u32x4 ph, pl, sh, sl;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float pw[2], dw[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int ii = 2 * i + e;
+                        const int qc = 16 * (ii >> 2) + 4 * g + (ii & 3);
+                        const bool band = qok[ii] && (uint32_t)(qc - c) < (uint32_t)a.win.kw;
+                        const float p = band ? __expf(a.scale * sacc[ii >> 2][ii & 3] - ql[ii]) : 0.0f;
+                        pw[e] = p;
+                        dw[e] = a.scale * p * (pacc[ii >> 2][ii & 3] - qd[ii]);
+                    }
+                    const uint32_t hp = mf_pack(pw[0], pw[1]), hs = mf_pack(dw[0], dw[1]);
+                    ph[i] = hp;
+                    pl[i] = mf_pack(pw[0] - bf16_lo(hp), pw[1] - bf16_hi(hp));
+                    sh[i] = hs;
+                    sl[i] = mf_pack(dw[0] - bf16_lo(hs), dw[1] - bf16_hi(hs));
+                }
+                p_hi[rho] = __builtin_bit_cast(mf_bf16x8, ph);
+                p_lo[rho] = __builtin_bit_cast(mf_bf16x8, pl);
+                s_hi[rho] = __builtin_bit_cast(mf_bf16x8, sh);
+                s_lo[rho] = __builtin_bit_cast(mf_bf16x8, sl);
+            }
+            // dv^T += dO^T P^T and dk^T += Q^T (scale dS)^T, the query rows read a
+            // channel pair at a time; element 8g + i of the k-slice is query 4g + i
+            // (i < 4) or 16 + 4g + i - 4
+#pragma unroll
+            for (int tau = 0; tau < D / 32; ++tau) {
+                uint32_t dq8[8], dg8[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int qr = i < 4 ? 4 * g + i : 12 + 4 * g + i;
+                    dq8[i] = *reinterpret_cast<const uint32_t*>(qs + qr * RS + 32 * tau + 2 * c);
+                    dg8[i] = *reinterpret_cast<const uint32_t*>(gs + qr * RS + 32 * tau + 2 * c);
+                }
+                mf_u32x4 qe, qo, ge, go;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    qe[i] = __builtin_amdgcn_perm(dq8[2 * i + 1], dq8[2 * i], 0x05040100u);
+                    qo[i] = __builtin_amdgcn_perm(dq8[2 * i + 1], dq8[2 * i], 0x07060302u);
+                    ge[i] = __builtin_amdgcn_perm(dg8[2 * i + 1], dg8[2 * i], 0x05040100u);
+                    go[i] = __builtin_amdgcn_perm(dg8[2 * i + 1], dg8[2 * i], 0x07060302u);
+                }
+                const mf_bf16x8 qE = __builtin_bit_cast(mf_bf16x8, qe), qO = __builtin_bit_cast(mf_bf16x8, qo);
+                const mf_bf16x8 gE = __builtin_bit_cast(mf_bf16x8, ge), gO = __builtin_bit_cast(mf_bf16x8, go);
+#pragma unroll
+                for (int rho = 0; rho < R; ++rho) {
+                    if (!use[rho]) continue;
+                    dv[rho][tau][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gE, p_hi[rho], dv[rho][tau][0], 0, 0, 0);
+                    dv[rho][tau][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gE, p_lo[rho], dv[rho][tau][0], 0, 0, 0);
+                    dv[rho][tau][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gO, p_hi[rho], dv[rho][tau][1], 0, 0, 0);
+                    dv[rho][tau][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gO, p_lo[rho], dv[rho][tau][1], 0, 0, 0);
+                    dk[rho][tau][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qE, s_hi[rho], dk[rho][tau][0], 0, 0, 0);
+                    dk[rho][tau][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qE, s_lo[rho], dk[rho][tau][0], 0, 0, 0);
+                    dk[rho][tau][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qO, s_hi[rho], dk[rho][tau][1], 0, 0, 0);
+                    dk[rho][tau][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qO, s_lo[rho], dk[rho][tau][1], 0, 0, 0);
+                }
+            }
+            wave_lds_sync();  // the segment's queries have been read before the next segment writes them
+        }
+    }
+
+#pragma unroll
+    for (int rho = 0; rho < R; ++rho) {
+        if (!kin[rho]) continue;
+        bf16_t* krow = reinterpret_cast<bf16_t*>(a.dk) + ktok[rho] * C + (int64_t)eta * D;
+        bf16_t* vrow = reinterpret_cast<bf16_t*>(a.dv) + ktok[rho] * C + (int64_t)eta * D;
+#pragma unroll
+        for (int tau = 0; tau < D / 32; ++tau) {  // channels 32*tau + 8g .. +7 of key c
+            uint4 w;
+            w.x = mf_pack(dk[rho][tau][0][0], dk[rho][tau][1][0]);
+            w.y = mf_pack(dk[rho][tau][0][1], dk[rho][tau][1][1]);
+            w.z = mf_pack(dk[rho][tau][0][2], dk[rho][tau][1][2]);
+            w.w = mf_pack(dk[rho][tau][0][3], dk[rho][tau][1][3]);
+            *reinterpret_cast<uint4*>(krow + 32 * tau + 8 * g) = w;
+            w.x = mf_pack(dv[rho][tau][0][0], dv[rho][tau][1][0]);
+            w.y = mf_pack(dv[rho][tau][0][1], dv[rho][tau][1][1]);
+            w.z = mf_pack(dv[rho][tau][0][2], dv[rho][tau][1][2]);
+            w.w = mf_pack(dv[rho][tau][0][3], dv[rho][tau][1][3]);
+            *reinterpret_cast<uint4*>(vrow + 32 * tau + 8 * g) = w;
+        }
+    }
+}
+
 // Backward per query: a_p = exp(s_p - lse), ds_p = a_p (<dO, V[p]> - <dO, o>),
 // dq = scale * sum_p ds_p K[p]; <dO, o> is kept for the key kernel.
 template <typename T, int D, int Q>
@@ -749,11 +971,12 @@ hipError_t fixed_fwd_t(const FixedArgs& a, int64_t nb, hipStream_t s) {
 template <int D> hipError_t fixed_fwd_f32(const FixedArgs& a, int64_t nb, hipStream_t s) { return fixed_fwd_t<float, D>(a, nb, s); }
 template <int D> hipError_t fixed_fwd_bf16(const FixedArgs& a, int64_t nb, hipStream_t s) { return fixed_fwd_t<bf16_t, D>(a, nb, s); }
 
-// am (the matrix-core query kernel's arguments and block count) is null
-// where that kernel does not apply; rows of 256 channels keep the vector
-// kernel (the matrix-core one would not fit its registers).
+// am and ak (the matrix-core query and key kernels' arguments and block
+// counts) are null where those kernels do not apply; rows of 256 channels
+// keep the vector kernels (the matrix-core ones would not fit their registers).
 template <typename T, int D>
-hipError_t fixed_bwd_t(const FixedArgs& a, int64_t nb, const FixedArgs* am, int64_t nbm, hipStream_t s) {
+hipError_t fixed_bwd_t(const FixedArgs& a, int64_t nb, const FixedArgs* am, int64_t nbm, const FixedArgs* ak,
+                       int64_t nbk, hipStream_t s) {
     {
         LaunchScope ls(DSA3D_K_BWD_QUERY, s);
         bool done = false;
@@ -784,6 +1007,19 @@ hipError_t fixed_bwd_t(const FixedArgs& a, int64_t nb, const FixedArgs* am, int6
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     LaunchScope ls(DSA3D_K_BWD_KEY, s);
+    if constexpr (std::is_same<T, bf16_t>::value && D >= 32 && D <= kMfmaPairMaxD) {
+        if (ak != nullptr) {
+            if constexpr (D <= kMfmaKeyPairMaxD) {
+                if (ak->win.dil_h == 1) {
+                    hipLaunchKernelGGL((dsa3d_fixed_bwd_key_mfma_kernel<D, 2>), dim3((unsigned)nbk), dim3(256), 0, s,
+                                       *ak);
+                    return hipGetLastError();
+                }
+            }
+            hipLaunchKernelGGL((dsa3d_fixed_bwd_key_mfma_kernel<D, 1>), dim3((unsigned)nbk), dim3(256), 0, s, *ak);
+            return hipGetLastError();
+        }
+    }
     if (a.group == kFixedGroup)
         hipLaunchKernelGGL((dsa3d_fixed_bwd_key_kernel<T, D, kFixedGroup>), dim3((unsigned)nb), dim3(256), 0, s, a);
     else
@@ -791,12 +1027,14 @@ hipError_t fixed_bwd_t(const FixedArgs& a, int64_t nb, const FixedArgs* am, int6
     return hipGetLastError();
 }
 template <int D>
-hipError_t fixed_bwd_f32(const FixedArgs& a, int64_t nb, const FixedArgs* am, int64_t nbm, hipStream_t s) {
-    return fixed_bwd_t<float, D>(a, nb, am, nbm, s);
+hipError_t fixed_bwd_f32(const FixedArgs& a, int64_t nb, const FixedArgs* am, int64_t nbm, const FixedArgs* ak,
+                         int64_t nbk, hipStream_t s) {
+    return fixed_bwd_t<float, D>(a, nb, am, nbm, ak, nbk, s);
 }
 template <int D>
-hipError_t fixed_bwd_bf16(const FixedArgs& a, int64_t nb, const FixedArgs* am, int64_t nbm, hipStream_t s) {
-    return fixed_bwd_t<bf16_t, D>(a, nb, am, nbm, s);
+hipError_t fixed_bwd_bf16(const FixedArgs& a, int64_t nb, const FixedArgs* am, int64_t nbm, const FixedArgs* ak,
+                          int64_t nbk, hipStream_t s) {
+    return fixed_bwd_t<bf16_t, D>(a, nb, am, nbm, ak, nbk, s);
 }
 
 }  // namespace
@@ -825,10 +1063,10 @@ hipError_t fixed_fwd_mfma(const FixedArgs& a, int64_t nb, hipStream_t s) {
 
 // Block order of the matrix-core kernels: four waves of 16 tokens along w per
 // block, each on R rows (2 when the h axis is not dilated and rows have at
-// most kMfmaPairMaxD channels).
-BlockOrder fixed_mfma_order(const dsa3d_desc& d) {
+// most pair_max_d channels).
+BlockOrder fixed_mfma_order(const dsa3d_desc& d, int pair_max_d) {
     dsa3d_desc dr = d;
-    dr.H = d.dil_h == 1 && d.head_dim <= kMfmaPairMaxD ? (d.H + 1) / 2 : d.H;
+    dr.H = d.dil_h == 1 && d.head_dim <= pair_max_d ? (d.H + 1) / 2 : d.H;
     return make_block_order(dr, 4 * kMfmaTokens, kGatherSupertile, "DSA3D_ORDER_FIXED_MFMA");
 }
 
@@ -837,7 +1075,7 @@ hipError_t launch_fixed_forward(const dsa3d_desc& d, const void* q, const void* 
     FixedArgs a = fixed_args(d);
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
     if (fixed_fwd_on_mfma(d)) {
-        a.ord = fixed_mfma_order(d);
+        a.ord = fixed_mfma_order(d, kMfmaPairMaxD);
         const int64_t nb = a.ord.nblk_bh * d.B * d.heads;
         if (nb == 0) return hipSuccess;
         switch (d.head_dim) {
@@ -862,12 +1100,13 @@ hipError_t launch_fixed_backward(const dsa3d_desc& d, const void* q, const void*
     a.dsum = reinterpret_cast<float*>(ws);
     const int64_t nb = a.ord.nblk_bh * d.B * d.heads;
     if (nb == 0) return hipSuccess;
-    FixedArgs am = a;
-    am.ord = fixed_mfma_order(d);
-    const int64_t nbm = am.ord.nblk_bh * d.B * d.heads;
-    const FixedArgs* pm = fixed_fwd_on_mfma(d) ? &am : nullptr;
-    if (d.dtype == DSA3D_F32) { DSA3D_DISPATCH_D(d.head_dim, fixed_bwd_f32, a, nb, nullptr, 0, s); }
-    DSA3D_DISPATCH_D(d.head_dim, fixed_bwd_bf16, a, nb, pm, nbm, s);
+    FixedArgs am = a, ak = a;
+    am.ord = fixed_mfma_order(d, kMfmaPairMaxD);
+    ak.ord = fixed_mfma_order(d, kMfmaKeyPairMaxD);
+    const int64_t nbm = am.ord.nblk_bh * d.B * d.heads, nbk = ak.ord.nblk_bh * d.B * d.heads;
+    const bool mf = fixed_fwd_on_mfma(d);
+    if (d.dtype == DSA3D_F32) { DSA3D_DISPATCH_D(d.head_dim, fixed_bwd_f32, a, nb, nullptr, 0, nullptr, 0, s); }
+    DSA3D_DISPATCH_D(d.head_dim, fixed_bwd_bf16, a, nb, mf ? &am : nullptr, nbm, mf ? &ak : nullptr, nbk, s);
 }
 
 }  // namespace dsa3d
