@@ -98,6 +98,24 @@ def algorithmic(wl):
     }
 
 
+def fixed_on_mfma(wl):
+    """Rows per wave of the fixed window's matrix-core kernels, per kernel, or
+    None where libdsa3d runs the fixed window on the vector units: bf16 rows of
+    32-256 channels (32-128 for the backward), no dilation along w, k_w <= 17;
+    two rows per wave when h is not dilated and rows have at most 128 channels
+    (64 for the key kernel)."""
+    d = wl.head_dim
+    if wl.offsets != "none" or wl.dtype != "bf16" or d not in (32, 64, 128, 256) or wl.dilation[2] != 1 \
+            or wl.window[2] > 17:
+        return None
+    und = wl.dilation[1] == 1
+    rows = {"forward": 2 if und and d <= 128 else 1}
+    if d <= 128:
+        rows["bwd_query"] = 2 if und else 1
+        rows["bwd_key"] = 2 if und and d <= 64 else 1
+    return rows
+
+
 def cpu_baseline(wl, budget_s: float = 20.0):
     """The oracle, as it is, on a bounded sample of the same workload: the
     interior queries of a 16x24x24-token crop drawn with the workload's
@@ -369,8 +387,11 @@ def main():
     traffic = recorded_traffic(kname, wl.name)
     unit_flops = alg[dom + "_flops"]
     achieved_tf = unit_flops * units / mean_s / 1e12
-    roofline = {"bound": "alu", "kernel": dom, "achieved": round(achieved_tf, 3), "peak": VALU_F32_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved_tf / VALU_F32_PEAK_TFLOPS, 5),
+    mf_rows = fixed_on_mfma(wl)
+    on_mfma = mf_rows is not None and dom in mf_rows  # the fixed window's matrix-core kernels
+    peak = MFMA_BF16_PEAK_TFLOPS if on_mfma else VALU_F32_PEAK_TFLOPS
+    roofline = {"bound": "mfma" if on_mfma else "alu", "kernel": dom, "achieved": round(achieved_tf, 3),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved_tf / peak, 5),
                 "traffic": None if traffic is None else round(traffic),
                 "launch_ms": round(per_kernel[dom]["mean_ms"], 3), "units_per_launch": units,
                 "flops_per_unit": unit_flops}
@@ -390,7 +411,9 @@ def main():
     # query and output-gradient rows of each record once per 2x2 group of keys it reaches, 4.5 groups per
     # sample on average (18 buckets per group of 4 keys instead of 8 per key): 9*d*s*P. The fixed window
     # reads 2 rows per window column, shared by the 4 tokens of a task along w when w is not dilated:
-    # 2 * (4 + k_w - 1) / (4 * k_w) rows per sample. These bytes pass through each CU's vector L1 and its
+    # 2 * (4 + k_w - 1) / (4 * k_w) rows per sample; its matrix-core kernels load, per wave of R rows of
+    # 16 tokens, two tensors' rows of 32 tokens for each of the k_t * (k_h + R - 1) segments of the union
+    # of their windows. These bytes pass through each CU's vector L1 and its
     # texture-data path, which rocprofv3 shows 98-99% busy in all three kernels; the ceiling is the L1
     # load rate measured with a probe kernel streaming 16-byte loads from an L1-resident buffer,
     # 64 B per clock per CU (256 CUs at 2.4 GHz).
@@ -398,12 +421,16 @@ def main():
     rows_per_sample = {"forward": 16, "bwd_query": 16, "bwd_key": 9}
     roofline_gather = {}
     for k in attn:
-        if wl.offsets == "none":
-            kw = wl.window[2]
-            rows = 2.0 * (4 + kw - 1) / (4 * kw) if wl.dilation[2] == 1 else 2.0
+        if mf_rows is not None and k in mf_rows:
+            r = mf_rows[k]
+            gather_unit = wl.window[0] * (wl.window[1] + r - 1) * 2 * 32 * wl.head_dim * s_el / (16 * r)
         else:
-            rows = rows_per_sample[k]
-        gather_unit = rows * wl.head_dim * s_el * wl.P
+            if wl.offsets == "none":
+                kw = wl.window[2]
+                rows = 2.0 * (4 + kw - 1) / (4 * kw) if wl.dilation[2] == 1 else 2.0
+            else:
+                rows = rows_per_sample[k]
+            gather_unit = rows * wl.head_dim * s_el * wl.P
         u = wl.tokens * wl.heads * args.steps / per_kernel[k]["launches"]
         tbs = gather_unit * u / (per_kernel[k]["mean_ms"] / 1e3) / 1e12
         roofline_gather[k] = {"bound": "l1", "achieved": round(tbs, 2), "peak": L1_LOAD_PEAK_TBS, "unit": "TB/s",

@@ -43,6 +43,24 @@ def test_fixed_window_accounting():
     assert alg["bwd_query_flops"] + alg["bwd_key_flops"] == alg["bwd_flops"] == 10 * d * P
 
 
+def test_fixed_window_matrix_core_eligibility():
+    """The shapes bench.py reports against the MFMA peak are those the library
+    runs on the matrix cores (bf16, 32-256 channels forward, 32-128 backward,
+    undilated w, k_w <= 17; two rows per wave where h is undilated)."""
+    wl = synth.WORKLOADS["1080p-bf16-fixed377"]
+    assert bench.fixed_on_mfma(wl) == {"forward": 2, "bwd_query": 2, "bwd_key": 1}
+    mk = lambda **kw: synth.Workload("f", 1, 2, 3, 4, kw.get("heads", 2), kw.get("d", 64), kw.get("win", (3, 7, 7)),
+                                     kw.get("dil", (1, 1, 1)), kw.get("dtype", "bf16"), "none", backward=True)
+    assert bench.fixed_on_mfma(mk(d=64)) == {"forward": 2, "bwd_query": 2, "bwd_key": 2}
+    assert bench.fixed_on_mfma(mk(d=256)) == {"forward": 1}
+    assert bench.fixed_on_mfma(mk(dil=(1, 2, 1))) == {"forward": 1, "bwd_query": 1, "bwd_key": 1}
+    assert bench.fixed_on_mfma(mk(dtype="f32")) is None
+    assert bench.fixed_on_mfma(mk(d=16)) is None
+    assert bench.fixed_on_mfma(mk(dil=(1, 1, 2))) is None
+    assert bench.fixed_on_mfma(mk(win=(1, 1, 19))) is None
+    assert bench.fixed_on_mfma(synth.WORKLOADS[synth.HEADLINE]) is None
+
+
 def test_code_hash_ignores_comments_and_layout():
     a = "int f(int x) {  // first\n    return x + 1; /* block\n comment */ }\n"
     b = "int f(int x)\n{\n    return x + 1;\n}\n"
