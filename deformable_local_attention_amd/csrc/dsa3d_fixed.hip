@@ -17,9 +17,10 @@
 //
 // Lane groups (L = head_dim/8 lanes, 8 channels each) and the block order are
 // those of the general kernels; a task owns a few neighbouring tokens along w.
-// For bf16 rows of 32-256 channels with an undilated w axis and k_w <= 17 the
-// forward runs on the matrix cores instead (dsa3d_fixed_fwd_mfma_kernel): the
-// queries of a row and their keys form a banded dense product there.
+// For bf16 rows with an undilated w axis and k_w <= 17 the kernels run on the
+// matrix cores instead (the forward for rows of 32-256 channels, the backward
+// for 32-128): the queries of a row and their keys form banded dense
+// products there.
 #include "dsa3d_attn_common.h"
 #include "dsa3d_internal.h"
 
