@@ -249,6 +249,24 @@ def test_fixed_window_whole(case):
     _run_whole(wl, synth.make_inputs(wl, "cpu", seed=41))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_fixed_window_matrix_core_path_is_bitwise_reproducible(d):
+    """Every sum of the matrix-core kernels runs over the window in a fixed
+    order: two runs give the same bits, and the backward leaves the forward's
+    outputs untouched."""
+    wl = synth.Workload("fixed", 1, 4, 9, 37, 2, d, (3, 7, 7), (1, 1, 1), "bf16", "none", backward=True)
+    x = {k: v.to(DEV) for k, v in synth.make_inputs(wl, "cpu", seed=47).items()}
+    outs = []
+    for _ in range(2):
+        ch = Chain(wl, x)
+        ch.run()
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (ch.out, ch.lse, ch.dq, ch.dk, ch.dv)])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_fixed_window_equals_general_path_at_zero_offsets(dtype):
     """offsets NULL and a zero offsets tensor. The vector kernels (f32) give
