@@ -233,7 +233,8 @@ def test_deterministic_mode_is_bitwise_reproducible_across_runs_and_pass_splits(
 # rows of 32-256 channels with an undilated w axis and k_w <= 17 take the
 # matrix-core forward: a row shorter than one wave's 16 tokens, rows of
 # 16 + 16 + 5 tokens, the widest band (k_w = 17), k_w = 1 with dilated t and
-# h, 256 channels; k_w = 19 and a dilated w axis take the vector kernels.
+# h, 256 channels, a window wider than the grid, one token per batch item;
+# k_w = 19 and a dilated w axis take the vector kernels.
 @pytest.mark.parametrize("case", [("f32", 2, 3, 5, 11, 2, 32, (3, 7, 7), (1, 1, 1)),
                                   ("bf16", 1, 4, 9, 13, 3, 128, (3, 7, 7), (1, 1, 1)),
                                   ("bf16", 2, 3, 4, 37, 2, 128, (3, 7, 7), (1, 1, 1)),
@@ -241,6 +242,8 @@ def test_deterministic_mode_is_bitwise_reproducible_across_runs_and_pass_splits(
                                   ("bf16", 1, 6, 7, 20, 3, 32, (3, 3, 1), (2, 3, 1)),
                                   ("bf16", 1, 2, 3, 18, 1, 256, (1, 3, 5), (1, 1, 1)),
                                   ("bf16", 1, 2, 3, 25, 2, 64, (1, 1, 19), (1, 1, 1)),
+                                  ("bf16", 1, 2, 2, 3, 2, 64, (5, 5, 7), (1, 1, 1)),
+                                  ("bf16", 2, 1, 1, 1, 3, 128, (3, 7, 7), (1, 1, 1)),
                                   ("bf16", 1, 5, 8, 10, 2, 64, (3, 3, 3), (1, 2, 2)),
                                   ("f32", 1, 2, 3, 4, 1, 8, (3, 7, 7), (2, 1, 1))])
 def test_fixed_window_whole(case):
