@@ -147,8 +147,10 @@ int dsa3d_forward(const dsa3d_desc* desc, const void* q, const void* k, const vo
  * offsets == NULL (and doffsets == NULL; one without the other is
  * DSA3D_ERR_INVALID_ARG) is the fixed window of dsa3d_forward: no offset
  * gradient; each key walks the queries whose window contains it, so dk and dv
- * are summed in a fixed order for either value of `deterministic`; the
- * workspace (DSA3D_WS_BACKWARD_FIXED) holds one float per (token, head). */
+ * are summed in a fixed order for either value of `deterministic` (bf16 rows
+ * of 32-128 channels with k_w <= 17 and no dilation along w run these sums on
+ * the matrix cores, also in a fixed order); the workspace
+ * (DSA3D_WS_BACKWARD_FIXED) holds one float per (token, head). */
 int dsa3d_backward(const dsa3d_desc* desc, const void* q, const void* k, const void* v,
                    const void* offsets, const void* out, const float* lse, const void* dout,
                    void* dq, void* dk, void* dv, void* doffsets,
