@@ -206,11 +206,66 @@ __device__ __forceinline__ uint32_t mf_pack(float lo, float hi) {  // two RNE bf
 
 // One window segment's operands: the two 16-key tiles of keys for the first
 // product (key 16*T + l%16, channels 32j + 8*(l/16) .. +7) and this lane's
-// part of the value rows (half l%2 of key l/2) on their way to LDS.
+// part of the value rows on their way to LDS.
 template <int D>
 struct MfmaSeg {
     mf_bf16x8 k[2][D / 32];
     uint4 v[D / 16];
+};
+
+// Staging of a segment's 32 rows (tokens w_first .. w_first + 31 of one
+// (frame, row)) into LDS: load i takes rows i*(512/D) + l/(D/8), lane l
+// reading the 16 bytes at channel 8*(l%(D/8)), so the lanes of one row read it
+// whole and in order and a load touches only full cache lines. The loads go
+// through a buffer resource spanning the grid row (no records when the row lies
+// outside the grid), and a row outside the segment or the grid gets an offset
+// past the records: either way the hardware returns zeros. Which rows lie in
+// the segment and the grid does not change along the window, so a lane's
+// offsets are fixed. (A grid row of the head-interleaved tensor must stay
+// below 2 GiB, the records limit.)
+constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 buffer resource: untyped 32-bit data format
+constexpr uint32_t kPastRecords = 0x80000000u;
+
+template <int D>
+struct SegStage {
+    static constexpr int kLanes = D / 8;       // lanes per row
+    static constexpr int kRows = 64 / kLanes;  // rows per load
+    static constexpr int kLoads = D / 16;      // loads per segment
+    static constexpr bool kTable = kLoads <= 8;  // offsets kept in registers (else formed per load)
+    int lds;                            // LDS element offset of this lane's 16 bytes in load 0
+    uint32_t off[kTable ? kLoads : 1];  // byte offset of load i from the segment row's first token
+    uint32_t off0, step, ok;            // the same formed per load: load 0's row (mod 2^32), step, bit i = in
+    int32_t nrec;                       // bytes of a grid row
+    __device__ SegStage(int lane, int32_t w_first, int span, int32_t W, int64_t C, int RS) {
+        const int row = lane / kLanes, ch = 8 * (lane % kLanes);
+        lds = row * RS + ch;
+        off0 = (uint32_t)(((int64_t)(w_first + row) * C + ch) * 2);
+        step = (uint32_t)(kRows * C * 2);
+        nrec = (int32_t)((int64_t)W * C * 2);
+        ok = 0;
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            const int r = i * kRows + row;
+            const bool in = r < span && (uint32_t)(w_first + r) < (uint32_t)W;
+            ok |= (uint32_t)in << i;
+            if constexpr (kTable) off[i] = in ? off0 + (uint32_t)i * step : kPastRecords;
+        }
+    }
+    // the resource of the grid row starting at `rowp` (its first token, this head)
+    __device__ __amdgpu_buffer_rsrc_t rsrc(const bf16_t* rowp, bool in_grid) const {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(rowp), (short)0, in_grid ? nrec : 0,
+                                                 kRawBufferWord3);
+    }
+    __device__ uint4 load(__amdgpu_buffer_rsrc_t r, int i) const {
+        uint32_t o;
+        if constexpr (kTable) o = off[i];
+        else o = ((ok >> i) & 1u) ? off0 + (uint32_t)i * step : kPastRecords;
+        const mf_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0);
+        return uint4{v[0], v[1], v[2], v[3]};
+    }
+    __device__ void put(bf16_t* s, int RS, int i, const uint4& x) const {
+        *reinterpret_cast<uint4*>(s + lds + i * kRows * RS) = x;
+    }
 };
 
 // A wave takes R rows h .. h+R-1 of 16 tokens (R = 2 when the window is not
@@ -253,13 +308,11 @@ dsa3d_fixed_fwd_mfma_kernel(FixedArgs a) {
     // in the grid and the segment: keys c and 16 + c of the first product,
     // key l/2 of the value staging.
     const int span = kMfmaTokens - 1 + a.win.kw;
-    const int kv = lane >> 1, half = lane & 1;
-    const int32_t wk0 = w0 - a.win.rw + c, wk1 = wk0 + 16, wkv = w0 - a.win.rw + kv;
+    const int32_t wk0 = w0 - a.win.rw + c, wk1 = wk0 + 16;
     const bool ok0 = c < span && (uint32_t)wk0 < (uint32_t)a.g.W;
     const bool ok1 = 16 + c < span && (uint32_t)wk1 < (uint32_t)a.g.W;
-    const bool okv = kv < span && (uint32_t)wkv < (uint32_t)a.g.W;
     const int64_t ko0 = (int64_t)wk0 * C + 8 * g, ko1 = (int64_t)wk1 * C + 8 * g;
-    const int64_t kov = (int64_t)wkv * C + half * (D / 2);
+    const SegStage<D> vst(lane, w0 - a.win.rw, span, a.g.W, C, RS);
     const int nu = a.win.kh + R - 1;  // segment rows of the union per frame
 
     // Q as the second operand of the first product: query c, channels 32j + 8g .. +7
@@ -289,19 +342,19 @@ dsa3d_fixed_fwd_mfma_kernel(FixedArgs a) {
             // a key outside the grid reads the zero row (offsets below stay within its 512 elements)
             const bf16_t* p0 = rin && ok0 ? K + rb + ko0 : zero;
             const bf16_t* p1 = rin && ok1 ? K + rb + ko1 : zero;
-            const bf16_t* pv = rin && okv ? V + rb + kov : zero;
             MfmaSeg<D> cur;
 #pragma unroll
             for (int j = 0; j < D / 32; ++j) {
                 cur.k[0][j] = *reinterpret_cast<const mf_bf16x8*>(p0 + 32 * j);
                 cur.k[1][j] = *reinterpret_cast<const mf_bf16x8*>(p1 + 32 * j);
             }
+            const __amdgpu_buffer_rsrc_t vr = vst.rsrc(V + rb, rin);
 #pragma unroll
-            for (int pc = 0; pc < D / 16; ++pc) cur.v[pc] = *reinterpret_cast<const uint4*>(pv + 8 * pc);
+            for (int pc = 0; pc < D / 16; ++pc) cur.v[pc] = vst.load(vr, pc);
             wave_lds_sync();  // the previous segment's values have been read
 #pragma unroll
             for (int pc = 0; pc < D / 16; ++pc)
-                *reinterpret_cast<uint4*>(vs + kv * RS + half * (D / 2) + 8 * pc) = cur.v[pc];
+                vst.put(vs, RS, pc, cur.v[pc]);
             bool use[R];
             mf_bf16x8 pb_hi[R], pb_lo[R];
 #pragma unroll
@@ -443,13 +496,11 @@ dsa3d_fixed_bwd_query_mfma_kernel(FixedArgs a) {
     bf16_t* ks = s_k[wv];
 
     const int span = kMfmaTokens - 1 + a.win.kw;
-    const int kv = lane >> 1, half = lane & 1;
-    const int32_t wk0 = w0 - a.win.rw + c, wk1 = wk0 + 16, wkv = w0 - a.win.rw + kv;
+    const int32_t wk0 = w0 - a.win.rw + c, wk1 = wk0 + 16;
     const bool ok0 = c < span && (uint32_t)wk0 < (uint32_t)a.g.W;
     const bool ok1 = 16 + c < span && (uint32_t)wk1 < (uint32_t)a.g.W;
-    const bool okv = kv < span && (uint32_t)wkv < (uint32_t)a.g.W;
     const int64_t ko0 = (int64_t)wk0 * C + 8 * g, ko1 = (int64_t)wk1 * C + 8 * g;
-    const int64_t kov = (int64_t)wkv * C + half * (D / 2);
+    const SegStage<D> kst_map(lane, w0 - a.win.rw, span, a.g.W, C, RS);
     const int nu = a.win.kh + R - 1;
 
     bool qin[R];
@@ -494,7 +545,6 @@ dsa3d_fixed_bwd_query_mfma_kernel(FixedArgs a) {
             const int64_t rb = rin ? ((int64_t)tok_b + ((int64_t)tt * a.g.H + hh) * a.g.W) * C : 0;
             const bf16_t* p0 = rin && ok0 ? V + rb + ko0 : zero;
             const bf16_t* p1 = rin && ok1 ? V + rb + ko1 : zero;
-            const bf16_t* pk = rin && okv ? K + rb + kov : zero;
             mf_bf16x8 va[2][D / 32];  // values as the second product's first operand
             uint4 kst[D / 16];        // this lane's part of the key rows, on their way to LDS
 #pragma unroll
@@ -502,11 +552,12 @@ dsa3d_fixed_bwd_query_mfma_kernel(FixedArgs a) {
                 va[0][j] = *reinterpret_cast<const mf_bf16x8*>(p0 + 32 * j);
                 va[1][j] = *reinterpret_cast<const mf_bf16x8*>(p1 + 32 * j);
             }
+            const __amdgpu_buffer_rsrc_t kr = kst_map.rsrc(K + rb, rin);
 #pragma unroll
-            for (int pc = 0; pc < D / 16; ++pc) kst[pc] = *reinterpret_cast<const uint4*>(pk + 8 * pc);
+            for (int pc = 0; pc < D / 16; ++pc) kst[pc] = kst_map.load(kr, pc);
 #pragma unroll
             for (int pc = 0; pc < D / 16; ++pc)
-                *reinterpret_cast<uint4*>(ks + kv * RS + half * (D / 2) + 8 * pc) = kst[pc];
+                kst_map.put(ks, RS, pc, kst[pc]);
             wave_lds_sync();  // the segment's keys are in LDS
             mf_bf16x8 ka[2][D / 32];  // keys as the first product's first operand: key 16T + c, channels 32j + 8g
 #pragma unroll
@@ -641,10 +692,7 @@ dsa3d_fixed_bwd_key_mfma_kernel(FixedArgs a) {
     float* st_ds = s_st[wv][1];
 
     const int span = kMfmaTokens - 1 + a.win.kw;
-    const int kv = lane >> 1, half = lane & 1;
-    const int32_t wkv = w0 - a.win.rw + kv;  // query column staged by this lane
-    const bool okv = kv < span && (uint32_t)wkv < (uint32_t)a.g.W;
-    const int64_t kov = (int64_t)wkv * C + half * (D / 2);
+    const SegStage<D> qst_map(lane, w0 - a.win.rw, span, a.g.W, C, RS);  // the segment's queries
     const int32_t wst = w0 - a.win.rw + (lane & 31);  // query column whose statistics this lane stages
     const bool okst = (lane & 31) < span && (uint32_t)wst < (uint32_t)a.g.W;
     const int nu = a.win.kh + R - 1;
@@ -677,21 +725,20 @@ dsa3d_fixed_bwd_key_mfma_kernel(FixedArgs a) {
             const bool rin = (uint32_t)tt < (uint32_t)a.g.T && (uint32_t)hh < (uint32_t)a.g.H;
             const int64_t rtok = (int64_t)tok_b + ((int64_t)tt * a.g.H + hh) * a.g.W;
             const int64_t rb = rin ? rtok * C : 0;
-            const bf16_t* pq = rin && okv ? Qp + rb + kov : zero;
-            const bf16_t* pg = rin && okv ? Gp + rb + kov : zero;
+            const __amdgpu_buffer_rsrc_t qr = qst_map.rsrc(Qp + rb, rin), gres = qst_map.rsrc(Gp + rb, rin);
             uint4 qst[D / 16], gst[D / 16];
 #pragma unroll
             for (int pc = 0; pc < D / 16; ++pc) {
-                qst[pc] = *reinterpret_cast<const uint4*>(pq + 8 * pc);
-                gst[pc] = *reinterpret_cast<const uint4*>(pg + 8 * pc);
+                qst[pc] = qst_map.load(qr, pc);
+                gst[pc] = qst_map.load(gres, pc);
             }
             const bool sin = rin && okst;
             const float lq = sin ? a.lse[(rtok + wst) * a.g.heads + eta] : 0.0f;
             const float dq = sin ? a.dsum[(rtok + wst) * a.g.heads + eta] : 0.0f;
 #pragma unroll
             for (int pc = 0; pc < D / 16; ++pc) {
-                *reinterpret_cast<uint4*>(qs + kv * RS + half * (D / 2) + 8 * pc) = qst[pc];
-                *reinterpret_cast<uint4*>(gs + kv * RS + half * (D / 2) + 8 * pc) = gst[pc];
+                qst_map.put(qs, RS, pc, qst[pc]);
+                qst_map.put(gs, RS, pc, gst[pc]);
             }
             if (lane < 32) {
                 st_lse[lane] = lq;
@@ -1046,7 +1093,7 @@ size_t fixed_bwd_workspace_bytes(const dsa3d_desc& d) {
 
 bool fixed_fwd_on_mfma(const dsa3d_desc& d) {
     return d.dtype == DSA3D_BF16 && (d.head_dim == 32 || d.head_dim == 64 || d.head_dim == 128 || d.head_dim == 256) &&
-           d.dil_w == 1 && d.kw <= kMfmaMaxKw;
+           d.dil_w == 1 && d.kw <= kMfmaMaxKw && (int64_t)d.W * d.heads * d.head_dim * 2 <= (int64_t)INT32_MAX;
 }
 
 template <int D>
