@@ -39,7 +39,8 @@ struct FixedArgs {
     void* dq;
     void* dk;
     void* dv;
-    float* dsum;  // <dO, o> per task, [B,T,H,W,heads]
+    float* dsum;  // <dO, o> per task, [B,T,H,W,heads]; the matrix-core kernels keep (lse, <dO, o>)
+                  // pairs in head-major order, [B,heads,T,H,W], so a row of queries is contiguous
     int32_t group;  // tokens per task along w: kFixedGroup, or 1 with a dilated w axis
     TaskGrid g;
     BlockOrder ord;
@@ -489,6 +490,7 @@ dsa3d_fixed_bwd_query_mfma_kernel(FixedArgs a) {
     const int32_t b = (int32_t)(bh / a.g.nheads);
     const int32_t eta = a.g.head0 + (int32_t)(bh - (int64_t)b * a.g.nheads);
     const uint32_t tok_b = (uint32_t)b * (uint32_t)a.g.T * (uint32_t)a.g.H * (uint32_t)a.g.W;
+    const int64_t thw = (int64_t)a.g.T * a.g.H * a.g.W;
     const int64_t C = (int64_t)a.g.heads * D;
     const bf16_t* K = reinterpret_cast<const bf16_t*>(a.k) + (int64_t)eta * D;
     const bf16_t* V = reinterpret_cast<const bf16_t*>(a.v) + (int64_t)eta * D;
@@ -530,9 +532,10 @@ dsa3d_fixed_bwd_query_mfma_kernel(FixedArgs a) {
         part += __shfl_xor(part, 16, 64);
         part += __shfl_xor(part, 32, 64);
         dsum[rho] = part;
-        const int64_t ti = qtok[rho] * a.g.heads + eta;
-        lse[rho] = qin[rho] ? a.lse[ti] : 0.0f;
-        if (qin[rho] && g == 0) a.dsum[ti] = part;
+        lse[rho] = qin[rho] ? a.lse[qtok[rho] * a.g.heads + eta] : 0.0f;
+        if (qin[rho] && g == 0)
+            reinterpret_cast<float2*>(a.dsum)[((int64_t)b * a.g.heads + eta) * thw + (qtok[rho] - tok_b)] =
+                make_float2(lse[rho], part);
 #pragma unroll
         for (int tau = 0; tau < D / 32; ++tau) dacc[rho][tau][0] = dacc[rho][tau][1] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -682,6 +685,8 @@ dsa3d_fixed_bwd_key_mfma_kernel(FixedArgs a) {
     const int32_t b = (int32_t)(bh / a.g.nheads);
     const int32_t eta = a.g.head0 + (int32_t)(bh - (int64_t)b * a.g.nheads);
     const uint32_t tok_b = (uint32_t)b * (uint32_t)a.g.T * (uint32_t)a.g.H * (uint32_t)a.g.W;
+    const int64_t thw = (int64_t)a.g.T * a.g.H * a.g.W;
+    const float2* stats = reinterpret_cast<const float2*>(a.dsum) + ((int64_t)b * a.g.heads + eta) * thw;
     const int64_t C = (int64_t)a.g.heads * D;
     const bf16_t* Qp = reinterpret_cast<const bf16_t*>(a.q) + (int64_t)eta * D;
     const bf16_t* Gp = reinterpret_cast<const bf16_t*>(a.dout) + (int64_t)eta * D;
@@ -733,16 +738,15 @@ dsa3d_fixed_bwd_key_mfma_kernel(FixedArgs a) {
                 gst[pc] = qst_map.load(gres, pc);
             }
             const bool sin = rin && okst;
-            const float lq = sin ? a.lse[(rtok + wst) * a.g.heads + eta] : 0.0f;
-            const float dq = sin ? a.dsum[(rtok + wst) * a.g.heads + eta] : 0.0f;
+            const float2 sq = sin ? stats[rtok - tok_b + wst] : make_float2(0.0f, 0.0f);  // (lse, <dO, o>)
 #pragma unroll
             for (int pc = 0; pc < D / 16; ++pc) {
                 qst_map.put(qs, RS, pc, qst[pc]);
                 qst_map.put(gs, RS, pc, gst[pc]);
             }
             if (lane < 32) {
-                st_lse[lane] = lq;
-                st_ds[lane] = sin ? dq : 0.0f;
+                st_lse[lane] = sq.x;
+                st_ds[lane] = sq.y;
             }
             wave_lds_sync();  // the segment's queries are in LDS
             // first operands: query 16T + c, channels 32j + 8g
@@ -1087,8 +1091,8 @@ hipError_t fixed_bwd_bf16(const FixedArgs& a, int64_t nb, const FixedArgs* am, i
 
 }  // namespace
 
-size_t fixed_bwd_workspace_bytes(const dsa3d_desc& d) {
-    return (size_t)(d.B * d.T * d.H * d.W) * (size_t)d.heads * sizeof(float) + 256;
+size_t fixed_bwd_workspace_bytes(const dsa3d_desc& d) {  // room for a float pair per task
+    return (size_t)(d.B * d.T * d.H * d.W) * (size_t)d.heads * 2 * sizeof(float) + 256;
 }
 
 bool fixed_fwd_on_mfma(const dsa3d_desc& d) {

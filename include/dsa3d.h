@@ -150,7 +150,7 @@ int dsa3d_forward(const dsa3d_desc* desc, const void* q, const void* k, const vo
  * are summed in a fixed order for either value of `deterministic` (bf16 rows
  * of 32-128 channels with k_w <= 17 and no dilation along w run these sums on
  * the matrix cores, also in a fixed order); the workspace
- * (DSA3D_WS_BACKWARD_FIXED) holds one float per (token, head). */
+ * (DSA3D_WS_BACKWARD_FIXED) holds two floats per (token, head). */
 int dsa3d_backward(const dsa3d_desc* desc, const void* q, const void* k, const void* v,
                    const void* offsets, const void* out, const float* lse, const void* dout,
                    void* dq, void* dk, void* dv, void* doffsets,

@@ -131,7 +131,7 @@ def test_workspace_sizes():
     assert 28 * 3072 * 4 <= cw <= 28 * 3072 * 4 * (256 * 68) + 1024
     assert dsa.dsa3d_workspace_size(conv, 7) == 0
     # the fixed-window backward keeps one float per (token, head)
-    assert dsa.dsa3d_workspace_size(conv, dsa.WS_BACKWARD_FIXED) == 256 * 68 * 120 * 24 * 4 + 256
+    assert dsa.dsa3d_workspace_size(conv, dsa.WS_BACKWARD_FIXED) == 256 * 68 * 120 * 24 * 8 + 256
     bad = _desc(window=(2, 2, 2))
     assert dsa.dsa3d_workspace_size(bad, dsa.WS_BACKWARD) == 0
     # one head with 2^30 tokens x 27 samples cannot be numbered in 32 bits
