@@ -101,12 +101,12 @@ def algorithmic(wl):
 def fixed_on_mfma(wl):
     """Rows per wave of the fixed window's matrix-core kernels, per kernel, or
     None where libdsa3d runs the fixed window on the vector units: bf16 rows of
-    32-256 channels (32-128 for the backward), no dilation along w, k_w <= 17;
-    two rows per wave when h is not dilated and rows have at most 128 channels
-    (64 for the key kernel)."""
+    32-256 channels (32-128 for the backward), no dilation along w, k_w <= 17,
+    a grid row of all heads below 2 GiB; two rows per wave when h is not
+    dilated and rows have at most 128 channels (64 for the key kernel)."""
     d = wl.head_dim
     if wl.offsets != "none" or wl.dtype != "bf16" or d not in (32, 64, 128, 256) or wl.dilation[2] != 1 \
-            or wl.window[2] > 17:
+            or wl.window[2] > 17 or wl.W * wl.heads * d * 2 > 2**31 - 1:
         return None
     und = wl.dilation[1] == 1
     rows = {"forward": 2 if und and d <= 128 else 1}

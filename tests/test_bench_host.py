@@ -58,6 +58,10 @@ def test_fixed_window_matrix_core_eligibility():
     assert bench.fixed_on_mfma(mk(d=16)) is None
     assert bench.fixed_on_mfma(mk(dil=(1, 1, 2))) is None
     assert bench.fixed_on_mfma(mk(win=(1, 1, 19))) is None
+    # a grid row of all heads at 2 GiB or more leaves the buffer loads' 31-bit record range
+    wide = synth.Workload("f", 1, 1, 1, 2**16, 128, 128, (3, 7, 7), (1, 1, 1), "bf16", "none", backward=True)
+    assert bench.fixed_on_mfma(wide) is None
+    assert bench.fixed_on_mfma(wide.with_grid(W=2**16 - 1)) is not None
     assert bench.fixed_on_mfma(synth.WORKLOADS[synth.HEADLINE]) is None
 
 
