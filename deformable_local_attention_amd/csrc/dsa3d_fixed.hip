@@ -306,8 +306,8 @@ dsa3d_fixed_fwd_mfma_kernel(FixedArgs a) {
     }
 
     // This lane's key columns (the same in every segment) and whether they lie
-    // in the grid and the segment: keys c and 16 + c of the first product,
-    // key l/2 of the value staging.
+    // in the grid and the segment: keys c and 16 + c of the first product; the
+    // value rows are staged whole.
     const int span = kMfmaTokens - 1 + a.win.kw;
     const int32_t wk0 = w0 - a.win.rw + c, wk1 = wk0 + 16;
     const bool ok0 = c < span && (uint32_t)wk0 < (uint32_t)a.g.W;
