@@ -13,6 +13,7 @@ allocate outputs and workspaces with torch.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import threading
 from typing import Optional, Sequence, Tuple
@@ -127,12 +128,62 @@ def desc_like(q: torch.Tensor, window, dilation=(1, 1, 1), scale: float = 0.0, d
     return make_desc(B, T, H, W, nh, d, window, dilation, q.dtype, scale, deterministic)
 
 
-def _ptr(t: Optional[torch.Tensor]):
-    if t is None:
-        return None
-    if not t.is_contiguous():
-        raise ValueError("libdsa3d needs contiguous tensors")
-    return ctypes.c_void_p(t.data_ptr())
+_TORCH_DTYPE = {DSA3D_F32: torch.float32, DSA3D_BF16: torch.bfloat16}
+
+
+class _Args:
+    """Checks the tensors of one call against its descriptor before any
+    pointer reaches the library: each must be a contiguous tensor on the same
+    GPU, of the expected element type and size (a tensor with the expected
+    number of dimensions must have exactly the expected shape; another view of
+    the same elements, such as [N, C] for [B,T,H,W,heads,d], is accepted).
+    Raises ValueError (TypeError for a non-tensor)."""
+
+    def __init__(self, fn: str, desc: Desc):
+        self.fn = fn
+        self.dt = _TORCH_DTYPE.get(desc.dtype)  # None: the library reports the unsupported dtype
+        tok = (desc.B, desc.T, desc.H, desc.W)
+        self.act = tok + (desc.heads, desc.head_dim)
+        self.off = tok + (desc.heads, desc.P, 3)
+        self.lse = tok + (desc.heads,)
+        self.C = desc.heads * desc.head_dim
+        self.F = desc.heads * desc.P * 3
+        self.tensors = []
+
+    def __call__(self, name: str, t, shape, dtype="run", optional: bool = False):
+        if t is None:
+            if optional:
+                return None
+            raise ValueError(f"{self.fn}: {name} is required")
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{self.fn}: {name} must be a torch.Tensor, not {type(t).__name__}")
+        want = self.dt if dtype == "run" else dtype
+        if want is not None and t.dtype != want:
+            raise ValueError(f"{self.fn}: {name} has dtype {t.dtype}, expected {want}")
+        if shape is not None:
+            n = math.prod(shape)
+            if t.numel() != n or (t.dim() == len(shape) and tuple(t.shape) != tuple(shape)):
+                raise ValueError(f"{self.fn}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{self.fn}: {name} is not contiguous")
+        self.tensors.append((name, t))
+        return t
+
+    def pointers(self, *ts):
+        """Device pointers of the checked tensors, once every one of them is
+        known to lie on one GPU (type and size errors are reported first)."""
+        for name, t in self.tensors:
+            if t.device.type != "cuda":
+                raise ValueError(f"{self.fn}: {name} is on {t.device}; libdsa3d takes GPU tensors")
+            if t.device != self.tensors[0][1].device:
+                raise ValueError(f"{self.fn}: {name} is on {t.device}, the others on {self.tensors[0][1].device}")
+        return [None if t is None else ctypes.c_void_p(t.data_ptr()) for t in ts]
+
+    def workspace(self, t):
+        """(the checked workspace, its size in bytes)."""
+        if t is None:
+            return None, 0
+        return self("workspace", t, None, dtype=None), t.numel() * t.element_size()
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -171,43 +222,58 @@ def dsa3d_workspace_min(desc: Desc, kind: int) -> int:
 
 
 def dsa3d_offset_proj_forward(desc: Desc, q, w, bias, offsets, stream=None):
+    a = _Args("dsa3d_offset_proj_forward", desc)
+    args = (a("q", q, a.act), a("w", w, (a.F, a.C)), a("bias", bias, (a.F,), optional=True),
+            a("offsets", offsets, a.off))
     _check("dsa3d_offset_proj_forward",
-           lib().dsa3d_offset_proj_forward(ctypes.byref(desc), _ptr(q), _ptr(w), _ptr(bias), _ptr(offsets),
-                                           _stream(stream)))
+           lib().dsa3d_offset_proj_forward(ctypes.byref(desc), *a.pointers(*args), _stream(stream)))
 
 
 def dsa3d_forward(desc: Desc, q, k, v, offsets, out, lse, stream=None):
-    _check("dsa3d_forward",
-           lib().dsa3d_forward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(offsets), _ptr(out), _ptr(lse),
-                               _stream(stream)))
+    a = _Args("dsa3d_forward", desc)
+    args = (a("q", q, a.act), a("k", k, a.act), a("v", v, a.act), a("offsets", offsets, a.off, optional=True),
+            a("out", out, a.act), a("lse", lse, a.lse, torch.float32))
+    _check("dsa3d_forward", lib().dsa3d_forward(ctypes.byref(desc), *a.pointers(*args), _stream(stream)))
 
 
 def dsa3d_backward(desc: Desc, q, k, v, offsets, out, lse, dout, dq, dk, dv, doffsets, workspace,
                    stream=None):
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a = _Args("dsa3d_backward", desc)
+    args = (a("q", q, a.act), a("k", k, a.act), a("v", v, a.act), a("offsets", offsets, a.off, optional=True),
+            a("out", out, a.act), a("lse", lse, a.lse, torch.float32), a("dout", dout, a.act),
+            a("dq", dq, a.act), a("dk", dk, a.act), a("dv", dv, a.act),
+            a("doffsets", doffsets, a.off, optional=True))
+    ws, nbytes = a.workspace(workspace)
     _check("dsa3d_backward",
-           lib().dsa3d_backward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(offsets), _ptr(out), _ptr(lse),
-                                _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(doffsets), _ptr(workspace), nbytes,
-                                _stream(stream)))
+           lib().dsa3d_backward(ctypes.byref(desc), *a.pointers(*args, ws), nbytes, _stream(stream)))
 
 
 def dsa3d_offset_proj_backward(desc: Desc, q, w, doffsets, dq_accum, dw, dbias, workspace, stream=None):
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a = _Args("dsa3d_offset_proj_backward", desc)
+    args = (a("q", q, a.act), a("w", w, (a.F, a.C)), a("doffsets", doffsets, a.off),
+            a("dq_accum", dq_accum, a.act), a("dw", dw, (a.F, a.C), torch.float32),
+            a("dbias", dbias, (a.F,), torch.float32, optional=True))
+    ws, nbytes = a.workspace(workspace)
     _check("dsa3d_offset_proj_backward",
-           lib().dsa3d_offset_proj_backward(ctypes.byref(desc), _ptr(q), _ptr(w), _ptr(doffsets), _ptr(dq_accum),
-                                            _ptr(dw), _ptr(dbias), _ptr(workspace), nbytes, _stream(stream)))
+           lib().dsa3d_offset_proj_backward(ctypes.byref(desc), *a.pointers(*args, ws), nbytes,
+                                            _stream(stream)))
 
 
 def dsa3d_dwconv_forward(desc: Desc, q, wt, bias, y, stream=None):
+    a = _Args("dsa3d_dwconv_forward", desc)
+    args = (a("q", q, a.act), a("wt", wt, (a.C, 3, 3, 3)), a("bias", bias, (a.C,), optional=True),
+            a("y", y, a.act))
     _check("dsa3d_dwconv_forward",
-           lib().dsa3d_dwconv_forward(ctypes.byref(desc), _ptr(q), _ptr(wt), _ptr(bias), _ptr(y), _stream(stream)))
+           lib().dsa3d_dwconv_forward(ctypes.byref(desc), *a.pointers(*args), _stream(stream)))
 
 
 def dsa3d_dwconv_backward(desc: Desc, q, wt, dy, dq_accum, dwt, dbias, workspace, stream=None):
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a = _Args("dsa3d_dwconv_backward", desc)
+    args = (a("q", q, a.act), a("wt", wt, (a.C, 3, 3, 3)), a("dy", dy, a.act), a("dq_accum", dq_accum, a.act),
+            a("dwt", dwt, (a.C, 3, 3, 3), torch.float32), a("dbias", dbias, (a.C,), torch.float32, optional=True))
+    ws, nbytes = a.workspace(workspace)
     _check("dsa3d_dwconv_backward",
-           lib().dsa3d_dwconv_backward(ctypes.byref(desc), _ptr(q), _ptr(wt), _ptr(dy), _ptr(dq_accum), _ptr(dwt),
-                                       _ptr(dbias), _ptr(workspace), nbytes, _stream(stream)))
+           lib().dsa3d_dwconv_backward(ctypes.byref(desc), *a.pointers(*args, ws), nbytes, _stream(stream)))
 
 
 def dsa3d_set_launch_log(log: Optional[LaunchLog]):
@@ -215,8 +281,10 @@ def dsa3d_set_launch_log(log: Optional[LaunchLog]):
 
 
 def dsa3d_debug_geometry(desc: Desc, offsets, base, frac, stream=None):
+    a = _Args("dsa3d_debug_geometry", desc)
+    args = (a("offsets", offsets, a.off), a("base", base, a.off, torch.int32), a("frac", frac, a.off, torch.float32))
     _check("dsa3d_debug_geometry",
-           lib().dsa3d_debug_geometry(ctypes.byref(desc), _ptr(offsets), _ptr(base), _ptr(frac), _stream(stream)))
+           lib().dsa3d_debug_geometry(ctypes.byref(desc), *a.pointers(*args), _stream(stream)))
 
 
 class launch_timer:

@@ -152,12 +152,14 @@ def _check(rc: int, what: str):
 # ----------------------------------------------------------------------------
 
 def forward_queries(grid, window, dilation, scale, qpos, q, off, box_origin, K, V,
-                    want_attn=False):
+                    want_attn=False, threads=1):
     """Forward of listed queries of one head.
 
     grid (T,H,W); qpos [n,3] int absolute coordinates; q [n,d]; off [n,P,3]
     (rounded to single precision first); K, V [BT,BH,BW,d] the box at
-    box_origin. Returns o [n,d], lse [n] (and attn [n,P]).
+    box_origin. Returns o [n,d], lse [n] (and attn [n,P]). With threads > 1
+    the queries are split into that many runs of consecutive queries, each a
+    call of its own on a thread pool (the calls share only read-only inputs).
     """
     qpos = np.ascontiguousarray(qpos, dtype=np.int32)
     q, K, V, off = _f64(q), _f64(K), _f64(V), _f32(off)
@@ -166,18 +168,35 @@ def forward_queries(grid, window, dilation, scale, qpos, q, off, box_origin, K, 
     pr = _problem(grid, d, window, dilation, scale, box_origin, K.shape[:3])
     o = np.zeros((n, d)); lse = np.zeros(n)
     attn = np.zeros((n, P)) if want_attn else None
-    rc = lib().orc_forward(ctypes.byref(pr), n, _ptr(qpos), _ptr(q), _ptr(off), _ptr(K), _ptr(V),
-                           _ptr(o), _ptr(lse), _ptr(attn))
-    _check(rc, "forward")
+
+    def run(r):
+        i0, i1 = r
+        if i1 <= i0:
+            return 0
+        return lib().orc_forward(ctypes.byref(pr), i1 - i0, _ptr(qpos[i0:i1]), _ptr(q[i0:i1]), _ptr(off[i0:i1]),
+                                 _ptr(K), _ptr(V), _ptr(o[i0:i1]), _ptr(lse[i0:i1]),
+                                 None if attn is None else _ptr(attn[i0:i1]))
+
+    for rc in _pool_map(run, _runs(n, threads), threads):
+        _check(rc, "forward")
     return (o, lse, attn) if want_attn else (o, lse)
 
 
+def _runs(n: int, parts: int):
+    parts = max(1, min(int(parts or 1), n)) if n else 1
+    edges = [n * i // parts for i in range(parts + 1)]
+    return list(zip(edges[:-1], edges[1:]))
+
+
 def backward_queries(grid, window, dilation, scale, qpos, q, off, box_origin, K, V, dout,
-                     dK=None, dV=None):
+                     dK=None, dV=None, want_kv=True, threads=1):
     """Backward of listed queries of one head.
 
     Returns dq [n,d], doff [n,P,3], and dK, dV [BT,BH,BW,d] holding the
     contributions of these queries only (accumulated into dK/dV if given).
+    With want_kv False no key/value gradient is formed (dK, dV returned as
+    None) and, with threads > 1, runs of consecutive queries are computed by
+    concurrent calls.
     """
     qpos = np.ascontiguousarray(qpos, dtype=np.int32)
     q, K, V, off, dout = _f64(q), _f64(K), _f64(V), _f32(off), _f64(dout)
@@ -185,12 +204,24 @@ def backward_queries(grid, window, dilation, scale, qpos, q, off, box_origin, K,
     P = window[0] * window[1] * window[2]
     pr = _problem(grid, d, window, dilation, scale, box_origin, K.shape[:3])
     dq = np.zeros((n, d)); doff = np.zeros((n, P, 3))
-    dK = np.zeros(K.shape) if dK is None else dK
-    dV = np.zeros(V.shape) if dV is None else dV
-    assert dK.dtype == np.float64 and dK.flags.c_contiguous and dV.flags.c_contiguous
-    rc = lib().orc_backward(ctypes.byref(pr), n, _ptr(qpos), _ptr(q), _ptr(off), _ptr(K), _ptr(V),
-                            _ptr(dout), _ptr(dq), _ptr(doff), _ptr(dK), _ptr(dV))
-    _check(rc, "backward")
+    if want_kv:
+        dK = np.zeros(K.shape) if dK is None else dK
+        dV = np.zeros(V.shape) if dV is None else dV
+        assert dK.dtype == np.float64 and dK.flags.c_contiguous and dV.flags.c_contiguous
+        threads = 1
+    else:
+        dK = dV = None
+
+    def run(r):
+        i0, i1 = r
+        if i1 <= i0:
+            return 0
+        return lib().orc_backward(ctypes.byref(pr), i1 - i0, _ptr(qpos[i0:i1]), _ptr(q[i0:i1]), _ptr(off[i0:i1]),
+                                  _ptr(K), _ptr(V), _ptr(dout[i0:i1]), _ptr(dq[i0:i1]), _ptr(doff[i0:i1]),
+                                  _ptr(dK), _ptr(dV))
+
+    for rc in _pool_map(run, _runs(n, threads), threads):
+        _check(rc, "backward")
     return dq, doff, dK, dV
 
 

@@ -223,7 +223,9 @@ int orc_forward(const orc_problem* pr, long nq, const int32_t* qpos, const doubl
 /* Backward of nq queries of one (batch item, head), recomputing the forward.
  * dout [nq,d]. Outputs: dq [nq,d] and doff [nq,P,3] are written; dK and dV
  * [BT,BH,BW,d] are ACCUMULATED (+=) so that the caller may split the queries
- * of one head over several calls. */
+ * of one head over several calls. dK and dV may both be NULL when only the
+ * query-side gradients are wanted (then calls on the same box may run
+ * concurrently). */
 int orc_backward(const orc_problem* pr, long nq, const int32_t* qpos, const double* q,
                  const float* off, const double* K, const double* V, const double* dout,
                  double* dq, double* doff, double* dK, double* dV) {
@@ -280,11 +282,12 @@ int orc_backward(const orc_problem* pr, long nq, const int32_t* qpos, const doub
                 const double* Kc = K + r * d;
                 const double* Vc = V + r * d;
                 double dot = 0.0;
-                for (int e = 0; e < d; ++e) {
-                    dK[r * d + e] += w * gk[e];
-                    dV[r * d + e] += w * gv[e];
-                    dot += gk[e] * Kc[e] + gv[e] * Vc[e];
-                }
+                for (int e = 0; e < d; ++e) dot += gk[e] * Kc[e] + gv[e] * Vc[e];
+                if (dK && dV)
+                    for (int e = 0; e < d; ++e) {
+                        dK[r * d + e] += w * gk[e];
+                        dV[r * d + e] += w * gv[e];
+                    }
                 dop[0] += dw[0] * dot;
                 dop[1] += dw[1] * dot;
                 dop[2] += dw[2] * dot;

@@ -8,6 +8,7 @@ fed to its own attention -- the projection itself is checked separately).
 from __future__ import annotations
 
 import math
+import os
 from typing import Dict, List, Sequence, Tuple
 
 import numpy as np
@@ -142,6 +143,142 @@ def oracle_dkdv_at_keys(wl, x: Dict[str, torch.Tensor], offsets: torch.Tensor, d
         else:
             out_k.append(np.zeros(d)); out_v.append(np.zeros(d))
     return np.array(out_k), np.array(out_v)
+
+
+# ---------------------------------------------------------------------------
+# Full-size parity: one (batch item, head) of the device tensors at a time
+# ---------------------------------------------------------------------------
+
+def head_slab(t: torch.Tensor, b: int, e: int, dtype=np.float32) -> np.ndarray:
+    """t[b, :, :, :, e] (a [B,T,H,W,heads,...] tensor) as a host array,
+    widened exactly (bf16 and f32 values are exact in float32)."""
+    return t[b, :, :, :, e].to(torch.float32).cpu().numpy().astype(dtype, copy=False)
+
+
+def face_tokens(T: int, H: int, W: int) -> np.ndarray:
+    """Every token on the six faces of a T x H x W grid, [n,3] (t,h,w)."""
+    pos = oracle.grid_positions(T, H, W)
+    on = ((pos[:, 0] == 0) | (pos[:, 0] == T - 1) | (pos[:, 1] == 0) | (pos[:, 1] == H - 1) |
+          (pos[:, 2] == 0) | (pos[:, 2] == W - 1))
+    return pos[on]
+
+
+def random_tokens(T: int, H: int, W: int, n: int, rng) -> np.ndarray:
+    """n distinct random tokens of the grid, [n,3]."""
+    flat = rng.choice(T * H * W, size=min(n, T * H * W), replace=False)
+    return np.stack([flat // (H * W), (flat // W) % H, flat % W], 1).astype(np.int32)
+
+
+def interior_tokens(T: int, H: int, W: int, n: int, rng, margin: int = 1) -> np.ndarray:
+    """n random tokens at least `margin` tokens away from every face (fewer
+    if the grid has no interior)."""
+    lo = np.array([min(margin, (X - 1) // 2) for X in (T, H, W)])
+    hi = np.array([T, H, W]) - lo
+    out = np.stack([rng.integers(lo[a], hi[a], size=n) for a in range(3)], 1).astype(np.int32)
+    return np.unique(out, axis=0)
+
+
+def grid_corner_tokens(T: int, H: int, W: int) -> np.ndarray:
+    return np.unique(np.array([(t, h, w) for t in (0, T - 1) for h in (0, H - 1) for w in (0, W - 1)],
+                              dtype=np.int32), axis=0)
+
+
+class HeadOracle:
+    """The oracle on one (batch item, head) of a full-size problem held on the
+    device: the head's key and value rows are copied to the host once (the
+    oracle's box is then the whole grid), and queries are evaluated in bulk.
+
+    offsets: a [B,T,H,W,heads,P,3] device tensor, or None for the fixed window
+    (every offset zero)."""
+
+    def __init__(self, wl, x: Dict[str, torch.Tensor], b: int, e: int, offsets=None, dout=None, threads=None):
+        self.wl, self.b, self.e = wl, b, e
+        self.grid = (wl.T, wl.H, wl.W)
+        self.scale = oracle.default_scale(wl.head_dim)
+        self.threads = threads or min(16, os.cpu_count() or 1)
+        self.K = head_slab(x["k"], b, e, np.float64)
+        self.V = head_slab(x["v"], b, e, np.float64)
+        self.q = head_slab(x["q"], b, e)
+        self.g = None if dout is None else head_slab(dout, b, e)
+        self.off = None if offsets is None else head_slab(offsets, b, e)
+
+    def _rows(self, a, pos):
+        return a[pos[:, 0], pos[:, 1], pos[:, 2]]
+
+    def offsets_at(self, pos) -> np.ndarray:
+        if self.off is None:
+            return np.zeros((len(pos), self.wl.P, 3), dtype=np.float32)
+        return self._rows(self.off, pos)
+
+    def forward(self, pos):
+        wl = self.wl
+        return oracle.forward_queries(self.grid, wl.window, wl.dilation, self.scale, pos, self._rows(self.q, pos),
+                                      self.offsets_at(pos), (0, 0, 0), self.K, self.V, threads=self.threads)
+
+    def backward_queries(self, pos):
+        """dq [n,d] and doffsets [n,P,3] of the listed queries."""
+        wl = self.wl
+        dq, doff, _, _ = oracle.backward_queries(self.grid, wl.window, wl.dilation, self.scale, pos,
+                                                 self._rows(self.q, pos), self.offsets_at(pos), (0, 0, 0), self.K,
+                                                 self.V, self._rows(self.g, pos), want_kv=False,
+                                                 threads=self.threads)
+        return dq, doff
+
+    def queries_reaching(self, keys) -> np.ndarray:
+        """Every query with a sample whose trilinear cell has one of `keys`
+        ([n,3]) as a corner (the float32 position arithmetic of the operator,
+        vectorised over the candidates around each key)."""
+        wl = self.wl
+        T, H, W = self.grid
+        rad = np.array([(wl.window[a] - 1) // 2 * wl.dilation[a] for a in range(3)])
+        if self.off is None:
+            m = np.zeros(3)
+        else:
+            a = np.abs(self.off.reshape(-1, 3))
+            a = np.where(np.isfinite(a) & (a < 2.0 ** 30), a, 0.0)
+            m = a.max(0)
+        R = rad + np.ceil(m).astype(np.int64) + 2
+        wp = window_points(wl.window, wl.dilation)
+        chosen = np.zeros((T, H, W), dtype=bool)
+        for key in np.asarray(keys):
+            lo = np.maximum(0, key - R)
+            hi = np.minimum(np.array(self.grid) - 1, key + R)
+            cand = oracle.grid_positions(*(hi - lo + 1)) + lo
+            off = self.offsets_at(cand)
+            with np.errstate(invalid="ignore", over="ignore"):
+                pos = (cand[:, None, :] + wp[None]).astype(np.float32) + off.astype(np.float32)
+                ok = np.all(np.isfinite(pos) & (np.abs(pos) < 2.0 ** 30), axis=2)
+                fl = np.floor(np.where(ok[..., None], pos, 0)).astype(np.int64)
+            hit = ok & np.all((fl == key) | (fl + 1 == key), axis=2)
+            sel = cand[hit.any(1)]
+            chosen[sel[:, 0], sel[:, 1], sel[:, 2]] = True
+        return np.argwhere(chosen).astype(np.int32)
+
+    def dkdv_at(self, keys):
+        """dK and dV rows [n,d] at `keys`: the backward of every query that
+        reaches one of them, accumulated over the whole grid."""
+        wl = self.wl
+        keys = np.asarray(keys)
+        qpos = self.queries_reaching(keys)
+        if len(qpos) == 0:
+            z = np.zeros((len(keys), wl.head_dim))
+            return z, z.copy()
+        _, _, dK, dV = oracle.backward_queries(self.grid, wl.window, wl.dilation, self.scale, qpos,
+                                               self._rows(self.q, qpos), self.offsets_at(qpos), (0, 0, 0), self.K,
+                                               self.V, self._rows(self.g, qpos))
+        return self._rows(dK, keys), self._rows(dV, keys)
+
+
+def rows_at(t: torch.Tensor, b: int, e: int, pos) -> np.ndarray:
+    """Rows t[b, t, h, w, e] of a device tensor at positions pos [n,3], widened to float64."""
+    ii = torch.as_tensor(np.asarray(pos, dtype=np.int64), device=t.device)
+    return to_np(t[b][ii[:, 0], ii[:, 1], ii[:, 2], e])
+
+
+def errors(gpu: np.ndarray, ref: np.ndarray) -> Dict[str, float]:
+    """Per-tensor error figures: relative L2, max abs, and the reference's max abs."""
+    return {"rel_l2": rel_l2(gpu, ref), "max_abs": float(np.abs(gpu - ref).max()) if gpu.size else 0.0,
+            "ref_max_abs": float(np.abs(ref).max()) if ref.size else 0.0, "n": int(gpu.shape[0]) if gpu.ndim else 1}
 
 
 def sample_queries(wl, heads, n_random, seed=0, faces=16):

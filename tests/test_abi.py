@@ -168,3 +168,61 @@ def test_product_never_imports_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower() or f == "synth.py" and "import oracle" not in text, f
+
+
+def _cpu_tensors(dtype=torch.bfloat16, B=1, T=2, H=3, W=4, heads=2, d=16, window=(3, 3, 3)):
+    P = window[0] * window[1] * window[2]
+    act = lambda: torch.zeros((B, T, H, W, heads, d), dtype=dtype)
+    return dict(desc=dsa.make_desc(B, T, H, W, heads, d, window, dtype=dtype), q=act(), k=act(), v=act(),
+                off=torch.zeros((B, T, H, W, heads, P, 3), dtype=dtype), out=act(),
+                lse=torch.zeros((B, T, H, W, heads), dtype=torch.float32))
+
+
+@pytest.mark.parametrize("bad,match", [
+    ("k_dtype", "dtype"),          # f32 keys in a bf16 run
+    ("off_dtype", "dtype"),        # f32 offsets in a bf16 run
+    ("lse_dtype", "dtype"),        # bf16 lse (always float32)
+    ("k_heads", "shape"),          # keys with fewer heads
+    ("off_points", "shape"),       # offsets built for another P
+    ("out_small", "shape"),        # an output with fewer elements
+    ("not_contiguous", "contiguous"),
+    ("cpu", "GPU"),                # host tensors of the right type and shape
+])
+def test_binding_rejects_mismatched_tensors_before_the_library(bad, match):
+    """The binding checks every tensor against the descriptor (type, size,
+    contiguity, device) and raises before any pointer reaches libdsa3d: a
+    wrong tensor is an error, never an out-of-bounds device access."""
+    t = _cpu_tensors()
+    if bad == "k_dtype":
+        t["k"] = t["k"].float()
+    elif bad == "off_dtype":
+        t["off"] = t["off"].float()
+    elif bad == "lse_dtype":
+        t["lse"] = t["lse"].bfloat16()
+    elif bad == "k_heads":
+        t["k"] = t["k"][:, :, :, :, :1].contiguous()
+    elif bad == "off_points":
+        t["off"] = torch.zeros(t["off"].shape[:5] + (26, 3), dtype=torch.bfloat16)
+    elif bad == "out_small":
+        t["out"] = t["out"].reshape(-1)[:-8].clone()
+    elif bad == "not_contiguous":
+        t["q"] = t["q"].transpose(4, 5).contiguous().transpose(4, 5)
+    with pytest.raises(ValueError, match=match):
+        dsa.dsa3d_forward(t["desc"], t["q"], t["k"], t["v"], t["off"], t["out"], t["lse"])
+
+
+def test_binding_checks_backward_and_projection_tensors():
+    t = _cpu_tensors()
+    d = t["desc"]
+    act = lambda: torch.zeros_like(t["q"])
+    with pytest.raises(ValueError, match="dk"):
+        dsa.dsa3d_backward(d, t["q"], t["k"], t["v"], t["off"], t["out"], t["lse"], act(), act(),
+                           torch.zeros(5, dtype=torch.bfloat16), act(), torch.zeros_like(t["off"]), None)
+    with pytest.raises(ValueError, match="dw"):
+        F, C = 2 * 27 * 3, 2 * 16
+        dsa.dsa3d_offset_proj_backward(d, t["q"], torch.zeros((F, C), dtype=torch.bfloat16), t["off"], act(),
+                                       torch.zeros((F, C), dtype=torch.bfloat16), None, None)
+    with pytest.raises(ValueError, match="wt"):
+        dsa.dsa3d_dwconv_forward(d, t["q"], torch.zeros((32, 3, 3), dtype=torch.bfloat16), None, act())
+    with pytest.raises(TypeError):
+        dsa.dsa3d_forward(d, t["q"], t["k"], t["v"], t["off"], t["out"], [0.0])

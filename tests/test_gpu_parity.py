@@ -7,8 +7,11 @@ values widened exactly. Small grids are checked whole; the full-size
 workloads on sampled queries and key tokens, in the same launch configuration
 as the benchmark.
 """
+import json
 import math
+import os
 import sys
+import time
 
 import numpy as np
 import pytest
@@ -18,7 +21,9 @@ import oracle
 import deformable_local_attention_amd as dsa
 from deformable_local_attention_amd import synth
 from deformable_local_attention_amd.chain import Chain
-from gpu_helpers import (gather, oracle_dkdv_at_keys, oracle_queries, rel_l2, sample_queries, to_np, to_np32)
+from gpu_helpers import (HeadOracle, errors, face_tokens, gather, grid_corner_tokens, interior_tokens,
+                         oracle_dkdv_at_keys, oracle_queries, random_tokens, rel_l2, rows_at, sample_queries, to_np,
+                         to_np32)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -222,6 +227,22 @@ def test_deterministic_mode_is_bitwise_reproducible_across_runs_and_pass_splits(
         for a, b in zip(outs[0], other):
             assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
+@pytest.mark.parametrize("det", [False, True])
+def test_multi_pass_backward_against_oracle(det):
+    """The backward with the smallest workspace it accepts (one head per pass:
+    four passes) and with room for two heads (two passes), against the oracle
+    on the whole grid."""
+    wl = _wl("multi-pass", T=4, H=6, W=9, heads=4, d=64, window=(3, 5, 5), sigma=2.0, dtype="bf16", det=det)
+    x = synth.make_inputs(wl, "cpu", seed=53)
+    desc = dsa.desc_like(x["q"], wl.window, wl.dilation, 0.0, det)
+    one = dsa.dsa3d_workspace_min(desc, dsa.WS_BACKWARD)
+    full = dsa.dsa3d_workspace_size(desc, dsa.WS_BACKWARD)
+    assert full > 3 * one
+    for ws in (one, 2 * one + 256):
+        say(f"[multi-pass] workspace {ws} B ({ws / one:.2f} x the one-head minimum)")
+        _run_whole(wl, x, det=det, ws_bytes=ws)
 
 
 # ---------------------------------------------------------------------------
@@ -439,17 +460,91 @@ def _free():
     torch.cuda.empty_cache()
 
 
-def _sampled_attention_checks(wl, ch, xd, n_random, seed, dkdv_keys=0):
-    qs = sample_queries(wl, heads=[0, wl.heads - 1], n_random=n_random, seed=seed)
-    say(f"[sampled] {len(qs)} queries")
-    r = oracle_queries(wl, xd, ch.offsets, qs, dout=xd.get("dout") if wl.backward else None)
-    _check("o (sampled)", gather(ch.out, qs), r["o"], wl.dtype)
-    lerr = float(np.abs(gather(ch.lse.unsqueeze(-1), qs)[:, 0] - r["lse"]).max())
-    assert lerr <= 1e-3, lerr
-    if wl.backward:
-        _check("doff (sampled)", gather(ch.doff, qs), r["doff"], wl.dtype)
-        return qs, r
-    return qs, r
+PARITY_LOG = os.environ.get("DSA3D_PARITY_LOG")
+
+
+def _log_errors(test: str, rows):
+    """Per-tensor error figures of a full-size test, one JSON line each, to the
+    file named by DSA3D_PARITY_LOG (if set)."""
+    for r in rows:
+        say(f"    {r['tensor']:8s} head {str(r['head']):>4s}: rel-L2 {r['rel_l2']:.3e}  max|err| {r['max_abs']:.3e}"
+            f"  (max|ref| {r['ref_max_abs']:.3e}, {r['n']} rows)")
+    if PARITY_LOG:
+        os.makedirs(os.path.dirname(os.path.abspath(PARITY_LOG)), exist_ok=True)
+        with open(PARITY_LOG, "a") as f:
+            for r in rows:
+                f.write(json.dumps(dict(test=test, **r)) + "\n")
+
+
+def _full_size_parity(test, wl, xd, offsets, out, lse, dq=None, dk=None, dv=None, doff=None, dout=None,
+                      q_heads=None, k_heads=None, n_random=4096, n_random_k_heads=512, n_interior_keys=12, seed=0,
+                      b=0):
+    """Oracle parity of a full-size run on sampled outputs.
+
+    Queries: every token on the six faces of the grid plus n_random random
+    tokens, for each head of q_heads (default: the first and the last head);
+    n_random_k_heads random tokens for every other head of k_heads. Keys (when
+    the run has a backward): the 8 grid corners, n_interior_keys random
+    interior keys and 4 random face keys of every head of k_heads (default:
+    every third head and the last one, so that every backward pass over a
+    range of heads is covered). Each tensor is compared per head and over all
+    the heads together."""
+    rng = np.random.default_rng(seed)
+    T, H, W = wl.T, wl.H, wl.W
+    heads = wl.heads
+    q_heads = sorted(set(q_heads if q_heads is not None else [0, heads - 1]))
+    k_heads = sorted(set(k_heads if k_heads is not None else list(range(0, heads, 3)) + [heads - 1]))
+    bwd = dq is not None
+    tol = F32_TOL if wl.dtype == "f32" else BF16_TOL
+    acc = {}   # tensor -> ([gpu rows], [ref rows])
+    rows = []
+
+    def compare(name, head, gpu, ref):
+        e = errors(gpu, ref)
+        rows.append(dict(tensor=name, head=str(head), **e))
+        acc.setdefault(name, ([], []))
+        acc[name][0].append(gpu.reshape(len(gpu), -1))
+        acc[name][1].append(ref.reshape(len(ref), -1))
+
+    for e in sorted(set(q_heads) | set(k_heads if bwd else [])):
+        t0 = time.time()
+        ho = HeadOracle(wl, xd, b, e, offsets, dout)
+        if e in q_heads:
+            pos = np.unique(np.concatenate([face_tokens(T, H, W), random_tokens(T, H, W, n_random, rng)]), axis=0)
+        else:
+            pos = random_tokens(T, H, W, n_random_k_heads, rng)
+        o_ref, lse_ref = ho.forward(pos)
+        compare("o", e, rows_at(out, b, e, pos), o_ref)
+        compare("lse", e, rows_at(lse.unsqueeze(-1), b, e, pos), lse_ref[:, None])
+        nk = 0
+        if bwd:
+            dq_ref, doff_ref = ho.backward_queries(pos)
+            compare("dq", e, rows_at(dq, b, e, pos), dq_ref)
+            if doff is not None:
+                compare("doff", e, rows_at(doff, b, e, pos), doff_ref)
+            if e in k_heads:
+                keys = np.unique(np.concatenate([grid_corner_tokens(T, H, W),
+                                                 interior_tokens(T, H, W, n_interior_keys, rng),
+                                                 face_tokens(T, H, W)[rng.choice(len(face_tokens(T, H, W)), 4)]]),
+                                 axis=0)
+                kk, vv = ho.dkdv_at(keys)
+                compare("dk", e, rows_at(dk, b, e, keys), kk)
+                compare("dv", e, rows_at(dv, b, e, keys), vv)
+                nk = len(keys)
+        say(f"[full] head {e}: {len(pos)} queries, {nk} keys in {time.time() - t0:.1f} s")
+        del ho
+    for name, (g, r) in acc.items():
+        g, r = np.concatenate(g), np.concatenate(r)
+        rows.append(dict(tensor=name, head="all", **errors(g, r)))
+    _log_errors(test, rows)
+    for r in rows:
+        if r["tensor"] == "lse":
+            assert r["max_abs"] <= (F32_TOL if wl.dtype == "f32" else 1e-3), r
+        elif wl.dtype == "f32":
+            assert r["max_abs"] <= tol, r
+        else:
+            assert r["rel_l2"] <= tol, r
+    return rows
 
 
 @pytest.mark.slow
@@ -473,12 +568,8 @@ def test_720p_dil2_workload_full_size_sampled():
     q2 = xd["q"].view(N, C)
     ref = oracle.offset_proj(to_np(q2[rows]), to_np(xd["proj_w"]), to_np(xd["proj_b"]))
     _check("offsets rows", to_np(ch.offsets.view(N, F)[rows]), ref, "bf16")
-    qs, r = _sampled_attention_checks(wl, ch, xd, n_random=96, seed=1)
-    _check("dq_attn (sampled)", gather(dq_attn, qs), r["dq"], "bf16")
-    keys = sample_queries(wl, heads=[0, wl.heads - 1], n_random=4, seed=2, faces=0)[:12]
-    kk, vv = oracle_dkdv_at_keys(wl, xd, ch.offsets, xd["dout"], keys)
-    _check("dk (keys)", gather(ch.dk, keys), kk, "bf16")
-    _check("dv (keys)", gather(ch.dv, keys), vv, "bf16")
+    _full_size_parity("720p-bf16-proj-dil2", wl, xd, ch.offsets, ch.out, ch.lse, dq=dq_attn, dk=ch.dk, dv=ch.dv,
+                      doff=ch.doff, dout=xd["dout"], seed=1)
     # projection backward on the GPU's doffsets (its input)
     g = to_np(ch.doff.view(N, F))
     add = g[rows] @ to_np(xd["proj_w"])
@@ -524,8 +615,8 @@ def test_720p_conv_workload_full_size_sampled():
     pin2 = ch.pin.view(N, C)
     ref = oracle.offset_proj(to_np(pin2[rows]), to_np(xd["proj_w"]), to_np(xd["proj_b"]))
     _check("offsets rows", to_np(ch.offsets.view(N, F)[rows]), ref, "bf16")
-    qs, r = _sampled_attention_checks(wl, ch, xd, n_random=64, seed=9)
-    _check("dq_attn (sampled)", gather(dq_attn, qs), r["dq"], "bf16")
+    _full_size_parity("720p-bf16-conv-dil2", wl, xd, ch.offsets, ch.out, ch.lse, dq=dq_attn, dk=ch.dk, dv=ch.dv,
+                      doff=ch.doff, dout=xd["dout"], seed=9)
     g = to_np(ch.doff.view(N, F)[rows])
     _check("d(conv output) rows", to_np(ch.dpin.view(N, C)[rows]), g @ to_np(xd["proj_w"]), "bf16")
     dq_c, dcw_ref, dcb_ref = oracle.dwconv3d_backward(q_c, cw, sub(ch.dpin))
@@ -548,7 +639,8 @@ def test_1080p_projection_workload_full_size_sampled():
     rows = np.random.default_rng(0).choice(N, 256, replace=False)
     ref = oracle.offset_proj(to_np(xd["q"].view(N, C)[rows]), to_np(xd["proj_w"]), to_np(xd["proj_b"]))
     _check("offsets rows", to_np(ch.offsets.view(N, F)[rows]), ref, "bf16")
-    _sampled_attention_checks(wl, ch, xd, n_random=64, seed=3)
+    _full_size_parity("1080p-bf16-proj", wl, xd, ch.offsets, ch.out, ch.lse, q_heads=[0, 11, wl.heads - 1],
+                      seed=3)
     del ch, xd
     _free()
 
@@ -562,18 +654,8 @@ def test_1080p_fixed_377_workload_full_size_sampled():
     ch = Chain(wl, xd)
     ch.run()
     torch.cuda.synchronize()
-    # a zero offsets tensor as a broadcast view (no memory) for the oracle helpers
-    zeros = torch.zeros((), dtype=xd["q"].dtype, device=DEV).expand(tuple(xd["q"].shape[:5]) + (wl.P, 3))
-    qs = sample_queries(wl, heads=[0, wl.heads - 1], n_random=48, seed=7)
-    say(f"[sampled] {len(qs)} queries")
-    r = oracle_queries(wl, xd, zeros, qs, dout=xd["dout"])
-    _check("o (sampled)", gather(ch.out, qs), r["o"], "bf16")
-    assert float(np.abs(gather(ch.lse.unsqueeze(-1), qs)[:, 0] - r["lse"]).max()) <= 1e-3
-    _check("dq (sampled)", gather(ch.dq, qs), r["dq"], "bf16")
-    keys = sample_queries(wl, heads=[0, wl.heads - 1], n_random=3, seed=8, faces=0)[:8]
-    kk, vv = oracle_dkdv_at_keys(wl, xd, zeros, xd["dout"], keys)
-    _check("dk (keys)", gather(ch.dk, keys), kk, "bf16")
-    _check("dv (keys)", gather(ch.dv, keys), vv, "bf16")
+    _full_size_parity("1080p-bf16-fixed377", wl, xd, None, ch.out, ch.lse, dq=ch.dq, dk=ch.dk, dv=ch.dv,
+                      dout=xd["dout"], seed=7)
     del ch, xd
     _free()
 
@@ -587,12 +669,8 @@ def test_1080p_p75_deterministic_workload_full_size_sampled():
     ch = Chain(wl, xd)
     ch.run()
     torch.cuda.synchronize()
-    qs, r = _sampled_attention_checks(wl, ch, xd, n_random=64, seed=5)
-    _check("dq (sampled)", gather(ch.dq, qs), r["dq"], "bf16")
-    keys = sample_queries(wl, heads=[0, wl.heads - 1], n_random=3, seed=6, faces=0)[:10]
-    kk, vv = oracle_dkdv_at_keys(wl, xd, ch.offsets, xd["dout"], keys)
-    _check("dk (keys)", gather(ch.dk, keys), kk, "bf16")
-    _check("dv (keys)", gather(ch.dv, keys), vv, "bf16")
+    _full_size_parity("1080p-bf16-p75-det", wl, xd, ch.offsets, ch.out, ch.lse, dq=ch.dq, dk=ch.dk, dv=ch.dv,
+                      doff=ch.doff, dout=xd["dout"], seed=5)
     # bitwise reproducibility of the whole chain at full size
     ref = [t.clone() for t in (ch.dk, ch.dv)]
     ch.run()
