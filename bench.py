@@ -116,19 +116,37 @@ def fixed_on_mfma(wl):
     return rows
 
 
+def host_cpu():
+    """(usable cores, cores the OS reports, CPU model) of this host."""
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return usable, os.cpu_count() or 1, model
+
+
 def cpu_baseline(wl, budget_s: float = 20.0):
     """The oracle, as it is, on a bounded sample of the same workload: the
     interior queries of a 16x24x24-token crop drawn with the workload's
-    distributions, on as many heads as there are usable host cores (heads are
-    independent and run in parallel). Returns tokens/s for whole tokens (all
+    distributions, one head per usable host core (heads are independent and
+    run in parallel, one thread each). Returns tokens/s for whole tokens (all
     heads), scaled from the heads sampled."""
     import numpy as np
 
     import oracle
     from deformable_local_attention_amd import synth
 
-    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
-    cores = max(1, min(cores, 16, wl.heads))
+    usable, nproc, model = host_cpu()
+    # the CPU share granted to this process: OMP_NUM_THREADS where the host
+    # sets it (a GPU job's share of a shared host), else every usable core
+    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    cores = max(1, min(usable, share) if share > 0 else usable)
     crop = wl.with_grid(B=1, T=min(wl.T, 16), H=min(wl.H, 24), W=min(wl.W, 24), heads=cores, name=wl.name + "-crop")
     x = synth.make_inputs(crop, "cpu", seed=0, with_grad=True)
     if crop.offsets in ("proj", "conv"):
@@ -174,6 +192,7 @@ def cpu_baseline(wl, budget_s: float = 20.0):
     n = len(pos) * reps
     token_heads_per_s = n * cores / dt
     return {"value": token_heads_per_s / wl.heads, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "host": {"usable_cores": usable, "nproc": nproc, "omp_num_threads": share or None, "cpu_model": model},
             "sample": (f"fp64 oracle, {'fwd+bwd' if crop.backward else 'fwd'}: the {len(pos)} interior queries of a "
                        f"{T}x{H}x{W}-token crop (the workload's window, dilation and input distributions), "
                        f"{cores} heads in parallel, {reps} passes, {dt:.1f} s on {cores} threads; tokens/s counts "
@@ -209,6 +228,10 @@ def kernel_source_hash(read=None) -> str:
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# What `traffic` counts: the bytes a launch moves beyond the L2 caches (rocprofv3 FETCH_SIZE + WRITE_SIZE, each
+# scaled by its reading for a plain device copy of known size), which includes hits in the memory-side cache,
+# so it is an upper bound on the HBM bytes.
+TRAFFIC_SCOPE = "beyond-L2 bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated; includes memory-side cache hits)"
 
 
 def recorded_traffic(kernel: str, workload: str):
@@ -303,6 +326,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--fast", action="store_true", help="float32 (non-deterministic) K/V-gradient accumulation")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--alt-steps", type=int, default=2,
+                    help="steps timed again with deterministic=0 after a deterministic run (0: none)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="summarise rocprofv3 FETCH_SIZE/WRITE_SIZE counter CSVs into HBM bytes per launch")
@@ -392,12 +417,12 @@ def main():
     peak = MFMA_BF16_PEAK_TFLOPS if on_mfma else VALU_F32_PEAK_TFLOPS
     roofline = {"bound": "mfma" if on_mfma else "alu", "kernel": dom, "achieved": round(achieved_tf, 3),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved_tf / peak, 5),
-                "traffic": None if traffic is None else round(traffic),
+                "traffic": None if traffic is None else round(traffic), "traffic_scope": TRAFFIC_SCOPE,
                 "launch_ms": round(per_kernel[dom]["mean_ms"], 3), "units_per_launch": units,
                 "flops_per_unit": unit_flops}
     roofline_hbm = {"bound": "hbm", "kernel": dom, "achieved": round(achieved_gbs, 2), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 5),
-                    "traffic": None if traffic is None else round(traffic),
+                    "traffic": None if traffic is None else round(traffic), "traffic_scope": TRAFFIC_SCOPE,
                     "launch_ms": round(per_kernel[dom]["mean_ms"], 3), "units_per_launch": units,
                     "bytes_per_unit": unit_bytes}
     step_flops = wl.tokens * wl.heads * (alg["fwd_flops"] + (alg["bwd_flops"] if wl.backward else 0))
@@ -405,6 +430,14 @@ def main():
                      "achieved": round(step_flops / (ms_per_step / 1e3) / 1e12, 3), "peak": VALU_F32_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(step_flops / (ms_per_step / 1e3) / 1e12 / VALU_F32_PEAK_TFLOPS, 5),
                      "flops_per_token": step_flops // wl.tokens}
+
+    # The whole step's algorithmic bytes (each attention tensor read or written once: forward and backward
+    # per (token, head) as above) over the step time, against the HBM peak: the metric's "achieved HBM GB/s".
+    step_bytes = wl.tokens * wl.heads * (alg["fwd_bytes"] + (alg["bwd_bytes"] if wl.backward else 0))
+    step_gbs = step_bytes / (ms_per_step / 1e3) / 1e9
+    roofline_hbm_step = {"bound": "hbm", "scope": "whole step, attention tensors", "achieved": round(step_gbs, 2),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 5),
+                         "bytes_per_step": step_bytes}
 
     # The gathers: in the forward and the query kernel every sample reads the head's rows of its 8 corner
     # tokens in two tensors (keys and values), 16*d*s*P bytes per (token, head). The key kernel reads the
@@ -476,11 +509,27 @@ def main():
                    "chain": {"proj": "proj+", "conv": "dwconv+proj+"}.get(wl.offsets, "") + ("fwd+bwd" if wl.backward else "fwd"),
                    "deterministic": wl.deterministic},
         "roofline": roofline, "roofline_hbm": roofline_hbm, "roofline_step": roofline_step,
+        "roofline_hbm_step": roofline_hbm_step,
         "roofline_gather": roofline_gather,
         **({"roofline_proj": roofline_proj} if roofline_proj else {}),
         **({"roofline_conv": roofline_conv} if roofline_conv else {}),
         "kernels": {k: {"launches": v["launches"], "mean_ms": round(v["mean_ms"], 3)} for k, v in per_kernel.items()},
     }
+    if wl.backward and wl.deterministic and args.alt_steps > 0:
+        # the same step with the fast (order-free) K/V-gradient accumulation, on the same buffers
+        ch.desc.deterministic = 0
+        ch.run()
+        ev2, ev3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev2.record(stream)
+        for _ in range(args.alt_steps):
+            ch.run()
+        ev3.record(stream)
+        torch.cuda.synchronize()
+        ch.desc.deterministic = 1
+        ms_fast = ev2.elapsed_time(ev3) / args.alt_steps
+        result["deterministic_0"] = {"ms_per_step": round(ms_fast, 3),
+                                     "value": round(wl.tokens / (ms_fast / 1e3), 1), "steps": args.alt_steps}
+        log(f"[bench] deterministic=0: {ms_fast:.2f} ms/step, {wl.tokens / ms_fast / 1e3:.3f} M tokens/s")
     if args.cpu_baseline == "on":
         log("[bench] timing the CPU oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline(wl)
