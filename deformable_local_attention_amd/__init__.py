@@ -28,15 +28,17 @@ __all__ = [
     "DSA3D_F32", "DSA3D_BF16", "WS_FORWARD", "WS_BACKWARD", "WS_PROJ_BACKWARD", "WS_DWCONV_BACKWARD",
     "WS_BACKWARD_FIXED",
     "dsa3d_dwconv_forward", "dsa3d_dwconv_backward", "dwconv", "dwconv_backward",
-    "dsa3d_set_launch_log", "LaunchLog", "launch_timer", "KERNELS",
+    "dsa3d_set_launch_log", "LaunchLog", "launch_timer", "KERNELS", "dsa3d_backward_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
 ]
 
 DSA3D_F32, DSA3D_BF16 = 0, 1
 WS_FORWARD, WS_BACKWARD, WS_PROJ_BACKWARD, WS_DWCONV_BACKWARD, WS_BACKWARD_FIXED = 0, 1, 2, 3, 4
+NOALLOC_SCRATCH_BYTES = 64 << 20  # DSA3D_NOALLOC_SCRATCH_BYTES
 EXPORTS = ("dsa3d_version", "dsa3d_status_string", "dsa3d_validate", "dsa3d_workspace_size",
            "dsa3d_workspace_min", "dsa3d_offset_proj_forward", "dsa3d_forward", "dsa3d_backward",
            "dsa3d_offset_proj_backward", "dsa3d_debug_geometry", "dsa3d_dwconv_forward", "dsa3d_dwconv_backward",
-           "dsa3d_set_launch_log")
+           "dsa3d_set_launch_log", "dsa3d_backward_noalloc")
 # kernel ids of the launch log (dsa3d_kernel)
 KERNELS = {1: "proj_forward", 2: "forward", 3: "bwd_query", 4: "bwd_key", 5: "fill", 6: "proj_bwd_dq",
            7: "proj_bwd_dw", 8: "split_sum", 9: "colsum", 10: "geometry", 11: "bwd_scan", 12: "bwd_count",
@@ -101,6 +103,7 @@ def lib() -> ctypes.CDLL:
                 "dsa3d_dwconv_forward": ([dp, vp, vp, vp, vp, vp], ctypes.c_int),
                 "dsa3d_dwconv_backward": ([dp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
                 "dsa3d_set_launch_log": ([ctypes.POINTER(LaunchLog)], ctypes.c_int),
+                "dsa3d_backward_noalloc": ([dp] + [vp] * 12, ctypes.c_int),
             }
             for name, (args, res) in sig.items():
                 f = getattr(L, name)
@@ -246,6 +249,16 @@ def dsa3d_backward(desc: Desc, q, k, v, offsets, out, lse, dout, dq, dk, dv, dof
     ws, nbytes = a.workspace(workspace)
     _check("dsa3d_backward",
            lib().dsa3d_backward(ctypes.byref(desc), *a.pointers(*args, ws), nbytes, _stream(stream)))
+
+
+def dsa3d_backward_noalloc(desc: Desc, q, k, v, offsets, out, lse, dout, dq, dk, dv, doffsets, stream=None):
+    a = _Args("dsa3d_backward_noalloc", desc)
+    args = (a("q", q, a.act), a("k", k, a.act), a("v", v, a.act), a("offsets", offsets, a.off, optional=True),
+            a("out", out, a.act), a("lse", lse, a.lse, torch.float32), a("dout", dout, a.act),
+            a("dq", dq, a.act), a("dk", dk, a.act), a("dv", dv, a.act),
+            a("doffsets", doffsets, a.off, optional=True))
+    _check("dsa3d_backward_noalloc",
+           lib().dsa3d_backward_noalloc(ctypes.byref(desc), *a.pointers(*args), _stream(stream)))
 
 
 def dsa3d_offset_proj_backward(desc: Desc, q, w, doffsets, dq_accum, dw, dbias, workspace, stream=None):

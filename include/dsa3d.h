@@ -39,13 +39,15 @@
  *  - Calls only enqueue work on `stream` (a hipStream_t; NULL = the null
  *    stream) and return; they never synchronise and never allocate device
  *    memory. Scratch memory is the caller's workspace, sized by
- *    dsa3d_workspace_size().
+ *    dsa3d_workspace_size() (dsa3d_backward_noalloc uses a fixed array of the
+ *    library instead).
  *  - Errors: a negative dsa3d_status. Argument errors are found before any
  *    work is enqueued. A HIP launch error gives DSA3D_ERR_HIP. No C++
  *    exception crosses this boundary.
  *  - Calls on distinct streams may run concurrently if they share no output
  *    or workspace. The only mutable state is the opt-in, per-thread launch
- *    log (dsa3d_set_launch_log).
+ *    log (dsa3d_set_launch_log) and the per-GPU scratch array of
+ *    dsa3d_backward_noalloc.
  */
 #ifndef DSA3D_H
 #define DSA3D_H
@@ -155,6 +157,28 @@ int dsa3d_backward(const dsa3d_desc* desc, const void* q, const void* k, const v
                    const void* offsets, const void* out, const float* lse, const void* dout,
                    void* dq, void* dk, void* dv, void* doffsets,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Size of the fixed scratch array of dsa3d_backward_noalloc, per GPU, in bytes. */
+#define DSA3D_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation: the
+ * backward of dsa3d_backward (same arguments, outputs, errors and
+ * determinism) without a workspace argument. Its scratch memory is a fixed
+ * array of DSA3D_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, which
+ * that GPU holds from the library's load until the process ends; the call
+ * itself allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine). A problem whose one-head pass needs more than the array
+ * (dsa3d_workspace_min with DSA3D_WS_BACKWARD, or DSA3D_WS_BACKWARD_FIXED
+ * when offsets is NULL, above the limit) returns DSA3D_ERR_WORKSPACE before
+ * any work is enqueued; otherwise the heads are processed in as many passes
+ * as the array requires. `stream` must belong to the current device. Every
+ * call on a GPU shares that GPU's array and leaves its contents there: calls
+ * that overlap in time on one GPU (on different streams, or from different
+ * host threads) race on it and give wrong results, so serialise them. */
+int dsa3d_backward_noalloc(const dsa3d_desc* desc, const void* q, const void* k, const void* v,
+                           const void* offsets, const void* out, const float* lse, const void* dout,
+                           void* dq, void* dk, void* dv, void* doffsets, void* stream);
 
 /* Backward of the offset projection for doffsets [N, F]:
  *   dq_accum[n, c] += sum_f doffsets[n, f] * w[f, c]   (added to the dtype tensor,

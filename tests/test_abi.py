@@ -23,7 +23,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     declared = _declared_functions()
-    assert len(declared) == 13, declared
+    assert len(declared) == 14, declared
     out = subprocess.run(["nm", "-D", "--defined-only", dsa.library_path()], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT (dsa3d_\w+)", out))
@@ -226,3 +226,23 @@ def test_binding_checks_backward_and_projection_tensors():
         dsa.dsa3d_dwconv_forward(d, t["q"], torch.zeros((32, 3, 3), dtype=torch.bfloat16), None, act())
     with pytest.raises(TypeError):
         dsa.dsa3d_forward(d, t["q"], t["k"], t["v"], t["off"], t["out"], [0.0])
+
+
+def test_noalloc_backward_rejects_problems_beyond_its_scratch_on_the_host():
+    """dsa3d_backward_noalloc checks the problem against its fixed 64 MiB
+    scratch array before it touches the GPU: the 1080p 3x5x5 problem (about
+    5 GB per head) is refused with DSA3D_ERR_WORKSPACE, an invalid
+    descriptor with its own error."""
+    import ctypes
+    big = dsa.make_desc(1, 256, 68, 120, 24, 128, (3, 5, 5), dtype=torch.bfloat16, deterministic=True)
+    assert dsa.dsa3d_workspace_min(big, dsa.WS_BACKWARD) > dsa.NOALLOC_SCRATCH_BYTES
+    L = dsa.lib()
+    nul = [None] * 12
+    assert L.dsa3d_backward_noalloc(ctypes.byref(big), *nul) == -4  # DSA3D_ERR_WORKSPACE
+    assert L.dsa3d_backward_noalloc(ctypes.byref(_desc(window=(2, 3, 3))), *nul) == INVALID
+    fixed = dsa.make_desc(1, 256, 68, 120, 24, 128, (3, 7, 7), dtype=torch.bfloat16)
+    assert dsa.dsa3d_workspace_min(fixed, dsa.WS_BACKWARD_FIXED) > dsa.NOALLOC_SCRATCH_BYTES
+    assert L.dsa3d_backward_noalloc(ctypes.byref(fixed), *nul) == -4
+    assert dsa.NOALLOC_SCRATCH_BYTES == 64 << 20
+    text = open(HEADER).read()
+    assert "#define DSA3D_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
