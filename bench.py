@@ -131,6 +131,42 @@ def host_cpu():
     return usable, os.cpu_count() or 1, model
 
 
+def cpu_baseline_block(wl, budget_s: float = 20.0):
+    """The oracle's transformer block (float64 numpy and the attention oracle,
+    one head per thread) forward and backward on a bounded crop of the block
+    workload: 4 frames of 12 x 12 tokens with the workload's channels, heads
+    and window. Returns whole tokens per second."""
+    import numpy as np
+
+    import oracle
+    from deformable_local_attention_amd import synth
+
+    usable, nproc, model = host_cpu()
+    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    cores = max(1, min(usable, share) if share > 0 else usable)
+    crop = wl.with_grid(B=1, T=min(wl.T, 4), H=min(wl.H, 12), W=min(wl.W, 12), name=wl.name + "-crop")
+    x = synth.make_inputs(crop, "cpu", seed=0)
+    f64 = lambda t: t.double().numpy()
+    p = {"ln_g": f64(x["ln_g"]), "ln_b": f64(x["ln_b"]), "w_qkv": f64(x["w_qkv"]), "b_qkv": f64(x["b_qkv"]),
+         "w_off": f64(x["proj_w"]), "b_off": f64(x["proj_b"]), "w_out": f64(x["w_out"]), "b_out": f64(x["b_out"])}
+    xx, dy = f64(x["x"]), f64(x["dout"])
+
+    def one_pass():
+        t0 = time.perf_counter()
+        oracle.block_backward(xx, p, dy, crop.heads, crop.window, crop.dilation, crop.ln_eps)
+        return time.perf_counter() - t0
+
+    dt1 = one_pass()
+    reps = max(1, int(math.ceil((budget_s - dt1) / dt1)))
+    dt = sum(one_pass() for _ in range(reps))
+    return {"value": crop.tokens * reps / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "host": {"usable_cores": usable, "nproc": nproc, "omp_num_threads": share or None, "cpu_model": model},
+            "sample": (f"float64 oracle block (layer norm, projections, attention forward and backward) on a "
+                       f"{crop.T}x{crop.H}x{crop.W}-token crop with {crop.heads} heads x {crop.head_dim}; {reps} "
+                       f"passes in {dt:.1f} s (the backward recomputes the forward); the attention runs one head per "
+                       f"thread, numpy's products on its own threads")}
+
+
 def cpu_baseline(wl, budget_s: float = 20.0):
     """The oracle, as it is, on a bounded sample of the same workload: the
     interior queries of a 16x24x24-token crop drawn with the workload's
@@ -347,7 +383,7 @@ def main():
 
     import deformable_local_attention_amd as dsa
     from deformable_local_attention_amd import synth
-    from deformable_local_attention_amd.chain import Chain
+    from deformable_local_attention_amd.chain import make_chain
 
     if args.copy_calibration:
         copy_calibration()
@@ -360,7 +396,7 @@ def main():
     log(f"[bench] {synth.describe(wl)}; steps={args.steps} warmup={args.warmup}")
     t0 = time.perf_counter()
     x = synth.make_inputs(wl, "cuda:0", seed=0)
-    ch = Chain(wl, x)
+    ch = make_chain(wl, x)
     torch.cuda.synchronize()
     log(f"[bench] inputs drawn and buffers allocated in {time.perf_counter() - t0:.1f} s; "
         f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB on the device")
@@ -484,6 +520,28 @@ def main():
 
     # the depthwise convolution of the "conv" offset network: HBM-bound, algorithmic bytes per token
     # forward 2Cs (q read, y written), dq 3Cs (dy read, dq read and written), weight sums 2Cs (q, dy read)
+    # the transformer block's own kernels: the layer norm is HBM-bound (forward reads x and writes h, 2Cs per
+    # token, plus 8 B of statistics; backward reads x, dy and the residual gradient and writes dx, 4Cs + 8 B),
+    # the q/k/v and output projections are bf16 contractions of 2*C*C flops per token each (MFMA)
+    roofline_block = None
+    if wl.block:
+        s_el = 4 if wl.dtype == "f32" else 2
+        roofline_block = {}
+        ln_bytes = {"layernorm": 2 * wl.C * s_el + 8, "layernorm_bwd": 4 * wl.C * s_el + 8}
+        for k, per_tok in ln_bytes.items():
+            if k in per_kernel:
+                gbs = per_tok * wl.tokens / (per_kernel[k]["mean_ms"] / 1e3) / 1e9
+                roofline_block[k] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                     "launch_ms": round(per_kernel[k]["mean_ms"], 3)}
+        lin_flops = 2.0 * wl.tokens * wl.C * wl.C  # one C x C projection
+        for k in ("linear_forward", "linear_bwd_dx", "linear_bwd_dw"):
+            if k in per_kernel:
+                tf = lin_flops / (per_kernel[k]["mean_ms"] / 1e3) / 1e12
+                roofline_block[k] = {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                                     "launch_ms": round(per_kernel[k]["mean_ms"], 3), "flops_per_launch": lin_flops}
+
     roofline_conv = None
     if wl.offsets == "conv":
         s_el = 4 if wl.dtype == "f32" else 2
@@ -500,19 +558,25 @@ def main():
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == "bf16" else "f32", "data": "synthetic (seeded N(0,1) q/k/v/dO; offsets "
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": ("synthetic (seeded N(0,1) block input x and dO; random-init layer-norm, q/k/v and output "
+                 "projection weights; offsets from a Linear with N(0,0.02) weights of q)") if wl.block else
+        "synthetic (seeded N(0,1) q/k/v/dO; offsets "
         + (f"N(0,{wl.offset_sigma})" if wl.offsets == "direct" else "none: fixed window, every offset zero"
            if wl.offsets == "none" else "from a Linear with N(0,0.02) weights"
            + (" of a depthwise 3x3x3 conv with N(0,0.2) weights" if wl.offsets == "conv" else "")) + ")",
         "config": {"workload": wl.name, "grid": [wl.B, wl.T, wl.H, wl.W], "heads": wl.heads, "head_dim": wl.head_dim,
                    "window": list(wl.window), "P": wl.P, "dilation": list(wl.dilation), "offsets": wl.offsets,
-                   "chain": {"proj": "proj+", "conv": "dwconv+proj+"}.get(wl.offsets, "") + ("fwd+bwd" if wl.backward else "fwd"),
+                   "chain": ("layernorm+qkv+" if wl.block else "") + {"proj": "proj+", "conv": "dwconv+proj+"}.get(
+                       wl.offsets, "") + ("fwd" if not wl.block else "fwd+out_proj+residual")
+                       + ("+bwd" if wl.backward else ""),
                    "deterministic": wl.deterministic},
         "roofline": roofline, "roofline_hbm": roofline_hbm, "roofline_step": roofline_step,
         "roofline_hbm_step": roofline_hbm_step,
         "roofline_gather": roofline_gather,
         **({"roofline_proj": roofline_proj} if roofline_proj else {}),
         **({"roofline_conv": roofline_conv} if roofline_conv else {}),
+        **({"roofline_block": roofline_block} if roofline_block else {}),
         "kernels": {k: {"launches": v["launches"], "mean_ms": round(v["mean_ms"], 3)} for k, v in per_kernel.items()},
     }
     if wl.backward and wl.deterministic and args.alt_steps > 0:
@@ -532,7 +596,7 @@ def main():
         log(f"[bench] deterministic=0: {ms_fast:.2f} ms/step, {wl.tokens / ms_fast / 1e3:.3f} M tokens/s")
     if args.cpu_baseline == "on":
         log("[bench] timing the CPU oracle on a bounded sample ...")
-        result["cpu_baseline"] = cpu_baseline(wl)
+        result["cpu_baseline"] = cpu_baseline_block(wl) if wl.block else cpu_baseline(wl)
         log(f"[bench] cpu baseline: {result['cpu_baseline']['value']:.1f} tokens/s")
     print(json.dumps(result), flush=True)
 

@@ -29,7 +29,9 @@ __all__ = [
     "WS_BACKWARD_FIXED",
     "dsa3d_dwconv_forward", "dsa3d_dwconv_backward", "dwconv", "dwconv_backward",
     "dsa3d_set_launch_log", "LaunchLog", "launch_timer", "KERNELS", "dsa3d_backward_noalloc",
-    "NOALLOC_SCRATCH_BYTES",
+    "NOALLOC_SCRATCH_BYTES", "dsa3d_layernorm_forward", "dsa3d_layernorm_workspace_size", "dsa3d_layernorm_backward",
+    "dsa3d_linear_forward", "dsa3d_linear_workspace_size", "dsa3d_linear_backward", "layernorm", "linear",
+    "dtype_code",
 ]
 
 DSA3D_F32, DSA3D_BF16 = 0, 1
@@ -38,11 +40,14 @@ NOALLOC_SCRATCH_BYTES = 64 << 20  # DSA3D_NOALLOC_SCRATCH_BYTES
 EXPORTS = ("dsa3d_version", "dsa3d_status_string", "dsa3d_validate", "dsa3d_workspace_size",
            "dsa3d_workspace_min", "dsa3d_offset_proj_forward", "dsa3d_forward", "dsa3d_backward",
            "dsa3d_offset_proj_backward", "dsa3d_debug_geometry", "dsa3d_dwconv_forward", "dsa3d_dwconv_backward",
-           "dsa3d_set_launch_log", "dsa3d_backward_noalloc")
+           "dsa3d_set_launch_log", "dsa3d_backward_noalloc", "dsa3d_layernorm_forward",
+           "dsa3d_layernorm_workspace_size", "dsa3d_layernorm_backward", "dsa3d_linear_forward",
+           "dsa3d_linear_workspace_size", "dsa3d_linear_backward")
 # kernel ids of the launch log (dsa3d_kernel)
 KERNELS = {1: "proj_forward", 2: "forward", 3: "bwd_query", 4: "bwd_key", 5: "fill", 6: "proj_bwd_dq",
            7: "proj_bwd_dw", 8: "split_sum", 9: "colsum", 10: "geometry", 11: "bwd_scan", 12: "bwd_count",
-           13: "bwd_sort", 14: "transpose", 15: "dwconv", 16: "dwconv_wgrad", 17: "dwconv_dq"}
+           13: "bwd_sort", 14: "transpose", 15: "dwconv", 16: "dwconv_wgrad", 17: "dwconv_dq", 18: "layernorm",
+           19: "layernorm_bwd", 20: "linear_forward", 21: "linear_bwd_dx", 22: "linear_bwd_dw"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -88,7 +93,7 @@ def lib() -> ctypes.CDLL:
                 raise ImportError(f"libdsa3d.so not found at {path}: build it with "
                                   "`python -m deformable_local_attention_amd.build` (needs ROCm hipcc)")
             L = ctypes.CDLL(path)
-            vp, sz, dp = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Desc)
+            vp, sz, dp, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Desc), ctypes.c_int64
             sig = {
                 "dsa3d_version": ([], ctypes.c_int),
                 "dsa3d_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -104,6 +109,12 @@ def lib() -> ctypes.CDLL:
                 "dsa3d_dwconv_backward": ([dp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
                 "dsa3d_set_launch_log": ([ctypes.POINTER(LaunchLog)], ctypes.c_int),
                 "dsa3d_backward_noalloc": ([dp] + [vp] * 12, ctypes.c_int),
+                "dsa3d_layernorm_forward": ([ctypes.c_int, i64, i64, ctypes.c_float] + [vp] * 6, ctypes.c_int),
+                "dsa3d_layernorm_workspace_size": ([i64, i64], sz),
+                "dsa3d_layernorm_backward": ([ctypes.c_int, i64, i64] + [vp] * 9 + [sz, vp], ctypes.c_int),
+                "dsa3d_linear_forward": ([ctypes.c_int, i64, i64, i64] + [vp] * 6, ctypes.c_int),
+                "dsa3d_linear_workspace_size": ([ctypes.c_int, i64, i64, i64], sz),
+                "dsa3d_linear_backward": ([ctypes.c_int, i64, i64, i64] + [vp] * 8 + [sz, vp], ctypes.c_int),
             }
             for name, (args, res) in sig.items():
                 f = getattr(L, name)
@@ -142,8 +153,12 @@ class _Args:
     the same elements, such as [N, C] for [B,T,H,W,heads,d], is accepted).
     Raises ValueError (TypeError for a non-tensor)."""
 
-    def __init__(self, fn: str, desc: Desc):
+    def __init__(self, fn: str, desc: Optional[Desc], dtype: Optional[int] = None):
         self.fn = fn
+        self.tensors = []
+        if desc is None:  # the block's calls: plain sizes, shapes given per tensor
+            self.dt = _TORCH_DTYPE.get(dtype)
+            return
         self.dt = _TORCH_DTYPE.get(desc.dtype)  # None: the library reports the unsupported dtype
         tok = (desc.B, desc.T, desc.H, desc.W)
         self.act = tok + (desc.heads, desc.head_dim)
@@ -151,7 +166,6 @@ class _Args:
         self.lse = tok + (desc.heads,)
         self.C = desc.heads * desc.head_dim
         self.F = desc.heads * desc.P * 3
-        self.tensors = []
 
     def __call__(self, name: str, t, shape, dtype="run", optional: bool = False):
         if t is None:
@@ -287,6 +301,80 @@ def dsa3d_dwconv_backward(desc: Desc, q, wt, dy, dq_accum, dwt, dbias, workspace
     ws, nbytes = a.workspace(workspace)
     _check("dsa3d_dwconv_backward",
            lib().dsa3d_dwconv_backward(ctypes.byref(desc), *a.pointers(*args, ws), nbytes, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# the transformer block around the operator: layer normalisation and linear layers
+# ---------------------------------------------------------------------------
+
+def dtype_code(dtype: torch.dtype) -> int:
+    return {torch.float32: DSA3D_F32, torch.bfloat16: DSA3D_BF16}.get(dtype, -1)
+
+
+def dsa3d_layernorm_forward(dtype: int, M: int, N: int, eps: float, x, gamma, beta, y, stats, stream=None):
+    a = _Args("dsa3d_layernorm_forward", None, dtype)
+    args = (a("x", x, (M, N)), a("gamma", gamma, (N,), optional=True), a("beta", beta, (N,), optional=True),
+            a("y", y, (M, N)), a("stats", stats, (M, 2), torch.float32))
+    _check("dsa3d_layernorm_forward",
+           lib().dsa3d_layernorm_forward(dtype, M, N, float(eps), *a.pointers(*args), _stream(stream)))
+
+
+def dsa3d_layernorm_workspace_size(M: int, N: int) -> int:
+    return lib().dsa3d_layernorm_workspace_size(M, N)
+
+
+def dsa3d_layernorm_backward(dtype: int, M: int, N: int, x, gamma, stats, dy, dres, dx, dgamma, dbeta, workspace,
+                             stream=None):
+    a = _Args("dsa3d_layernorm_backward", None, dtype)
+    args = (a("x", x, (M, N)), a("gamma", gamma, (N,), optional=True), a("stats", stats, (M, 2), torch.float32),
+            a("dy", dy, (M, N)), a("dres", dres, (M, N), optional=True), a("dx", dx, (M, N)),
+            a("dgamma", dgamma, (N,), torch.float32, optional=True),
+            a("dbeta", dbeta, (N,), torch.float32, optional=True))
+    ws, nbytes = a.workspace(workspace)
+    _check("dsa3d_layernorm_backward",
+           lib().dsa3d_layernorm_backward(dtype, M, N, *a.pointers(*args, ws), nbytes, _stream(stream)))
+
+
+def dsa3d_linear_forward(dtype: int, M: int, N: int, K: int, x, w, bias, residual, y, stream=None):
+    a = _Args("dsa3d_linear_forward", None, dtype)
+    args = (a("x", x, (M, K)), a("w", w, (N, K)), a("bias", bias, (N,), optional=True),
+            a("residual", residual, (M, N), optional=True), a("y", y, (M, N)))
+    _check("dsa3d_linear_forward", lib().dsa3d_linear_forward(dtype, M, N, K, *a.pointers(*args), _stream(stream)))
+
+
+def dsa3d_linear_workspace_size(dtype: int, M: int, N: int, K: int) -> int:
+    return lib().dsa3d_linear_workspace_size(dtype, M, N, K)
+
+
+def dsa3d_linear_backward(dtype: int, M: int, N: int, K: int, x, w, dy, dres, dx, dw, dbias, workspace,
+                          stream=None):
+    a = _Args("dsa3d_linear_backward", None, dtype)
+    args = (a("x", x, (M, K)), a("w", w, (N, K)), a("dy", dy, (M, N)), a("dres", dres, (M, K), optional=True),
+            a("dx", dx, (M, K)), a("dw", dw, (N, K), torch.float32),
+            a("dbias", dbias, (N,), torch.float32, optional=True))
+    ws, nbytes = a.workspace(workspace)
+    _check("dsa3d_linear_backward",
+           lib().dsa3d_linear_backward(dtype, M, N, K, *a.pointers(*args, ws), nbytes, _stream(stream)))
+
+
+def layernorm(x, gamma, beta, eps: float = 1e-6, stream=None):
+    """Layer normalisation over the last axis; returns (y, stats [rows, 2] float32)."""
+    N = x.shape[-1]
+    M = x.numel() // N
+    y = torch.empty_like(x)
+    stats = torch.empty((M, 2), dtype=torch.float32, device=x.device)
+    dsa3d_layernorm_forward(dtype_code(x.dtype), M, N, eps, x, gamma, beta, y, stats, stream)
+    return y, stats
+
+
+def linear(x, w, bias=None, residual=None, stream=None):
+    """y = x . w^T + bias (+ residual) over the last axis of x."""
+    K = x.shape[-1]
+    M = x.numel() // K
+    N = w.shape[0]
+    y = torch.empty(tuple(x.shape[:-1]) + (N,), dtype=x.dtype, device=x.device)
+    dsa3d_linear_forward(dtype_code(x.dtype), M, N, K, x, w, bias, residual, y, stream)
+    return y
 
 
 def dsa3d_set_launch_log(log: Optional[LaunchLog]):

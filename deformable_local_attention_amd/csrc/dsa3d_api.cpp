@@ -185,6 +185,90 @@ int dsa3d_dwconv_backward(const dsa3d_desc* d, const void* q, const void* wt, co
                                                     static_cast<hipStream_t>(stream)));
 }
 
+static int check_dtype(int dtype) { return dtype == DSA3D_F32 || dtype == DSA3D_BF16 ? DSA3D_OK : DSA3D_ERR_UNSUPPORTED; }
+
+static bool size_ok(int64_t x) { return x >= 1 && x < (int64_t(1) << 31); }
+
+static int check_layernorm(int dtype, int64_t M, int64_t N) {
+    if (!size_ok(M) || !size_ok(N)) return DSA3D_ERR_INVALID_ARG;
+    if (check_dtype(dtype) != DSA3D_OK) return DSA3D_ERR_UNSUPPORTED;
+    if (N % 8 != 0 || N > 4096) return DSA3D_ERR_UNSUPPORTED;
+    return DSA3D_OK;
+}
+
+static int check_linear(int dtype, int64_t M, int64_t N, int64_t K) {
+    if (!size_ok(M) || !size_ok(N) || !size_ok(K)) return DSA3D_ERR_INVALID_ARG;
+    if (((M + 255) / 256) * ((N + 255) / 256) >= (int64_t(1) << 31) ||
+        ((N + 255) / 256) * ((K + 255) / 256) >= (int64_t(1) << 31))
+        return DSA3D_ERR_UNSUPPORTED;
+    return check_dtype(dtype);
+}
+
+int dsa3d_layernorm_forward(int dtype, int64_t M, int64_t N, float eps, const void* x, const void* gamma,
+                            const void* beta, void* y, float* stats, void* stream) {
+    int rc = check_layernorm(dtype, M, N);
+    if (rc != DSA3D_OK) return rc;
+    if (!(eps > 0.0f) || eps == __builtin_inff()) return DSA3D_ERR_INVALID_ARG;
+    if ((rc = check_ptrs({x, y, stats})) != DSA3D_OK) return rc;
+    if ((gamma && !aligned16(gamma)) || (beta && !aligned16(beta))) return DSA3D_ERR_MISALIGNED;
+    if (x == y) return DSA3D_ERR_INVALID_ARG;
+    return hip_status(
+        dsa3d::launch_layernorm_forward(dtype, M, N, eps, x, gamma, beta, y, stats, static_cast<hipStream_t>(stream)));
+}
+
+size_t dsa3d_layernorm_workspace_size(int64_t M, int64_t N) {
+    if (!size_ok(M) || !size_ok(N) || N % 8 != 0 || N > 4096) return 0;
+    return dsa3d::layernorm_bwd_workspace_bytes(M, N);
+}
+
+int dsa3d_layernorm_backward(int dtype, int64_t M, int64_t N, const void* x, const void* gamma, const float* stats,
+                             const void* dy, const void* dres, void* dx, float* dgamma, float* dbeta, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    int rc = check_layernorm(dtype, M, N);
+    if (rc != DSA3D_OK) return rc;
+    if ((rc = check_ptrs({x, stats, dy, dx})) != DSA3D_OK) return rc;
+    if ((gamma && !aligned16(gamma)) || (dgamma && !aligned16(dgamma)) || (dbeta && !aligned16(dbeta)) ||
+        (dres && !aligned16(dres)))
+        return DSA3D_ERR_MISALIGNED;
+    if (dx == x || dx == dy) return DSA3D_ERR_INVALID_ARG;
+    if (workspace == nullptr || workspace_bytes < dsa3d::layernorm_bwd_workspace_bytes(M, N)) return DSA3D_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return DSA3D_ERR_MISALIGNED;
+    return hip_status(dsa3d::launch_layernorm_backward(dtype, M, N, x, gamma, stats, dy, dres, dx, dgamma, dbeta,
+                                                       workspace, static_cast<hipStream_t>(stream)));
+}
+
+int dsa3d_linear_forward(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* w, const void* bias,
+                         const void* residual, void* y, void* stream) {
+    int rc = check_linear(dtype, M, N, K);
+    if (rc != DSA3D_OK) return rc;
+    if ((rc = check_ptrs({x, w, y})) != DSA3D_OK) return rc;
+    if ((bias && !aligned16(bias)) || (residual && !aligned16(residual))) return DSA3D_ERR_MISALIGNED;
+    if (x == y || w == y) return DSA3D_ERR_INVALID_ARG;
+    return hip_status(dsa3d::launch_linear_forward(dtype, M, N, K, x, w, bias, residual, y, DSA3D_K_LINEAR_FORWARD,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+size_t dsa3d_linear_workspace_size(int dtype, int64_t M, int64_t N, int64_t K) {
+    if (check_linear(dtype, M, N, K) != DSA3D_OK) return 0;
+    return dsa3d::linear_bwd_workspace_bytes(dtype, M, N, K);
+}
+
+int dsa3d_linear_backward(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* w, const void* dy,
+                          const void* dres, void* dx, float* dw, float* dbias, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    int rc = check_linear(dtype, M, N, K);
+    if (rc != DSA3D_OK) return rc;
+    if ((rc = check_ptrs({x, w, dy, dx, dw})) != DSA3D_OK) return rc;
+    if ((dbias && !aligned16(dbias)) || (dres && !aligned16(dres))) return DSA3D_ERR_MISALIGNED;
+    if (dx == dy || dx == w || dx == x) return DSA3D_ERR_INVALID_ARG;
+    if (workspace == nullptr || workspace_bytes < dsa3d::linear_bwd_workspace_bytes(dtype, M, N, K))
+        return DSA3D_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return DSA3D_ERR_MISALIGNED;
+    const dsa3d::LinearKernelIds ids{DSA3D_K_TRANSPOSE, DSA3D_K_LINEAR_BWD_DX, DSA3D_K_LINEAR_BWD_DW};
+    return hip_status(dsa3d::launch_linear_backward(dtype, M, N, K, x, w, dy, dres, dx, dw, dbias, workspace, ids,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
 int dsa3d_debug_geometry(const dsa3d_desc* d, const void* offsets, int32_t* base, float* frac, void* stream) {
     int rc = dsa3d_validate(d);
     if (rc != DSA3D_OK) return rc;

@@ -106,6 +106,19 @@ int64_t bwd_heads_per_pass(const dsa3d_desc& d, size_t ws_bytes);
 void proj_bwd_splits(const dsa3d_desc& d, int& dw_splits, int& db_splits);
 size_t proj_bwd_workspace_bytes(const dsa3d_desc& d);
 
+// Linear layers y[M, N] = x[M, K] . w[N, K]^T + bias (+ residual): the offset
+// projection is one (M = tokens, N = heads*P*3, K = heads*head_dim).
+struct LinearKernelIds {
+    int transpose, dx, dw;  // launch-log ids of the backward's kernels
+};
+void linear_bwd_splits(int dtype, int64_t M, int64_t N, int64_t K, int& dw_splits, int& db_splits);
+size_t linear_bwd_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K);
+hipError_t launch_linear_forward(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* w,
+                                 const void* bias, const void* residual, void* y, int kernel_id, hipStream_t s);
+hipError_t launch_linear_backward(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* w,
+                                  const void* dy, const void* dres, void* dx, float* dw, float* db, void* ws,
+                                  const LinearKernelIds& ids, hipStream_t s);
+
 hipError_t launch_forward(const dsa3d_desc& d, const void* q, const void* k, const void* v, const void* off,
                           void* out, float* lse, hipStream_t s);
 hipError_t launch_backward(const dsa3d_desc& d, const void* q, const void* k, const void* v, const void* off,
@@ -123,6 +136,12 @@ hipError_t launch_fixed_forward(const dsa3d_desc& d, const void* q, const void* 
 hipError_t launch_fixed_backward(const dsa3d_desc& d, const void* q, const void* k, const void* v, const void* o,
                                  const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws,
                                  hipStream_t s);
+size_t layernorm_bwd_workspace_bytes(int64_t M, int64_t N);
+hipError_t launch_layernorm_forward(int dtype, int64_t M, int64_t N, float eps, const void* x, const void* gamma,
+                                    const void* beta, void* y, float* stats, hipStream_t s);
+hipError_t launch_layernorm_backward(int dtype, int64_t M, int64_t N, const void* x, const void* gamma,
+                                     const float* stats, const void* dy, const void* dres, void* dx, float* dgamma,
+                                     float* dbeta, void* ws, hipStream_t s);
 hipError_t launch_dwconv_forward(const dsa3d_desc& d, const void* q, const void* w, const void* bias, void* y,
                                  hipStream_t s);
 hipError_t launch_dwconv_backward(const dsa3d_desc& d, const void* q, const void* w, const void* dy, void* dq,

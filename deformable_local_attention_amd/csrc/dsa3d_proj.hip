@@ -27,6 +27,8 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr int BM = 128, BN = 128, BK = 32;
 
+// OUT_BIAS: C = A.B + bias; OUT_ACCUM: C = A.B + bias + R (one rounding; R may be C itself);
+// OUT_PARTIAL: float32 partial products of one K split.
 enum GemmOut { OUT_BIAS = 0, OUT_ACCUM = 1, OUT_PARTIAL = 2 };
 
 struct GemmArgs {
@@ -37,7 +39,8 @@ struct GemmArgs {
     int64_t k_split;   // K range of one blockIdx.z slice (multiple of BK)
     void* C;           // output: dtype tensor (OUT_BIAS, OUT_ACCUM) or float32 partials
     int64_t ldc;
-    const void* bias;  // [N] or null (OUT_BIAS)
+    const void* bias;  // [N] or null (OUT_BIAS, OUT_ACCUM)
+    const void* R;     // OUT_ACCUM: C = A.B + bias + R, R with C's layout (R == C: accumulate in place)
     int a_vec, b_vec;  // 8-element vector loads are in bounds and aligned
 };
 
@@ -195,8 +198,9 @@ __global__ void __launch_bounds__(256) dsa3d_gemm_kernel(GemmArgs g) {
                     const float bb = g.bias ? load_scalar<T>(reinterpret_cast<const T*>(g.bias) + n) : 0.0f;
                     store_scalar<T>(reinterpret_cast<T*>(g.C) + m * g.ldc + n, x + bb);
                 } else if (MODE == OUT_ACCUM) {
-                    T* p = reinterpret_cast<T*>(g.C) + m * g.ldc + n;
-                    store_scalar<T>(p, load_scalar<T>(p) + x);
+                    const float bb = g.bias ? load_scalar<T>(reinterpret_cast<const T*>(g.bias) + n) : 0.0f;
+                    const float r = load_scalar<T>(reinterpret_cast<const T*>(g.R) + m * g.ldc + n);
+                    store_scalar<T>(reinterpret_cast<T*>(g.C) + m * g.ldc + n, r + (x + bb));
                 } else {
                     reinterpret_cast<float*>(g.C)[(int64_t)blockIdx.z * g.M * g.ldc + m * g.ldc + n] = x;
                 }
@@ -385,8 +389,9 @@ __device__ __forceinline__ void x_epilogue(const GemmArgs& g, f32x16_t acc[4][4]
     for (int j = 0; j < 4; ++j) {
         const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
         if (EDGE && n >= g.N) continue;
-        const float bb = (MODE == OUT_BIAS && g.bias) ? load_scalar<bf16_t>(reinterpret_cast<const bf16_t*>(g.bias) + n)
-                                                      : 0.0f;
+        const float bb = (MODE != OUT_PARTIAL && g.bias)
+                             ? load_scalar<bf16_t>(reinterpret_cast<const bf16_t*>(g.bias) + n)
+                             : 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -397,8 +402,8 @@ __device__ __forceinline__ void x_epilogue(const GemmArgs& g, f32x16_t acc[4][4]
                 if (MODE == OUT_BIAS) {
                     store_scalar<bf16_t>(reinterpret_cast<bf16_t*>(g.C) + m * g.ldc + n, x + bb);
                 } else if (MODE == OUT_ACCUM) {
-                    bf16_t* p = reinterpret_cast<bf16_t*>(g.C) + m * g.ldc + n;
-                    store_scalar<bf16_t>(p, load_scalar<bf16_t>(p) + x);
+                    const float r = load_scalar<bf16_t>(reinterpret_cast<const bf16_t*>(g.R) + m * g.ldc + n);
+                    store_scalar<bf16_t>(reinterpret_cast<bf16_t*>(g.C) + m * g.ldc + n, r + (x + bb));
                 } else {
                     reinterpret_cast<float*>(g.C)[(int64_t)blockIdx.z * g.M * g.ldc + m * g.ldc + n] = x;
                 }
@@ -617,6 +622,7 @@ __device__ __forceinline__ void y_epilogue(const GemmArgs& g, f32x16_t acc[4][4]
     const int64_t mq = m0 + wm * 128, nq = n0 + wn * 128;  // this wave's quarter
     char* tile = lds + wave * 32768;                        // 128 rows x 256 B, 16-byte chunk c of row m at c ^ (m & 15)
     const bf16_t* bias = reinterpret_cast<const bf16_t*>(g.bias);
+    const bf16_t* R = reinterpret_cast<const bf16_t*>(g.R);
     bf16_t* C = reinterpret_cast<bf16_t*>(g.C);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -624,7 +630,7 @@ __device__ __forceinline__ void y_epilogue(const GemmArgs& g, f32x16_t acc[4][4]
         for (int e4 = 0; e4 < 4; ++e4) {
             const int nl = 32 * j + 8 * e4 + 4 * (lane >> 5);  // first of 4 columns
             float add[4] = {0.f, 0.f, 0.f, 0.f};
-            if (MODE == OUT_BIAS && bias) {
+            if (bias) {
                 const int64_t n = nq + nl;
                 if (n + 4 <= g.N) {
                     const uint2 bw = *reinterpret_cast<const uint2*>(bias + n);
@@ -640,8 +646,9 @@ __device__ __forceinline__ void y_epilogue(const GemmArgs& g, f32x16_t acc[4][4]
                 if (MODE == OUT_ACCUM) {
                     const int64_t m = mq + ml, n = nq + nl;
                     if (m < g.M && n + 4 <= g.N) {
-                        const uint2 o = *reinterpret_cast<const uint2*>(C + m * g.ldc + n);
-                        x[0] += bf16_lo(o.x); x[1] += bf16_hi(o.x); x[2] += bf16_lo(o.y); x[3] += bf16_hi(o.y);
+                        const uint2 o = *reinterpret_cast<const uint2*>(R + m * g.ldc + n);
+                        x[0] = bf16_lo(o.x) + x[0]; x[1] = bf16_hi(o.x) + x[1];
+                        x[2] = bf16_lo(o.y) + x[2]; x[3] = bf16_hi(o.y) + x[3];
                     }
                 }
                 const uint2 w = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
@@ -901,128 +908,156 @@ static hipError_t gemm_any(GemmArgs g, int splits, int kernel_id, hipStream_t s)
     return gemm<T, AK, BKC, MODE>(g, splits, kernel_id, s);
 }
 
-// Split counts of the two long reductions over the N_tok rows.
-void proj_bwd_splits(const dsa3d_desc& d, int& dw_splits, int& db_splits) {
-    const int64_t ntok = d.B * d.T * d.H * d.W;
-    const int64_t F = (int64_t)d.heads * d.P * 3, C = (int64_t)d.heads * d.head_dim;
-    const int64_t tm = d.dtype == DSA3D_BF16 ? XM : BM, tn = d.dtype == DSA3D_BF16 ? XN : BN;
-    const int64_t tiles = ((F + tm - 1) / tm) * ((C + tn - 1) / tn);
+// Split counts of the two long reductions over the M rows of a linear layer's
+// backward (dW over the rows, db over the rows).
+void linear_bwd_splits(int dtype, int64_t M, int64_t N, int64_t K, int& dw_splits, int& db_splits) {
+    const int64_t tm = dtype == DSA3D_BF16 ? XM : BM, tn = dtype == DSA3D_BF16 ? XN : BN;
+    const int64_t tiles = ((N + tm - 1) / tm) * ((K + tn - 1) / tn);
     int64_t s = (1024 + tiles - 1) / std::max<int64_t>(tiles, 1);
-    s = std::max<int64_t>(1, std::min<int64_t>(s, std::max<int64_t>(1, ntok / (4 * XK))));
+    s = std::max<int64_t>(1, std::min<int64_t>(s, std::max<int64_t>(1, M / (4 * XK))));
     s = std::min<int64_t>(s, 64);
     dw_splits = (int)s;
     // column sums: up to 1024 splits of at least 256 rows
-    db_splits = (int)std::max<int64_t>(1, std::min<int64_t>(1024, ntok / 256));
+    db_splits = (int)std::max<int64_t>(1, std::min<int64_t>(1024, M / 256));
+}
+
+size_t linear_bwd_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K) {
+    int sw, sb;
+    linear_bwd_splits(dtype, M, N, K, sw, sb);
+    size_t bytes = (size_t)sw * N * K * 4 + (size_t)sb * N * 4;
+    if (dtype == DSA3D_BF16) bytes += 256 + (size_t)N * K * 2;  // w transposed, 256-aligned
+    return bytes + 256;
+}
+
+void proj_bwd_splits(const dsa3d_desc& d, int& dw_splits, int& db_splits) {
+    linear_bwd_splits(d.dtype, d.B * d.T * d.H * d.W, (int64_t)d.heads * d.P * 3, (int64_t)d.heads * d.head_dim,
+                      dw_splits, db_splits);
 }
 
 size_t proj_bwd_workspace_bytes(const dsa3d_desc& d) {
-    int sw, sb;
-    proj_bwd_splits(d, sw, sb);
-    const int64_t F = (int64_t)d.heads * d.P * 3, C = (int64_t)d.heads * d.head_dim;
-    size_t bytes = (size_t)sw * F * C * 4 + (size_t)sb * F * 4;
-    if (d.dtype == DSA3D_BF16) bytes += 256 + (size_t)F * C * 2;  // w transposed, 256-aligned
-    return bytes + 256;
+    return linear_bwd_workspace_bytes(d.dtype, d.B * d.T * d.H * d.W, (int64_t)d.heads * d.P * 3,
+                                      (int64_t)d.heads * d.head_dim);
+}
+
+hipError_t launch_linear_forward(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* w,
+                                 const void* bias, const void* residual, void* y, int kernel_id, hipStream_t s) {
+    GemmArgs g{};
+    g.A = x; g.lda = K;
+    g.B = w; g.ldb = K;
+    g.M = M; g.N = N; g.K = K;
+    g.k_split = round_up(g.K, BK);
+    g.C = y; g.ldc = N;
+    g.bias = bias;
+    g.R = residual;
+    const bool f32 = dtype == DSA3D_F32;
+    if (residual == nullptr) {
+        if (f32) return gemm<float, true, true, OUT_BIAS>(g, 1, kernel_id, s);
+        if (ntgemm_ok(g)) return ntgemm<OUT_BIAS>(g, kernel_id, s);
+        return gemm_any<bf16_t, true, true, OUT_BIAS>(g, 1, kernel_id, s);
+    }
+    if (f32) return gemm<float, true, true, OUT_ACCUM>(g, 1, kernel_id, s);
+    if (ntgemm_ok(g) && aligned16(residual)) return ntgemm<OUT_ACCUM>(g, kernel_id, s);
+    return gemm_any<bf16_t, true, true, OUT_ACCUM>(g, 1, kernel_id, s);
 }
 
 hipError_t launch_proj_forward(const dsa3d_desc& d, const void* q, const void* w, const void* bias, void* off,
                                hipStream_t s) {
-    GemmArgs g{};
-    g.A = q; g.lda = (int64_t)d.heads * d.head_dim;
-    g.B = w; g.ldb = g.lda;
-    g.M = d.B * d.T * d.H * d.W;
-    g.N = (int64_t)d.heads * d.P * 3;
-    g.K = g.lda;
-    g.k_split = round_up(g.K, BK);
-    g.C = off; g.ldc = g.N;
-    g.bias = bias;
-    if (d.dtype == DSA3D_F32) return gemm<float, true, true, OUT_BIAS>(g, 1, DSA3D_K_PROJ_FORWARD, s);
-    if (ntgemm_ok(g)) return ntgemm<OUT_BIAS>(g, DSA3D_K_PROJ_FORWARD, s);
-    return gemm_any<bf16_t, true, true, OUT_BIAS>(g, 1, DSA3D_K_PROJ_FORWARD, s);
+    return launch_linear_forward(d.dtype, d.B * d.T * d.H * d.W, (int64_t)d.heads * d.P * 3,
+                                 (int64_t)d.heads * d.head_dim, q, w, bias, nullptr, off, DSA3D_K_PROJ_FORWARD, s);
 }
 
-hipError_t launch_proj_backward(const dsa3d_desc& d, const void* q, const void* w, const void* doff, void* dq,
-                                float* dw, float* db, void* ws, hipStream_t s) {
-    const int64_t ntok = d.B * d.T * d.H * d.W;
-    const int64_t F = (int64_t)d.heads * d.P * 3, C = (int64_t)d.heads * d.head_dim;
-    if (ntok == 0) return hipSuccess;
-    const bool f32 = d.dtype == DSA3D_F32;
+hipError_t launch_linear_backward(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* w,
+                                  const void* dy, const void* dres, void* dx, float* dw, float* db, void* ws,
+                                  const LinearKernelIds& ids, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    const bool f32 = dtype == DSA3D_F32;
     hipError_t e;
     int sw, sb;
-    proj_bwd_splits(d, sw, sb);
-    // dq[ntok, C] += doff[ntok, F] . W[F, C]
+    linear_bwd_splits(dtype, M, N, K, sw, sb);
+    // dx[M, K] = dres + dy[M, N] . w[N, K]
     GemmArgs g{};
-    g.A = doff; g.lda = F;
-    g.B = w; g.ldb = C;
-    g.M = ntok; g.N = C; g.K = F;
-    g.k_split = round_up(F, BK);
-    g.C = dq; g.ldc = C;
-    // bf16: with W transposed into the workspace ([C, F], K-contiguous) the
+    g.A = dy; g.lda = N;
+    g.B = w; g.ldb = K;
+    g.M = M; g.N = K; g.K = N;
+    g.k_split = round_up(N, BK);
+    g.C = dx; g.ldc = K;
+    g.R = dres;
+    // bf16: with w transposed into the workspace ([K, N], contiguous along N) the
     // product takes the DMA-fed kernel
-    const uintptr_t wt_at = round_up((int64_t)(reinterpret_cast<uintptr_t>(ws) + (size_t)sw * F * C * 4 +
-                                               (size_t)sb * F * 4), 256);
+    const uintptr_t wt_at = round_up((int64_t)(reinterpret_cast<uintptr_t>(ws) + (size_t)sw * N * K * 4 +
+                                               (size_t)sb * N * 4), 256);
     GemmArgs gt = g;
     gt.B = reinterpret_cast<const void*>(wt_at);
-    gt.ldb = F;
+    gt.ldb = N;
     if (!f32 && ntgemm_ok(gt)) {
         {
-            LaunchScope ls(DSA3D_K_TRANSPOSE, s);
-            hipLaunchKernelGGL(dsa3d_transpose_kernel, dim3((unsigned)((C + 63) / 64), (unsigned)((F + 63) / 64)),
+            LaunchScope ls(ids.transpose, s);
+            hipLaunchKernelGGL(dsa3d_transpose_kernel, dim3((unsigned)((K + 63) / 64), (unsigned)((N + 63) / 64)),
                                dim3(256), 0, s, reinterpret_cast<const bf16_t*>(w), reinterpret_cast<bf16_t*>(wt_at),
-                               F, C);
+                               N, K);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        e = ntgemm<OUT_ACCUM>(gt, DSA3D_K_PROJ_BWD_DQ, s);
+        e = dres ? ntgemm<OUT_ACCUM>(gt, ids.dx, s) : ntgemm<OUT_BIAS>(gt, ids.dx, s);
+    } else if (dres) {
+        e = f32 ? gemm<float, true, false, OUT_ACCUM>(g, 1, ids.dx, s)
+                : gemm_any<bf16_t, true, false, OUT_ACCUM>(g, 1, ids.dx, s);
     } else {
-        e = f32 ? gemm<float, true, false, OUT_ACCUM>(g, 1, DSA3D_K_PROJ_BWD_DQ, s)
-                : gemm_any<bf16_t, true, false, OUT_ACCUM>(g, 1, DSA3D_K_PROJ_BWD_DQ, s);
+        e = f32 ? gemm<float, true, false, OUT_BIAS>(g, 1, ids.dx, s)
+                : gemm_any<bf16_t, true, false, OUT_BIAS>(g, 1, ids.dx, s);
     }
     if (e != hipSuccess) return e;
-    // dW[F, C] = doff^T . q, split over the token rows, then a fixed-order sum
+    // dw[N, K] = dy^T . x, split over the rows, then a fixed-order sum
     float* part = reinterpret_cast<float*>(ws);
     GemmArgs h{};
-    h.A = doff; h.lda = F;   // a(m=f, k=n) = doff[n*F + f]: M-contiguous
-    h.B = q; h.ldb = C;      // b(k=n, n=c) = q[n*C + c]: N-contiguous
-    h.M = F; h.N = C; h.K = ntok;
-    h.k_split = round_up((ntok + sw - 1) / sw, XK);  // a multiple of both kernels' K slice
-    const int splits = (int)((ntok + h.k_split - 1) / h.k_split);
-    h.C = part; h.ldc = C;
-    e = f32 ? gemm<float, false, false, OUT_PARTIAL>(h, splits, DSA3D_K_PROJ_BWD_DW, s)
-              : gemm_any<bf16_t, false, false, OUT_PARTIAL>(h, splits, DSA3D_K_PROJ_BWD_DW, s);
+    h.A = dy; h.lda = N;   // a(m=n, k=row) = dy[row*N + n]: M-contiguous
+    h.B = x; h.ldb = K;    // b(k=row, n=c) = x[row*K + c]: N-contiguous
+    h.M = N; h.N = K; h.K = M;
+    h.k_split = round_up((M + sw - 1) / sw, XK);  // a multiple of both kernels' K slice
+    const int splits = (int)((M + h.k_split - 1) / h.k_split);
+    h.C = part; h.ldc = K;
+    e = f32 ? gemm<float, false, false, OUT_PARTIAL>(h, splits, ids.dw, s)
+            : gemm_any<bf16_t, false, false, OUT_PARTIAL>(h, splits, ids.dw, s);
     if (e != hipSuccess) return e;
-    const int64_t nw = F * C;
+    const int64_t nw = N * K;
     {
         LaunchScope ls(DSA3D_K_SPLIT_SUM, s);
-        hipLaunchKernelGGL(dsa3d_split_sum_kernel, dim3((unsigned)std::min<int64_t>((nw + 255) / 256, 65536)), dim3(256), 0,
-                           s, part, dw, nw, splits);
+        hipLaunchKernelGGL(dsa3d_split_sum_kernel, dim3((unsigned)std::min<int64_t>((nw + 255) / 256, 65536)),
+                           dim3(256), 0, s, part, dw, nw, splits);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (db) {
-        float* bpart = part + (size_t)sw * F * C;
-        const int64_t rps = (ntok + sb - 1) / sb;
-        const int bsplits = (int)((ntok + rps - 1) / rps);
+        float* bpart = part + (size_t)sw * N * K;
+        const int64_t rps = (M + sb - 1) / sb;
+        const int bsplits = (int)((M + rps - 1) / rps);
         {
             LaunchScope ls(DSA3D_K_COLSUM, s);
-            if (!f32 && F % 8 == 0 && aligned16(doff) && aligned16(bpart)) {
-                dim3 grid((unsigned)((F / 8 + 255) / 256), (unsigned)bsplits);
-                hipLaunchKernelGGL(dsa3d_colsum8_kernel, grid, dim3(256), 0, s, (const bf16_t*)doff, bpart, ntok, F,
-                                   rps);
+            if (!f32 && N % 8 == 0 && aligned16(dy) && aligned16(bpart)) {
+                dim3 grid((unsigned)((N / 8 + 255) / 256), (unsigned)bsplits);
+                hipLaunchKernelGGL(dsa3d_colsum8_kernel, grid, dim3(256), 0, s, (const bf16_t*)dy, bpart, M, N, rps);
             } else {
-                dim3 grid((unsigned)((F + 255) / 256), (unsigned)bsplits);
+                dim3 grid((unsigned)((N + 255) / 256), (unsigned)bsplits);
                 if (f32)
-                    hipLaunchKernelGGL((dsa3d_colsum_kernel<float>), grid, dim3(256), 0, s, (const float*)doff, bpart,
-                                       ntok, F, rps);
+                    hipLaunchKernelGGL((dsa3d_colsum_kernel<float>), grid, dim3(256), 0, s, (const float*)dy, bpart,
+                                       M, N, rps);
                 else
-                    hipLaunchKernelGGL((dsa3d_colsum_kernel<bf16_t>), grid, dim3(256), 0, s, (const bf16_t*)doff,
-                                       bpart, ntok, F, rps);
+                    hipLaunchKernelGGL((dsa3d_colsum_kernel<bf16_t>), grid, dim3(256), 0, s, (const bf16_t*)dy,
+                                       bpart, M, N, rps);
             }
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
         LaunchScope ls(DSA3D_K_SPLIT_SUM, s);
-        hipLaunchKernelGGL(dsa3d_split_sum_kernel, dim3((unsigned)((F + 255) / 256)), dim3(256), 0, s, bpart, db, F,
+        hipLaunchKernelGGL(dsa3d_split_sum_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, bpart, db, N,
                            bsplits);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_proj_backward(const dsa3d_desc& d, const void* q, const void* w, const void* doff, void* dq,
+                                float* dw, float* db, void* ws, hipStream_t s) {
+    const LinearKernelIds ids{DSA3D_K_TRANSPOSE, DSA3D_K_PROJ_BWD_DQ, DSA3D_K_PROJ_BWD_DW};
+    return launch_linear_backward(d.dtype, d.B * d.T * d.H * d.W, (int64_t)d.heads * d.P * 3,
+                                  (int64_t)d.heads * d.head_dim, q, w, doff, dq, dq, dw, db, ws, ids, s);
 }
 
 }  // namespace dsa3d

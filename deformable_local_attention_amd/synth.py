@@ -13,7 +13,8 @@ to 68 rows; 720p gives 45 x 80.
 
 Draw order (one generator, seed 0 unless stated): q, k, v (float32 N(0,1),
 then rounded to the run dtype), projection weight W (N(0, 0.02)), bias (zeros),
-direct offsets (N(0, sigma)), upstream gradient dO (N(0,1)).
+direct offsets (N(0, sigma)), upstream gradient dO (N(0,1)). Block workloads
+draw the block's input and parameters instead (see make_inputs).
 """
 from __future__ import annotations
 
@@ -43,6 +44,10 @@ class Workload:
     weight_sigma: float = 0.02            # std of projection weights
     backward: bool = False                # chain includes the backward pass
     deterministic: bool = False           # K/V-gradient accumulation mode
+    block: bool = False                   # the whole transformer block around the operator (layer norm,
+                                          # q/k/v projections, offset projection, attention, output
+                                          # projection with the residual add); offsets must be "proj"
+    ln_eps: float = 1e-6                  # the block's layer-normalisation epsilon
     description: str = ""
 
     @property
@@ -101,6 +106,13 @@ WORKLOADS: Dict[str, Workload] = {
                  offset_sigma=2.0, backward=True, deterministic=True,
                  description="bf16 fwd + bwd, 256x68x120 tokens, 24x128 heads, 3x5x5 window, "
                              "offsets N(0,2), deterministic K/V gradients"),
+        Workload("720p-bf16-block", 1, 64, 45, 80, 16, 64, (3, 3, 3), (1, 2, 2), "bf16", "proj",
+                 backward=True, block=True,
+                 description="bf16 transformer block fwd + bwd: layer norm, q/k/v projections, offset projection, "
+                             "3D-DSA, output projection + residual; 64x45x80 tokens, 16x64 heads, dilation (1,2,2)"),
+        Workload("1080p-bf16-block", 1, 256, 68, 120, 24, 128, (3, 3, 3), (1, 1, 1), "bf16", "proj",
+                 backward=True, block=True,
+                 description="bf16 transformer block fwd + bwd around 3D-DSA, 256x68x120 tokens, 24x128 heads"),
     ]
 }
 
@@ -134,7 +146,10 @@ def make_inputs(wl: Workload, device="cpu", seed: int = 0,
 
     Returns q, k, v [B,T,H,W,heads,d]; for direct offsets `offsets`
     [B,T,H,W,heads,P,3]; for projected offsets `proj_w` [heads*P*3, C] and
-    `proj_b` [heads*P*3]; and `dout` when the chain has a backward pass.
+    `proj_b` [heads*P*3]; and `dout` when the chain has a backward pass. A
+    block workload instead returns the block's input x [B,T,H,W,C], its
+    parameters (ln_g, ln_b, w_qkv, b_qkv, proj_w, proj_b, w_out, b_out) and
+    `dout` [B,T,H,W,C], the gradient of the block's output.
     """
     dev = torch.device(device)
     gen = torch.Generator(device=dev)
@@ -142,6 +157,24 @@ def make_inputs(wl: Workload, device="cpu", seed: int = 0,
     dt = wl.torch_dtype
     shp = (wl.B, wl.T, wl.H, wl.W, wl.heads, wl.head_dim)
     out = {}
+    if wl.block:
+        # the block's input and parameters: x ~ N(0,1); layer-norm gain 1 + N(0, 0.1^2), shift N(0, 0.1^2);
+        # q/k/v and output projections N(0, 1/C) (so q, k, v and the output keep unit scale), their
+        # biases N(0, 0.1^2); the offset projection N(0, weight_sigma^2) with zero bias; dO of y ~ N(0,1)
+        C, F = wl.C, wl.F
+        xs = (wl.B, wl.T, wl.H, wl.W, C)
+        out["x"] = _randn(xs, 1.0, dt, gen, dev)
+        out["ln_g"] = _randn((C,), 0.1, torch.float32, gen, dev).add_(1.0).to(dt)
+        out["ln_b"] = _randn((C,), 0.1, dt, gen, dev)
+        out["w_qkv"] = _randn((3 * C, C), C ** -0.5, dt, gen, dev)
+        out["b_qkv"] = _randn((3 * C,), 0.1, dt, gen, dev)
+        out["proj_w"] = _randn((F, C), wl.weight_sigma, dt, gen, dev)
+        out["proj_b"] = torch.zeros(F, dtype=dt, device=dev)
+        out["w_out"] = _randn((C, C), C ** -0.5, dt, gen, dev)
+        out["b_out"] = _randn((C,), 0.1, dt, gen, dev)
+        if with_grad if with_grad is not None else wl.backward:
+            out["dout"] = _randn(xs, 1.0, dt, gen, dev)
+        return out
     out["q"] = _randn(shp, 1.0, dt, gen, dev)
     out["k"] = _randn(shp, 1.0, dt, gen, dev)
     out["v"] = _randn(shp, 1.0, dt, gen, dev)
@@ -181,5 +214,5 @@ def describe(wl: Workload) -> str:
     return (f"{wl.name}: B={wl.B} T={wl.T} H={wl.H} W={wl.W} heads={wl.heads} d={wl.head_dim} "
             f"window={wl.window} dil={wl.dilation} P={wl.P} {wl.dtype} offsets={wl.offsets}"
             + (f" sigma={wl.offset_sigma}" if wl.offsets == "direct" else "")
-            + (" +bwd" if wl.backward else "") + (" det" if wl.deterministic else ""))
+            + (" +bwd" if wl.backward else "") + (" det" if wl.deterministic else "") + (" block" if wl.block else ""))
 

@@ -216,6 +216,66 @@ int dsa3d_dwconv_backward(const dsa3d_desc* desc, const void* q, const void* wt,
                           void* dq_accum, float* dwt, float* dbias,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * The transformer block around the operator. The pages wrap their attention in
+ * layer normalisation and residual connections as usual, and its queries, keys
+ * and values come from (and its output goes through) dense projections
+ * [MegaSlide-DiT, §5.3 Implementation considerations]. These calls give that
+ * block without leaving the library: per token,
+ *   h = LayerNorm(x); q|k|v = h.W_qkv^T + b_qkv; o = 3D-DSA(q, k, v, offsets);
+ *   y = x + o.W_out^T + b_out
+ * (each of q, k, v is one dsa3d_linear_forward with its [C, C] slice of W_qkv;
+ * the residual add is the output projection's epilogue). They take plain
+ * sizes instead of a descriptor: rows M (tokens), widths N and K; tensors are
+ * dense row-major device tensors of `dtype` (DSA3D_F32 or DSA3D_BF16) unless
+ * stated, 16-byte aligned, owned by the caller; calls are asynchronous on
+ * `stream` and allocate nothing; errors as for every call.
+ * ------------------------------------------------------------------------- */
+
+/* Layer normalisation over the last axis of x [M, N]:
+ *   mean = sum(x)/N, var = sum((x - mean)^2)/N, rstd = 1/sqrt(var + eps),
+ *   y = (x - mean) * rstd * gamma + beta
+ * gamma/beta [N] (NULL: 1 and 0). stats [M, 2] float32 receives (mean, rstd)
+ * per row for the backward. Float32 arithmetic, one rounding per element of y.
+ * Needs N % 8 == 0, N <= 4096, eps > 0 (DSA3D_ERR_UNSUPPORTED /
+ * DSA3D_ERR_INVALID_ARG otherwise). y may not alias x. */
+int dsa3d_layernorm_forward(int dtype, int64_t M, int64_t N, float eps, const void* x, const void* gamma,
+                            const void* beta, void* y, float* stats, void* stream);
+
+/* Workspace bytes of dsa3d_layernorm_backward (split partials of dgamma/dbeta). */
+size_t dsa3d_layernorm_workspace_size(int64_t M, int64_t N);
+
+/* Backward of dsa3d_layernorm_forward for dy = dL/dy [M, N], with the forward's
+ * stats: xh = (x - mean)*rstd, g = dy*gamma,
+ *   dx = dres + rstd * (g - mean(g) - xh * mean(g*xh))   (one rounding)
+ *   dgamma = sum over rows of dy*xh, dbeta = sum over rows of dy
+ *   (float32 [N], overwritten, either may be NULL; summed in a fixed order).
+ * dres [M, N] is the gradient reaching x by another path (the block's residual
+ * connection), NULL for none; it may be dx itself (add in place). */
+int dsa3d_layernorm_backward(int dtype, int64_t M, int64_t N, const void* x, const void* gamma, const float* stats,
+                             const void* dy, const void* dres, void* dx, float* dgamma, float* dbeta,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Linear layer y[M, N] = x[M, K] . w[N, K]^T + bias[N] (+ residual[M, N]), on
+ * the matrix cores for bf16, accumulated in float32 and rounded once. bias and
+ * residual may be NULL; residual may be y itself (an in-place add). Sizes each
+ * in [1, 2^31). */
+int dsa3d_linear_forward(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* w,
+                         const void* bias, const void* residual, void* y, void* stream);
+
+/* Workspace bytes of dsa3d_linear_backward (split partials of dw and dbias
+ * and, for bf16, w transposed). */
+size_t dsa3d_linear_workspace_size(int dtype, int64_t M, int64_t N, int64_t K);
+
+/* Backward of dsa3d_linear_forward for dy = dL/dy [M, N]:
+ *   dx[M, K] = dres + dy . w   (one rounding; dres [M, K] NULL for none, or dx
+ *                               itself to add in place)
+ *   dw[N, K] = dy^T . x (float32, overwritten), dbias[N] = column sums of dy
+ *   (float32, overwritten, may be NULL); dw and dbias summed in a fixed order. */
+int dsa3d_linear_backward(int dtype, int64_t M, int64_t N, int64_t K, const void* x, const void* w, const void* dy,
+                          const void* dres, void* dx, float* dw, float* dbias, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 /* Test hook: the integer base corner floor(pos) and the float32 fraction f of
  * every sample, both [B,T,H,W,heads,P,3] (int32, float32). A sample whose
  * position is NaN, infinite or |pos| >= 2^30 reports base INT32_MIN and f 0. */
@@ -242,7 +302,12 @@ typedef enum {
     DSA3D_K_TRANSPOSE = 14,     /* projection backward: W transposed for the dq product */
     DSA3D_K_DWCONV = 15,        /* depthwise convolution forward */
     DSA3D_K_DWCONV_WGRAD = 16,  /* depthwise convolution backward: split weight and bias sums */
-    DSA3D_K_DWCONV_DQ = 17      /* depthwise convolution backward: dq += conv with the mirrored kernel */
+    DSA3D_K_DWCONV_DQ = 17,     /* depthwise convolution backward: dq += conv with the mirrored kernel */
+    DSA3D_K_LAYERNORM = 18,     /* layer normalisation forward */
+    DSA3D_K_LAYERNORM_BWD = 19, /* layer normalisation backward: dx and partial dgamma/dbeta */
+    DSA3D_K_LINEAR_FORWARD = 20,/* linear layer y = x.w^T + bias (+ residual) */
+    DSA3D_K_LINEAR_BWD_DX = 21, /* linear layer backward: dx (+)= dy.w */
+    DSA3D_K_LINEAR_BWD_DW = 22  /* linear layer backward: split dw = dy^T.x */
 } dsa3d_kernel;
 
 typedef struct dsa3d_launch_log {

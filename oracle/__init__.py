@@ -405,3 +405,112 @@ def dwconv3d_backward(q, w, dy) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
                 dq += wt[:, i, j, k] * gp[:, 2 - i:2 - i + T, 2 - j:2 - j + H, 2 - k:2 - k + W]
                 dw[:, i, j, k] = (g * xp[:, i:i + T, j:j + H, k:k + W]).sum(axis=(0, 1, 2, 3))
     return dq, dw, g.sum(axis=(0, 1, 2, 3))
+
+
+# ----------------------------------------------------------------------------
+# The transformer block around the operator. The pages keep layer normalisation
+# and residual connections around their attention as usual, with dense
+# projections for the queries, keys, values and output [MegaSlide-DiT, §5.3
+# Implementation considerations]. Read as the plain pre-norm block:
+#   h = LayerNorm(x); q, k, v = h W_q^T + b_q, h W_k^T + b_k, h W_v^T + b_v;
+#   offsets = q W_off^T + b_off; o = 3D-DSA(q, k, v, offsets); y = x + o W_out^T + b_out
+# over each token's C channels, all in float64 (the attention's offsets are
+# rounded to single precision by the attention oracle, as everywhere).
+# ----------------------------------------------------------------------------
+
+def layernorm(x, gamma=None, beta=None, eps: float = 1e-6):
+    """Over the last axis: (x - mean) / sqrt(var + eps) * gamma + beta, with the
+    population variance. Returns (y, mean, rstd), float64."""
+    x = _f64(x)
+    mean = x.mean(axis=-1, keepdims=True)
+    var = ((x - mean) ** 2).mean(axis=-1, keepdims=True)
+    rstd = 1.0 / np.sqrt(var + eps)
+    y = (x - mean) * rstd
+    if gamma is not None:
+        y = y * _f64(gamma)
+    if beta is not None:
+        y = y + _f64(beta)
+    return y, mean[..., 0], rstd[..., 0]
+
+
+def layernorm_backward(x, gamma, dy, eps: float = 1e-6):
+    """Gradients of layernorm for dL/dy = dy: (dx, dgamma, dbeta), float64.
+    With xh the normalised input and g = dy * gamma:
+    dx = rstd * (g - mean(g) - xh * mean(g * xh)); dgamma = sum of dy * xh and
+    dbeta = sum of dy over every axis but the last."""
+    x, dy = _f64(x), _f64(dy)
+    _, mean, rstd = layernorm(x, None, None, eps)
+    xh = (x - mean[..., None]) * rstd[..., None]
+    g = dy * (_f64(gamma) if gamma is not None else 1.0)
+    dx = rstd[..., None] * (g - g.mean(axis=-1, keepdims=True) - xh * (g * xh).mean(axis=-1, keepdims=True))
+    axes = tuple(range(x.ndim - 1))
+    return dx, (dy * xh).sum(axis=axes), dy.sum(axis=axes)
+
+
+def linear(x2d, w, b=None) -> np.ndarray:
+    """y[M, N] = x[M, K] @ w[N, K]^T + b[N], float64."""
+    return offset_proj(x2d, w, b)
+
+
+def linear_backward(x2d, w, dy2d) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """(dx = dy @ w, dw = dy^T @ x, db = column sums of dy), float64."""
+    return offset_proj_backward(x2d, w, dy2d)
+
+
+BLOCK_PARAMS = ("ln_g", "ln_b", "w_qkv", "b_qkv", "w_off", "b_off", "w_out", "b_out")
+
+
+def block_forward(x, p, heads: int, window, dilation=(1, 1, 1), eps: float = 1e-6):
+    """The block on x [B,T,H,W,C] with parameters p (BLOCK_PARAMS: ln_g/ln_b [C],
+    w_qkv [3C, C], b_qkv [3C], w_off [heads*P*3, C], b_off [heads*P*3],
+    w_out [C, C], b_out [C]). Returns a dict of every intermediate: h, q, k, v
+    ([B,T,H,W,heads,d]), offsets, o, lse and the output y [B,T,H,W,C]."""
+    x = _f64(x)
+    B, T, H, W, C = x.shape
+    d = C // heads
+    P = window[0] * window[1] * window[2]
+    x2 = x.reshape(-1, C)
+    h, _, _ = layernorm(x2, p["ln_g"], p["ln_b"], eps)
+    wqkv, bqkv = _f64(p["w_qkv"]), _f64(p["b_qkv"])
+    q2, k2, v2 = (linear(h, wqkv[i * C:(i + 1) * C], bqkv[i * C:(i + 1) * C]) for i in range(3))
+    act = lambda a: a.reshape(B, T, H, W, heads, d)
+    off = linear(q2, p["w_off"], p["b_off"]).reshape(B, T, H, W, heads, P, 3)
+    o, lse = forward(act(q2), act(k2), act(v2), off, window, dilation)
+    y = x2 + linear(o.reshape(-1, C), p["w_out"], p["b_out"])
+    return {"h": h.reshape(B, T, H, W, C), "q": act(q2), "k": act(k2), "v": act(v2), "offsets": off, "o": o,
+            "lse": lse, "y": y.reshape(B, T, H, W, C)}
+
+
+def block_backward(x, p, dy, heads: int, window, dilation=(1, 1, 1), eps: float = 1e-6):
+    """Gradients of block_forward for dL/dy = dy: a dict with dx and the
+    gradient of every parameter (d<name>), plus the attention's inputs'
+    gradients dq, dk, dv, doffsets and do, all float64. The chain rule through
+    the block: the output projection, the attention (its offsets depend on q
+    through the offset projection), the q/k/v projections and the layer
+    normalisation, plus the residual path dx += dy."""
+    x, dy = _f64(x), _f64(dy)
+    B, T, H, W, C = x.shape
+    d = C // heads
+    f = block_forward(x, p, heads, window, dilation, eps)
+    x2, dy2 = x.reshape(-1, C), dy.reshape(-1, C)
+    do2, dw_out, db_out = linear_backward(f["o"].reshape(-1, C), p["w_out"], dy2)
+    dq, dk, dv, doff = backward(f["q"], f["k"], f["v"], f["offsets"], do2.reshape(B, T, H, W, heads, d), window,
+                                dilation)
+    q2 = f["q"].reshape(-1, C)
+    dq_off, dw_off, db_off = linear_backward(q2, p["w_off"], doff.reshape(q2.shape[0], -1))
+    dq2 = dq.reshape(-1, C) + dq_off
+    h2 = f["h"].reshape(-1, C)
+    wqkv = _f64(p["w_qkv"])
+    dh = np.zeros_like(h2)
+    dw_qkv = np.zeros_like(wqkv)
+    db_qkv = np.zeros(3 * C)
+    for i, g in enumerate((dq2, dk.reshape(-1, C), dv.reshape(-1, C))):
+        a, b, c = linear_backward(h2, wqkv[i * C:(i + 1) * C], g)
+        dh += a
+        dw_qkv[i * C:(i + 1) * C] = b
+        db_qkv[i * C:(i + 1) * C] = c
+    dx_ln, dln_g, dln_b = layernorm_backward(x2, p["ln_g"], dh, eps)
+    dx = dy2 + dx_ln
+    return {"dx": dx.reshape(x.shape), "dln_g": dln_g, "dln_b": dln_b, "dw_qkv": dw_qkv, "db_qkv": db_qkv,
+            "dw_off": dw_off, "db_off": db_off, "dw_out": dw_out, "db_out": db_out, "dq": dq, "dk": dk, "dv": dv,
+            "doffsets": doff, "do": do2.reshape(B, T, H, W, heads, d), "dh": dh.reshape(x.shape)}

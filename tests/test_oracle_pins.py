@@ -545,3 +545,151 @@ def test_dwconv_backward_adjoint_and_finite_differences():
     for c in range(2):
         e = np.zeros_like(b); e[c] = eps
         assert abs((L(q, w, b + e) - L(q, w, b - e)) / (2 * eps) - db[c]) < 1e-6
+
+
+# ---------------------------------------------------------------------------
+# The transformer block around the operator (layer normalisation, linear
+# layers, residual; [MegaSlide-DiT, §5.3 Implementation considerations]).
+# ---------------------------------------------------------------------------
+
+def test_layernorm_matches_torch_with_autograd():
+    """Forward and all three gradients against torch's layer_norm in float64
+    (an independent library routine) with autograd."""
+    rng = np.random.default_rng(71)
+    x = rng.standard_normal((37, 48)) * 3.0 + 1.5
+    g = 1.0 + 0.3 * rng.standard_normal(48)
+    b = 0.2 * rng.standard_normal(48)
+    dy = rng.standard_normal((37, 48))
+    eps = 1e-6
+    y, mean, rstd = oracle.layernorm(x, g, b, eps)
+    xt = torch.tensor(x, requires_grad=True)
+    gt = torch.tensor(g, requires_grad=True)
+    bt = torch.tensor(b, requires_grad=True)
+    yt = torch.nn.functional.layer_norm(xt, (48,), gt, bt, eps)
+    yt.backward(torch.tensor(dy))
+    assert np.abs(y - yt.detach().numpy()).max() < 1e-12
+    dx, dg, db = oracle.layernorm_backward(x, g, dy, eps)
+    assert np.abs(dx - xt.grad.numpy()).max() < 1e-11
+    assert np.abs(dg - gt.grad.numpy()).max() < 1e-11
+    assert np.abs(db - bt.grad.numpy()).max() < 1e-11
+    assert np.allclose(mean, x.mean(1)) and np.allclose(rstd, 1.0 / np.sqrt(x.var(1) + eps))
+
+
+def test_layernorm_invariants():
+    """Without affine parameters every row has mean 0 and (population) variance
+    var/(var+eps); the result is invariant under x -> a*x + c for a > 0 (up to
+    eps); gamma and beta act per channel (a channel permutation commutes)."""
+    rng = np.random.default_rng(72)
+    x = rng.standard_normal((20, 64))
+    y, _, _ = oracle.layernorm(x, None, None, 1e-12)
+    assert np.abs(y.mean(1)).max() < 1e-12
+    assert np.abs(y.var(1) - 1.0).max() < 1e-9
+    y2, _, _ = oracle.layernorm(2.5 * x - 7.0, None, None, 1e-12)
+    assert np.abs(y2 - y).max() < 1e-9
+    g, b = rng.standard_normal(64), rng.standard_normal(64)
+    perm = rng.permutation(64)
+    ya, _, _ = oracle.layernorm(x, g, b)
+    yp, _, _ = oracle.layernorm(x[:, perm], g[perm], b[perm])
+    assert np.abs(ya[:, perm] - yp).max() < 1e-12
+
+
+def test_layernorm_backward_finite_differences():
+    rng = np.random.default_rng(73)
+    x = rng.standard_normal((5, 16))
+    g = 1.0 + 0.5 * rng.standard_normal(16)
+    b = rng.standard_normal(16)
+    G = rng.standard_normal((5, 16))
+    loss = lambda xx, gg, bb: float((oracle.layernorm(xx, gg, bb)[0] * G).sum())
+    dx, dg, db = oracle.layernorm_backward(x, g, G)
+    eps = 1e-6
+    for _ in range(12):
+        i, j = rng.integers(5), rng.integers(16)
+        xp, xm = x.copy(), x.copy()
+        xp[i, j] += eps
+        xm[i, j] -= eps
+        fd = (loss(xp, g, b) - loss(xm, g, b)) / (2 * eps)
+        assert abs(fd - dx[i, j]) <= 1e-6 * max(1.0, abs(fd))
+    for arr, grad in ((g, dg), (b, db)):
+        j = rng.integers(16)
+        ap, am = arr.copy(), arr.copy()
+        ap[j] += eps
+        am[j] -= eps
+        args_p = (x, ap, b) if arr is g else (x, g, ap)
+        args_m = (x, am, b) if arr is g else (x, g, am)
+        fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        assert abs(fd - grad[j]) <= 1e-6 * max(1.0, abs(fd))
+
+
+def _block_params(C, heads, P, rng, off_scale=0.2):
+    return {"ln_g": 1.0 + 0.2 * rng.standard_normal(C), "ln_b": 0.1 * rng.standard_normal(C),
+            "w_qkv": rng.standard_normal((3 * C, C)) / np.sqrt(C), "b_qkv": 0.1 * rng.standard_normal(3 * C),
+            "w_off": off_scale * rng.standard_normal((heads * P * 3, C)),
+            "b_off": 0.3 * rng.standard_normal(heads * P * 3),
+            "w_out": rng.standard_normal((C, C)) / np.sqrt(C), "b_out": 0.1 * rng.standard_normal(C)}
+
+
+def test_block_residual_and_projections():
+    """With a zero output projection the block is the identity (the residual
+    path); the block's q/k/v are the linear maps of the normalised input, and
+    its attention output is the attention oracle's on them."""
+    rng = np.random.default_rng(74)
+    heads, d, window = 2, 4, (3, 3, 3)
+    C, P = heads * d, 27
+    x = rng.standard_normal((1, 3, 3, 4, C))
+    p = _block_params(C, heads, P, rng)
+    p0 = dict(p, w_out=np.zeros((C, C)), b_out=np.zeros(C))
+    assert np.array_equal(oracle.block_forward(x, p0, heads, window)["y"], x)
+    f = oracle.block_forward(x, p, heads, window)
+    h = (x - x.mean(-1, keepdims=True)) / np.sqrt(x.var(-1, keepdims=True) + 1e-6) * p["ln_g"] + p["ln_b"]
+    assert np.abs(f["h"] - h).max() < 1e-12
+    q = h @ p["w_qkv"][:C].T + p["b_qkv"][:C]
+    assert np.abs(f["q"].reshape(q.shape) - q).max() < 1e-12
+    o, _ = oracle.forward(f["q"], f["k"], f["v"], f["offsets"], window)
+    assert np.abs(f["o"] - o).max() < 1e-12
+    assert np.abs(f["y"] - (x + o.reshape(x.shape) @ p["w_out"].T + p["b_out"])).max() < 1e-12
+
+
+@pytest.mark.parametrize("off_scale,eps,tol", [(0.0, 1e-4, 1e-7), (0.2, 1e-3, 1e-2)])
+def test_block_backward_finite_differences(off_scale, eps, tol):
+    """The block's gradients (through the output projection, the attention with
+    offsets that depend on q, the q/k/v projections, the layer normalisation
+    and the residual path) against central finite differences of the whole
+    block's forward. With a zero offset projection the loss is smooth and the
+    check is tight; with offsets that follow q, the single-precision rounding
+    of the offsets (part of the operator) makes the loss a staircase at the
+    1e-7 scale and its kinks at integer positions are crossed by some of the
+    many samples a parameter moves, so the step is larger and the bound looser:
+    the offsets' path carries about twice the direct share of dq here, so a
+    dropped or mis-signed term is an O(1) error."""
+    rng = np.random.default_rng(75)
+    heads, d, window = 2, 4, (3, 3, 3)
+    C, P = heads * d, 27
+    x = rng.standard_normal((1, 3, 3, 4, C))
+    p = _block_params(C, heads, P, rng, off_scale=off_scale)
+    G = rng.standard_normal(x.shape)
+    loss = lambda xx, pp: float((oracle.block_forward(xx, pp, heads, window)["y"] * G).sum())
+    g = oracle.block_backward(x, p, G, heads, window)
+
+    def fd(name, idx):
+        if name == "x":
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            return (loss(xp, p) - loss(xm, p)) / (2 * eps)
+        pp, pm = dict(p), dict(p)
+        pp[name] = p[name].copy()
+        pm[name] = p[name].copy()
+        pp[name][idx] += eps
+        pm[name][idx] -= eps
+        return (loss(x, pp) - loss(x, pm)) / (2 * eps)
+
+    # with the tight bound, the offset projection's own parameters are left out:
+    # perturbing them moves the (single-precision) offsets directly
+    names = [n for n in oracle.BLOCK_PARAMS if off_scale > 0 or n not in ("w_off", "b_off")]
+    checks = [("x", "dx")] * 6 + [(n, "d" + n) for n in names for _ in range(2)]
+    for name, gname in checks:
+        arr = x if name == "x" else p[name]
+        idx = tuple(int(rng.integers(s)) for s in arr.shape)
+        ref = fd(name, idx)
+        err = abs(ref - g[gname][idx]) / max(1.0, abs(ref))
+        assert err <= tol, (name, idx, ref, g[gname][idx])
