@@ -69,7 +69,11 @@ def lib():
                                        ctypes.c_void_p, ctypes.c_void_p]
             L.orc_forward.argtypes = [P(_Problem), ctypes.c_long] + [ctypes.c_void_p] * 8
             L.orc_backward.argtypes = [P(_Problem), ctypes.c_long] + [ctypes.c_void_p] * 10
-            for f in (L.orc_geometry, L.orc_forward, L.orc_backward):
+            L.orc_forward_hybrid.argtypes = ([P(_Problem), ctypes.c_long] + [ctypes.c_void_p] * 5 + [ctypes.c_int] +
+                                             [ctypes.c_void_p] * 4)
+            L.orc_backward_hybrid.argtypes = ([P(_Problem), ctypes.c_long] + [ctypes.c_void_p] * 5 + [ctypes.c_int] +
+                                              [ctypes.c_void_p] * 9)
+            for f in (L.orc_geometry, L.orc_forward, L.orc_backward, L.orc_forward_hybrid, L.orc_backward_hybrid):
                 f.restype = ctypes.c_int
             _lib = L
     return _lib
@@ -514,3 +518,83 @@ def block_backward(x, p, dy, heads: int, window, dilation=(1, 1, 1), eps: float 
     return {"dx": dx.reshape(x.shape), "dln_g": dln_g, "dln_b": dln_b, "dw_qkv": dw_qkv, "db_qkv": db_qkv,
             "dw_off": dw_off, "db_off": db_off, "dw_out": dw_out, "db_out": db_out, "dq": dq, "dk": dk, "dv": dv,
             "doffsets": doff, "do": do2.reshape(B, T, H, W, heads, d), "dh": dh.reshape(x.shape)}
+
+
+# ----------------------------------------------------------------------------
+# Hybrid attention: sparse global tokens with local 3D-DSA [MegaSlide-DiT, §11
+# Limitations and Discussion, future work (i)]: each query's P samples and the
+# G global tokens of its (batch item, head) share one softmax (see the C file).
+# ----------------------------------------------------------------------------
+
+def forward_hybrid(q, k, v, off, gk, gv, window, dilation=(1, 1, 1), scale=None, threads=None):
+    """q, k, v [B,T,H,W,heads,d], off [B,T,H,W,heads,P,3], gk, gv [B,G,heads,d].
+    Returns o [B,T,H,W,heads,d] and lse [B,T,H,W,heads], float64."""
+    q, k, v, off, gk, gv = _f64(q), _f64(k), _f64(v), _f32(off), _f64(gk), _f64(gv)
+    B, T, H, W, nh, d = q.shape
+    G = gk.shape[1]
+    P = window[0] * window[1] * window[2]
+    scale = default_scale(d) if scale is None else scale
+    pos = grid_positions(T, H, W)
+    N = T * H * W
+    o = np.zeros_like(q); lse = np.zeros((B, T, H, W, nh))
+
+    def one(bh):
+        b, h = bh
+        pr = _problem((T, H, W), d, window, dilation, scale, (0, 0, 0), (T, H, W))
+        oo = np.zeros((N, d)); ll = np.zeros(N)
+        # every array handed to the C call is held by a name for the call's duration
+        qq = np.ascontiguousarray(q[b, :, :, :, h].reshape(N, d))
+        ff = np.ascontiguousarray(off[b, :, :, :, h].reshape(N, P, 3))
+        kk = np.ascontiguousarray(k[b, :, :, :, h])
+        vv = np.ascontiguousarray(v[b, :, :, :, h])
+        gkk = np.ascontiguousarray(gk[b, :, h])
+        gvv = np.ascontiguousarray(gv[b, :, h])
+        rc = lib().orc_forward_hybrid(ctypes.byref(pr), N, _ptr(pos), _ptr(qq), _ptr(ff), _ptr(kk), _ptr(vv), G,
+                                      _ptr(gkk), _ptr(gvv), _ptr(oo), _ptr(ll))
+        _check(rc, "forward_hybrid")
+        o[b, :, :, :, h] = oo.reshape(T, H, W, d)
+        lse[b, :, :, :, h] = ll.reshape(T, H, W)
+
+    _pool_map(one, [(b, h) for b in range(B) for h in range(nh)], threads)
+    return o, lse
+
+
+def backward_hybrid(q, k, v, off, gk, gv, dout, window, dilation=(1, 1, 1), scale=None, threads=None):
+    """Gradients of forward_hybrid: dq, dk, dv [B,T,H,W,heads,d], doff
+    [B,T,H,W,heads,P,3], dgk, dgv [B,G,heads,d], float64."""
+    q, k, v, off, gk, gv, dout = _f64(q), _f64(k), _f64(v), _f32(off), _f64(gk), _f64(gv), _f64(dout)
+    B, T, H, W, nh, d = q.shape
+    G = gk.shape[1]
+    P = window[0] * window[1] * window[2]
+    scale = default_scale(d) if scale is None else scale
+    pos = grid_positions(T, H, W)
+    N = T * H * W
+    dq = np.zeros_like(q); dk = np.zeros_like(k); dv = np.zeros_like(v); doff = np.zeros(off.shape)
+    dgk = np.zeros_like(gk); dgv = np.zeros_like(gv)
+
+    def one(bh):
+        b, h = bh
+        pr = _problem((T, H, W), d, window, dilation, scale, (0, 0, 0), (T, H, W))
+        dqq = np.zeros((N, d)); dff = np.zeros((N, P, 3))
+        dK = np.zeros((T, H, W, d)); dV = np.zeros((T, H, W, d))
+        dGK = np.zeros((G, d)); dGV = np.zeros((G, d))
+        qq = np.ascontiguousarray(q[b, :, :, :, h].reshape(N, d))
+        ff = np.ascontiguousarray(off[b, :, :, :, h].reshape(N, P, 3))
+        kk = np.ascontiguousarray(k[b, :, :, :, h])
+        vv = np.ascontiguousarray(v[b, :, :, :, h])
+        gkk = np.ascontiguousarray(gk[b, :, h])
+        gvv = np.ascontiguousarray(gv[b, :, h])
+        gg = np.ascontiguousarray(dout[b, :, :, :, h].reshape(N, d))
+        rc = lib().orc_backward_hybrid(ctypes.byref(pr), N, _ptr(pos), _ptr(qq), _ptr(ff), _ptr(kk), _ptr(vv), G,
+                                       _ptr(gkk), _ptr(gvv), _ptr(gg), _ptr(dqq), _ptr(dff), _ptr(dK), _ptr(dV),
+                                       _ptr(dGK), _ptr(dGV))
+        _check(rc, "backward_hybrid")
+        dq[b, :, :, :, h] = dqq.reshape(T, H, W, d)
+        doff[b, :, :, :, h] = dff.reshape(T, H, W, P, 3)
+        dk[b, :, :, :, h] = dK
+        dv[b, :, :, :, h] = dV
+        dgk[b, :, h] = dGK
+        dgv[b, :, h] = dGV
+
+    _pool_map(one, [(b, h) for b in range(B) for h in range(nh)], threads)
+    return dq, dk, dv, doff, dgk, dgv

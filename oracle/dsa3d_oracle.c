@@ -298,3 +298,127 @@ int orc_backward(const orc_problem* pr, long nq, const int32_t* qpos, const doub
     free(kp); free(vp); free(s); free(a); free(da); free(gk); free(gv);
     return rc;
 }
+
+/* Hybrid attention: sparse global tokens combined with local 3D-DSA
+ * [MegaSlide-DiT, §11 Limitations and Discussion, future work (i)]. The pages
+ * only name the idea; the reading here is the plainest one: every query of a
+ * (batch item, head) attends, in ONE softmax, to its P sampled points (steps
+ * 1-3) and to G global tokens whose key and value rows GK[g], GV[g] are the
+ * same for every query of that (batch item, head):
+ *   rows j = 0..P-1: k_p, v_p;  rows j = P..P+G-1: GK[j-P], GV[j-P]
+ *   s_j = scale * <q, row_j>;  a = softmax(s) over all P+G rows;  o = sum_j a_j v_j
+ * Backward over the same rows: da_j = <dO, v_j>, ds_j = a_j (da_j - sum_i a_i da_i),
+ * dq = scale * sum_j ds_j k_j; the local rows scatter into dK, dV and the offsets
+ * as in steps 8-9; the global rows give dGK[g] += scale ds_g q, dGV[g] += a_g dO.
+ * GK, GV [G,d]; dGK, dGV [G,d] accumulated (+=). */
+int orc_forward_hybrid(const orc_problem* pr, long nq, const int32_t* qpos, const double* q,
+                       const float* off, const double* K, const double* V, int G,
+                       const double* GK, const double* GV, double* o, double* lse) {
+    if (orc_check(pr) || G < 0) return ORC_ERR_ARG;
+    const int P = pr->kt * pr->kh * pr->kw, d = pr->d, R = P + G;
+    double* kp = malloc(sizeof(double) * (size_t)R * d);
+    double* vp = malloc(sizeof(double) * (size_t)R * d);
+    double* s = malloc(sizeof(double) * R);
+    double* a = malloc(sizeof(double) * R);
+    int rc = (kp && vp && s && a) ? 0 : ORC_ERR_MEM;
+    for (long i = 0; i < nq && rc == 0; ++i) {
+        rc = sample_rows(pr, qpos + 3 * i, off + i * P * 3, K, V, kp, vp);
+        if (rc) break;
+        for (long e = 0; e < (long)G * d; ++e) {
+            kp[(long)P * d + e] = GK[e];
+            vp[(long)P * d + e] = GV[e];
+        }
+        attend(R, d, pr->scale, q + i * d, kp, s, a, lse + i);
+        for (int e = 0; e < d; ++e) {
+            double acc = 0.0;
+            for (int j = 0; j < R; ++j) acc += a[j] * vp[(long)j * d + e];
+            o[i * d + e] = acc;
+        }
+    }
+    free(kp); free(vp); free(s); free(a);
+    return rc;
+}
+
+int orc_backward_hybrid(const orc_problem* pr, long nq, const int32_t* qpos, const double* q,
+                        const float* off, const double* K, const double* V, int G,
+                        const double* GK, const double* GV, const double* dout,
+                        double* dq, double* doff, double* dK, double* dV, double* dGK, double* dGV) {
+    if (orc_check(pr) || G < 0) return ORC_ERR_ARG;
+    const int P = pr->kt * pr->kh * pr->kw, d = pr->d, R = P + G;
+    double* kp = malloc(sizeof(double) * (size_t)R * d);
+    double* vp = malloc(sizeof(double) * (size_t)R * d);
+    double* s = malloc(sizeof(double) * R);
+    double* a = malloc(sizeof(double) * R);
+    double* da = malloc(sizeof(double) * R);
+    double* gk = malloc(sizeof(double) * d);
+    double* gv = malloc(sizeof(double) * d);
+    int rc = (kp && vp && s && a && da && gk && gv) ? 0 : ORC_ERR_MEM;
+    for (long i = 0; i < nq && rc == 0; ++i) {
+        const int32_t* x = qpos + 3 * i;
+        const double* qi = q + i * d;
+        const double* gi = dout + i * d;
+        const float* oi = off + i * P * 3;
+        rc = sample_rows(pr, x, oi, K, V, kp, vp);
+        if (rc) break;
+        for (long e = 0; e < (long)G * d; ++e) {
+            kp[(long)P * d + e] = GK[e];
+            vp[(long)P * d + e] = GV[e];
+        }
+        double lse;
+        attend(R, d, pr->scale, qi, kp, s, a, &lse);
+        double sum_ada = 0.0;
+        for (int j = 0; j < R; ++j) {
+            double acc = 0.0;
+            for (int e = 0; e < d; ++e) acc += gi[e] * vp[(long)j * d + e];
+            da[j] = acc;
+            sum_ada += a[j] * acc;
+        }
+        for (int e = 0; e < d; ++e) {
+            double acc = 0.0;
+            for (int j = 0; j < R; ++j) acc += a[j] * (da[j] - sum_ada) * kp[(long)j * d + e];
+            dq[i * d + e] = pr->scale * acc;
+        }
+        /* the global rows */
+        for (int g = 0; g < G; ++g) {
+            const double ds = a[P + g] * (da[P + g] - sum_ada);
+            for (int e = 0; e < d; ++e) {
+                dGK[(long)g * d + e] += pr->scale * ds * qi[e];
+                dGV[(long)g * d + e] += a[P + g] * gi[e];
+            }
+        }
+        /* the local rows: dK, dV and the offsets */
+        for (int p = 0; p < P; ++p) {
+            const double ds = a[p] * (da[p] - sum_ada);
+            for (int e = 0; e < d; ++e) {
+                gk[e] = pr->scale * ds * qi[e];
+                gv[e] = a[p] * gi[e];
+            }
+            double* dop = doff + (i * P + p) * 3;
+            dop[0] = dop[1] = dop[2] = 0.0;
+            int32_t base[3];
+            float frac[3];
+            if (!sample_point(pr, x, p, oi + 3L * p, base, frac)) continue;
+            for (int c = 0; c < 8; ++c) {
+                double w, dw[3];
+                long r = corner(pr, base, frac, c, &w, dw);
+                if (r == -1) { rc = ORC_ERR_BOX; break; }
+                if (r < 0) continue;
+                const double* Kc = K + r * d;
+                const double* Vc = V + r * d;
+                double dot = 0.0;
+                for (int e = 0; e < d; ++e) dot += gk[e] * Kc[e] + gv[e] * Vc[e];
+                if (dK && dV)
+                    for (int e = 0; e < d; ++e) {
+                        dK[r * d + e] += w * gk[e];
+                        dV[r * d + e] += w * gv[e];
+                    }
+                dop[0] += dw[0] * dot;
+                dop[1] += dw[1] * dot;
+                dop[2] += dw[2] * dot;
+            }
+            if (rc) break;
+        }
+    }
+    free(kp); free(vp); free(s); free(a); free(da); free(gk); free(gv);
+    return rc;
+}

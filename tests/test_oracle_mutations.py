@@ -34,6 +34,13 @@ MUTANTS = {
     "doff_without_value_term": ("dot += gk[e] * Kc[e] + gv[e] * Vc[e];", "dot += gk[e] * Kc[e];"),
     "dk_missing_corner_weight": ("dK[r * d + e] += w * gk[e];", "dK[r * d + e] += gk[e];"),
     "border_wraps": ("if (t < 0 || t >= pr->T ||", "if (t < -1 || t >= pr->T ||"),
+    # hybrid attention (global tokens in the softmax)
+    "hybrid_dgk_without_scale": ("dGK[(long)g * d + e] += pr->scale * ds * qi[e];",
+                                 "dGK[(long)g * d + e] += ds * qi[e];"),
+    "hybrid_dgv_unweighted": ("dGV[(long)g * d + e] += a[P + g] * gi[e];", "dGV[(long)g * d + e] += gi[e];"),
+    "hybrid_keys_from_values": ("kp[(long)P * d + e] = GK[e];", "kp[(long)P * d + e] = GV[e];"),
+    "hybrid_dq_without_global_rows": ("for (int j = 0; j < R; ++j) acc += a[j] * (da[j] - sum_ada) * kp[(long)j * d + e];",
+                                      "for (int j = 0; j < P; ++j) acc += a[j] * (da[j] - sum_ada) * kp[(long)j * d + e];"),
 }
 
 # a quick selection of the pins (each is a plain function of the loaded oracle)
@@ -45,6 +52,7 @@ PIN_CALLS = [
     ("geometry", pins.test_geometry_is_single_precision_floor_and_fraction),
     ("affine", pins.test_affine_field_is_reproduced_at_the_sample_position),
     ("softmax", pins.test_attention_weights_are_a_distribution_and_uniform_for_zero_keys),
+    ("hybrid_route", lambda: pins.test_hybrid_matches_grid_sample_route_with_global_keys((3, 3, 3), (1, 1, 1), 0.8, 5)),
 ]
 
 

@@ -127,7 +127,9 @@ def test_integer_offsets_are_exact_gathers():
 #    with autograd for every gradient, in float64.
 # ---------------------------------------------------------------------------
 
-def _torch_route(q, k, v, off, window, dilation, scale, dout):
+def _torch_route(q, k, v, off, window, dilation, scale, dout, gk=None, gv=None):
+    """The route with autograd; with gk, gv [B,G,heads,d] the G global rows of
+    each (batch, head) join the softmax (returns their gradients too)."""
     B, T, H, W, nh, d = q.shape
     P = off.shape[-2]
     pts = torch.tensor(_window_points(window, dilation), dtype=torch.int64)            # [P,3]
@@ -159,14 +161,23 @@ def _torch_route(q, k, v, off, window, dilation, scale, dout):
                                          align_corners=True)[..., 0]
     qf = qt.permute(0, 4, 5, 1, 2, 3).reshape(B * nh, d, T * H * W, 1)
     s = scale * (qf * ks).sum(1)                         # [B*nh, N, P]
+    if gk is not None:
+        gkt = torch.tensor(gk, requires_grad=True)
+        gvt = torch.tensor(gv, requires_grad=True)
+        G = gk.shape[1]
+        gkf = gkt.permute(0, 2, 3, 1).reshape(B * nh, d, 1, G)     # [B*nh, d, 1, G]
+        gvf = gvt.permute(0, 2, 3, 1).reshape(B * nh, d, 1, G)
+        s = torch.cat([s, scale * (qf * gkf).sum(1)], -1)          # [B*nh, N, P+G]
+        vs = torch.cat([vs, gvf.expand(B * nh, d, T * H * W, G)], -1)
     a = torch.softmax(s, -1)
     o = (a.unsqueeze(1) * vs).sum(-1)                    # [B*nh, d, N]
     lse = torch.logsumexp(s, -1)
     o = o.reshape(B, nh, d, T, H, W).permute(0, 3, 4, 5, 1, 2)
     lse = lse.reshape(B, nh, T, H, W).permute(0, 2, 3, 4, 1)
     (o * torch.tensor(dout)).sum().backward()
-    return (o.detach().numpy(), lse.detach().numpy(), qt.grad.numpy(), kt.grad.numpy(),
-            vt.grad.numpy(), ot.grad.numpy())
+    out = (o.detach().numpy(), lse.detach().numpy(), qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy(),
+           ot.grad.numpy())
+    return out + ((gkt.grad.numpy(), gvt.grad.numpy()) if gk is not None else ())
 
 
 @pytest.mark.parametrize("window,dilation,sigma", [((3, 3, 3), (1, 1, 1), 0.7), ((3, 5, 5), (1, 1, 1), 2.0),
@@ -693,3 +704,87 @@ def test_block_backward_finite_differences(off_scale, eps, tol):
         ref = fd(name, idx)
         err = abs(ref - g[gname][idx]) / max(1.0, abs(ref))
         assert err <= tol, (name, idx, ref, g[gname][idx])
+
+
+# ---------------------------------------------------------------------------
+# Hybrid attention: G global tokens join each query's softmax ([MegaSlide-DiT,
+# §11 Limitations and Discussion, future work (i)]).
+# ---------------------------------------------------------------------------
+
+def test_hybrid_without_global_tokens_is_the_operator():
+    rng = np.random.default_rng(81)
+    window = (3, 3, 3)
+    q, k, v, off = _inputs(1, 3, 4, 5, 2, 8, window, 1.0, rng)
+    dout = _rand(*q.shape, rng=rng)
+    empty = np.zeros((1, 0, 2, 8))
+    o, lse = oracle.forward(q, k, v, off, window)
+    oh, lh = oracle.forward_hybrid(q, k, v, off, empty, empty, window)
+    assert np.array_equal(o, oh) and np.array_equal(lse, lh)
+    ref = oracle.backward(q, k, v, off, dout, window)
+    got = oracle.backward_hybrid(q, k, v, off, empty, empty, dout, window)
+    for a, b in zip(ref, got[:4]):
+        assert np.array_equal(a, b)
+    assert got[4].shape == (1, 0, 2, 8)
+
+
+@pytest.mark.parametrize("window,dilation,sigma,G", [((3, 3, 3), (1, 1, 1), 0.8, 5), ((3, 5, 5), (1, 1, 1), 2.0, 16),
+                                                     ((1, 3, 3), (1, 2, 2), 1.3, 1)])
+def test_hybrid_matches_grid_sample_route_with_global_keys(window, dilation, sigma, G):
+    """The hybrid forward and every gradient (q, k, v, offsets and the global
+    rows) against torch: grid_sample for the local samples, the global rows
+    appended to each query's logits, one softmax, autograd."""
+    rng = np.random.default_rng(82)
+    q, k, v, off = _inputs(2, 3, 4, 5, 2, 8, window, sigma, rng)
+    gk, gv = _rand(2, G, 2, 8, rng=rng), _rand(2, G, 2, 8, rng=rng)
+    dout = _rand(*q.shape, rng=rng)
+    scale = 1 / math.sqrt(8)
+    o, lse = oracle.forward_hybrid(q, k, v, off, gk, gv, window, dilation)
+    got = oracle.backward_hybrid(q, k, v, off, gk, gv, dout, window, dilation)
+    r = _torch_route(q, k, v, off, window, dilation, scale, dout, gk, gv)
+    for name, mine, ref in zip(["o", "lse", "dq", "dk", "dv", "doff", "dgk", "dgv"], [o, lse] + list(got), r):
+        err = np.abs(mine - ref).max()
+        assert err < 1e-10 * max(1.0, np.abs(ref).max()), (name, err)
+
+
+def test_hybrid_global_tokens_as_grid_tokens_equal_dense_attention():
+    """With a single-point window at zero offset and global tokens that are
+    copies of grid tokens, each query attends to itself plus those tokens:
+    plain dense attention over that list (written here directly)."""
+    rng = np.random.default_rng(83)
+    B, T, H, W, nh, d = 1, 2, 3, 4, 2, 6
+    q, k, v = (_rand(B, T, H, W, nh, d, rng=rng) for _ in range(3))
+    off = np.zeros((B, T, H, W, nh, 1, 3), dtype=np.float32)
+    picks = [(0, 0, 0), (1, 2, 3), (0, 1, 2)]
+    gk = np.stack([k[0, t, h, w] for (t, h, w) in picks])[None]   # [1, G, nh, d]
+    gv = np.stack([v[0, t, h, w] for (t, h, w) in picks])[None]
+    o, lse = oracle.forward_hybrid(q, k, v, off, gk, gv, (1, 1, 1))
+    scale = 1 / math.sqrt(d)
+    for t in range(T):
+        for h in range(H):
+            for w in range(W):
+                for n in range(nh):
+                    keys = [k[0, t, h, w, n]] + [gk[0, g, n] for g in range(len(picks))]
+                    vals = [v[0, t, h, w, n]] + [gv[0, g, n] for g in range(len(picks))]
+                    s = scale * np.array(keys) @ q[0, t, h, w, n]
+                    e = np.exp(s - s.max())
+                    assert np.abs(o[0, t, h, w, n] - (e / e.sum()) @ np.array(vals)).max() < 1e-12
+                    assert abs(lse[0, t, h, w, n] - (s.max() + np.log(e.sum()))) < 1e-12
+
+
+def test_hybrid_backward_finite_differences_of_global_rows():
+    rng = np.random.default_rng(84)
+    window = (3, 3, 3)
+    q, k, v, off = _inputs(1, 2, 3, 4, 1, 4, window, 0.9, rng)
+    gk, gv = _rand(1, 3, 1, 4, rng=rng), _rand(1, 3, 1, 4, rng=rng)
+    G_ = _rand(*q.shape, rng=rng)
+    loss = lambda a, b: float((oracle.forward_hybrid(q, k, v, off, a, b, window)[0] * G_).sum())
+    _, _, _, _, dgk, dgv = oracle.backward_hybrid(q, k, v, off, gk, gv, G_, window)
+    eps = 1e-6
+    for arr, grad, first in ((gk, dgk, True), (gv, dgv, False)):
+        for _ in range(4):
+            idx = tuple(int(rng.integers(s)) for s in arr.shape)
+            ap, am = arr.copy(), arr.copy()
+            ap[idx] += eps
+            am[idx] -= eps
+            fd = (loss(ap, gv) - loss(am, gv)) / (2 * eps) if first else (loss(gk, ap) - loss(gk, am)) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-7 * max(1.0, abs(fd))
