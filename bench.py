@@ -542,6 +542,20 @@ def main():
                                      "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                                      "launch_ms": round(per_kernel[k]["mean_ms"], 3), "flops_per_launch": lin_flops}
 
+    # hybrid attention's global rows (vector units): per (token, head) the forward forms G logits and a
+    # weighted sum of G rows (4*d*G flops), the query kernel G logits, G <dO, GV> products and the dq update
+    # (6*d*G), the rows kernel the same logits and products plus the dGK/dGV updates (8*d*G)
+    roofline_hybrid = None
+    if wl.global_tokens:
+        G = wl.global_tokens
+        roofline_hybrid = {}
+        for k, per in (("hybrid_forward", 4), ("hybrid_bwd_query", 6), ("hybrid_bwd_rows", 8)):
+            if k in per_kernel:
+                tf = per * wl.head_dim * G * wl.tokens * wl.heads / (per_kernel[k]["mean_ms"] / 1e3) / 1e12
+                roofline_hybrid[k] = {"bound": "alu", "achieved": round(tf, 2), "peak": VALU_F32_PEAK_TFLOPS,
+                                      "unit": "TFLOP/s", "frac": round(tf / VALU_F32_PEAK_TFLOPS, 4),
+                                      "launch_ms": round(per_kernel[k]["mean_ms"], 3)}
+
     roofline_conv = None
     if wl.offsets == "conv":
         s_el = 4 if wl.dtype == "f32" else 2
@@ -567,6 +581,7 @@ def main():
            + (" of a depthwise 3x3x3 conv with N(0,0.2) weights" if wl.offsets == "conv" else "")) + ")",
         "config": {"workload": wl.name, "grid": [wl.B, wl.T, wl.H, wl.W], "heads": wl.heads, "head_dim": wl.head_dim,
                    "window": list(wl.window), "P": wl.P, "dilation": list(wl.dilation), "offsets": wl.offsets,
+                   **({"global_tokens": wl.global_tokens} if wl.global_tokens else {}),
                    "chain": ("layernorm+qkv+" if wl.block else "") + {"proj": "proj+", "conv": "dwconv+proj+"}.get(
                        wl.offsets, "") + ("fwd" if not wl.block else "fwd+out_proj+residual")
                        + ("+bwd" if wl.backward else ""),
@@ -577,6 +592,7 @@ def main():
         **({"roofline_proj": roofline_proj} if roofline_proj else {}),
         **({"roofline_conv": roofline_conv} if roofline_conv else {}),
         **({"roofline_block": roofline_block} if roofline_block else {}),
+        **({"roofline_hybrid": roofline_hybrid} if roofline_hybrid else {}),
         "kernels": {k: {"launches": v["launches"], "mean_ms": round(v["mean_ms"], 3)} for k, v in per_kernel.items()},
     }
     if wl.backward and wl.deterministic and args.alt_steps > 0:

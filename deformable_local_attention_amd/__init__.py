@@ -31,7 +31,8 @@ __all__ = [
     "dsa3d_set_launch_log", "LaunchLog", "launch_timer", "KERNELS", "dsa3d_backward_noalloc",
     "NOALLOC_SCRATCH_BYTES", "dsa3d_layernorm_forward", "dsa3d_layernorm_workspace_size", "dsa3d_layernorm_backward",
     "dsa3d_linear_forward", "dsa3d_linear_workspace_size", "dsa3d_linear_backward", "layernorm", "linear",
-    "dtype_code",
+    "dtype_code", "dsa3d_forward_hybrid", "dsa3d_backward_hybrid", "dsa3d_hybrid_workspace_size",
+    "dsa3d_hybrid_workspace_min", "forward_hybrid", "backward_hybrid",
 ]
 
 DSA3D_F32, DSA3D_BF16 = 0, 1
@@ -42,12 +43,14 @@ EXPORTS = ("dsa3d_version", "dsa3d_status_string", "dsa3d_validate", "dsa3d_work
            "dsa3d_offset_proj_backward", "dsa3d_debug_geometry", "dsa3d_dwconv_forward", "dsa3d_dwconv_backward",
            "dsa3d_set_launch_log", "dsa3d_backward_noalloc", "dsa3d_layernorm_forward",
            "dsa3d_layernorm_workspace_size", "dsa3d_layernorm_backward", "dsa3d_linear_forward",
-           "dsa3d_linear_workspace_size", "dsa3d_linear_backward")
+           "dsa3d_linear_workspace_size", "dsa3d_linear_backward", "dsa3d_forward_hybrid", "dsa3d_backward_hybrid",
+           "dsa3d_hybrid_workspace_size", "dsa3d_hybrid_workspace_min")
 # kernel ids of the launch log (dsa3d_kernel)
 KERNELS = {1: "proj_forward", 2: "forward", 3: "bwd_query", 4: "bwd_key", 5: "fill", 6: "proj_bwd_dq",
            7: "proj_bwd_dw", 8: "split_sum", 9: "colsum", 10: "geometry", 11: "bwd_scan", 12: "bwd_count",
            13: "bwd_sort", 14: "transpose", 15: "dwconv", 16: "dwconv_wgrad", 17: "dwconv_dq", 18: "layernorm",
-           19: "layernorm_bwd", 20: "linear_forward", 21: "linear_bwd_dx", 22: "linear_bwd_dw"}
+           19: "layernorm_bwd", 20: "linear_forward", 21: "linear_bwd_dx", 22: "linear_bwd_dw",
+           23: "hybrid_forward", 24: "hybrid_bwd_query", 25: "hybrid_bwd_rows"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -115,6 +118,10 @@ def lib() -> ctypes.CDLL:
                 "dsa3d_linear_forward": ([ctypes.c_int, i64, i64, i64] + [vp] * 6, ctypes.c_int),
                 "dsa3d_linear_workspace_size": ([ctypes.c_int, i64, i64, i64], sz),
                 "dsa3d_linear_backward": ([ctypes.c_int, i64, i64, i64] + [vp] * 8 + [sz, vp], ctypes.c_int),
+                "dsa3d_forward_hybrid": ([dp] + [vp] * 4 + [ctypes.c_int32] + [vp] * 5, ctypes.c_int),
+                "dsa3d_backward_hybrid": ([dp] + [vp] * 7 + [ctypes.c_int32] + [vp] * 9 + [sz, vp], ctypes.c_int),
+                "dsa3d_hybrid_workspace_size": ([dp, ctypes.c_int32, ctypes.c_int], sz),
+                "dsa3d_hybrid_workspace_min": ([dp, ctypes.c_int32, ctypes.c_int], sz),
             }
             for name, (args, res) in sig.items():
                 f = getattr(L, name)
@@ -301,6 +308,69 @@ def dsa3d_dwconv_backward(desc: Desc, q, wt, dy, dq_accum, dwt, dbias, workspace
     ws, nbytes = a.workspace(workspace)
     _check("dsa3d_dwconv_backward",
            lib().dsa3d_dwconv_backward(ctypes.byref(desc), *a.pointers(*args, ws), nbytes, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# hybrid attention: global tokens in each query's softmax
+# ---------------------------------------------------------------------------
+
+def dsa3d_forward_hybrid(desc: Desc, q, k, v, offsets, G: int, gk, gv, out, lse, stream=None):
+    a = _Args("dsa3d_forward_hybrid", desc)
+    grow = (desc.B, G, desc.heads, desc.head_dim)
+    args = (a("q", q, a.act), a("k", k, a.act), a("v", v, a.act), a("offsets", offsets, a.off, optional=True))
+    glob = (a("gk", gk, grow), a("gv", gv, grow))
+    outs = (a("out", out, a.act), a("lse", lse, a.lse, torch.float32))
+    p = a.pointers(*args, *glob, *outs)
+    _check("dsa3d_forward_hybrid", lib().dsa3d_forward_hybrid(ctypes.byref(desc), *p[:4], G, *p[4:],
+                                                              _stream(stream)))
+
+
+def dsa3d_hybrid_workspace_size(desc: Desc, G: int, kind: int) -> int:
+    return lib().dsa3d_hybrid_workspace_size(ctypes.byref(desc), G, kind)
+
+
+def dsa3d_hybrid_workspace_min(desc: Desc, G: int, kind: int) -> int:
+    return lib().dsa3d_hybrid_workspace_min(ctypes.byref(desc), G, kind)
+
+
+def dsa3d_backward_hybrid(desc: Desc, q, k, v, offsets, out, lse, dout, G: int, gk, gv, dq, dk, dv, doffsets, dgk,
+                          dgv, workspace, stream=None):
+    a = _Args("dsa3d_backward_hybrid", desc)
+    grow = (desc.B, G, desc.heads, desc.head_dim)
+    first = (a("q", q, a.act), a("k", k, a.act), a("v", v, a.act), a("offsets", offsets, a.off, optional=True),
+             a("out", out, a.act), a("lse", lse, a.lse, torch.float32), a("dout", dout, a.act))
+    rest = (a("gk", gk, grow), a("gv", gv, grow), a("dq", dq, a.act), a("dk", dk, a.act), a("dv", dv, a.act),
+            a("doffsets", doffsets, a.off, optional=True), a("dgk", dgk, grow), a("dgv", dgv, grow))
+    ws, nbytes = a.workspace(workspace)
+    p = a.pointers(*first, *rest, ws)
+    _check("dsa3d_backward_hybrid", lib().dsa3d_backward_hybrid(ctypes.byref(desc), *p[:7], G, *p[7:], nbytes,
+                                                                _stream(stream)))
+
+
+def forward_hybrid(q, k, v, offsets, gk, gv, window, dilation=(1, 1, 1), scale: float = 0.0, stream=None):
+    """Returns (out, lse) of the joint softmax over the local samples and the
+    G global rows gk, gv [B, G, heads, d]."""
+    desc = desc_like(q, window, dilation, scale)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:5], dtype=torch.float32, device=q.device)
+    dsa3d_forward_hybrid(desc, q, k, v, offsets, gk.shape[1], gk, gv, out, lse, stream)
+    return out, lse
+
+
+def backward_hybrid(q, k, v, offsets, out, lse, dout, gk, gv, window, dilation=(1, 1, 1), scale: float = 0.0,
+                    deterministic: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Returns (dq, dk, dv, doffsets, dgk, dgv)."""
+    desc = desc_like(q, window, dilation, scale, deterministic)
+    G = gk.shape[1]
+    if workspace is None:
+        n = dsa3d_hybrid_workspace_size(desc, G, WS_BACKWARD if offsets is not None else WS_BACKWARD_FIXED)
+        workspace = torch.empty((n + 15) // 16 * 16, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    doff = torch.empty_like(offsets) if offsets is not None else None
+    dgk, dgv = torch.empty_like(gk), torch.empty_like(gv)
+    dsa3d_backward_hybrid(desc, q, k, v, offsets, out, lse, dout, G, gk, gv, dq, dk, dv, doff, dgk, dgv, workspace,
+                          stream)
+    return dq, dk, dv, doff, dgk, dgv
 
 
 # ---------------------------------------------------------------------------

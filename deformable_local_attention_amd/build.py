@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdsa3d.so")
 SOURCES = ["dsa3d_attn.hip", "dsa3d_bwd.hip", "dsa3d_fixed.hip", "dsa3d_proj.hip", "dsa3d_conv.hip",
-           "dsa3d_noalloc.hip", "dsa3d_block.hip", "dsa3d_api.cpp"]
+           "dsa3d_noalloc.hip", "dsa3d_block.hip", "dsa3d_hybrid.hip",
+           "dsa3d_api.cpp"]
 ARCH = os.environ.get("DSA3D_OFFLOAD_ARCH", "gfx950")
 
 

@@ -13,7 +13,8 @@ from typing import Dict, Optional
 import torch
 
 from . import (WS_BACKWARD, WS_BACKWARD_FIXED, WS_DWCONV_BACKWARD, WS_PROJ_BACKWARD, desc_like, dsa3d_backward,
-               dsa3d_dwconv_backward, dsa3d_dwconv_forward, dsa3d_forward, dsa3d_offset_proj_backward,
+               dsa3d_backward_hybrid, dsa3d_dwconv_backward, dsa3d_dwconv_forward, dsa3d_forward,
+               dsa3d_forward_hybrid, dsa3d_hybrid_workspace_size, dsa3d_offset_proj_backward,
                dsa3d_offset_proj_forward, dsa3d_workspace_size)
 from .synth import Workload
 
@@ -45,7 +46,15 @@ class Chain:
             self.dv = torch.empty_like(q)
             self.doff = None if self.fixed else torch.empty_like(self.offsets)
             kind = WS_BACKWARD_FIXED if self.fixed else WS_BACKWARD
-            n = dsa3d_workspace_size(self.desc, kind) if bwd_workspace_bytes is None else bwd_workspace_bytes
+            self.G = wl.global_tokens
+            if self.G:
+                self.dgk, self.dgv = torch.empty_like(inputs["gk"]), torch.empty_like(inputs["gv"])
+            if bwd_workspace_bytes is not None:
+                n = bwd_workspace_bytes
+            elif self.G:
+                n = dsa3d_hybrid_workspace_size(self.desc, self.G, kind)
+            else:
+                n = dsa3d_workspace_size(self.desc, kind)
             self.ws = torch.empty(max(16, (n + 15) // 16 * 16), dtype=torch.uint8, device=dev) if n else None
             if self.proj:
                 self.dw = torch.empty(inputs["proj_w"].shape, dtype=torch.float32, device=dev)
@@ -65,20 +74,31 @@ class Chain:
             dsa3d_dwconv_forward(self.desc, x["q"], x["conv_w"], x["conv_b"], self.pin, stream)
         if self.proj:
             dsa3d_offset_proj_forward(self.desc, self.pin, x["proj_w"], x["proj_b"], self.offsets, stream)
-        dsa3d_forward(self.desc, x["q"], x["k"], x["v"], self.offsets, self.out, self.lse, stream)
-        if self.backward:
+        G = self.wl.global_tokens
+        if G:
+            dsa3d_forward_hybrid(self.desc, x["q"], x["k"], x["v"], self.offsets, G, x["gk"], x["gv"], self.out,
+                                 self.lse, stream)
+        else:
+            dsa3d_forward(self.desc, x["q"], x["k"], x["v"], self.offsets, self.out, self.lse, stream)
+        if not self.backward:
+            return
+        if G:
+            dsa3d_backward_hybrid(self.desc, x["q"], x["k"], x["v"], self.offsets, self.out, self.lse, x["dout"], G,
+                                  x["gk"], x["gv"], self.dq, self.dk, self.dv, self.doff, self.dgk, self.dgv,
+                                  self.ws, stream)
+        else:
             dsa3d_backward(self.desc, x["q"], x["k"], x["v"], self.offsets, self.out, self.lse, x["dout"],
                            self.dq, self.dk, self.dv, self.doff, self.ws, stream)
-            if self.conv:
-                # the projection's input gradient starts from zero (a device clear, no arithmetic)
-                self.dpin.zero_()
-                dsa3d_offset_proj_backward(self.desc, self.pin, x["proj_w"], self.doff, self.dpin, self.dw, self.db,
-                                           self.pws, stream)
-                dsa3d_dwconv_backward(self.desc, x["q"], x["conv_w"], self.dpin, self.dq, self.dcw, self.dcb,
-                                      self.cws, stream)
-            elif self.proj:
-                dsa3d_offset_proj_backward(self.desc, x["q"], x["proj_w"], self.doff, self.dq, self.dw, self.db,
-                                           self.pws, stream)
+        if self.conv:
+            # the projection's input gradient starts from zero (a device clear, no arithmetic)
+            self.dpin.zero_()
+            dsa3d_offset_proj_backward(self.desc, self.pin, x["proj_w"], self.doff, self.dpin, self.dw, self.db,
+                                       self.pws, stream)
+            dsa3d_dwconv_backward(self.desc, x["q"], x["conv_w"], self.dpin, self.dq, self.dcw, self.dcb,
+                                  self.cws, stream)
+        elif self.proj:
+            dsa3d_offset_proj_backward(self.desc, x["q"], x["proj_w"], self.doff, self.dq, self.dw, self.db,
+                                       self.pws, stream)
 
 
 class BlockChain:

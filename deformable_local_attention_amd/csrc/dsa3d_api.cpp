@@ -3,6 +3,7 @@
 // no HIP allocation happens here.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "dsa3d.h"
@@ -182,6 +183,51 @@ int dsa3d_dwconv_backward(const dsa3d_desc* d, const void* q, const void* wt, co
     if (workspace == nullptr || workspace_bytes < need) return DSA3D_ERR_WORKSPACE;
     if (!aligned16(workspace)) return DSA3D_ERR_MISALIGNED;
     return hip_status(dsa3d::launch_dwconv_backward(*d, q, wt, dy, dq_accum, dwt, dbias, workspace,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
+static bool hybrid_g_ok(int32_t G) { return G >= 1 && G <= 1024; }
+
+size_t dsa3d_hybrid_workspace_size(const dsa3d_desc* d, int32_t G, int kind) {
+    if (dsa3d_validate(d) != DSA3D_OK || !hybrid_g_ok(G)) return 0;
+    if (kind != DSA3D_WS_BACKWARD && kind != DSA3D_WS_BACKWARD_FIXED) return 0;
+    return std::max(dsa3d_workspace_size(d, kind), dsa3d::hybrid_global_workspace_bytes(*d, G));
+}
+
+size_t dsa3d_hybrid_workspace_min(const dsa3d_desc* d, int32_t G, int kind) {
+    if (dsa3d_validate(d) != DSA3D_OK || !hybrid_g_ok(G)) return 0;
+    if (kind != DSA3D_WS_BACKWARD && kind != DSA3D_WS_BACKWARD_FIXED) return 0;
+    const size_t local = dsa3d_workspace_min(d, kind);
+    if (local == 0) return 0;
+    return std::max(local, dsa3d::hybrid_global_workspace_bytes(*d, G));
+}
+
+int dsa3d_forward_hybrid(const dsa3d_desc* d, const void* q, const void* k, const void* v, const void* offsets,
+                         int32_t G, const void* gk, const void* gv, void* out, float* lse, void* stream) {
+    int rc = dsa3d_validate(d);
+    if (rc != DSA3D_OK) return rc;
+    if (!hybrid_g_ok(G)) return DSA3D_ERR_INVALID_ARG;
+    if ((rc = check_ptrs({gk, gv})) != DSA3D_OK) return rc;
+    if ((rc = dsa3d_forward(d, q, k, v, offsets, out, lse, stream)) != DSA3D_OK) return rc;
+    return hip_status(dsa3d::launch_hybrid_forward(*d, G, q, gk, gv, out, lse, static_cast<hipStream_t>(stream)));
+}
+
+int dsa3d_backward_hybrid(const dsa3d_desc* d, const void* q, const void* k, const void* v, const void* offsets,
+                          const void* out, const float* lse, const void* dout, int32_t G, const void* gk,
+                          const void* gv, void* dq, void* dk, void* dv, void* doffsets, void* dgk, void* dgv,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = dsa3d_validate(d);
+    if (rc != DSA3D_OK) return rc;
+    if (!hybrid_g_ok(G)) return DSA3D_ERR_INVALID_ARG;
+    if ((rc = check_ptrs({gk, gv, dgk, dgv})) != DSA3D_OK) return rc;
+    if (workspace == nullptr || workspace_bytes < dsa3d::hybrid_global_workspace_bytes(*d, G))
+        return DSA3D_ERR_WORKSPACE;
+    // the operator's backward (it checks its own arguments and workspace), then the global rows on the
+    // same workspace
+    if ((rc = dsa3d_backward(d, q, k, v, offsets, out, lse, dout, dq, dk, dv, doffsets, workspace, workspace_bytes,
+                             stream)) != DSA3D_OK)
+        return rc;
+    return hip_status(dsa3d::launch_hybrid_backward(*d, G, q, gk, gv, out, lse, dout, dq, dgk, dgv, workspace,
                                                     static_cast<hipStream_t>(stream)));
 }
 

@@ -136,6 +136,12 @@ hipError_t launch_fixed_forward(const dsa3d_desc& d, const void* q, const void* 
 hipError_t launch_fixed_backward(const dsa3d_desc& d, const void* q, const void* k, const void* v, const void* o,
                                  const float* lse, const void* dout, void* dq, void* dk, void* dv, void* ws,
                                  hipStream_t s);
+size_t hybrid_global_workspace_bytes(const dsa3d_desc& d, int32_t G);
+hipError_t launch_hybrid_forward(const dsa3d_desc& d, int32_t G, const void* q, const void* gk, const void* gv,
+                                 void* out, float* lse, hipStream_t s);
+hipError_t launch_hybrid_backward(const dsa3d_desc& d, int32_t G, const void* q, const void* gk, const void* gv,
+                                  const void* out, const float* lse, const void* dout, void* dq, void* dgk, void* dgv,
+                                  void* ws, hipStream_t s);
 size_t layernorm_bwd_workspace_bytes(int64_t M, int64_t N);
 hipError_t launch_layernorm_forward(int dtype, int64_t M, int64_t N, float eps, const void* x, const void* gamma,
                                     const void* beta, void* y, float* stats, hipStream_t s);

@@ -48,6 +48,7 @@ class Workload:
                                           # q/k/v projections, offset projection, attention, output
                                           # projection with the residual add); offsets must be "proj"
     ln_eps: float = 1e-6                  # the block's layer-normalisation epsilon
+    global_tokens: int = 0                # hybrid attention: G global key/value rows per (batch, head)
     description: str = ""
 
     @property
@@ -106,6 +107,10 @@ WORKLOADS: Dict[str, Workload] = {
                  offset_sigma=2.0, backward=True, deterministic=True,
                  description="bf16 fwd + bwd, 256x68x120 tokens, 24x128 heads, 3x5x5 window, "
                              "offsets N(0,2), deterministic K/V gradients"),
+        Workload("1080p-bf16-p75-hybrid64", 1, 256, 68, 120, 24, 128, (3, 5, 5), (1, 1, 1), "bf16", "direct",
+                 offset_sigma=2.0, backward=True, deterministic=True, global_tokens=64,
+                 description="bf16 hybrid attention fwd + bwd: the 3x5x5 deformable samples plus 64 global tokens per "
+                             "head in one softmax, 256x68x120 tokens, 24x128 heads, deterministic"),
         Workload("720p-bf16-block", 1, 64, 45, 80, 16, 64, (3, 3, 3), (1, 2, 2), "bf16", "proj",
                  backward=True, block=True,
                  description="bf16 transformer block fwd + bwd: layer norm, q/k/v projections, offset projection, "
@@ -188,6 +193,11 @@ def make_inputs(wl: Workload, device="cpu", seed: int = 0,
         out["offsets"] = _randn(shp[:5] + (wl.P, 3), wl.offset_sigma, dt, gen, dev)
     if with_grad if with_grad is not None else wl.backward:
         out["dout"] = _randn(shp, 1.0, dt, gen, dev)
+    if wl.global_tokens:
+        # hybrid attention's global key and value rows, N(0,1), [B, G, heads, d]
+        gs = (wl.B, wl.global_tokens, wl.heads, wl.head_dim)
+        out["gk"] = _randn(gs, 1.0, dt, gen, dev)
+        out["gv"] = _randn(gs, 1.0, dt, gen, dev)
     return out
 
 
@@ -214,5 +224,6 @@ def describe(wl: Workload) -> str:
     return (f"{wl.name}: B={wl.B} T={wl.T} H={wl.H} W={wl.W} heads={wl.heads} d={wl.head_dim} "
             f"window={wl.window} dil={wl.dilation} P={wl.P} {wl.dtype} offsets={wl.offsets}"
             + (f" sigma={wl.offset_sigma}" if wl.offsets == "direct" else "")
-            + (" +bwd" if wl.backward else "") + (" det" if wl.deterministic else "") + (" block" if wl.block else ""))
+            + (" +bwd" if wl.backward else "") + (" det" if wl.deterministic else "") + (" block" if wl.block else "")
+            + (f" G={wl.global_tokens}" if wl.global_tokens else ""))
 

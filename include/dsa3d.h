@@ -217,6 +217,42 @@ int dsa3d_dwconv_backward(const dsa3d_desc* desc, const void* q, const void* wt,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Hybrid attention: G global tokens combined with the local 3D-DSA samples
+ * [MegaSlide-DiT, §11 Limitations and Discussion, future work (i): sparse
+ * global tokens with local 3D-DSA]. The pages only name the idea; the reading
+ * here: every query of a (batch item, head) attends in ONE softmax to its P
+ * samples and to the G global rows gk[b, g, head, :], gv[b, g, head, :]
+ * (shared by all queries of that batch item and head; the caller decides what
+ * they are: learned tokens, pooled summaries, a strided subset of the grid):
+ *   s_g = scale * <q, gk_g>;  a = softmax over the P + G logits;
+ *   o = sum_p a_p v_p + sum_g a_g gv_g;  lse = log of the joint denominator.
+ * gk, gv, dgk, dgv: [B, G, heads, head_dim] in the run dtype; 1 <= G <= 1024.
+ * offsets == NULL: the fixed window as for dsa3d_forward/dsa3d_backward.
+ * ------------------------------------------------------------------------- */
+
+/* Forward: writes out and lse of the joint softmax (lse float32). */
+int dsa3d_forward_hybrid(const dsa3d_desc* desc, const void* q, const void* k, const void* v, const void* offsets,
+                         int32_t G, const void* gk, const void* gv, void* out, float* lse, void* stream);
+
+/* Workspace bytes of dsa3d_backward_hybrid: the backward's own (the recommended
+ * size, for `kind` DSA3D_WS_BACKWARD or DSA3D_WS_BACKWARD_FIXED) or the global
+ * rows' partial sums, whichever is larger; the _min variant uses the
+ * backward's one-head minimum. 0 for an invalid descriptor or G. */
+size_t dsa3d_hybrid_workspace_size(const dsa3d_desc* desc, int32_t G, int kind);
+size_t dsa3d_hybrid_workspace_min(const dsa3d_desc* desc, int32_t G, int kind);
+
+/* Backward of dsa3d_forward_hybrid for dout: dq, dk, dv, doffsets as for
+ * dsa3d_backward (of the joint softmax), plus dgk = scale * sum over the
+ * queries of ds_g q and dgv = sum over the queries of a_g dout (each summed in
+ * float32 in a fixed order and rounded once). `out` and `lse` are the hybrid
+ * forward's. Deterministic mode as for dsa3d_backward; dq, dgk and dgv are
+ * reproducible in both modes. */
+int dsa3d_backward_hybrid(const dsa3d_desc* desc, const void* q, const void* k, const void* v, const void* offsets,
+                          const void* out, const float* lse, const void* dout, int32_t G, const void* gk,
+                          const void* gv, void* dq, void* dk, void* dv, void* doffsets, void* dgk, void* dgv,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * The transformer block around the operator. The pages wrap their attention in
  * layer normalisation and residual connections as usual, and its queries, keys
  * and values come from (and its output goes through) dense projections
@@ -307,7 +343,10 @@ typedef enum {
     DSA3D_K_LAYERNORM_BWD = 19, /* layer normalisation backward: dx and partial dgamma/dbeta */
     DSA3D_K_LINEAR_FORWARD = 20,/* linear layer y = x.w^T + bias (+ residual) */
     DSA3D_K_LINEAR_BWD_DX = 21, /* linear layer backward: dx (+)= dy.w */
-    DSA3D_K_LINEAR_BWD_DW = 22  /* linear layer backward: split dw = dy^T.x */
+    DSA3D_K_LINEAR_BWD_DW = 22, /* linear layer backward: split dw = dy^T.x */
+    DSA3D_K_HYBRID_FORWARD = 23,   /* hybrid attention: global rows merged into the local softmax */
+    DSA3D_K_HYBRID_BWD_QUERY = 24, /* hybrid backward: the global rows' share of dq */
+    DSA3D_K_HYBRID_BWD_ROWS = 25   /* hybrid backward: partial dGK/dGV per slab of queries */
 } dsa3d_kernel;
 
 typedef struct dsa3d_launch_log {

@@ -598,3 +598,59 @@ def backward_hybrid(q, k, v, off, gk, gv, dout, window, dilation=(1, 1, 1), scal
 
     _pool_map(one, [(b, h) for b in range(B) for h in range(nh)], threads)
     return dq, dk, dv, doff, dgk, dgv
+
+
+def forward_hybrid_queries(grid, window, dilation, scale, qpos, q, off, box_origin, K, V, GK, GV, threads=1):
+    """forward_queries with the G global rows GK, GV [G, d] of the head joining
+    the softmax. Returns o [n,d], lse [n]."""
+    qpos = np.ascontiguousarray(qpos, dtype=np.int32)
+    q, K, V, off, GK, GV = _f64(q), _f64(K), _f64(V), _f32(off), _f64(GK), _f64(GV)
+    n, d = q.shape
+    G = GK.shape[0]
+    pr = _problem(grid, d, window, dilation, scale, box_origin, K.shape[:3])
+    o = np.zeros((n, d)); lse = np.zeros(n)
+
+    def run(r):
+        i0, i1 = r
+        if i1 <= i0:
+            return 0
+        return lib().orc_forward_hybrid(ctypes.byref(pr), i1 - i0, _ptr(qpos[i0:i1]), _ptr(q[i0:i1]),
+                                        _ptr(off[i0:i1]), _ptr(K), _ptr(V), G, _ptr(GK), _ptr(GV), _ptr(o[i0:i1]),
+                                        _ptr(lse[i0:i1]))
+
+    for rc in _pool_map(run, _runs(n, threads), threads):
+        _check(rc, "forward_hybrid")
+    return o, lse
+
+
+def backward_hybrid_queries(grid, window, dilation, scale, qpos, q, off, box_origin, K, V, GK, GV, dout,
+                            want_kv=False, threads=1):
+    """Gradients of listed queries with the global rows: dq [n,d], doff
+    [n,P,3], their contributions dGK, dGV [G,d] to the global rows' gradients
+    (with threads > 1, the runs' sums added in run order) and, with want_kv
+    (one run), dK, dV over the box; else those two are None."""
+    qpos = np.ascontiguousarray(qpos, dtype=np.int32)
+    q, K, V, off, GK, GV, dout = _f64(q), _f64(K), _f64(V), _f32(off), _f64(GK), _f64(GV), _f64(dout)
+    n, d = q.shape
+    G = GK.shape[0]
+    P = window[0] * window[1] * window[2]
+    pr = _problem(grid, d, window, dilation, scale, box_origin, K.shape[:3])
+    dq = np.zeros((n, d)); doff = np.zeros((n, P, 3))
+    dK = np.zeros(K.shape) if want_kv else None
+    dV = np.zeros(V.shape) if want_kv else None
+    runs = _runs(n, 1 if want_kv else threads)
+    dgk = [np.zeros((G, d)) for _ in runs]
+    dgv = [np.zeros((G, d)) for _ in runs]
+
+    def run(i):
+        i0, i1 = runs[i]
+        if i1 <= i0:
+            return 0
+        return lib().orc_backward_hybrid(ctypes.byref(pr), i1 - i0, _ptr(qpos[i0:i1]), _ptr(q[i0:i1]),
+                                         _ptr(off[i0:i1]), _ptr(K), _ptr(V), G, _ptr(GK), _ptr(GV),
+                                         _ptr(dout[i0:i1]), _ptr(dq[i0:i1]), _ptr(doff[i0:i1]), _ptr(dK), _ptr(dV),
+                                         _ptr(dgk[i]), _ptr(dgv[i]))
+
+    for rc in _pool_map(run, list(range(len(runs))), len(runs)):
+        _check(rc, "backward_hybrid")
+    return dq, doff, sum(dgk), sum(dgv), dK, dV

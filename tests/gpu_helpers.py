@@ -191,8 +191,15 @@ class HeadOracle:
     offsets: a [B,T,H,W,heads,P,3] device tensor, or None for the fixed window
     (every offset zero)."""
 
-    def __init__(self, wl, x: Dict[str, torch.Tensor], b: int, e: int, offsets=None, dout=None, threads=None):
+    def __init__(self, wl, x: Dict[str, torch.Tensor], b: int, e: int, offsets=None, dout=None, threads=None,
+                 global_rows=None):
+        """global_rows: (gk, gv) device tensors [B, G, heads, d] of hybrid
+        attention (their rows join each query's softmax), or None."""
         self.wl, self.b, self.e = wl, b, e
+        self.GK = self.GV = None
+        if global_rows is not None:
+            self.GK = global_rows[0][b, :, e].to(torch.float32).cpu().numpy().astype(np.float64)
+            self.GV = global_rows[1][b, :, e].to(torch.float32).cpu().numpy().astype(np.float64)
         self.grid = (wl.T, wl.H, wl.W)
         self.scale = oracle.default_scale(wl.head_dim)
         self.threads = threads or min(16, os.cpu_count() or 1)
@@ -212,12 +219,31 @@ class HeadOracle:
 
     def forward(self, pos):
         wl = self.wl
+        if self.GK is not None:
+            return oracle.forward_hybrid_queries(self.grid, wl.window, wl.dilation, self.scale, pos,
+                                                 self._rows(self.q, pos), self.offsets_at(pos), (0, 0, 0), self.K,
+                                                 self.V, self.GK, self.GV, threads=self.threads)
         return oracle.forward_queries(self.grid, wl.window, wl.dilation, self.scale, pos, self._rows(self.q, pos),
                                       self.offsets_at(pos), (0, 0, 0), self.K, self.V, threads=self.threads)
+
+    def global_grads(self):
+        """dGK, dGV [G,d] of the hybrid attention: every query of the head."""
+        wl = self.wl
+        pos = oracle.grid_positions(*self.grid)
+        _, _, dgk, dgv, _, _ = oracle.backward_hybrid_queries(
+            self.grid, wl.window, wl.dilation, self.scale, pos, self.q.reshape(-1, wl.head_dim),
+            self.offsets_at(pos), (0, 0, 0), self.K, self.V, self.GK, self.GV, self.g.reshape(-1, wl.head_dim),
+            threads=self.threads)
+        return dgk, dgv
 
     def backward_queries(self, pos):
         """dq [n,d] and doffsets [n,P,3] of the listed queries."""
         wl = self.wl
+        if self.GK is not None:
+            dq, doff, _, _, _, _ = oracle.backward_hybrid_queries(
+                self.grid, wl.window, wl.dilation, self.scale, pos, self._rows(self.q, pos), self.offsets_at(pos),
+                (0, 0, 0), self.K, self.V, self.GK, self.GV, self._rows(self.g, pos), threads=self.threads)
+            return dq, doff
         dq, doff, _, _ = oracle.backward_queries(self.grid, wl.window, wl.dilation, self.scale, pos,
                                                  self._rows(self.q, pos), self.offsets_at(pos), (0, 0, 0), self.K,
                                                  self.V, self._rows(self.g, pos), want_kv=False,
@@ -263,9 +289,14 @@ class HeadOracle:
         if len(qpos) == 0:
             z = np.zeros((len(keys), wl.head_dim))
             return z, z.copy()
-        _, _, dK, dV = oracle.backward_queries(self.grid, wl.window, wl.dilation, self.scale, qpos,
-                                               self._rows(self.q, qpos), self.offsets_at(qpos), (0, 0, 0), self.K,
-                                               self.V, self._rows(self.g, qpos))
+        if self.GK is not None:
+            _, _, _, _, dK, dV = oracle.backward_hybrid_queries(
+                self.grid, wl.window, wl.dilation, self.scale, qpos, self._rows(self.q, qpos), self.offsets_at(qpos),
+                (0, 0, 0), self.K, self.V, self.GK, self.GV, self._rows(self.g, qpos), want_kv=True)
+        else:
+            _, _, dK, dV = oracle.backward_queries(self.grid, wl.window, wl.dilation, self.scale, qpos,
+                                                   self._rows(self.q, qpos), self.offsets_at(qpos), (0, 0, 0),
+                                                   self.K, self.V, self._rows(self.g, qpos))
         return self._rows(dK, keys), self._rows(dV, keys)
 
 

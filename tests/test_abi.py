@@ -23,7 +23,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     declared = _declared_functions()
-    assert len(declared) == 20, declared
+    assert len(declared) == 24, declared
     out = subprocess.run(["nm", "-D", "--defined-only", dsa.library_path()], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT (dsa3d_\w+)", out))

@@ -478,7 +478,7 @@ def _log_errors(test: str, rows):
 
 def _full_size_parity(test, wl, xd, offsets, out, lse, dq=None, dk=None, dv=None, doff=None, dout=None,
                       q_heads=None, k_heads=None, n_random=4096, n_random_k_heads=512, n_interior_keys=12, seed=0,
-                      b=0):
+                      b=0, global_rows=None, dgk=None, dgv=None):
     """Oracle parity of a full-size run on sampled outputs.
 
     Queries: every token on the six faces of the grid plus n_random random
@@ -488,7 +488,9 @@ def _full_size_parity(test, wl, xd, offsets, out, lse, dq=None, dk=None, dv=None
     interior keys and 4 random face keys of every head of k_heads (default:
     every third head and the last one, so that every backward pass over a
     range of heads is covered). Each tensor is compared per head and over all
-    the heads together."""
+    the heads together. Hybrid attention: global_rows = (gk, gv) join each
+    query's softmax, and dgk/dgv of the q_heads are compared with the oracle's
+    sums over every query of the head."""
     rng = np.random.default_rng(seed)
     T, H, W = wl.T, wl.H, wl.W
     heads = wl.heads
@@ -508,7 +510,7 @@ def _full_size_parity(test, wl, xd, offsets, out, lse, dq=None, dk=None, dv=None
 
     for e in sorted(set(q_heads) | set(k_heads if bwd else [])):
         t0 = time.time()
-        ho = HeadOracle(wl, xd, b, e, offsets, dout)
+        ho = HeadOracle(wl, xd, b, e, offsets, dout, global_rows=global_rows)
         if e in q_heads:
             pos = np.unique(np.concatenate([face_tokens(T, H, W), random_tokens(T, H, W, n_random, rng)]), axis=0)
         else:
@@ -531,6 +533,10 @@ def _full_size_parity(test, wl, xd, offsets, out, lse, dq=None, dk=None, dv=None
                 compare("dk", e, rows_at(dk, b, e, keys), kk)
                 compare("dv", e, rows_at(dv, b, e, keys), vv)
                 nk = len(keys)
+            if dgk is not None and e in q_heads:
+                gk_ref, gv_ref = ho.global_grads()
+                compare("dgk", e, to_np(dgk[b, :, e]), gk_ref)
+                compare("dgv", e, to_np(dgv[b, :, e]), gv_ref)
         say(f"[full] head {e}: {len(pos)} queries, {nk} keys in {time.time() - t0:.1f} s")
         del ho
     for name, (g, r) in acc.items():
