@@ -81,8 +81,10 @@ constexpr int kBufferWord3 = 0x00020000;  // gfx9 buffer resource: untyped 32-bi
 
 template <typename T>
 __device__ __forceinline__ void neighbour_rsrc(const T* x, const ConvGrid& g, int64_t row, RowRsrc& rs) {
-    const int32_t h = (int32_t)(row % g.H);
-    const int32_t t = (int32_t)((row / g.H) % g.T);
+    // rows number fewer than 2^31 (B*T*H*W < 2^31): 32-bit division
+    const uint32_t r32 = (uint32_t)row;
+    const int32_t h = (int32_t)(r32 % (uint32_t)g.H);
+    const int32_t t = (int32_t)((r32 / (uint32_t)g.H) % (uint32_t)g.T);
     const int32_t nrec = (int32_t)((int64_t)g.W * g.C * (int64_t)sizeof(T));
 #pragma unroll
     for (int dt = -1; dt <= 1; ++dt)
@@ -185,6 +187,122 @@ __global__ void __launch_bounds__(256) dsa3d_dwconv_kernel(const T* x, const T* 
                                w0, w1, wa, bb, orow);
     }
 }
+
+namespace {
+
+// bf16 rows, two channels per lane, on v_dot2_f32_bf16: each lane owns the
+// channel pair (c, c+1), loaded as one 32-bit word per input row and column.
+// The nine rows of a column are paired ((0,1), (2,3), (4,5), (6,7), (8,zero))
+// into words that hold one channel of two rows, so one dot2 multiplies two taps
+// of a channel by their (bf16, exact) weights and adds both products into the
+// float32 sum: 15 dot2 per output element instead of 27 multiply-adds, and no
+// widening of the inputs. A column's pairs are formed once (byte permutes)
+// and serve the three outputs along w that read it. Rows come through buffer
+// resources (a row outside the grid has no records and a column outside a
+// row lies past them: the hardware's range check supplies the zero padding).
+// MIRROR: the kernel mirrored through its centre (the input gradient);
+// ACCUM: added to the output (one rounding), without bias.
+struct ColPairs {
+    uint32_t p[5][2];  // [row pair][channel of the lane's pair]
+};
+
+__device__ __forceinline__ void pair_column(const uint32_t x[9], ColPairs& cp) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        cp.p[j][0] = __builtin_amdgcn_perm(x[2 * j + 1], x[2 * j], 0x05040100u);  // channel c of rows 2j, 2j+1
+        cp.p[j][1] = __builtin_amdgcn_perm(x[2 * j + 1], x[2 * j], 0x07060302u);  // channel c+1
+    }
+    cp.p[4][0] = x[8] & 0xffffu;
+    cp.p[4][1] = x[8] >> 16;
+}
+
+template <bool MIRROR, bool ACCUM>
+__global__ void __launch_bounds__(256) dsa3d_dwconv_pair_kernel(const bf16_t* x, const bf16_t* wt, const bf16_t* bias,
+                                                                bf16_t* out, ConvGrid g, int32_t run, int64_t ngroups) {
+    const uint32_t nrows = (uint32_t)g.B * (uint32_t)g.T * (uint32_t)g.H;  // < 2^31
+    const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int64_t row = lb % nrows;
+    const uint32_t cg = (lb / nrows) % (uint32_t)ngroups;
+    const int32_t ri = (int32_t)(lb / nrows / (uint32_t)ngroups);
+    const int64_t c = (int64_t)cg * 512 + 2 * (int64_t)threadIdx.x;  // the lane's channel pair (c, c+1)
+    if (c >= g.C) return;  // C is even: a pair is whole or absent
+    const int32_t w0 = ri * run;
+    const int32_t w1 = min(g.W, w0 + run);
+    // weight words: [column k][row pair j][channel], each (row 2j, row 2j+1) as bf16 (lo, hi)
+    uint32_t wp[3][5][2];
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+        const bf16_t* wc = wt + (c + ch) * 27;
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+#pragma unroll
+            for (int j = 0; j < 5; ++j) {
+                const int r0 = 2 * j, r1 = 2 * j + 1;
+                const int t0 = MIRROR ? 26 - (r0 * 3 + k) : r0 * 3 + k;
+                const int t1 = MIRROR ? 26 - (r1 * 3 + k) : r1 * 3 + k;
+                const uint32_t lo = wc[t0];
+                const uint32_t hi = r1 < 9 ? (uint32_t)wc[t1] : 0u;
+                wp[k][j][ch] = lo | (hi << 16);
+            }
+    }
+    float bb[2] = {0.0f, 0.0f};
+    if (!ACCUM && bias) {
+        bb[0] = load_scalar<bf16_t>(bias + c);
+        bb[1] = load_scalar<bf16_t>(bias + c + 1);
+    }
+    RowRsrc rs;
+    neighbour_rsrc(x, g, row, rs);
+    const int64_t C2 = g.C * 2;  // bytes per token
+    auto load_column = [&](int32_t w, uint32_t v[9]) {
+        const uint32_t voff = (uint32_t)((int64_t)w * C2 + c * 2);  // w = -1 wraps past the records
+#pragma unroll
+        for (int r = 0; r < 9; ++r) v[r] = __builtin_amdgcn_raw_buffer_load_b32(rs.r[r], voff, 0, 0);
+    };
+    ColPairs ca, cb, cc;
+    uint32_t raw[9];
+    load_column(w0 - 1, raw);
+    pair_column(raw, ca);
+    load_column(w0, raw);
+    pair_column(raw, cb);
+    load_column(w0 + 1, raw);  // a column past the row reads zeros
+    bf16_t* orow = out + row * g.W * g.C + c;
+    // One output: columns (l, m, r) = (w-1, w, w+1); column w+1 arrived during
+    // the previous output and is paired now, column w+2 is requested now. The
+    // loop is unrolled by three so that the three column buffers rotate by
+    // name instead of being copied.
+    auto step = [&](int32_t w, const ColPairs& l, const ColPairs& m, ColPairs& r) {
+        pair_column(raw, r);
+        load_column(w + 2, raw);
+        float acc[2];
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch) {
+            float s = bb[ch];
+#pragma unroll
+            for (int j = 0; j < 5; ++j) {
+                s = dot2_bf16(l.p[j][ch], wp[0][j][ch], s);
+                s = dot2_bf16(m.p[j][ch], wp[1][j][ch], s);
+                s = dot2_bf16(r.p[j][ch], wp[2][j][ch], s);
+            }
+            acc[ch] = s;
+        }
+        uint32_t* o = reinterpret_cast<uint32_t*>(orow + (int64_t)w * g.C);
+        if (ACCUM) {
+            const uint32_t old = *o;
+            acc[0] = bf16_lo(old) + acc[0];
+            acc[1] = bf16_hi(old) + acc[1];
+        }
+        *o = pack_bf16x2(acc[0], acc[1]);
+    };
+    for (int32_t w = w0; w < w1; w += 3) {
+        step(w, ca, cb, cc);
+        if (w + 1 >= w1) break;
+        step(w + 1, cb, cc, ca);
+        if (w + 2 >= w1) break;
+        step(w + 2, cc, ca, cb);
+    }
+}
+
+}  // namespace
 
 namespace {
 
@@ -296,6 +414,15 @@ hipError_t conv_launch(const dsa3d_desc& d, const void* x, const void* w, const 
     const int64_t ngroups = (g.C + 255) / 256;
     const int64_t nblocks = rows * ngroups * nrun;
     LaunchScope ls(kernel_id, s);
+    if constexpr (sizeof(T) == 2) {
+        if (conv_rows_buffered(g, sizeof(T))) {
+            const int64_t ngroups2 = (g.C + 511) / 512;
+            hipLaunchKernelGGL((dsa3d_dwconv_pair_kernel<MIRROR, ACCUM>), dim3((unsigned)(rows * ngroups2 * nrun)),
+                               dim3(256), 0, s, reinterpret_cast<const bf16_t*>(x), reinterpret_cast<const bf16_t*>(w),
+                               reinterpret_cast<const bf16_t*>(bias), reinterpret_cast<bf16_t*>(out), g, run, ngroups2);
+            return hipGetLastError();
+        }
+    }
     bool buffered = false;
     if constexpr (!ACCUM) buffered = conv_rows_buffered(g, sizeof(T));
     if constexpr (!ACCUM) {

@@ -15,16 +15,16 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN stays a quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+// Round to nearest even, by gfx950's packed conversion (v_cvt_pk_bf16_f32);
+// checked bit for bit against the integer rounding x + 0x7fff + lsb on ties,
+// denormals, infinities and overflow (NaN stays NaN; its payload may differ).
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
-}
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return pack_bf16x2(f, 0.0f) & 0xffffu; }
 
 // v_dot2_f32_bf16: c + a.lo*b.lo + a.hi*b.hi (products of bf16 are exact in f32).
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
