@@ -129,7 +129,12 @@ int dsa3d_offset_proj_forward(const dsa3d_desc* desc, const void* q, const void*
 int dsa3d_forward(const dsa3d_desc* desc, const void* q, const void* k, const void* v,
                   const void* offsets, void* out, float* lse, void* stream);
 
-/* Backward for a loss L given dout = dL/dout. Writes dq (the attention path's
+/* Backward for a loss L given dout = dL/dout: the gradients the pages' own
+ * implementation takes by autograd through grid_sample, softmax and the
+ * weighted sum [MegaSlide-DiT, §5.3 Implementation considerations], i.e. of
+ * the definition above with the derivative of the trilinear weights taken
+ * inside the sample's cell (from the right at an exact integer position).
+ * Writes dq (the attention path's
  * share), dk, dv and doffsets (dL/doffsets); every element of the four
  * outputs is overwritten. `out` and `lse` are the forward's outputs for the
  * same inputs. No atomic operation touches a gradient: each query's dq and
