@@ -542,16 +542,37 @@ def main():
                                      "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                                      "launch_ms": round(per_kernel[k]["mean_ms"], 3), "flops_per_launch": lin_flops}
 
-    # hybrid attention's global rows (vector units): per (token, head) the forward forms G logits and a
-    # weighted sum of G rows (4*d*G flops), the query kernel G logits, G <dO, GV> products and the dq update
-    # (6*d*G), the rows kernel the same logits and products plus the dGK/dGV updates (8*d*G)
+    # hybrid attention's global rows. bf16 rows of 32-128 channels run on the matrix cores, where the kernels
+    # are HBM-bound: algorithmic bytes per (token, head) are, forward, q read, the local o read and the merged
+    # o written, lse read and written (3*d*s + 8); query kernel, q, dO and o read, dq read and written, lse read
+    # and <dO, o> written (5*d*s + 8); rows kernel, q and dO read, lse and <dO, o> read (2*d*s + 8) (the G
+    # global rows themselves are negligible). Beside it, the bf16 products issued: forward S and the split-weight
+    # O product (6*d*G flops per (token, head)), query kernel S, dP and the split dq product (8*d*G), rows kernel
+    # S, dP and the split dGK, dGV products (12*d*G), against the bf16 matrix-core peak. Other rows run on the
+    # vector units: 4*d*G, 6*d*G and 8*d*G flops against the vector ALU peak.
     roofline_hybrid = None
     if wl.global_tokens:
         G = wl.global_tokens
         roofline_hybrid = {}
-        for k, per in (("hybrid_forward", 4), ("hybrid_bwd_query", 6), ("hybrid_bwd_rows", 8)):
-            if k in per_kernel:
-                tf = per * wl.head_dim * G * wl.tokens * wl.heads / (per_kernel[k]["mean_ms"] / 1e3) / 1e12
+        on_mfma = wl.dtype == "bf16" and wl.head_dim in (32, 64, 128)
+        s_el = 4 if wl.dtype == "f32" else 2
+        for k, per, nbytes, issued in (("hybrid_forward", 4, 3, 6), ("hybrid_bwd_query", 6, 5, 8),
+                                       ("hybrid_bwd_rows", 8, 2, 12)):
+            if k not in per_kernel:
+                continue
+            sec = per_kernel[k]["mean_ms"] / 1e3
+            units = wl.tokens * wl.heads
+            if on_mfma:
+                per_unit = nbytes * wl.head_dim * s_el + 8
+                gbs = per_unit * units / sec / 1e9
+                tf = issued * wl.head_dim * G * units / sec / 1e12
+                roofline_hybrid[k] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": round(gbs / HBM_PEAK_GBS, 4), "launch_ms": round(per_kernel[k]["mean_ms"], 3),
+                                      "bytes_per_unit": per_unit,
+                                      "mfma_issued": {"achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                                                      "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}}
+            else:
+                tf = per * wl.head_dim * G * units / sec / 1e12
                 roofline_hybrid[k] = {"bound": "alu", "achieved": round(tf, 2), "peak": VALU_F32_PEAK_TFLOPS,
                                       "unit": "TFLOP/s", "frac": round(tf / VALU_F32_PEAK_TFLOPS, 4),
                                       "launch_ms": round(per_kernel[k]["mean_ms"], 3)}

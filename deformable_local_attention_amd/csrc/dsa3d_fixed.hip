@@ -23,6 +23,7 @@
 // products there.
 #include "dsa3d_attn_common.h"
 #include "dsa3d_internal.h"
+#include "dsa3d_mfma.h"
 
 #include <type_traits>
 
@@ -187,23 +188,10 @@ __global__ void __launch_bounds__(256) dsa3d_fixed_fwd_kernel(FixedArgs a) {
 // which each lane reads its eight (key, channel) elements. Keys outside the
 // grid are zero rows (logit 0, value 0), as in the gathering kernels; keys past
 // the segment lie outside every band.
-typedef __attribute__((ext_vector_type(8))) __bf16 mf_bf16x8;
-typedef __attribute__((ext_vector_type(2))) __bf16 mf_bf16x2;
-typedef __attribute__((ext_vector_type(4))) float mf_f32x4;
-typedef __attribute__((ext_vector_type(4))) uint32_t mf_u32x4;
-
 constexpr int kMfmaTokens = 16;  // queries per wave
 constexpr int kMfmaMaxKw = 17;   // 15 + k_w keys fit two 16-key tiles
 constexpr int kMfmaPairMaxD = 128;  // rows of up to this many channels go two to a wave
 constexpr int kMfmaKeyPairMaxD = 64;  // the same for the backward per key (more accumulators)
-// The running maximum is raised only when a logit exceeds it by more than
-// this, so most segments skip the rescale; weights stay below e^8.
-constexpr float kMfmaLazyMax = 8.0f;
-
-__device__ __forceinline__ uint32_t mf_pack(float lo, float hi) {  // two RNE bf16 in one word
-    const mf_bf16x2 v = {(__bf16)lo, (__bf16)hi};
-    return __builtin_bit_cast(uint32_t, v);
-}
 
 // One window segment's operands: the two 16-key tiles of keys for the first
 // product (key 16*T + l%16, channels 32j + 8*(l/16) .. +7) and this lane's

@@ -76,6 +76,13 @@ CASES = {
     "f32-d256-G40": dict(T=2, H=3, W=4, heads=1, d=256, G=40),
     "f32-d8-p1-G3": dict(T=3, H=4, W=5, heads=2, d=8, window=(1, 1, 1), sigma=0.5, G=3),
     "bf16-fixed377-G8": dict(T=3, H=9, W=20, heads=2, d=128, window=(3, 7, 7), dtype="bf16", G=8, offsets="none"),
+    # bf16 rows of 32/64/128 channels take the matrix-core kernels: ragged key
+    # slices and staging rounds, several query blocks per head, several slabs
+    "bf16-d32-b2-h3-G17": dict(B=2, T=3, H=5, W=7, heads=3, d=32, sigma=1.5, dtype="bf16", G=17),
+    "bf16-d128-G1": dict(T=3, H=4, W=6, heads=2, d=128, dtype="bf16", G=1),
+    "bf16-d64-G100-slabs": dict(T=4, H=12, W=20, heads=2, d=64, sigma=1.0, dtype="bf16", G=100),
+    "bf16-d128-G70-blocks": dict(T=5, H=12, W=11, heads=1, d=128, window=(3, 5, 5), sigma=2.0, dtype="bf16",
+                                 G=70),
 }
 
 
