@@ -491,48 +491,12 @@ __global__ void __launch_bounds__(256, 1) dsa3d_xgemm_kernel(GemmArgs g) {
 // bf16 products whose operands are both K-contiguous (the projection forward,
 // and dq with W transposed beforehand): the same 256x256 tile and 4 waves of
 // 128x128, but the operand tiles travel from memory straight into LDS
-// (global_load_lds_dwordx4: each lane's 16 bytes land at M0 + 16*lane) through
-// a ring of four 32-deep stages, so three slices are in flight while one is
-// multiplied and no register holds staged data. Each wave waits for its own
-// copies with an exact vmcnt, then one barrier per slice publishes the stage
-// and frees the oldest one for the next copy.
-//
-// LDS rows are 64 B (32 bf16 of K); chunk c of row r sits at c ^ ((r>>1)&3).
-// One copy instruction fills 1 KiB = rows 16q..16q+15, lane l taking row
-// 16q + l/4, stored chunk l%4 (so it reads the logical chunk that maps there).
-//
-// The products are formed transposed (D = B.A^T per 32x32 tile): a lane then
-// holds 4 consecutive output columns of one row, which the epilogue writes to
-// LDS as 8-byte pieces and streams out as whole 16-byte row chunks.
+// (global_load_lds_dwordx4: each lane's 16 bytes land at M0 + 16*lane), so no
+// register holds staged data. The products are formed transposed (D = B.A^T
+// per 32x32 tile): a lane then holds 4 consecutive output columns of one row,
+// which the epilogue writes to LDS as 8-byte pieces and streams out as whole
+// 16-byte row chunks.
 // ---------------------------------------------------------------------------
-constexpr int YK = 32, Y_STAGES = 4;
-constexpr int Y_ROW = YK * 2;                 // 64 B
-constexpr int Y_TILE = 256 * Y_ROW;           // 16 KiB per operand
-constexpr int Y_STAGE = 2 * Y_TILE;           // A then B
-constexpr int Y_LDS = Y_STAGES * Y_STAGE;     // 128 KiB
-
-__device__ __forceinline__ uint32_t yswz(uint32_t r) { return (r >> 1) & 3u; }
-
-// This wave's four copy instructions of one operand tile: lane offsets (bytes,
-// from the tile's first row at k = 0) and the logical K chunk each lane reads.
-struct YOperand {
-    const char* base;  // src + r0*ld, in bytes
-    uint32_t off[4];
-    uint32_t kc;       // first k (elements) of this lane's chunk within a slice
-    __device__ __forceinline__ void init(const bf16_t* src, int64_t ld, int64_t rows, int64_t r0, int wave,
-                                         int lane) {
-        base = reinterpret_cast<const char*>(src + r0 * ld);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t r = 16u * (4u * wave + q) + (uint32_t)(lane >> 2);
-            const int64_t rr = std::min<int64_t>(r0 + r, rows - 1) - r0;
-            off[q] = (uint32_t)(rr * ld * 2);
-        }
-        // the row of instruction q differs by 16 rows, so its swizzle term is the same for all q
-        kc = (((uint32_t)(lane & 3)) ^ yswz((uint32_t)(lane >> 2))) * 8u;
-    }
-};
-
 // M0 carries the LDS address of the copy; it is saved and restored around it
 // (one wait state between setting M0 and the copy).
 __device__ __forceinline__ void y_copy(const char* gbase, uint32_t voff, uint32_t lds_addr) {
@@ -548,65 +512,16 @@ __device__ __forceinline__ void y_copy(const char* gbase, uint32_t voff, uint32_
         : "memory");
 }
 
-// Issue this wave's copies of slice [k0, k0+32) of both operands into a stage.
-// On the last, partial slice a lane whose chunk starts at or past kend reads
-// the last in-bounds chunk instead; y_zero_tail clears it once it has landed.
-__device__ __forceinline__ void y_issue(const YOperand& a, const YOperand& b, int64_t k0, int64_t kend,
-                                        uint32_t stage_addr, int wave) {
-    const bool full = k0 + YK <= kend;
-    const int64_t gk = k0 + a.kc;
-    const uint32_t back = (full || gk < kend) ? 0u : (uint32_t)((gk - (kend - 8)) * 2);
-    const char* ga = a.base + k0 * 2;
-    const char* gb = b.base + k0 * 2;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) y_copy(ga, a.off[q] + a.kc * 2 - back, stage_addr + (4 * wave + q) * 1024);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) y_copy(gb, b.off[q] + b.kc * 2 - back, stage_addr + Y_TILE + (4 * wave + q) * 1024);
-}
-
-__device__ __forceinline__ void y_zero_tail(char* stage, const YOperand& a, int64_t k0, int64_t kend, int wave,
-                                            int lane) {
-    if (k0 + a.kc < kend) return;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        *reinterpret_cast<uint4*>(stage + (4 * wave + q) * 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4*>(stage + Y_TILE + (4 * wave + q) * 1024 + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
-    }
-}
-
 template <int N>
 __device__ __forceinline__ void y_wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Wait until at most `slices` slices of this wave's copies (8 each) are in flight.
-__device__ __forceinline__ void y_wait_slices(int64_t slices) {
-    static_assert(Y_STAGES <= 6, "vmcnt holds at most 63 outstanding copies");
-    switch (slices) {
-        case 0: y_wait_vm<0>(); break;
-        case 1: y_wait_vm<8>(); break;
-        case 2: y_wait_vm<16>(); break;
-        case 3: y_wait_vm<24>(); break;
-        case 4: y_wait_vm<32>(); break;
-        default: y_wait_vm<40>(); break;
-    }
-}
-
 __device__ __forceinline__ void y_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Operand fragments of one k16 step (s = 0, 1) of a stage: lane l holds row
-// l%32 of each 32-row tile and 8 consecutive k (chunk 2s + l/32).
+// Operand fragments of one k16 step: lane l holds row l%32 of each 32-row
+// tile and 8 consecutive k.
 struct YFrag { bf16x8_t a[4], b[4]; };
-
-__device__ __forceinline__ void y_read(const char* stage, uint32_t a_off, uint32_t b_off, uint32_t sw, uint32_t kh,
-                                       uint32_t s, YFrag& f) {
-    const uint32_t c = ((2u * s + kh) ^ sw) * 16u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f.a[i] = *reinterpret_cast<const bf16x8_t*>(stage + a_off + i * 32 * Y_ROW + c);
-        f.b[i] = *reinterpret_cast<const bf16x8_t*>(stage + Y_TILE + b_off + i * 32 * Y_ROW + c);
-    }
-}
 
 // acc[i][j] = B_j . A_i^T (the transposed 32x32 product), for MFMA number
 // 4i + j of the step.
@@ -673,9 +588,83 @@ __device__ __forceinline__ void y_epilogue(const GemmArgs& g, f32x16_t acc[4][4]
     }
 }
 
+// ---------------------------------------------------------------------------
+// The main loop of the DMA-fed kernel takes 64-deep slices through two stages
+// of 64 KiB (A then B, 256 rows of 128 B each). A lane's 16-byte copies then
+// come eight to a row, so each row's share of a slice is one 128-byte request
+// (with 32-deep slices it was two 64-byte ones), and the four waves meet at a
+// barrier once per 64 MFMAs of 32x32x16. The copies of slice t+2 go into the
+// stage slice t releases at the barrier in the middle of its last k16 step:
+// four of a wave's sixteen right after that barrier, the other twelve spread
+// over the first two steps of slice t+1, so that they neither arrive in one
+// burst (the in-order wave then waits for the texture unit to take them, with
+// its MFMAs behind them) nor too late to land before slice t+1 ends.
+//
+// LDS rows are 128 B; chunk c of row r sits at c ^ ((r/2) mod 8), so the 16
+// rows of a 16-lane group of a fragment read (two rows per 64-bank line) fall
+// on all 64 banks once. Copy instruction q of a wave fills rows 64w + 8q ..
+// +7, lane l taking row 64w + 8q + l/8 and stored chunk l%8.
+// ---------------------------------------------------------------------------
+constexpr int ZK = 64;
+constexpr int Z_ROW = ZK * 2;              // 128 B
+constexpr int Z_TILE = 256 * Z_ROW;        // 32 KiB per operand
+constexpr int Z_STAGE = 2 * Z_TILE;        // A then B
+constexpr int Z_LDS = 2 * Z_STAGE;         // 128 KiB
+
+__device__ __forceinline__ uint32_t zswz(uint32_t r) { return (r >> 1) & 7u; }
+
+struct ZOperand {
+    const char* base;  // src + r0*ld, in bytes
+    uint32_t off[8];   // byte offset of this lane's row in copy instruction q
+    uint32_t kc[2];    // first k (elements) of this lane's chunk: even and odd q
+    __device__ __forceinline__ void init(const bf16_t* src, int64_t ld, int64_t rows, int64_t r0, int wave,
+                                         int lane) {
+        base = reinterpret_cast<const char*>(src + r0 * ld);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint32_t r = 64u * (uint32_t)wave + 8u * q + (uint32_t)(lane >> 3);
+            const int64_t rr = std::min<int64_t>(r0 + r, rows - 1) - r0;
+            off[q] = (uint32_t)(rr * ld * 2);
+        }
+        // row 64w + 8q + l/8 has swizzle term ((8q + l/8) / 2) mod 8, which depends on q only by its parity
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+            kc[p] = (((uint32_t)(lane & 7)) ^ zswz(8u * p + (uint32_t)(lane >> 3))) * 8u;
+    }
+    // copy instruction q of slice [k0, k0 + 64) into the operand's tile at tile_addr (LDS); on the last,
+    // partial slice a lane whose chunk starts at or past kend reads the last in-bounds chunk instead, and
+    // z_zero_tail clears it once it has landed
+    __device__ __forceinline__ void copy(int q, int64_t k0, int64_t kend, uint32_t tile_addr, int wave) const {
+        const uint32_t c = kc[q & 1];
+        const int64_t gk = k0 + c;
+        const uint32_t back = (k0 + ZK <= kend || gk < kend) ? 0u : (uint32_t)((gk - (kend - 8)) * 2);
+        y_copy(base + k0 * 2, off[q] + c * 2 - back, tile_addr + (8u * (uint32_t)wave + q) * 1024u);
+    }
+};
+
+__device__ __forceinline__ void z_zero_tail(char* stage, const ZOperand& a, int64_t k0, int64_t kend, int wave,
+                                            int lane) {
+    if (k0 + ZK <= kend) return;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        if (k0 + a.kc[q & 1] < kend) continue;
+        const int o = (8 * wave + q) * 1024 + lane * 16;
+        *reinterpret_cast<uint4*>(stage + o) = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(stage + Z_TILE + o) = make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+// Operand fragments of k16 step s (0..3) of a stage: lane l holds row l%32 of
+// each 32-row tile and 8 consecutive k (chunk 2s + l/32).
+__device__ __forceinline__ void z_read_piece(const char* stage, uint32_t a_off, uint32_t b_off, uint32_t c, int i,
+                                             YFrag& f) {
+    if (i < 4) f.a[i] = *reinterpret_cast<const bf16x8_t*>(stage + a_off + i * 32 * Z_ROW + c);
+    else f.b[i - 4] = *reinterpret_cast<const bf16x8_t*>(stage + Z_TILE + b_off + (i - 4) * 32 * Z_ROW + c);
+}
+
 template <int MODE>
 __global__ void __launch_bounds__(256, 1) dsa3d_ntgemm_kernel(GemmArgs g) {
-    __shared__ __attribute__((aligned(1024))) char lds[Y_LDS];
+    __shared__ __attribute__((aligned(1024))) char lds[Z_LDS];
     const int lane = threadIdx.x % 64;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     const int wm = wave / 2, wn = wave % 2;
@@ -683,7 +672,7 @@ __global__ void __launch_bounds__(256, 1) dsa3d_ntgemm_kernel(GemmArgs g) {
     const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
     const int64_t m0 = (int64_t)(lb / ntn) * XM, n0 = (int64_t)(lb % ntn) * XN;
     const int64_t K = g.K;
-    YOperand opa, opb;
+    ZOperand opa, opb;
     opa.init(reinterpret_cast<const bf16_t*>(g.A), g.lda, g.M, m0, wave, lane);
     opb.init(reinterpret_cast<const bf16_t*>(g.B), g.ldb, g.N, n0, wave, lane);
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
@@ -697,71 +686,102 @@ __global__ void __launch_bounds__(256, 1) dsa3d_ntgemm_kernel(GemmArgs g) {
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     const uint32_t r = (uint32_t)(lane & 31), kh = (uint32_t)(lane >> 5);
-    const uint32_t a_off = ((uint32_t)wm * 128u + r) * Y_ROW;
-    const uint32_t b_off = ((uint32_t)wn * 128u + r) * Y_ROW;
-    const uint32_t sw = yswz(r);
+    const uint32_t a_off = ((uint32_t)wm * 128u + r) * Z_ROW;
+    const uint32_t b_off = ((uint32_t)wn * 128u + r) * Z_ROW;
+    const uint32_t sw = zswz(r);
 
-    // Slices 0..S-1 fill the ring. Iteration t multiplies slice t in two k16
-    // steps; between them every wave waits for its copies of slice t+1 and
-    // meets the others at the barrier, after which stage t (read completely
-    // into registers by then) takes slice t+S and the first fragments of
-    // slice t+1 are read. The copies and reads of the second step sit between
-    // its MFMAs, so the matrix pipe keeps running while they issue.
-    const int64_t nk = (K + YK - 1) / YK;
-#pragma unroll
-    for (int t = 0; t < Y_STAGES; ++t)
-        if (t < nk) y_issue(opa, opb, (int64_t)t * YK, K, lds0 + t * Y_STAGE, wave);
-    YFrag f0, f1;
+    // Slices 0 and 1 fill the two stages; iteration t multiplies slice t in
+    // four k16 steps, the next step's fragments read during the current one's
+    // MFMAs. In the last step each wave waits for its copies of slice t+1 and
+    // meets the others at the barrier, after which slice t's stage takes the
+    // first copies of slice t+2 and the first fragments of slice t+1 are read,
+    // both between that step's remaining MFMAs.
+    const int64_t nk = (K + ZK - 1) / ZK;
+    YFrag f, fn;
     if (nk > 0) {
-        const int64_t after = std::min<int64_t>(nk - 1, Y_STAGES - 1);  // slices issued after slice 0
-        y_wait_slices(after);
-        if (YK > K) y_zero_tail(lds, opa, 0, K, wave, lane);
-        y_barrier();
-        y_read(lds, a_off, b_off, sw, kh, 0, f0);
-    }
-    for (int64_t t = 0; t < nk; ++t) {
-        const char* stage = lds + (t % Y_STAGES) * Y_STAGE;
-        y_read(stage, a_off, b_off, sw, kh, 1, f1);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) y_mma(f0, q / 4, q % 4, acc);
+        for (int q = 0; q < 8; ++q) {
+            opa.copy(q, 0, K, lds0, wave);
+            opb.copy(q, 0, K, lds0 + Z_TILE, wave);
+        }
+        if (nk > 1) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                opa.copy(q, ZK, K, lds0 + Z_STAGE, wave);
+                opb.copy(q, ZK, K, lds0 + Z_STAGE + Z_TILE, wave);
+            }
+            y_wait_vm<16>();  // slice 0 has landed (slice 1's 16 copies may still be in flight)
+        } else {
+            y_wait_vm<0>();
+        }
+        z_zero_tail(lds, opa, 0, K, wave, lane);
+        y_barrier();
+        const uint32_t c0 = ((0u + kh) ^ sw) * 16u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) z_read_piece(lds, a_off, b_off, c0, i, f);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // copy ci (0..15) of a slice: A and B in turn, instruction ci/2 of each
+    auto copy_ci = [&](int ci, int64_t k0, uint32_t st) {
+        if (ci & 1) opb.copy(ci >> 1, k0, K, st + Z_TILE, wave);
+        else opa.copy(ci >> 1, k0, K, st, wave);
+    };
+    for (int64_t t = 0; t < nk; ++t) {
+        const char* stage = lds + (t & 1) * Z_STAGE;
+        // copies 4..15 of slice t+1 (its first four went out after the last
+        // barrier; slice 1 came whole with slice 0) spread over the first two
+        // steps, one after every third MFMA: a burst of copies fills the
+        // texture unit's queues, and the wave, which issues in order, would
+        // stall behind them with its MFMAs
+        const bool spread = t >= 1 && t + 1 < nk;
+        const int64_t k1 = (t + 1) * ZK;
+        const uint32_t st1 = lds0 + (uint32_t)(((t + 1) & 1) * Z_STAGE);
+#pragma unroll
+        for (uint32_t s = 0; s < 3; ++s) {
+            const uint32_t c = ((2u * (s + 1) + kh) ^ sw) * 16u;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) z_read_piece(stage, a_off, b_off, c, i, fn);
+            // keep the reads ahead of this step's products: left to itself the
+            // compiler sinks each read to just before its first use and waits
+            // for it there, once every four MFMAs
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                y_mma(f, q / 4, q % 4, acc);
+                if (s < 2 && q % 3 == 0) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (spread) copy_ci(4 + (int)s * 6 + q / 3, k1, st1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            f = fn;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) y_mma(f, q / 4, q % 4, acc);
         __builtin_amdgcn_sched_barrier(0);
         const bool more = t + 1 < nk;
         if (more) {
-            // copies issued after slice t+1's: min(nk-2-t, S-2) slices of 8
-            const int64_t after = std::min<int64_t>(nk - 2 - t, Y_STAGES - 2);
-            y_wait_slices(after);
-            char* next = lds + ((t + 1) % Y_STAGES) * Y_STAGE;
-            if ((t + 2) * YK > K) y_zero_tail(next, opa, (t + 1) * YK, K, wave, lane);
+            y_wait_vm<0>();  // this wave's copies of slice t+1
+            z_zero_tail(lds + ((t + 1) & 1) * Z_STAGE, opa, (t + 1) * ZK, K, wave, lane);
         }
         y_barrier();
         __builtin_amdgcn_sched_barrier(0);
         {
-            const bool refill = more && t + Y_STAGES < nk;
-            const int64_t k0 = (t + Y_STAGES) * YK;
-            const uint32_t st = lds0 + (t % Y_STAGES) * Y_STAGE;
-            const char* ga = opa.base + k0 * 2;
-            const char* gb = opb.base + k0 * 2;
-            const int64_t gk = k0 + opa.kc;
-            const uint32_t back = (k0 + YK <= K || gk < K) ? 0u : (uint32_t)((gk - (K - 8)) * 2);
-            const char* next = lds + ((t + 1) % Y_STAGES) * Y_STAGE;
+            const bool refill = t + 2 < nk;
+            const int64_t k2 = (t + 2) * ZK;
+            const uint32_t st = lds0 + (uint32_t)((t & 1) * Z_STAGE);
+            const char* next = lds + ((t + 1) & 1) * Z_STAGE;
             const uint32_t c0 = ((0u + kh) ^ sw) * 16u;
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                y_mma(f1, q / 4, q % 4, acc);
+            for (int q = 8; q < 16; ++q) {
+                y_mma(f, q / 4, q % 4, acc);
                 __builtin_amdgcn_sched_barrier(0);
-                if (q < 8) {
-                    if (refill) {
-                        const int qq = q & 3;
-                        if (q < 4) y_copy(ga, opa.off[qq] + opa.kc * 2 - back, st + (4 * wave + qq) * 1024);
-                        else y_copy(gb, opb.off[qq] + opb.kc * 2 - back, st + Y_TILE + (4 * wave + qq) * 1024);
-                    }
-                } else {
-                    const int i = q - 8;
-                    if (i < 4) f0.a[i] = *reinterpret_cast<const bf16x8_t*>(next + a_off + i * 32 * Y_ROW + c0);
-                    else f0.b[i - 4] = *reinterpret_cast<const bf16x8_t*>(next + Y_TILE + b_off + (i - 4) * 32 * Y_ROW + c0);
-                }
+                if (refill && (q & 1) == 0) copy_ci((q - 8) / 2, k2, st);  // copies 0..3 of slice t+2
+                if (more) z_read_piece(next, a_off, b_off, c0, q - 8, fn);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            f = fn;
         }
     }
     y_barrier();  // every wave is done with the stages before they hold the output tile

@@ -96,10 +96,12 @@ def test_layernorm_rejects_unsupported_widths():
 # linear layers
 # ---------------------------------------------------------------------------
 
-# (M, N, K): the 256x256 DMA-fed kernel (K, N multiples of 8), ragged tiles,
-# shapes only the 128x128 kernel takes (N odd), tiny ones
+# (M, N, K): the 256x256 DMA-fed kernel (K, N multiples of 8; 64-deep K
+# slices, the last one ragged at K = 72 and 200), ragged tiles, shapes only
+# the 128x128 kernel takes (N odd), tiny ones
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("M,N,K", [(2048, 1024, 1024), (1000, 264, 72), (333, 77, 40), (5, 8, 16)])
+@pytest.mark.parametrize("M,N,K", [(2048, 1024, 1024), (1000, 264, 72), (1536, 512, 200), (333, 77, 40),
+                                   (5, 8, 16)])
 @pytest.mark.parametrize("with_res", [False, True])
 def test_linear_forward_backward(dtype, M, N, K, with_res):
     say(f"[linear] {dtype} M={M} N={N} K={K} residual={with_res}")
