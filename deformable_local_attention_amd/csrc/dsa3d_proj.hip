@@ -7,8 +7,8 @@
 //
 // Three kernels, by operand layout and dtype:
 //  - dsa3d_ntgemm_kernel (bf16, both operands K-contiguous: the forward, and dq
-//    once W is transposed into the workspace): 256x256 tiles, operands copied
-//    from memory straight into a 4-stage LDS ring;
+//    once W is transposed into the workspace): 256x256 tiles, eight waves,
+//    operands copied from memory straight into two 64-deep LDS stages;
 //  - dsa3d_xgemm_kernel (bf16, any layout, used for dW): 256x256 tiles, two
 //    register-staged LDS stages, M/N-contiguous operands transposed in
 //    registers;
@@ -512,6 +512,29 @@ __device__ __forceinline__ void y_copy(const char* gbase, uint32_t voff, uint32_
         : "memory");
 }
 
+// Four copies into consecutive 1 KiB blocks of LDS with one M0 value: the
+// instruction offset adds to both the global and the LDS address, so copy q
+// takes offset q*1024 and a global base lowered by as much. (Writing M0 holds
+// the wave until the texture unit has taken the copies issued before, so one
+// M0 value serves four copies.)
+__device__ __forceinline__ void y_copy4(const char* gbase, uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3,
+                                        uint32_t lds_addr) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %6\n\t"
+        "global_load_lds_dwordx4 %3, %7 offset:1024\n\t"
+        "global_load_lds_dwordx4 %4, %8 offset:2048\n\t"
+        "global_load_lds_dwordx4 %5, %9 offset:3072\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_addr), "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(gbase), "s"(gbase - 1024), "s"(gbase - 2048),
+          "s"(gbase - 3072)
+        : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void y_wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -519,28 +542,22 @@ __device__ __forceinline__ void y_wait_vm() {
 
 __device__ __forceinline__ void y_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Operand fragments of one k16 step: lane l holds row l%32 of each 32-row
-// tile and 8 consecutive k.
-struct YFrag { bf16x8_t a[4], b[4]; };
-
-// acc[i][j] = B_j . A_i^T (the transposed 32x32 product), for MFMA number
-// 4i + j of the step.
-__device__ __forceinline__ void y_mma(const YFrag& f, int i, int j, f32x16_t acc[4][4]) {
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
-}
-
 // acc[i][j] element e: output row m = 32i + lane%32, columns n = 32j + 8*(e/4)
-// + 4*(lane/32) + e%4 (four consecutive per e/4), of this wave's quarter.
-template <int MODE>
-__device__ __forceinline__ void y_epilogue(const GemmArgs& g, f32x16_t acc[4][4], char* lds, int64_t m0, int64_t n0,
+// + 4*(lane/32) + e%4 (four consecutive per e/4), of this wave's 128 x 32*NJ
+// part of the tile. The part goes through LDS (rows of 64*NJ bytes at
+// lds + wave * 128 * 64*NJ, 16-byte chunk c of row m at c ^ (m mod 4*NJ)) and
+// out as whole 16-byte row chunks.
+template <int MODE, int NJ>
+__device__ __forceinline__ void y_epilogue(const GemmArgs& g, f32x16_t (*acc)[NJ], char* lds, int64_t m0, int64_t n0,
                                            int wm, int wn, int lane, int wave) {
-    const int64_t mq = m0 + wm * 128, nq = n0 + wn * 128;  // this wave's quarter
-    char* tile = lds + wave * 32768;                        // 128 rows x 256 B, 16-byte chunk c of row m at c ^ (m & 15)
+    constexpr int ROWB = 64 * NJ, NCH = 4 * NJ;
+    const int64_t mq = m0 + wm * 128, nq = n0 + wn * 32 * NJ;  // this wave's part
+    char* tile = lds + wave * 128 * ROWB;
     const bf16_t* bias = reinterpret_cast<const bf16_t*>(g.bias);
     const bf16_t* R = reinterpret_cast<const bf16_t*>(g.R);
     bf16_t* C = reinterpret_cast<bf16_t*>(g.C);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
             const int nl = 32 * j + 8 * e4 + 4 * (lane >> 5);  // first of 4 columns
@@ -567,43 +584,47 @@ __device__ __forceinline__ void y_epilogue(const GemmArgs& g, f32x16_t acc[4][4]
                     }
                 }
                 const uint2 w = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
-                const uint32_t chunk = ((uint32_t)nl >> 3) ^ ((uint32_t)ml & 15u);
-                *reinterpret_cast<uint2*>(tile + ml * 256 + chunk * 16 + (nl & 4) * 2) = w;
+                const uint32_t chunk = ((uint32_t)nl >> 3) ^ ((uint32_t)ml & (NCH - 1u));
+                *reinterpret_cast<uint2*>(tile + ml * ROWB + chunk * 16 + (nl & 4) * 2) = w;
             }
         }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-    // 128 rows x 16 chunks: lane takes chunk lane%16 of rows 4*it + lane/16
-    const int cl = lane & 15;
+    // 128 rows x NCH chunks: lane takes chunk lane % NCH of rows (64/NCH)*it + lane/NCH
+    const int cl = lane & (NCH - 1);
     const int64_t n = nq + cl * 8;
     if (n + 8 > g.N) return;
 #pragma unroll 4
-    for (int it = 0; it < 32; ++it) {
-        const int ml = 4 * it + (lane >> 4);
+    for (int it = 0; it < 2 * NCH; ++it) {
+        const int ml = (64 / NCH) * it + lane / NCH;
         const int64_t m = mq + ml;
         if (m >= g.M) break;
-        const uint4 v = *reinterpret_cast<const uint4*>(tile + ml * 256 + (((uint32_t)cl ^ ((uint32_t)ml & 15u)) * 16));
+        const uint4 v = *reinterpret_cast<const uint4*>(tile + ml * ROWB + (((uint32_t)cl ^ ((uint32_t)ml & (NCH - 1u))) * 16));
         *reinterpret_cast<uint4*>(C + m * g.ldc + n) = v;
     }
 }
 
 // ---------------------------------------------------------------------------
-// The main loop of the DMA-fed kernel takes 64-deep slices through two stages
-// of 64 KiB (A then B, 256 rows of 128 B each). A lane's 16-byte copies then
-// come eight to a row, so each row's share of a slice is one 128-byte request
-// (with 32-deep slices it was two 64-byte ones), and the four waves meet at a
-// barrier once per 64 MFMAs of 32x32x16. The copies of slice t+2 go into the
+// The tile is worked by eight waves, two per SIMD, each 128 rows x 64
+// columns of it (wave w: rows 128*(w/4), columns 64*(w%4)); a wave held up
+// issuing copies leaves its SIMD's matrix pipe to the other wave.
+//
+// The K loop takes 64-deep slices through two stages of 64 KiB (A then B, 256
+// rows of 128 B). A lane's 16-byte copies come eight to a row, so each row's
+// share of a slice is one 128-byte request, and the waves meet at a barrier
+// once per 32 of their MFMAs (32x32x16). The copies of slice t+2 go into the
 // stage slice t releases at the barrier in the middle of its last k16 step:
-// four of a wave's sixteen right after that barrier, the other twelve spread
-// over the first two steps of slice t+1, so that they neither arrive in one
-// burst (the in-order wave then waits for the texture unit to take them, with
-// its MFMAs behind them) nor too late to land before slice t+1 ends.
+// A's right after that barrier, B's in the first step of slice t+1, so that
+// they neither arrive in one burst nor too late to land before slice t+1
+// ends. A wave's four copies of an operand share one M0 value (writing M0
+// holds the wave until the texture unit has taken the copies before it).
 //
 // LDS rows are 128 B; chunk c of row r sits at c ^ ((r/2) mod 8), so the 16
 // rows of a 16-lane group of a fragment read (two rows per 64-bank line) fall
-// on all 64 banks once. Copy instruction q of a wave fills rows 64w + 8q ..
-// +7, lane l taking row 64w + 8q + l/8 and stored chunk l%8.
+// on all 64 banks once. Copy instruction q (0..3) of wave w fills rows
+// 32w + 8q .. +7 of an operand, lane l taking row 32w + 8q + l/8 and stored
+// chunk l%8.
 // ---------------------------------------------------------------------------
 constexpr int ZK = 64;
 constexpr int Z_ROW = ZK * 2;              // 128 B
@@ -615,59 +636,65 @@ __device__ __forceinline__ uint32_t zswz(uint32_t r) { return (r >> 1) & 7u; }
 
 struct ZOperand {
     const char* base;  // src + r0*ld, in bytes
-    uint32_t off[8];   // byte offset of this lane's row in copy instruction q
+    uint32_t off[4];   // byte offset of this lane's row in copy instruction q
     uint32_t kc[2];    // first k (elements) of this lane's chunk: even and odd q
     __device__ __forceinline__ void init(const bf16_t* src, int64_t ld, int64_t rows, int64_t r0, int wave,
                                          int lane) {
         base = reinterpret_cast<const char*>(src + r0 * ld);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const uint32_t r = 64u * (uint32_t)wave + 8u * q + (uint32_t)(lane >> 3);
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t r = 32u * (uint32_t)wave + 8u * q + (uint32_t)(lane >> 3);
             const int64_t rr = std::min<int64_t>(r0 + r, rows - 1) - r0;
             off[q] = (uint32_t)(rr * ld * 2);
         }
-        // row 64w + 8q + l/8 has swizzle term ((8q + l/8) / 2) mod 8, which depends on q only by its parity
 #pragma unroll
         for (int p = 0; p < 2; ++p)
             kc[p] = (((uint32_t)(lane & 7)) ^ zswz(8u * p + (uint32_t)(lane >> 3))) * 8u;
     }
-    // copy instruction q of slice [k0, k0 + 64) into the operand's tile at tile_addr (LDS); on the last,
-    // partial slice a lane whose chunk starts at or past kend reads the last in-bounds chunk instead, and
-    // z_zero_tail clears it once it has landed
-    __device__ __forceinline__ void copy(int q, int64_t k0, int64_t kend, uint32_t tile_addr, int wave) const {
+    __device__ __forceinline__ uint32_t voff(int q, int64_t k0, int64_t kend) const {
         const uint32_t c = kc[q & 1];
         const int64_t gk = k0 + c;
         const uint32_t back = (k0 + ZK <= kend || gk < kend) ? 0u : (uint32_t)((gk - (kend - 8)) * 2);
-        y_copy(base + k0 * 2, off[q] + c * 2 - back, tile_addr + (8u * (uint32_t)wave + q) * 1024u);
+        return off[q] + c * 2 - back;
+    }
+    // this wave's four copies of slice [k0, k0 + 64) into the operand's tile at tile_addr (LDS)
+    __device__ __forceinline__ void copy4(int64_t k0, int64_t kend, uint32_t tile_addr, int wave) const {
+        y_copy4(base + k0 * 2, voff(0, k0, kend), voff(1, k0, kend), voff(2, k0, kend), voff(3, k0, kend),
+                tile_addr + 4u * (uint32_t)wave * 1024u);
     }
 };
 
 __device__ __forceinline__ void z_zero_tail(char* stage, const ZOperand& a, int64_t k0, int64_t kend, int wave,
-                                            int lane) {
+                                             int lane) {
     if (k0 + ZK <= kend) return;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 4; ++q) {
         if (k0 + a.kc[q & 1] < kend) continue;
-        const int o = (8 * wave + q) * 1024 + lane * 16;
+        const int o = (4 * wave + q) * 1024 + lane * 16;
         *reinterpret_cast<uint4*>(stage + o) = make_uint4(0u, 0u, 0u, 0u);
         *reinterpret_cast<uint4*>(stage + Z_TILE + o) = make_uint4(0u, 0u, 0u, 0u);
     }
 }
 
-// Operand fragments of k16 step s (0..3) of a stage: lane l holds row l%32 of
-// each 32-row tile and 8 consecutive k (chunk 2s + l/32).
+struct YFrag { bf16x8_t a[4], b[2]; };
+
 __device__ __forceinline__ void z_read_piece(const char* stage, uint32_t a_off, uint32_t b_off, uint32_t c, int i,
-                                             YFrag& f) {
+                                              YFrag& f) {
     if (i < 4) f.a[i] = *reinterpret_cast<const bf16x8_t*>(stage + a_off + i * 32 * Z_ROW + c);
     else f.b[i - 4] = *reinterpret_cast<const bf16x8_t*>(stage + Z_TILE + b_off + (i - 4) * 32 * Z_ROW + c);
 }
 
+// MFMA q (0..7) of a k16 step: acc[q/2][q%2] = B_(q%2) . A_(q/2)^T
+__device__ __forceinline__ void y_mma(const YFrag& f, int q, f32x16_t acc[4][2]) {
+    acc[q / 2][q % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[q % 2], f.a[q / 2], acc[q / 2][q % 2], 0, 0, 0);
+}
+
 template <int MODE>
-__global__ void __launch_bounds__(256, 1) dsa3d_ntgemm_kernel(GemmArgs g) {
+__global__ void __launch_bounds__(512, 1) dsa3d_ntgemm_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(1024))) char lds[Z_LDS];
     const int lane = threadIdx.x % 64;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
-    const int wm = wave / 2, wn = wave % 2;
+    const int wm = wave / 4, wn = wave % 4;
     const uint32_t ntn = (uint32_t)((g.N + XN - 1) / XN);
     const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
     const int64_t m0 = (int64_t)(lb / ntn) * XM, n0 = (int64_t)(lb % ntn) * XN;
@@ -677,40 +704,34 @@ __global__ void __launch_bounds__(256, 1) dsa3d_ntgemm_kernel(GemmArgs g) {
     opb.init(reinterpret_cast<const bf16_t*>(g.B), g.ldb, g.N, n0, wave, lane);
     const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     const uint32_t r = (uint32_t)(lane & 31), kh = (uint32_t)(lane >> 5);
     const uint32_t a_off = ((uint32_t)wm * 128u + r) * Z_ROW;
-    const uint32_t b_off = ((uint32_t)wn * 128u + r) * Z_ROW;
+    const uint32_t b_off = ((uint32_t)wn * 64u + r) * Z_ROW;
     const uint32_t sw = zswz(r);
-
     // Slices 0 and 1 fill the two stages; iteration t multiplies slice t in
-    // four k16 steps, the next step's fragments read during the current one's
-    // MFMAs. In the last step each wave waits for its copies of slice t+1 and
-    // meets the others at the barrier, after which slice t's stage takes the
-    // first copies of slice t+2 and the first fragments of slice t+1 are read,
-    // both between that step's remaining MFMAs.
+    // four k16 steps, the next step's fragments read (and kept ahead of the
+    // products) during the current one's MFMAs. In the last step each wave
+    // waits for its copies of slice t+1 and meets the others at the barrier,
+    // after which slice t's stage takes A's copies of slice t+2 and the first
+    // fragments of slice t+1 are read, between that step's remaining MFMAs;
+    // B's copies of slice t+2 follow in slice t+1's first step.
     const int64_t nk = (K + ZK - 1) / ZK;
     YFrag f, fn;
     if (nk > 0) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            opa.copy(q, 0, K, lds0, wave);
-            opb.copy(q, 0, K, lds0 + Z_TILE, wave);
-        }
+        opa.copy4(0, K, lds0, wave);
+        opb.copy4(0, K, lds0 + Z_TILE, wave);
         if (nk > 1) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                opa.copy(q, ZK, K, lds0 + Z_STAGE, wave);
-                opb.copy(q, ZK, K, lds0 + Z_STAGE + Z_TILE, wave);
-            }
-            y_wait_vm<16>();  // slice 0 has landed (slice 1's 16 copies may still be in flight)
+            opa.copy4(ZK, K, lds0 + Z_STAGE, wave);
+            opb.copy4(ZK, K, lds0 + Z_STAGE + Z_TILE, wave);
+            y_wait_vm<8>();  // slice 0 has landed (slice 1's 8 copies may still be in flight)
         } else {
             y_wait_vm<0>();
         }
@@ -718,21 +739,11 @@ __global__ void __launch_bounds__(256, 1) dsa3d_ntgemm_kernel(GemmArgs g) {
         y_barrier();
         const uint32_t c0 = ((0u + kh) ^ sw) * 16u;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) z_read_piece(lds, a_off, b_off, c0, i, f);
+        for (int i = 0; i < 6; ++i) z_read_piece(lds, a_off, b_off, c0, i, f);
         __builtin_amdgcn_sched_barrier(0);
     }
-    // copy ci (0..15) of a slice: A and B in turn, instruction ci/2 of each
-    auto copy_ci = [&](int ci, int64_t k0, uint32_t st) {
-        if (ci & 1) opb.copy(ci >> 1, k0, K, st + Z_TILE, wave);
-        else opa.copy(ci >> 1, k0, K, st, wave);
-    };
     for (int64_t t = 0; t < nk; ++t) {
         const char* stage = lds + (t & 1) * Z_STAGE;
-        // copies 4..15 of slice t+1 (its first four went out after the last
-        // barrier; slice 1 came whole with slice 0) spread over the first two
-        // steps, one after every third MFMA: a burst of copies fills the
-        // texture unit's queues, and the wave, which issues in order, would
-        // stall behind them with its MFMAs
         const bool spread = t >= 1 && t + 1 < nk;
         const int64_t k1 = (t + 1) * ZK;
         const uint32_t st1 = lds0 + (uint32_t)(((t + 1) & 1) * Z_STAGE);
@@ -740,17 +751,14 @@ __global__ void __launch_bounds__(256, 1) dsa3d_ntgemm_kernel(GemmArgs g) {
         for (uint32_t s = 0; s < 3; ++s) {
             const uint32_t c = ((2u * (s + 1) + kh) ^ sw) * 16u;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) z_read_piece(stage, a_off, b_off, c, i, fn);
-            // keep the reads ahead of this step's products: left to itself the
-            // compiler sinks each read to just before its first use and waits
-            // for it there, once every four MFMAs
+            for (int i = 0; i < 6; ++i) z_read_piece(stage, a_off, b_off, c, i, fn);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                y_mma(f, q / 4, q % 4, acc);
-                if (s < 2 && q % 3 == 0) {
+            for (int q = 0; q < 8; ++q) {
+                y_mma(f, q, acc);
+                if (s == 0 && q == 1) {  // B's copies of slice t+1
                     __builtin_amdgcn_sched_barrier(0);
-                    if (spread) copy_ci(4 + (int)s * 6 + q / 3, k1, st1);
+                    if (spread) opb.copy4(k1, K, st1 + Z_TILE, wave);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -758,7 +766,7 @@ __global__ void __launch_bounds__(256, 1) dsa3d_ntgemm_kernel(GemmArgs g) {
             f = fn;
         }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) y_mma(f, q / 4, q % 4, acc);
+        for (int q = 0; q < 4; ++q) y_mma(f, q, acc);
         __builtin_amdgcn_sched_barrier(0);
         const bool more = t + 1 < nk;
         if (more) {
@@ -774,18 +782,25 @@ __global__ void __launch_bounds__(256, 1) dsa3d_ntgemm_kernel(GemmArgs g) {
             const char* next = lds + ((t + 1) & 1) * Z_STAGE;
             const uint32_t c0 = ((0u + kh) ^ sw) * 16u;
 #pragma unroll
-            for (int q = 8; q < 16; ++q) {
-                y_mma(f, q / 4, q % 4, acc);
+            for (int q = 4; q < 8; ++q) {
+                y_mma(f, q, acc);
                 __builtin_amdgcn_sched_barrier(0);
-                if (refill && (q & 1) == 0) copy_ci((q - 8) / 2, k2, st);  // copies 0..3 of slice t+2
-                if (more) z_read_piece(next, a_off, b_off, c0, q - 8, fn);
+                if (refill && q == 4) opa.copy4(k2, K, st, wave);  // A's copies of slice t+2
+                if (more) {
+                    if (q < 6) {
+                        z_read_piece(next, a_off, b_off, c0, 2 * (q - 4), fn);
+                        z_read_piece(next, a_off, b_off, c0, 2 * (q - 4) + 1, fn);
+                    } else {
+                        z_read_piece(next, a_off, b_off, c0, q - 2, fn);
+                    }
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
             f = fn;
         }
     }
     y_barrier();  // every wave is done with the stages before they hold the output tile
-    y_epilogue<MODE>(g, acc, lds, m0, n0, wm, wn, lane, wave);
+    y_epilogue<MODE, 2>(g, acc, lds, m0, n0, wm, wn, lane, wave);
 }
 
 // out[i] = sum_{z < nsplit} part[z*n + i], in order z = 0, 1, ...
@@ -914,7 +929,7 @@ static hipError_t ntgemm(GemmArgs g, int kernel_id, hipStream_t s) {
     const int64_t tiles = ((g.M + XM - 1) / XM) * ((g.N + XN - 1) / XN);
     if (tiles == 0) return hipSuccess;
     LaunchScope ls(kernel_id, s);
-    hipLaunchKernelGGL((dsa3d_ntgemm_kernel<MODE>), dim3((unsigned)tiles), dim3(256), 0, s, g);
+    hipLaunchKernelGGL((dsa3d_ntgemm_kernel<MODE>), dim3((unsigned)tiles), dim3(512), 0, s, g);
     return hipGetLastError();
 }
 
