@@ -360,25 +360,11 @@ __device__ __forceinline__ void x_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// One k16 step (s = 0..3 of a 64-deep slice) of 4x4 MFMAs on this wave's
-// quarter. Lane l supplies row l%32 of each 32-row operand tile and 8
-// consecutive k (chunk 2s + l/32 of the slice); both operands use the same k
+// Operand fragments of one k16 step (of 4x4 MFMAs on a wave's 128x128
+// quarter): lane l holds row l%32 of each 32-row tile and 8 consecutive k
+// (chunk 2s + l/32 of the slice in step s); both operands use the same k
 // assignment, so the hardware's k order inside one MFMA does not matter.
-__device__ __forceinline__ void x_mma_step(const char* As, const char* Bs, uint32_t a_off, uint32_t b_off,
-                                           uint32_t sw, uint32_t kh, uint32_t s, f32x16_t acc[4][4]) {
-    const uint32_t c = ((2u * s + kh) ^ sw) * 16u;
-    bf16x8_t a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        a[i] = *reinterpret_cast<const bf16x8_t*>(As + a_off + i * 32 * X_ROW_BYTES + c);
-        b[i] = *reinterpret_cast<const bf16x8_t*>(Bs + b_off + i * 32 * X_ROW_BYTES + c);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-}
+struct XFrag { bf16x8_t a[4], b[4]; };
 
 // Accumulator element e of tile (i, j) is row 8*(e/4) + 4*(lane/32) + e%4,
 // column lane%32 of that 32x32 tile. EDGE: the tile crosses the end of M or N.
@@ -457,26 +443,62 @@ __global__ void __launch_bounds__(256, 1) dsa3d_xgemm_kernel(GemmArgs g) {
         }
         x_barrier();
     }
+    // Fragments are read one k16 step ahead of their products (and kept there:
+    // left to itself the compiler sinks each read to its first use and waits
+    // for it once every four MFMAs). After the first step's products the next
+    // slice's registers go to the other stage (last read in the previous slice,
+    // before the barrier) and the loads of the slice after it are issued, a
+    // whole slice ahead of their use. The barrier sits in the middle of the
+    // last step, whose remaining products cover the next slice's first reads.
+    auto xread = [&](const char* As, const char* Bs, uint32_t s, XFrag& f) {
+        const uint32_t c = ((2u * s + kh) ^ sw) * 16u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f.a[i] = *reinterpret_cast<const bf16x8_t*>(As + a_off + i * 32 * X_ROW_BYTES + c);
+            f.b[i] = *reinterpret_cast<const bf16x8_t*>(Bs + b_off + i * 32 * X_ROW_BYTES + c);
+        }
+    };
+    auto xmma = [&](const XFrag& f, int q) {
+        acc[q / 4][q % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[q / 4], f.b[q % 4], acc[q / 4][q % 4], 0, 0, 0);
+    };
+    XFrag f, fn;
+    if (nk > 0) {
+        xread(XA(0), XB(0), 0, f);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     for (int64_t t = 0; t < nk; ++t) {
         const int cur = (int)(t & 1);
-        // First k16 step, then the hand-over of the next slice while those
-        // MFMAs run: its registers go to the other stage (last read in the
-        // previous slice, before the barrier) and the loads of the slice after
-        // it are issued, a whole slice ahead of their use.
-        x_mma_step(XA(cur), XB(cur), a_off, b_off, sw, kh, 0, acc);
+#pragma unroll
+        for (uint32_t s = 0; s < 3; ++s) {
+            xread(XA(cur), XB(cur), s + 1, fn);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) xmma(f, q);
+            __builtin_amdgcn_sched_barrier(0);
+            if (s == 0) {
+                if (t + 1 < nk) {
+                    x_store<AK>(sa, XA(cur ^ 1));
+                    x_store<BKC>(sb, XB(cur ^ 1));
+                }
+                if (t + 2 < nk) {
+                    x_load<AK>(opa, kb + (t + 2) * XK, ke, sa);
+                    x_load<BKC>(opb, kb + (t + 2) * XK, ke, sb);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            f = fn;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) xmma(f, q);
         __builtin_amdgcn_sched_barrier(0);
-        if (t + 1 < nk) {
-            x_store<AK>(sa, XA(cur ^ 1));
-            x_store<BKC>(sb, XB(cur ^ 1));
-        }
-        if (t + 2 < nk) {
-            x_load<AK>(opa, kb + (t + 2) * XK, ke, sa);
-            x_load<BKC>(opb, kb + (t + 2) * XK, ke, sb);
-        }
+        x_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + 1 < nk) xread(XA(cur ^ 1), XB(cur ^ 1), 0, fn);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (uint32_t ks = 1; ks < 4; ++ks) x_mma_step(XA(cur), XB(cur), a_off, b_off, sw, kh, ks, acc);
-        x_barrier();
+        for (int q = 8; q < 16; ++q) xmma(f, q);
+        __builtin_amdgcn_sched_barrier(0);
+        f = fn;
     }
 #undef XA
 #undef XB
