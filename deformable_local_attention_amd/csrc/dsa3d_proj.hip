@@ -368,12 +368,12 @@ struct XFrag { bf16x8_t a[4], b[4]; };
 
 // Accumulator element e of tile (i, j) is row 8*(e/4) + 4*(lane/32) + e%4,
 // column lane%32 of that 32x32 tile. EDGE: the tile crosses the end of M or N.
-template <int MODE, bool EDGE>
-__device__ __forceinline__ void x_epilogue(const GemmArgs& g, f32x16_t acc[4][4], int64_t m0, int64_t n0, int wm,
-                                           int wn, int lane) {
+template <int MODE, bool EDGE, int NJ>
+__device__ __forceinline__ void x_epilogue_t(const GemmArgs& g, f32x16_t (*acc)[NJ], int64_t m0, int64_t n0,
+                                             int wm, int wn, int lane) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < NJ; ++j) {
+        const int64_t n = n0 + wn * 32 * NJ + j * 32 + (lane & 31);
         if (EDGE && n >= g.N) continue;
         const float bb = (MODE != OUT_PARTIAL && g.bias)
                              ? load_scalar<bf16_t>(reinterpret_cast<const bf16_t*>(g.bias) + n)
@@ -504,9 +504,9 @@ __global__ void __launch_bounds__(256, 1) dsa3d_xgemm_kernel(GemmArgs g) {
 #undef XB
 
     if (m0 + XM <= g.M && n0 + XN <= g.N)
-        x_epilogue<MODE, false>(g, acc, m0, n0, wm, wn, lane);
+        x_epilogue_t<MODE, false, 4>(g, acc, m0, n0, wm, wn, lane);
     else
-        x_epilogue<MODE, true>(g, acc, m0, n0, wm, wn, lane);
+        x_epilogue_t<MODE, true, 4>(g, acc, m0, n0, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -825,6 +825,225 @@ __global__ void __launch_bounds__(512, 1) dsa3d_ntgemm_kernel(GemmArgs g) {
     y_epilogue<MODE, 2>(g, acc, lds, m0, n0, wm, wn, lane, wave);
 }
 
+// ---------------------------------------------------------------------------
+// bf16 products whose operands are both M/N-contiguous (dW = dy^T . x, the
+// offset projection's dW): the same 256x256 tile, eight waves and two 64-deep
+// LDS stages as the DMA-fed kernel, the tiles copied from memory as they lie
+// (an LDS row is one k: 256 columns, 512 B) and the MFMA operands read with
+// gfx950's transposing LDS read, ds_read_b64_tr_b16. In a 16-lane block of
+// that read, lane j receives element j%4 of the 8-byte pieces read by lanes
+// j/4, j/4 + 4, j/4 + 8 and j/4 + 12; so when lane L reads row k0 + L/4,
+// columns c0 + 4(L%4) .. +3, lane j receives column c0 + j of rows k0 .. k0+3,
+// and two such reads give a lane its 8 consecutive k of one column.
+//
+// The 32-byte unit u of LDS row r sits at u ^ (2 (r mod 4)): the 32 lanes a
+// transposing read serves at once (4 rows, two 32-byte units each) then fall
+// on distinct banks. Copy instruction q (0..3) of wave w fills rows
+// 2(4w + q) and 2(4w + q) + 1, lane l taking row 2(4w + q) + l/32 and stored
+// 16-byte slot l%32.
+// ---------------------------------------------------------------------------
+constexpr int T_ROWB = 512;              // one LDS row: 256 bf16 columns of one k
+constexpr int T_TILE = 64 * T_ROWB;      // 32 KiB: the 64 k rows of one operand
+constexpr int T_STAGE = 2 * T_TILE;      // A then B
+constexpr int T_LDS = 2 * T_STAGE;       // 128 KiB
+
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+
+struct TOperand {
+    const char* base;   // src + c0 (this tile's first column), in bytes
+    uint32_t ldb;       // bytes per k row
+    uint32_t colb[2];   // byte offset of this lane's 16 bytes within its row: even and odd q
+    // row of copy instruction q within the slice: 2(4w + q) + l/32 (its swizzle term depends on q's parity only)
+    static __device__ __forceinline__ uint32_t row(int q, int wave, int lane) {
+        return 2u * (4u * (uint32_t)wave + (uint32_t)q) + (uint32_t)(lane >> 5);
+    }
+    __device__ __forceinline__ void init(const bf16_t* src, int64_t ld, int64_t cols, int64_t c0, int wave,
+                                         int lane) {
+        base = reinterpret_cast<const char*>(src + c0);
+        ldb = (uint32_t)(ld * 2);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint32_t r = row(q, wave, lane);
+            const uint32_t p = (uint32_t)(lane & 31);
+            const uint32_t w = 2u * ((p >> 1) ^ (2u * (r & 3u))) + (p & 1u);  // the row's chunk stored at slot p
+            // columns past the end read the last in-bounds chunk (never stored)
+            const int64_t col = std::min<int64_t>(8 * (int64_t)w, cols - c0 - 8);
+            colb[q] = (uint32_t)(col * 2);
+        }
+    }
+    // byte offset of copy q of slice [k0, k0 + 64) from base + k0 * ldb: rows at or past kend read the last
+    // in-bounds row instead (t_zero_tail clears them once they have landed)
+    __device__ __forceinline__ uint32_t voff(int q, uint32_t last, int wave, int lane) const {
+        return min(row(q, wave, lane), last) * ldb + colb[q & 1];
+    }
+    __device__ __forceinline__ void copy4(int64_t k0, int64_t kend, uint32_t tile_addr, int wave, int lane) const {
+        const uint32_t last = (uint32_t)std::min<int64_t>(63, kend - 1 - k0);  // last in-bounds row of the slice
+        y_copy4(base + k0 * (int64_t)ldb, voff(0, last, wave, lane), voff(1, last, wave, lane),
+                voff(2, last, wave, lane), voff(3, last, wave, lane), tile_addr + 4u * (uint32_t)wave * 1024u);
+    }
+};
+
+__device__ __forceinline__ void t_zero_tail(char* stage, int64_t k0, int64_t kend, int wave, int lane) {
+    if (k0 + 64 <= kend) return;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (k0 + (int64_t)TOperand::row(q, wave, lane) < kend) continue;
+        const int o = (4 * wave + q) * 1024 + lane * 16;
+        *reinterpret_cast<uint4*>(stage + o) = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(stage + T_TILE + o) = make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+struct TFrag { bf16x8_t a[4], b[2]; };
+
+// The fragments of k16 step s: A tiles i (columns 32i + l%32 of the wave's
+// 128) and B tiles j (columns 32j + l%32 of its 64), k rows 16s + 8(l/32) .. +7.
+__device__ __forceinline__ bf16x8_t t_read8(const char* p) {
+    typedef s16x4_t __attribute__((address_space(3))) * lds_s16x4_ptr;
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p + 4 * T_ROWB));
+    typedef __attribute__((ext_vector_type(8))) short s16x8_t;
+    const s16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// A lane's transposing-read offsets: rows 8(l/32) + L/4 for L = l%16, the
+// swizzled 32-byte unit of its block's 16 columns, its 8 bytes within it.
+struct TReadOff {
+    uint32_t row_b;  // row and in-unit bytes: (8(l/32) + L/4) * 512 + 8(L%4)
+    uint32_t ua;     // A's unit before the swizzle, tile 0: 8 wm + block
+    uint32_t ub;     // B's, tile 0: 4 wn + block
+    uint32_t x;      // the swizzle term: 2 (L/4)
+    __device__ __forceinline__ uint32_t a(int i) const { return row_b + ((ua + 2u * i) ^ x) * 32u; }
+    __device__ __forceinline__ uint32_t b(int j) const { return row_b + ((ub + 2u * j) ^ x) * 32u; }
+};
+
+__device__ __forceinline__ void t_read_piece(const char* stage, const TReadOff& o, uint32_t s, int i, TFrag& f) {
+    const uint32_t ro = 16u * s * T_ROWB;
+    if (i < 4) f.a[i] = t_read8(stage + ro + o.a(i));
+    else f.b[i - 4] = t_read8(stage + T_TILE + ro + o.b(i - 4));
+}
+
+// acc[i][j] = A_i . B_j (element e: row 8*(e/4) + 4*(lane/32) + e%4, column lane%32 of the 32x32 tile)
+__device__ __forceinline__ void t_mma(const TFrag& f, int q, f32x16_t acc[4][2]) {
+    acc[q / 2][q % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[q / 2], f.b[q % 2], acc[q / 2][q % 2], 0, 0, 0);
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(512, 1) dsa3d_mngemm_kernel(GemmArgs g) {
+    __shared__ __attribute__((aligned(1024))) char lds[T_LDS];
+    const int lane = threadIdx.x % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int wm = wave / 4, wn = wave % 4;  // 128 rows x 64 columns of the tile
+    const uint32_t ntn = (uint32_t)((g.N + XN - 1) / XN);
+    const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int64_t m0 = (int64_t)(lb / ntn) * XM, n0 = (int64_t)(lb % ntn) * XN;
+    const int64_t kb = (int64_t)blockIdx.z * g.k_split;
+    const int64_t ke = std::min<int64_t>(g.K, kb + g.k_split);
+    TOperand opa, opb;
+    opa.init(reinterpret_cast<const bf16_t*>(g.A), g.lda, g.M, m0, wave, lane);
+    opb.init(reinterpret_cast<const bf16_t*>(g.B), g.ldb, g.N, n0, wave, lane);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+
+    f32x16_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    TReadOff ro;
+    {
+        const uint32_t L = (uint32_t)(lane & 15), blk = (uint32_t)((lane >> 4) & 1), kh = (uint32_t)(lane >> 5);
+        ro.row_b = (8u * kh + (L >> 2)) * T_ROWB + 8u * (L & 3u);
+        ro.ua = 8u * (uint32_t)wm + blk;
+        ro.ub = 4u * (uint32_t)wn + blk;
+        ro.x = 2u * (L >> 2);
+    }
+
+    // as in the DMA-fed kernel: two stages; after the barrier in the middle of
+    // slice t's last step its stage takes A's copies of slice t+2, and B's
+    // follow in slice t+1's first step
+    const int64_t nk = (ke - kb + 63) / 64;
+    TFrag f, fn;
+    if (nk > 0) {
+        opa.copy4(kb, ke, lds0, wave, lane);
+        opb.copy4(kb, ke, lds0 + T_TILE, wave, lane);
+        if (nk > 1) {
+            opa.copy4(kb + 64, ke, lds0 + T_STAGE, wave, lane);
+            opb.copy4(kb + 64, ke, lds0 + T_STAGE + T_TILE, wave, lane);
+            y_wait_vm<8>();  // slice 0 has landed (slice 1's 8 copies may still be in flight)
+        } else {
+            y_wait_vm<0>();
+        }
+        t_zero_tail(lds, kb, ke, wave, lane);
+        y_barrier();
+#pragma unroll
+        for (int i = 0; i < 6; ++i) t_read_piece(lds, ro, 0, i, f);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int64_t t = 0; t < nk; ++t) {
+        const char* stage = lds + (t & 1) * T_STAGE;
+        const bool spread = t >= 1 && t + 1 < nk;
+        const int64_t k1 = kb + (t + 1) * 64;
+        const uint32_t st1 = lds0 + (uint32_t)(((t + 1) & 1) * T_STAGE);
+#pragma unroll
+        for (uint32_t s = 0; s < 3; ++s) {
+#pragma unroll
+            for (int i = 0; i < 6; ++i) t_read_piece(stage, ro, s + 1, i, fn);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                t_mma(f, q, acc);
+                if (s == 0 && q == 1) {  // B's copies of slice t+1
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (spread) opb.copy4(k1, ke, st1 + T_TILE, wave, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            f = fn;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) t_mma(f, q, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        const bool more = t + 1 < nk;
+        if (more) {
+            y_wait_vm<0>();  // this wave's copies of slice t+1
+            t_zero_tail(lds + ((t + 1) & 1) * T_STAGE, k1, ke, wave, lane);
+        }
+        y_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            const bool refill = t + 2 < nk;
+            const int64_t k2 = kb + (t + 2) * 64;
+            const uint32_t st = lds0 + (uint32_t)((t & 1) * T_STAGE);
+            const char* next = lds + ((t + 1) & 1) * T_STAGE;
+#pragma unroll
+            for (int q = 4; q < 8; ++q) {
+                t_mma(f, q, acc);
+                __builtin_amdgcn_sched_barrier(0);
+                if (refill && q == 4) opa.copy4(k2, ke, st, wave, lane);  // A's copies of slice t+2
+                if (more) {
+                    if (q < 6) {
+                        t_read_piece(next, ro, 0, 2 * (q - 4), fn);
+                        t_read_piece(next, ro, 0, 2 * (q - 4) + 1, fn);
+                    } else {
+                        t_read_piece(next, ro, 0, q - 2, fn);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            f = fn;
+        }
+    }
+    if (m0 + XM <= g.M && n0 + XN <= g.N)
+        x_epilogue_t<MODE, false, 2>(g, acc, m0, n0, wm, wn, lane);
+    else
+        x_epilogue_t<MODE, true, 2>(g, acc, m0, n0, wm, wn, lane);
+}
+
 // out[i] = sum_{z < nsplit} part[z*n + i], in order z = 0, 1, ...
 __global__ void __launch_bounds__(256) dsa3d_split_sum_kernel(const float* part, float* out, int64_t n, int nsplit) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
@@ -955,11 +1174,31 @@ static hipError_t ntgemm(GemmArgs g, int kernel_id, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The transposing-read kernel needs both operands M/N-contiguous in 16-byte
+// pieces: M, N and the leading dimensions multiples of 8, 16-byte aligned
+// bases, K splits that are whole 64-deep slices.
+static bool mngemm_ok(const GemmArgs& g) {
+    return g.M % 8 == 0 && g.N % 8 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 && aligned16(g.A) && aligned16(g.B) &&
+           (g.k_split % 64 == 0 || g.k_split >= g.K);
+}
+
+template <int MODE>
+static hipError_t mngemm(GemmArgs g, int splits, int kernel_id, hipStream_t s) {
+    const int64_t tiles = ((g.M + XM - 1) / XM) * ((g.N + XN - 1) / XN);
+    if (tiles == 0) return hipSuccess;
+    LaunchScope ls(kernel_id, s);
+    hipLaunchKernelGGL((dsa3d_mngemm_kernel<MODE>), dim3((unsigned)tiles, 1, splits), dim3(512), 0, s, g);
+    return hipGetLastError();
+}
+
 // bf16 products go to the 256x256 kernel when its vector conditions hold,
 // everything else (float32, odd sizes) to the 128x128 one.
 template <typename T, bool AK, bool BKC, int MODE>
 static hipError_t gemm_any(GemmArgs g, int splits, int kernel_id, hipStream_t s) {
     if constexpr (sizeof(T) == 2) {
+        if constexpr (!AK && !BKC) {
+            if (mngemm_ok(g)) return mngemm<MODE>(g, splits, kernel_id, s);
+        }
         if (xgemm_ok(g, AK, BKC)) return xgemm<AK, BKC, MODE>(g, splits, kernel_id, s);
     }
     return gemm<T, AK, BKC, MODE>(g, splits, kernel_id, s);
