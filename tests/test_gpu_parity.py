@@ -90,6 +90,8 @@ def test_tiny_f32_workload(det):
 CASES = {
     "f32-ragged-b2-h3-d16": dict(B=2, T=3, H=5, W=7, heads=3, d=16, sigma=1.5),
     "bf16-ragged-p75-d128": dict(T=5, H=6, W=9, heads=2, d=128, window=(3, 5, 5), sigma=2.0, dtype="bf16"),
+    "bf16-odd-b2-p75-d128": dict(B=2, T=3, H=7, W=5, heads=3, d=128, window=(3, 5, 5), sigma=2.0, dtype="bf16"),
+    "bf16-single-token-d128": dict(T=1, H=1, W=1, heads=2, d=128, window=(3, 5, 5), sigma=1.0, dtype="bf16"),
     "f32-p1-d8": dict(T=4, H=5, W=6, heads=2, d=8, window=(1, 1, 1), sigma=0.7),
     "f32-d256-dil": dict(T=2, H=3, W=4, heads=1, d=256, window=(3, 3, 3), dil=(2, 1, 3), sigma=1.0),
     "bf16-d64-513": dict(T=4, H=7, W=6, heads=3, d=64, window=(5, 1, 3), dil=(1, 2, 2), sigma=0.3, dtype="bf16"),
