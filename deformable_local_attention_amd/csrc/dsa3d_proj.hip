@@ -778,7 +778,10 @@ __global__ void __launch_bounds__(512, 1) dsa3d_ntgemm_kernel(GemmArgs g) {
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 y_mma(f, q, acc);
-                if (s == 0 && q == 1) {  // B's copies of slice t+1
+                // B's copies of slice t+1: waves 0-3 in the first step, waves 4-7 (the
+                // other wave of each SIMD) a step later, so that the two waves of a SIMD
+                // do not both wait on the texture unit to take their copies
+                if (s == (wave < 4 ? 0u : 1u) && q == 1) {
                     __builtin_amdgcn_sched_barrier(0);
                     if (spread) opb.copy4(k1, K, st1 + Z_TILE, wave);
                     __builtin_amdgcn_sched_barrier(0);
@@ -807,7 +810,8 @@ __global__ void __launch_bounds__(512, 1) dsa3d_ntgemm_kernel(GemmArgs g) {
             for (int q = 4; q < 8; ++q) {
                 y_mma(f, q, acc);
                 __builtin_amdgcn_sched_barrier(0);
-                if (refill && q == 4) opa.copy4(k2, K, st, wave);  // A's copies of slice t+2
+                // A's copies of slice t+2: waves 4-7 two products after waves 0-3
+                if (refill && q == (wave < 4 ? 4 : 6)) opa.copy4(k2, K, st, wave);
                 if (more) {
                     if (q < 6) {
                         z_read_piece(next, a_off, b_off, c0, 2 * (q - 4), fn);
