@@ -130,6 +130,13 @@ def test_workspace_sizes():
     cw = dsa.dsa3d_workspace_size(conv, dsa.WS_DWCONV_BACKWARD)
     assert 28 * 3072 * 4 <= cw <= 28 * 3072 * 4 * (256 * 68) + 1024
     assert dsa.dsa3d_workspace_size(conv, 7) == 0
+    # sized for either split of the weight-gradient sums (the path depends on the input's alignment):
+    # 720p, 1024 channels: 480 groups of six rows against 6 x 5 tiles x 4 runs of 16 frames = 120
+    c720 = dsa.make_desc(1, 64, 45, 80, 16, 64, (3, 3, 3), dtype=torch.bfloat16)
+    assert dsa.dsa3d_workspace_size(c720, dsa.WS_DWCONV_BACKWARD) == 480 * 1024 * 27 * 4 + 480 * 1024 * 4 + 512
+    # one 512 x 512 frame of 64 channels: 64 x 32 tiles of 8 x 16 tokens outnumber the 512 row groups
+    wide = dsa.make_desc(1, 1, 512, 512, 1, 64, (3, 3, 3), dtype=torch.bfloat16)
+    assert dsa.dsa3d_workspace_size(wide, dsa.WS_DWCONV_BACKWARD) == 2048 * 64 * 27 * 4 + 2048 * 64 * 4 + 512
     # the fixed-window backward keeps one float per (token, head)
     assert dsa.dsa3d_workspace_size(conv, dsa.WS_BACKWARD_FIXED) == 256 * 68 * 120 * 24 * 8 + 256
     bad = _desc(window=(2, 2, 2))
