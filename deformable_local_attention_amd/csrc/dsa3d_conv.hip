@@ -330,9 +330,12 @@ constexpr int CT_ROWB = CT_SC * 128 + 128;           // bytes per slab row, padd
                                                      // r+1 start 32 banks apart
 constexpr int CT_SLOT = CT_SR * CT_ROWB;             // one frame's slab: 24,320 bytes
 constexpr int CT_PIECES = CT_SR * CT_SC * 8;         // 16-byte pieces per slab: 1,440
-constexpr int CT_LOADS = (CT_PIECES + 255) / 256;    // per thread: 6
+constexpr int CT_THREADS = 32 * CT_TH;               // a thread per output row and channel pair
+constexpr int CT_LOADS = (CT_PIECES + CT_THREADS - 1) / CT_THREADS;  // per thread: 6
 
 enum { CT_FWD = 0, CT_DQ = 1, CT_WGRAD = 2 };
+// the weight gradient's row sums ([row][channel][27 taps + bias] floats) reuse the three slots
+static_assert(CT_TH * 64 * 28 * 4 <= 3 * CT_SLOT, "the row sums must fit in the slab slots");
 
 struct TileCoords {
     int32_t b, ta, tb, h0, w0;
@@ -375,7 +378,7 @@ struct SlabPieces {
 __device__ __forceinline__ void slab_pieces(const ConvGrid& g, const TileCoords& tc, SlabPieces& sp) {
 #pragma unroll
     for (int i = 0; i < CT_LOADS; ++i) {
-        const int k = (int)threadIdx.x + 256 * i;
+        const int k = (int)threadIdx.x + CT_THREADS * i;
         const int piece = k >> 3, part = k & 7;
         const int srow = piece / CT_SC, scol = piece % CT_SC;
         const int32_t h = tc.h0 - 1 + srow, w = tc.w0 - 1 + scol;
@@ -409,12 +412,12 @@ __device__ __forceinline__ void slab_load(const bf16_t* x, const ConvGrid& g, co
 __device__ __forceinline__ void slab_store(char* slot, const SlabPieces& sp, const ct_u32x4 v[CT_LOADS]) {
 #pragma unroll
     for (int i = 0; i < CT_LOADS; ++i)
-        if (256 * (i + 1) <= CT_PIECES || (int)threadIdx.x + 256 * i < CT_PIECES)
+        if (CT_THREADS * (i + 1) <= CT_PIECES || (int)threadIdx.x + CT_THREADS * i < CT_PIECES)
             *reinterpret_cast<ct_u32x4*>(slot + sp.soff[i]) = v[i];
 }
 
 template <int MODE>
-__global__ void __launch_bounds__(256) dsa3d_dwconv_tile_kernel(const bf16_t* x, const bf16_t* wt,
+__global__ void __launch_bounds__(CT_THREADS) dsa3d_dwconv_tile_kernel(const bf16_t* x, const bf16_t* wt,
                                                                 const bf16_t* bias, bf16_t* out, const bf16_t* dy,
                                                                 float* part, float* partb, ConvGrid g, int32_t tc,
                                                                 int32_t ntc, int32_t nht, int32_t nwt) {
@@ -619,7 +622,7 @@ __global__ void __launch_bounds__(256) dsa3d_dwconv_tile_kernel(const bf16_t* x,
             dst[27] = sb[ch];
         }
         __syncthreads();
-        for (int i = (int)threadIdx.x; i < 64 * 28; i += 256) {
+        for (int i = (int)threadIdx.x; i < 64 * 28; i += CT_THREADS) {
             float s = 0.0f;
 #pragma unroll
             for (int rr = 0; rr < CT_TH; ++rr) s += red[rr * 64 * 28 + i];
@@ -780,7 +783,7 @@ hipError_t conv_launch(const dsa3d_desc& d, const void* x, const void* w, const 
         if (conv_tiled(d, x)) {
             const ConvTiles ct = conv_tiles(d, false);
             const int64_t nb = ct.groups * (g.C / 64);
-            hipLaunchKernelGGL((dsa3d_dwconv_tile_kernel<MIRROR ? CT_DQ : CT_FWD>), dim3((unsigned)nb), dim3(256), 0, s,
+            hipLaunchKernelGGL((dsa3d_dwconv_tile_kernel<MIRROR ? CT_DQ : CT_FWD>), dim3((unsigned)nb), dim3(CT_THREADS), 0, s,
                                reinterpret_cast<const bf16_t*>(x), reinterpret_cast<const bf16_t*>(w),
                                reinterpret_cast<const bf16_t*>(bias), reinterpret_cast<bf16_t*>(out), nullptr, nullptr,
                                nullptr, g, ct.tc, ct.ntc, ct.nht, ct.nwt);
@@ -854,7 +857,7 @@ hipError_t launch_dwconv_backward(const dsa3d_desc& d, const void* q, const void
     if (tiled) {
         LaunchScope ls(DSA3D_K_DWCONV_WGRAD, s);
         const ConvTiles ct = conv_tiles(d, true);
-        hipLaunchKernelGGL((dsa3d_dwconv_tile_kernel<CT_WGRAD>), dim3((unsigned)(ct.groups * (g.C / 64))), dim3(256),
+        hipLaunchKernelGGL((dsa3d_dwconv_tile_kernel<CT_WGRAD>), dim3((unsigned)(ct.groups * (g.C / 64))), dim3(CT_THREADS),
                            0, s, reinterpret_cast<const bf16_t*>(q), nullptr, nullptr, nullptr,
                            reinterpret_cast<const bf16_t*>(dy), part, partb, g, ct.tc, ct.ntc, ct.nht, ct.nwt);
     } else {
