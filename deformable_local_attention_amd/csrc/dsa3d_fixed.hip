@@ -693,7 +693,7 @@ dsa3d_fixed_bwd_key_mfma_kernel(FixedArgs a) {
     bool kin[R];
     int64_t ktok[R];
     mf_bf16x8 kb[R][D / 32], vb[R][D / 32];  // own keys and values as second operands: key c, channels 32j + 8g
-    mf_f32x4 dk[R][D / 32][2], dv[R][D / 32][2];  // rows 4g + r of tile (tau, par): channel 32*tau + 8g + 2r + par
+    mf_f32x4 dk[R][D / 32][2], dv[R][D / 32][2];  // rows 4g + r of tile (tau, par): channel 32*tau + 16*par + 4g + r
 #pragma unroll
     for (int rho = 0; rho < R; ++rho) {
         kin[rho] = w0 + c < a.g.W && h + rho < a.g.H;
@@ -796,39 +796,23 @@ dsa3d_fixed_bwd_key_mfma_kernel(FixedArgs a) {
                 s_hi[rho] = __builtin_bit_cast(mf_bf16x8, sh);
                 s_lo[rho] = __builtin_bit_cast(mf_bf16x8, sl);
             }
-            // dv^T += dO^T P^T and dk^T += Q^T (scale dS)^T, the query rows read a
-            // channel pair at a time; element 8g + i of the k-slice is query 4g + i
-            // (i < 4) or 16 + 4g + i - 4
+            // dv^T += dO^T P^T and dk^T += Q^T (scale dS)^T on tiles of 16 channels (tile (tau, par):
+            // channels 32*tau + 16*par ..), the first operands read with the transposing LDS read: lane
+            // c of block g receives channel c of the four queries 4g .. 4g+3, then of 16+4g .. 16+4g+3
 #pragma unroll
             for (int tau = 0; tau < D / 32; ++tau) {
-                uint32_t dq8[8], dg8[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int qr = i < 4 ? 4 * g + i : 12 + 4 * g + i;
-                    dq8[i] = *reinterpret_cast<const uint32_t*>(qs + qr * RS + 32 * tau + 2 * c);
-                    dg8[i] = *reinterpret_cast<const uint32_t*>(gs + qr * RS + 32 * tau + 2 * c);
-                }
-                mf_u32x4 qe, qo, ge, go;
+                for (int par = 0; par < 2; ++par) {
+                    const int toff = (4 * g + (c >> 2)) * RS + 32 * tau + 16 * par + 4 * (c & 3);
+                    const mf_bf16x8 qA = mf_read_tr8(qs + toff, 16 * RS), gA = mf_read_tr8(gs + toff, 16 * RS);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    qe[i] = __builtin_amdgcn_perm(dq8[2 * i + 1], dq8[2 * i], 0x05040100u);
-                    qo[i] = __builtin_amdgcn_perm(dq8[2 * i + 1], dq8[2 * i], 0x07060302u);
-                    ge[i] = __builtin_amdgcn_perm(dg8[2 * i + 1], dg8[2 * i], 0x05040100u);
-                    go[i] = __builtin_amdgcn_perm(dg8[2 * i + 1], dg8[2 * i], 0x07060302u);
-                }
-                const mf_bf16x8 qE = __builtin_bit_cast(mf_bf16x8, qe), qO = __builtin_bit_cast(mf_bf16x8, qo);
-                const mf_bf16x8 gE = __builtin_bit_cast(mf_bf16x8, ge), gO = __builtin_bit_cast(mf_bf16x8, go);
-#pragma unroll
-                for (int rho = 0; rho < R; ++rho) {
-                    if (!use[rho]) continue;
-                    dv[rho][tau][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gE, p_hi[rho], dv[rho][tau][0], 0, 0, 0);
-                    dv[rho][tau][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gE, p_lo[rho], dv[rho][tau][0], 0, 0, 0);
-                    dv[rho][tau][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gO, p_hi[rho], dv[rho][tau][1], 0, 0, 0);
-                    dv[rho][tau][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gO, p_lo[rho], dv[rho][tau][1], 0, 0, 0);
-                    dk[rho][tau][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qE, s_hi[rho], dk[rho][tau][0], 0, 0, 0);
-                    dk[rho][tau][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qE, s_lo[rho], dk[rho][tau][0], 0, 0, 0);
-                    dk[rho][tau][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qO, s_hi[rho], dk[rho][tau][1], 0, 0, 0);
-                    dk[rho][tau][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qO, s_lo[rho], dk[rho][tau][1], 0, 0, 0);
+                    for (int rho = 0; rho < R; ++rho) {
+                        if (!use[rho]) continue;
+                        dv[rho][tau][par] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gA, p_hi[rho], dv[rho][tau][par], 0, 0, 0);
+                        dv[rho][tau][par] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gA, p_lo[rho], dv[rho][tau][par], 0, 0, 0);
+                        dk[rho][tau][par] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qA, s_hi[rho], dk[rho][tau][par], 0, 0, 0);
+                        dk[rho][tau][par] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qA, s_lo[rho], dk[rho][tau][par], 0, 0, 0);
+                    }
                 }
             }
             wave_lds_sync();  // the segment's queries have been read before the next segment writes them
@@ -841,19 +825,16 @@ dsa3d_fixed_bwd_key_mfma_kernel(FixedArgs a) {
         bf16_t* krow = reinterpret_cast<bf16_t*>(a.dk) + ktok[rho] * C + (int64_t)eta * D;
         bf16_t* vrow = reinterpret_cast<bf16_t*>(a.dv) + ktok[rho] * C + (int64_t)eta * D;
 #pragma unroll
-        for (int tau = 0; tau < D / 32; ++tau) {  // channels 32*tau + 8g .. +7 of key c
-            uint4 w;
-            w.x = mf_pack(dk[rho][tau][0][0], dk[rho][tau][1][0]);
-            w.y = mf_pack(dk[rho][tau][0][1], dk[rho][tau][1][1]);
-            w.z = mf_pack(dk[rho][tau][0][2], dk[rho][tau][1][2]);
-            w.w = mf_pack(dk[rho][tau][0][3], dk[rho][tau][1][3]);
-            *reinterpret_cast<uint4*>(krow + 32 * tau + 8 * g) = w;
-            w.x = mf_pack(dv[rho][tau][0][0], dv[rho][tau][1][0]);
-            w.y = mf_pack(dv[rho][tau][0][1], dv[rho][tau][1][1]);
-            w.z = mf_pack(dv[rho][tau][0][2], dv[rho][tau][1][2]);
-            w.w = mf_pack(dv[rho][tau][0][3], dv[rho][tau][1][3]);
-            *reinterpret_cast<uint4*>(vrow + 32 * tau + 8 * g) = w;
-        }
+        for (int tau = 0; tau < D / 32; ++tau)
+#pragma unroll
+            for (int par = 0; par < 2; ++par) {  // channels 32*tau + 16*par + 4g .. +3 of key c
+                const mf_f32x4& k4 = dk[rho][tau][par];
+                const mf_f32x4& v4 = dv[rho][tau][par];
+                *reinterpret_cast<uint2*>(krow + 32 * tau + 16 * par + 4 * g) =
+                    make_uint2(mf_pack(k4[0], k4[1]), mf_pack(k4[2], k4[3]));
+                *reinterpret_cast<uint2*>(vrow + 32 * tau + 16 * par + 4 * g) =
+                    make_uint2(mf_pack(v4[0], v4[1]), mf_pack(v4[2], v4[3]));
+            }
     }
 }
 
