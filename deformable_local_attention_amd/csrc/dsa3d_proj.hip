@@ -5,13 +5,16 @@
 //           dW[F, C]          = doff^T . q                        (split over N_tok, fixed-order sum)
 //           db[F]             = column sums of doff               (split over N_tok, fixed-order sum)
 //
-// Three kernels, by operand layout and dtype:
+// Four kernels, by operand layout and dtype:
 //  - dsa3d_ntgemm_kernel (bf16, both operands K-contiguous: the forward, and dq
 //    once W is transposed into the workspace): 256x256 tiles, eight waves,
 //    operands copied from memory straight into two 64-deep LDS stages;
-//  - dsa3d_xgemm_kernel (bf16, any layout, used for dW): 256x256 tiles, two
-//    register-staged LDS stages, M/N-contiguous operands transposed in
-//    registers;
+//  - dsa3d_mngemm_kernel (bf16, both operands M/N-contiguous: dW): the same
+//    tiles, waves and stages, the tiles copied as they lie and the MFMA
+//    operands built by the transposing LDS read;
+//  - dsa3d_xgemm_kernel (bf16 layouts and alignments the two above do not
+//    take): 256x256 tiles, two register-staged LDS stages, M/N-contiguous
+//    operands transposed in registers;
 //  - dsa3d_gemm_kernel (float32 runs, and bf16 shapes the others cannot
 //    take): 128x128 tiles, four waves of 64x64, 32-deep K slices in padded LDS
 //    rows, v_mfma_f32_16x16x32_bf16 or v_mfma_f32_16x16x4_f32.
