@@ -370,11 +370,13 @@ def test_projection_forward_and_backward(dtype, shape):
 # (a second, partial block of channels), single-token rows and frames. bf16
 # with a multiple of 64 channels takes the LDS-tiled kernels (8 x 16 tiles of
 # the (h, w) plane, runs of 16 frames): ragged tiles in h (11 = 8 + 3) and w
-# (37 = 16 + 16 + 5) over two batch items, and frame runs 35 = 12 + 12 + 11.
+# (37 = 16 + 16 + 5) over two batch items, and frame runs 35 = 12 + 12 + 11;
+# 256 x 512 frames: 32 x 32 tiles per frame, 1,024 partials of the
+# weight-gradient sums.
 @pytest.mark.parametrize("dtype,shape", [("f32", (2, 3, 5, 7, 3, 8)), ("bf16", (2, 3, 5, 7, 3, 8)),
                                          ("bf16", (1, 4, 6, 30, 8, 64)), ("f32", (1, 1, 1, 5, 5, 128)),
                                          ("bf16", (1, 3, 2, 1, 5, 128)), ("bf16", (2, 5, 11, 37, 2, 64)),
-                                         ("bf16", (1, 35, 9, 17, 1, 64))])
+                                         ("bf16", (1, 35, 9, 17, 1, 64)), ("bf16", (1, 2, 256, 512, 1, 64))])
 def test_dwconv_forward_and_backward(dtype, shape):
     B, T, H, W, heads, hd = shape
     C = heads * hd
